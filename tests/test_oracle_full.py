@@ -1,0 +1,199 @@
+"""Pins of the oracle's full-vocabulary scoring and projection (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form, a library routine (scipy / torch CPU), brute force with plain Python
+floats, or a metamorphic relation that the definition fixes.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)["cases"]
+
+
+def test_golden_full_cases():
+    for c in _golden("full_cases.json"):
+        if "V" in c:
+            V = c["V"]
+            x = np.full((1, V), 0.375)
+            r = oracle.score_full(x, 1.0, [V // 3])
+            assert abs(r["entropy"][0] - c["entropy"]) < 1e-12, c["name"]
+            assert abs(r["logprob"][0] - c["logprob"]) < 1e-12, c["name"]
+        else:
+            r = oracle.score_full(np.array([c["x"]]), c["tau"], [c["target"]])
+            for k in ("lse", "logprob", "entropy"):
+                assert abs(r[k][0] - c[k]) < 1e-13, (c["name"], k)
+            assert r["status"][0] == 0
+
+
+def test_two_token_closed_form():
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        a, b = rng.normal(0, 4, size=2)
+        p = 1.0 / (1.0 + math.exp(-(a - b)))
+        r = oracle.score_full(np.array([[a, b]]), 1.0, [0])
+        h = -(p * math.log(p) + (1 - p) * math.log(1 - p))
+        assert abs(r["entropy"][0] - h) < 1e-12
+        assert abs(r["logprob"][0] - math.log(p)) < 1e-12
+
+
+def test_against_library_routines():
+    rng = np.random.default_rng(1)
+    x = rng.normal(0, 3, size=(8, 1000))
+    tau = rng.uniform(0.5, 1.5, size=8)
+    y = rng.integers(0, 1000, size=8)
+    r = oracle.score_full(x, tau, y)
+    z = x / tau[:, None]
+    lse = scipy.special.logsumexp(z, axis=1)
+    np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-11)
+    ls = torch.log_softmax(torch.from_numpy(z), dim=1).numpy()
+    np.testing.assert_allclose(r["logprob"], ls[np.arange(8), y], rtol=0, atol=1e-11)
+    ent = torch.distributions.Categorical(logits=torch.from_numpy(z)).entropy().numpy()
+    np.testing.assert_allclose(r["entropy"], ent, rtol=0, atol=1e-11)
+    p = scipy.special.softmax(z, axis=1)
+    np.testing.assert_allclose(r["entropy"], scipy.stats.entropy(p, axis=1), rtol=0, atol=1e-11)
+
+
+def test_brute_force_tiny_python_floats():
+    rng = np.random.default_rng(2)
+    for V in range(1, 9):
+        for _ in range(10):
+            xs = [float(v) for v in rng.normal(0, 2, size=V)]
+            tau = float(rng.uniform(0.3, 2.0))
+            y = int(rng.integers(0, V))
+            w = [math.exp(v / tau) for v in xs]
+            tot = sum(w)
+            probs = [wi / tot for wi in w]
+            r = oracle.score_full(np.array([xs]), tau, [y])
+            assert abs(r["logprob"][0] - math.log(probs[y])) < 1e-12
+            assert abs(r["entropy"][0] - (-sum(p * math.log(p) for p in probs))) < 1e-12
+            assert abs(r["lse"][0] - math.log(tot)) < 1e-12
+
+
+def test_shift_and_temperature_relations():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 2, size=(4, 500))
+    y = rng.integers(0, 500, size=4)
+    base = oracle.score_full(x, 1.0, y)
+    sh = oracle.score_full(x + 7.25, 1.0, y)
+    np.testing.assert_allclose(sh["logprob"], base["logprob"], atol=1e-12)
+    np.testing.assert_allclose(sh["entropy"], base["entropy"], atol=1e-12)
+    np.testing.assert_allclose(sh["lse"], base["lse"] + 7.25, atol=1e-12)
+    # temperature divides the logits: score(x, tau) == score(x / tau, 1), exact for tau = 2^j
+    for tau in (0.25, 0.5, 2.0, 4.0):
+        a = oracle.score_full(x, tau, y)
+        b = oracle.score_full(x / tau, 1.0, y)
+        for k in ("lse", "logprob", "entropy"):
+            np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_bounds():
+    rng = np.random.default_rng(4)
+    x = rng.normal(0, 5, size=(16, 300))
+    r = oracle.score_full(x, 1.0, rng.integers(0, 300, size=16))
+    assert (r["entropy"] >= 0).all() and (r["entropy"] <= math.log(300) + 1e-12).all()
+    assert (r["logprob"] <= 0).all()
+
+
+def test_neg_inf_logits_are_zero_probability():
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 1, size=(1, 20))
+    x2 = x.copy()
+    x2[0, [3, 7, 11]] = -np.inf
+    a = oracle.score_full(x2, 1.0, [0])
+    keep = [i for i in range(20) if i not in (3, 7, 11)]
+    b = oracle.score_full(x[:, keep], 1.0, [0])
+    for k in ("lse", "logprob", "entropy"):
+        assert abs(a[k][0] - b[k][0]) < 1e-12
+    assert a["status"][0] == 0
+    c = oracle.score_full(x2, 1.0, [3])
+    assert c["logprob"][0] == -np.inf and c["status"][0] == 0
+
+
+def test_bad_rows():
+    x = np.zeros((6, 4))
+    x[1, 2] = np.nan
+    x[2, 0] = np.inf
+    x[3, :] = -np.inf
+    tau = np.array([1.0, 1.0, 1.0, 1.0, 0.0, 1.0])
+    y = np.array([0, 0, 0, 0, 0, 4])
+    r = oracle.score_full(x, tau, y)
+    assert r["status"][0] == 0
+    assert (r["status"][1:] == oracle.ST_BAD_INPUT).all()
+    assert np.isnan(r["logprob"][1:]).all() and np.isnan(r["entropy"][1:]).all()
+
+
+def test_round_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([
+        rng.normal(0, 1, 20000).astype(np.float32),
+        rng.normal(0, 1e-38, 2000).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000
+    u = rng.integers(0, 2 ** 31, 1000).astype(np.uint32)
+    ties = ((u & np.uint32(0x7F7F0000)) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties])
+    ours = oracle.round_f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    nan = oracle.round_f32_to_bf16(np.array([np.nan], np.float32))
+    assert np.isnan(oracle.widen_bf16(nan))[0]
+
+
+def test_widen_bf16_matches_torch():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.widen_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(ours[fin], ref[fin])
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def test_projection_brute_force():
+    rng = np.random.default_rng(7)
+    T, H, V = 3, 17, 11
+    hid = rng.normal(0, 1, (T, H)).astype(np.float32)
+    w = torch.from_numpy(rng.normal(0, 0.1, (V, H)).astype(np.float32)).to(torch.bfloat16)
+    wbits = w.view(torch.int16).numpy().view(np.uint16)
+    x = oracle.logits_from_hidden(hid, "f32", wbits)
+    hb = torch.from_numpy(hid).to(torch.bfloat16).double()
+    wd = w.double()
+    for t in range(T):
+        for v in range(V):
+            s = math.fsum(float(hb[t, h]) * float(wd[v, h]) for h in range(H))
+            assert abs(x[t, v] - s) < 1e-14
+    # selected rows / columns
+    xs = oracle.logits_from_hidden(hid, "f32", wbits, rows=[2, 0], cols=[5, 1, 9])
+    np.testing.assert_array_equal(xs, x[[2, 0]][:, [5, 1, 9]])
+    # bf16 hidden input takes no extra rounding
+    hbits = torch.from_numpy(hid).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.logits_from_hidden(hbits, "bf16", wbits), x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_logits_from_logits(dtype):
+    rng = np.random.default_rng(8)
+    v = rng.normal(0, 2, (3, 9)).astype(np.float32)
+    if dtype == "bf16":
+        bits = torch.from_numpy(v).to(torch.bfloat16)
+        ref = bits.double().numpy()
+        arr = bits.view(torch.int16).numpy().view(np.uint16)
+    else:
+        arr, ref = v, v.astype(np.float64)
+    np.testing.assert_array_equal(oracle.logits_from_logits(arr, dtype), ref)
+    np.testing.assert_array_equal(oracle.logits_from_logits(arr, dtype, rows=[1]), ref[[1]])
