@@ -108,7 +108,14 @@ def logits_from_hidden(hidden, hidden_dtype: str, weight_bits, rows=None, cols=N
     w = np.asarray(weight_bits, dtype=np.uint16)
     if cols is not None:
         w = w[np.asarray(cols)]
-    return h64 @ widen_bf16(w).T
+    # Widening the whole weight to float64 at once would need 8 bytes per
+    # entry; widen it in blocks of vocabulary rows (each output element is
+    # still one float64 dot product over H).
+    out = np.empty((h64.shape[0], w.shape[0]), dtype=np.float64)
+    step = 16384
+    for v0 in range(0, w.shape[0], step):
+        out[:, v0:v0 + step] = h64 @ widen_bf16(w[v0:v0 + step]).T
+    return out
 
 
 # ---------------------------------------------------------------------------

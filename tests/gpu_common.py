@@ -1,0 +1,54 @@
+"""Helpers shared by the GPU parity tests (no scoring arithmetic here)."""
+
+import sys
+
+import numpy as np
+import torch
+
+# logprob / entropy / L1 tolerance for bf16 inputs with fp32 accumulation:
+# |gpu - oracle| <= ATOL + RTOL * |oracle|
+ATOL = 2e-3
+RTOL = 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tensor(bits, device=None):
+    """uint16 bf16 patterns (numpy) -> torch.bfloat16 on the GPU."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).to(device or dev()).view(torch.bfloat16)
+
+
+def to_dev(a, device=None):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device or dev())
+
+
+def assert_close(name, got, ref, atol=ATOL, rtol=RTOL, rows=None):
+    """Elementwise tolerance; NaN and -inf must sit in the same places."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if rows is not None:
+        got = got[rows]
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), f"{name}: NaN mismatch at {np.nonzero(nan_g != nan_r)[0][:10]}"
+    ninf_g, ninf_r = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(ninf_g, ninf_r), f"{name}: -inf mismatch at {np.nonzero(ninf_g != ninf_r)[0][:10]}"
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all(), f"{name}: non-finite where the oracle is finite"
+    err = np.abs(got[fin] - ref[fin])
+    bound = atol + rtol * np.abs(ref[fin])
+    if err.size:
+        worst = int(np.argmax(err - bound))
+        ok = bool((err <= bound).all())
+        say(f"  {name}: max abs err {err.max():.3e}, max rel err "
+            f"{(err / np.maximum(np.abs(ref[fin]), 1e-30)).max():.3e} over {err.size} values")
+        assert ok, (f"{name}: |err| {err[worst]:.4e} > bound {bound[worst]:.4e} at finite index {worst} "
+                    f"(gpu {got[fin][worst]!r}, oracle {ref[fin][worst]!r})")

@@ -1,0 +1,161 @@
+"""GPU parity: full-vocabulary scoring (logits input and fused LM head) vs the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import assert_close, bf16_tensor, dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    import logprob_entropy_sampling_amd as m
+    m.lib()
+    return m
+
+
+def _cmp_full(got, ref, rows=None):
+    st = got["status"].cpu().numpy()
+    if rows is not None:
+        st = st[rows]
+    assert np.array_equal(st, ref["status"]), "status mismatch"
+    for k in ("lse", "logprob", "entropy"):
+        assert_close(k, got[k].cpu().numpy(), ref[k], rows=rows)
+
+
+def test_logits_bf16_full_vocab_workload_rows(vsa):
+    say("logits_full: T=40 of the 512-row workload recipe, V=151936 bf16, per-row tau")
+    c = workloads.make(2, T=40)
+    lg = bf16_tensor(c["logits"])
+    got = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=to_dev(c["temperature"]))
+    ref = oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16"), c["temperature"], c["targets"])
+    _cmp_full(got, ref)
+
+
+@pytest.mark.parametrize("ld_pad", [0, 3, 5])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_logits_ragged_and_strided(vsa, dtype, ld_pad):
+    say(f"logits ragged: dtype={dtype} ld_pad={ld_pad} T=37 V=20001")
+    rng = np.random.default_rng(100)
+    T, V = 37, 20001
+    x = (rng.standard_normal((T, V + ld_pad)) * 3).astype(np.float32)
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x)
+        full = bf16_tensor(bits)
+        x64 = oracle.logits_from_logits(bits, "bf16")[:, :V]
+    else:
+        full = to_dev(x)
+        x64 = oracle.logits_from_logits(x, "f32")[:, :V]
+    lg = full[:, :V]
+    got = vsa.score_full(to_dev(y), logits=lg, temperature=to_dev(tau))
+    _cmp_full(got, oracle.score_full(x64, tau, y))
+
+
+def test_vocab_chunk_and_determinism(vsa):
+    say("vocab_chunk variants + bitwise run-to-run equality")
+    c = workloads.make(2, T=16)
+    lg = bf16_tensor(c["logits"])
+    y = to_dev(c["targets"])
+    tau = to_dev(c["temperature"])
+    ref = oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16"), c["temperature"], c["targets"])
+    outs = {}
+    for chunk in (1, 8192, 65536, 151936):
+        outs[chunk] = vsa.score_full(y, logits=lg, temperature=tau, vocab_chunk=chunk)
+        _cmp_full(outs[chunk], ref)
+    again = vsa.score_full(y, logits=lg, temperature=tau, vocab_chunk=8192)
+    for k in ("lse", "logprob", "entropy"):
+        assert torch.equal(again[k], outs[8192][k])
+
+
+def test_edge_rows(vsa):
+    say("edge rows: uniform, -inf, NaN, +inf, all -inf, bad tau, bad targets, T=1")
+    V = 9000
+    rows = []
+    x = np.zeros((11, V), np.float32)
+    x[1] = np.linspace(-3, 3, V)
+    x[1, ::7] = -np.inf
+    x[2] = 1.0
+    x[2, 5] = np.nan
+    x[3, 17] = np.inf
+    x[4] = -np.inf
+    x[5] = np.linspace(-2, 2, V)
+    x[6] = np.linspace(-2, 2, V)
+    x[7] = np.linspace(-2, 2, V)
+    x[8] = np.linspace(-2, 2, V)
+    x[9] = 0.5
+    x[10] = -np.inf
+    x[10, 4100] = np.nan  # a NaN that is the only non -inf value a thread sees
+    tau = np.array([1, 1, 1, 1, 1, 0, np.nan, 1, 1, 0.25, 1], np.float32)
+    y = np.array([3, 7, 0, 0, 0, 0, 0, -1, V, 8999, 0], np.int64)
+    bits = workloads.to_bf16_bits(x)
+    got = vsa.score_full(to_dev(y), logits=bf16_tensor(bits), temperature=to_dev(tau))
+    ref = oracle.score_full(oracle.logits_from_logits(bits, "bf16"), tau, y)
+    assert list(ref["status"]) == [0, 0, 4, 4, 4, 4, 4, 4, 4, 0, 4]
+    _cmp_full(got, ref)
+    assert abs(float(got["entropy"][0]) - math.log(V)) < 2e-3 + 1e-3 * math.log(V)
+    one = vsa.score_full(to_dev(y[:1]), logits=bf16_tensor(bits[:1]), temperature=1.0)
+    _cmp_full(one, oracle.score_full(oracle.logits_from_logits(bits[:1], "bf16"), 1.0, y[:1]))
+
+
+def test_fused_tiny_workload(vsa):
+    say("fused: tiny workload T=64 H=256 V=4096 fp32 hidden")
+    c = workloads.make(1)
+    got = vsa.score_full(to_dev(c["targets"]), hidden=to_dev(c["hidden"]), weight=bf16_tensor(c["weight"]))
+    x = oracle.logits_from_hidden(c["hidden"], "f32", c["weight"])
+    _cmp_full(got, oracle.score_full(x, c["temperature"], c["targets"]))
+
+
+@pytest.mark.parametrize("T,H,V", [(300, 200, 5003), (257, 64, 256), (1, 8, 1), (513, 1024, 30000)])
+def test_fused_ragged(vsa, T, H, V):
+    say(f"fused ragged: T={T} H={H} V={V} bf16 hidden, per-row tau")
+    rng = np.random.default_rng(T + H + V)
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.1).astype(np.float32))
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    got = vsa.score_full(to_dev(y), hidden=bf16_tensor(hb), weight=bf16_tensor(wb), temperature=to_dev(tau),
+                         vocab_chunk=512)
+    x = oracle.logits_from_hidden(hb, "bf16", wb)
+    _cmp_full(got, oracle.score_full(x, tau, y))
+
+
+def test_fused_strided_weight(vsa):
+    say("fused: padded leading dims (ld_hidden=136, ld_weight=264)")
+    rng = np.random.default_rng(5)
+    T, H, V = 130, 128, 3000
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, 136)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, 264)) * 0.1).astype(np.float32))
+    y = rng.integers(0, V, T).astype(np.int64)
+    got = vsa.score_full(to_dev(y), hidden=bf16_tensor(hb)[:, :H], weight=bf16_tensor(wb)[:, :H])
+    x = oracle.logits_from_hidden(hb[:, :H], "bf16", wb[:, :H])
+    _cmp_full(got, oracle.score_full(x, 1.0, y))
+
+
+def test_fused_full_size_sampled_rows(vsa):
+    say("fused: full LM-head workload T=4096 H=4096 V=151936; oracle on sampled rows")
+    c = workloads.make(4)
+    hid = bf16_tensor(c["hidden"])
+    w = bf16_tensor(c["weight"])
+    y = to_dev(c["targets"])
+    got = vsa.score_full(y, hidden=hid, weight=w, vocab_chunk=8192)
+    again = vsa.score_full(y, hidden=hid, weight=w, vocab_chunk=8192)
+    for k in ("lse", "logprob", "entropy"):
+        assert torch.equal(got[k], again[k]), k
+    st = got["status"].cpu().numpy()
+    ent = got["entropy"].cpu().numpy()
+    lp = got["logprob"].cpu().numpy()
+    assert (st == 0).all()
+    assert np.isfinite(ent).all() and (ent >= 0).all() and (ent <= math.log(151936) + 1e-3).all()
+    assert (lp <= 1e-6).all()
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3333, 4094, 4095])
+    x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
+    ref = oracle.score_full(x, 1.0, c["targets"][rows])
+    _cmp_full(got, ref, rows=rows)

@@ -1,0 +1,78 @@
+"""GPU parity: draft/target softmax L1 distance and accept_rate vs the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import assert_close, bf16_tensor, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    import logprob_entropy_sampling_amd as m
+    m.lib()
+    return m
+
+
+def test_workload_rows(vsa):
+    say("l1: 24 rows of the transforms/draft recipe, V=151936 bf16")
+    c = workloads.make(5, T=24)
+    got = vsa.l1_distance(bf16_tensor(c["logits"]), bf16_tensor(c["draft"]))
+    ref = oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16"),
+                             oracle.logits_from_logits(c["draft"], "bf16"))
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"])
+    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"])
+
+
+def test_identical_is_exactly_zero(vsa):
+    say("l1: identical rows -> exactly 0 and accept 1")
+    c = workloads.make(5, T=8, V=40000)
+    t = bf16_tensor(c["logits"])
+    got = vsa.l1_distance(t, t.clone())
+    assert (got["l1"] == 0).all() and (got["accept_rate"] == 1).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_and_bounds(vsa, dtype):
+    say(f"l1: ragged V, far-apart rows, NaN rows, dtype={dtype}")
+    rng = np.random.default_rng(3)
+    T, V = 20, 30001
+    a = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    b = a + (rng.standard_normal((T, V)) * rng.uniform(0, 6, (T, 1))).astype(np.float32)
+    b[3] = -30.0
+    b[3, 5] = 30.0
+    a[3] = -30.0
+    a[3, 9] = 30.0
+    a[7, 100] = np.nan
+    b[8] = -np.inf
+    if dtype == "bf16":
+        ab, bb = workloads.to_bf16_bits(a), workloads.to_bf16_bits(b)
+        ta, tb = bf16_tensor(ab), bf16_tensor(bb)
+        a64, b64 = oracle.logits_from_logits(ab, "bf16"), oracle.logits_from_logits(bb, "bf16")
+    else:
+        ta, tb = to_dev(a), to_dev(b)
+        a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    got = vsa.l1_distance(ta, tb)
+    ref = oracle.l1_distance(a64, b64)
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"])
+    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"])
+    l1 = got["l1"].cpu().numpy()
+    fin = np.isfinite(l1)
+    assert (l1[fin] <= 2.0).all() and (l1[fin] >= 0).all()
+    sym = vsa.l1_distance(tb, ta)
+    assert torch.allclose(sym["l1"][fin], got["l1"][fin], atol=2e-6)
+
+
+def test_full_size_sampled(vsa):
+    say("l1: full 2048-row workload; oracle on sampled rows")
+    c = workloads.make(5)
+    got = vsa.l1_distance(bf16_tensor(c["logits"]), bf16_tensor(c["draft"]))
+    rows = np.array([0, 1, 35, 1024, 2047])
+    ref = oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16", rows=rows),
+                             oracle.logits_from_logits(c["draft"], "bf16", rows=rows))
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"], rows=rows)
+    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"], rows=rows)
