@@ -173,7 +173,8 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  *                         padded; SUPPORT_TRUNCATED if L > cap (nullable)
  *   full_lse[t]           full-vocabulary LSE of z (nullable)
  * Source must be VS_SRC_LOGITS with VS_BF16 logits (else VS_E_UNSUPPORTED);
- * the transform parameters are never ignored.  A target outside S_t gives
+ * the transform parameters are never ignored.  support_ids_cap > 4096 with a
+ * non-NULL support_ids_out gives VS_E_UNSUPPORTED.  A target outside S_t gives
  * logprob -inf and TARGET_OUTSIDE_SUPPORT.  BAD_INPUT rows: NaN floats,
  * support_len 0, ids -1.  entropy, row_status, support_len, threshold_logit,
  * threshold_ties, full_lse nullable; logprob required.

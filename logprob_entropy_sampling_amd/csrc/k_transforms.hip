@@ -1,13 +1,848 @@
-// Sampling-transform support (placeholder until the kernel lands).
+// Sampling-transform support and support-conditioned scores over bf16 logits.
+//
+// The program of xorl issue #71 section 3: temperature, then stable token-id
+// top-k, inclusive top-p on the top-k renormalised masses, min-p against the
+// original row max.  Rank order is (logit descending, token id ascending);
+// each filter keeps a prefix of it, so the support is the shortest prefix
+// pi[0:L].  Its scores follow SkyRL PR #2004 (renormalise over the support).
+//
+// One 512-thread workgroup per row.  Tokens are compared through 16-bit
+// order-preserving keys (a larger key is a larger logit; -0 is folded onto
+// +0).  Every token with the same key has the same probability, so every cut
+// position and every support sum follows exactly from the histogram of key
+// counts:
+//   * 1024 segments of 64 keys, each with its token count, its mass
+//     sum c * exp(z - z_max) and sum c * exp(z - z_max) * (z - z_max) in fp64
+//     (one exp per distinct key, not per token);
+//   * rank and mass queries walk the segments in descending key order, then
+//     the 64 keys of one segment;
+//   * inside the threshold key, ties go by token id: the support holds its
+//     first r tokens.
+// Fast kernel: the row is held in registers and counted once into 65536
+// 16-bit counters packed two per LDS word (one branch-free atomic per token).
+// A counter that would pass 65535 (a key repeated that often) is detected from
+// the exact total and the row is handed to the stream kernel, which re-reads
+// the row from memory for every pass and counts with 32-bit bins in two
+// halves; it also serves rows too long for registers.  Dense support ids (at
+// most 4096) come from sorting the few candidate tokens in LDS.  All sums run
+// in a fixed order, so results are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace vs {
 
-int launch_transforms(const uint16_t*, int64_t, int64_t, int64_t, const float*, float, const int32_t*, const float*,
-                      const float*, const int64_t*, float*, float*, uint8_t*, int32_t*, float*, int32_t*, int64_t*,
-                      int64_t, float*, void*) {
-  return -1;
+namespace {
+
+constexpr int NT = 512;
+constexpr int NWAVE = NT / 64;
+constexpr int HALF = 32768;
+constexpr int SEGW = 64;
+constexpr int NSEG = 65536 / SEGW;       // 1024
+constexpr int SEG_PER_LANE = NSEG / 64;  // 16
+constexpr int COLLECT_MAX = 4096;
+constexpr uint32_t KEY_NEG_INF = 0x007Fu;
+
+struct Smem {
+  uint32_t hist[HALF];  // packed 16-bit counters (fast) or one half of 32-bit bins (stream); later candidates
+  uint32_t seg_count[NSEG];
+  double seg_mass[NSEG];
+  double seg_zmass[NSEG];
+  uint32_t fine[SEGW];  // 32-bit counts of one segment (stream kernel)
+  uint32_t lane_cnt[64], lane_cnt_before[64];
+  double lane_mass[64], lane_mass_before[64], lane_zmass[64], lane_zmass_before[64];
+  uint32_t red_u[NWAVE];
+  uint32_t bu[8];  // broadcast slots (integers)
+  double bd[8];    // broadcast slots (fp64)
+  int fine_seg;
+  uint32_t ncand;
+};
+
+// raw bf16 pattern -> order-preserving key (-0 folded onto +0)
+__device__ __forceinline__ uint32_t key16(uint32_t h) {
+  h = (h & 0x7FFFu) ? h : 0u;
+  return (h & 0x8000u) ? (h ^ 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (k ^ 0xFFFFu);
+  return __uint_as_float(h << 16);
+}
+__device__ __forceinline__ bool raw_bad(uint32_t h) { return (h & 0x7FFFu) >= 0x7F80u && h != 0xFF80u; }
+
+__device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) t += sm.red_u[i];
+  return t;
+}
+__device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) t = max(t, sm.red_u[i]);
+  return t;
+}
+// Exclusive prefix over threads in thread order; also returns the total.
+__device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
+  const int lane = threadIdx.x & 63;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) sm.red_u[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    const uint32_t t = sm.red_u[i];
+    if (i < int(threadIdx.x >> 6)) before += t;
+    total += t;
+  }
+  return before + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Key sources.  each(f) calls f(key, column) for every token of this thread
+// (register keys also visit padding columns, whose key 0 lies below every
+// real key); slice(j, f) does the same for slice j, slices being in column
+// order and, inside a slice, columns increasing with (thread, position).
+// ---------------------------------------------------------------------------
+template <int NV>
+struct RegKeys {
+  uint32_t kw[NV][4];  // two keys per word
+
+  // Loads the row, converts it to keys and counts every key into the packed
+  // 16-bit counters `hist` (already zeroed); returns bad (NaN or +inf seen)
+  // and this thread's max key.  Vectors go in groups of 8 (128 bytes per
+  // thread in flight): each group is loaded, converted and counted before the
+  // next, which bounds the registers the unrolled loop needs.
+  __device__ __forceinline__ void load_count(const uint16_t* rowp, int V, uint32_t* hist, uint32_t& bad,
+                                             uint32_t& kmax) {
+    const int tid = threadIdx.x;
+    const bool aligned = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
+    bad = 0;
+    kmax = 0;
+    constexpr int G = 8;
+#pragma unroll
+    for (int g = 0; g < NV; g += G) {
+      uint32_t wv[G][4];
+#pragma unroll
+      for (int jj = 0; jj < G && g + jj < NV; ++jj) {
+        const int q = tid + NT * (g + jj);
+        if (aligned && 8 * q + 8 <= V) {
+          const uint4 v = reinterpret_cast<const uint4*>(rowp)[q];
+          wv[jj][0] = v.x;
+          wv[jj][1] = v.y;
+          wv[jj][2] = v.z;
+          wv[jj][3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c0 = 8 * q + 2 * e;
+            // padding columns get the raw pattern 0xFFFF, whose key is 0
+            const uint32_t lo = c0 < V ? uint32_t(rowp[c0]) : 0xFFFFu;
+            const uint32_t hi = c0 + 1 < V ? uint32_t(rowp[c0 + 1]) : 0xFFFFu;
+            wv[jj][e] = lo | (hi << 16);
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < G && g + jj < NV; ++jj) {
+        const int q = tid + NT * (g + jj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = wv[jj][e];
+          const uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+          const int c0 = 8 * q + 2 * e;
+          bad |= (c0 < V && raw_bad(lo)) ? 1u : 0u;
+          bad |= (c0 + 1 < V && raw_bad(hi)) ? 1u : 0u;
+          // -0 -> +0; then negative halves invert all 16 bits, positive ones set the top bit
+          w &= ~(((lo & 0x7FFFu) ? 0u : 0x8000u) | ((hi & 0x7FFFu) ? 0u : 0x80000000u));
+          const uint32_t neg = ((w >> 15) & 0x00010001u) * 0xFFFFu;
+          w ^= neg | 0x80008000u;
+          kw[g + jj][e] = w;
+          const uint32_t k0 = w & 0xFFFFu, k1 = w >> 16;
+          kmax = max(kmax, max(k0, k1));
+          atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+          atomicAdd(&hist[k1 >> 1], (k1 & 1u) ? 0x10000u : 1u);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // An empty asm that claims to rewrite every packed word: values unpacked in
+  // an earlier pass cannot be reused, so the unpacked keys (twice the
+  // registers) never stay live across the kernel.  No instruction is emitted.
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(kw[j][e]));
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F f) {
+    opaque();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      slice(j, f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __device__ __forceinline__ int slices() const { return NV; }
+  template <class F>
+  __device__ __forceinline__ void slice(int j, F f) const {
+    const int c0 = 8 * (int(threadIdx.x) + NT * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f(kw[j][e] & 0xFFFFu, c0 + 2 * e);
+      f(kw[j][e] >> 16, c0 + 2 * e + 1);
+    }
+  }
+};
+
+struct StreamKeys {
+  const uint16_t* rowp;
+  int V;
+  __device__ __forceinline__ void opaque() {}
+  __device__ __forceinline__ bool aligned() const { return (reinterpret_cast<uintptr_t>(rowp) & 15) == 0; }
+
+  // One streaming pass: convert and count every key into the packed 16-bit
+  // counters (no padding), returning bad and this thread's max key.
+  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& bad, uint32_t& kmax) const {
+    bad = 0;
+    kmax = 0;
+    auto one = [&](uint32_t h) {
+      bad |= raw_bad(h) ? 1u : 0u;
+      const uint32_t k = key16(h);
+      kmax = max(kmax, k);
+      atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
+    };
+    const int nvec = aligned() ? V / 8 : 0;
+    const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    int q = threadIdx.x;
+    for (; q + 3 * NT < nvec; q += 4 * NT) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = pv[q + u * NT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          one(w[e] & 0xFFFFu);
+          one(w[e] >> 16);
+        }
+      }
+    }
+    for (; q < nvec; q += NT) {
+      const uint4 v = pv[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        one(w[e] & 0xFFFFu);
+        one(w[e] >> 16);
+      }
+    }
+    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += NT) one(rowp[c]);
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+    const int nvec = aligned() ? V / 8 : 0;
+    const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    for (int q = threadIdx.x; q < nvec; q += NT) {
+      const uint4 v = pv[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f(key16(w[e] & 0xFFFFu), 8 * q + 2 * e);
+        f(key16(w[e] >> 16), 8 * q + 2 * e + 1);
+      }
+    }
+    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += NT) f(key16(rowp[c]), c);
+  }
+  __device__ __forceinline__ int slices() const { return (V + NT - 1) / NT; }
+  template <class F>
+  __device__ __forceinline__ void slice(int j, F f) const {
+    const int c = int(threadIdx.x) + NT * j;
+    if (c < V) f(key16(rowp[c]), c);
+  }
+};
+
+// fp64 weight of a key relative to the row max: exp(x / tau - z_max), the
+// quantity the program compares with min_p and sums for the masses.
+__device__ __forceinline__ double key_weight(uint32_t k, double tau, double z0) {
+  return exp(double(key_logit(k)) / tau - z0);
+}
+
+struct RowArgs {
+  int64_t row;
+  int V;
+  float tauf;
+  int kk;
+  float pf, mpf;
+  int64_t y;
+  const uint16_t* rowp;
+  float* logprob;
+  float* entropy;
+  uint8_t* status;
+  int32_t* support_len;
+  float* threshold_logit;
+  int32_t* threshold_ties;
+  int64_t* ids_out;
+  int cap;
+  float* full_lse;
+};
+
+__device__ void write_bad(const RowArgs& a) {
+  const float nanf = __builtin_nanf("");
+  if (threadIdx.x == 0) {
+    a.logprob[a.row] = nanf;
+    if (a.entropy) a.entropy[a.row] = nanf;
+    if (a.status) a.status[a.row] = kRowBad;
+    if (a.support_len) a.support_len[a.row] = 0;
+    if (a.threshold_logit) a.threshold_logit[a.row] = nanf;
+    if (a.threshold_ties) a.threshold_ties[a.row] = 0;
+    if (a.full_lse) a.full_lse[a.row] = nanf;
+  }
+  if (a.ids_out)
+    for (int i = threadIdx.x; i < a.cap; i += NT) a.ids_out[a.row * a.cap + i] = -1;
+}
+
+__device__ __forceinline__ bool params_ok(const RowArgs& a) {
+  return tau_ok(a.tauf) && (a.pf == a.pf) && a.pf > 0.0f && (a.mpf == a.mpf) && a.mpf <= 1.0f && a.y >= 0 &&
+         a.y < a.V;
+}
+
+// Segment summary from the counts of its 64 keys (ascending key order).
+template <class CountFn>
+__device__ __forceinline__ void summarize_segment(int seg, CountFn count, double tau, double z0, Smem& sm) {
+  uint32_t cnt = 0;
+  double mass = 0.0, zm = 0.0;
+  for (int b = 0; b < SEGW; ++b) {
+    const uint32_t key = uint32_t(seg * SEGW + b);
+    const uint32_t c = count(key);
+    if (c) {
+      cnt += c;
+      const double d = double(key_logit(key)) / tau - z0;
+      const double e = exp(d);
+      if (e > 0.0) {
+        mass += double(c) * e;
+        zm += double(c) * e * d;
+      }
+    }
+  }
+  sm.seg_count[seg] = cnt;
+  sm.seg_mass[seg] = mass;
+  sm.seg_zmass[seg] = zm;
+}
+
+// Everything after the histogram: cuts, scores, descriptor, dense ids.
+// `fine(s)` makes the 64 key counts of segment s readable through count(key).
+template <class Keys, class FineFn, class CountFn>
+__device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double z0, Smem& sm,
+                           FineFn fine, CountFn count) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const bool w0 = tid < 64;
+
+  // lane l of wave 0 owns segments 1023-16l .. 1008-16l (descending keys)
+  if (w0) {
+    uint32_t c = 0;
+    double m = 0.0, zm = 0.0;
+    for (int i = 0; i < SEG_PER_LANE; ++i) {
+      const int s = NSEG - 1 - SEG_PER_LANE * lane - i;
+      c += sm.seg_count[s];
+      m += sm.seg_mass[s];
+      zm += sm.seg_zmass[s];
+    }
+    sm.lane_cnt[lane] = c;
+    sm.lane_mass[lane] = m;
+    sm.lane_zmass[lane] = zm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t c = 0;
+    double m = 0.0, zm = 0.0;
+    for (int l = 0; l < 64; ++l) {
+      sm.lane_cnt_before[l] = c;
+      sm.lane_mass_before[l] = m;
+      sm.lane_zmass_before[l] = zm;
+      c += sm.lane_cnt[l];
+      m += sm.lane_mass[l];
+      zm += sm.lane_zmass[l];
+    }
+    sm.bd[7] = m;  // total mass relative to the row max
+  }
+  __syncthreads();
+  const double total_mass = sm.bd[7];
+
+  // Segment holding rank r (0-based): bu[0] = segment, bu[1] = tokens above it,
+  // bd[0] / bd[1] = mass / z-mass above it.
+  auto seg_of_rank = [&](uint32_t r) {
+    if (w0) {
+      const uint32_t cb = sm.lane_cnt_before[lane];
+      if (r >= cb && r < cb + sm.lane_cnt[lane]) {
+        uint32_t c = cb;
+        double m = sm.lane_mass_before[lane], zm = sm.lane_zmass_before[lane];
+        int s = NSEG - 1 - SEG_PER_LANE * lane;
+        for (int i = 0; i < SEG_PER_LANE; ++i, --s) {
+          if (r < c + sm.seg_count[s]) break;
+          c += sm.seg_count[s];
+          m += sm.seg_mass[s];
+          zm += sm.seg_zmass[s];
+        }
+        sm.bu[0] = uint32_t(s);
+        sm.bu[1] = c;
+        sm.bd[0] = m;
+        sm.bd[1] = zm;
+      }
+    }
+    __syncthreads();
+  };
+  // First segment whose running mass (descending) reaches T, 0 < T < total.
+  auto seg_of_mass = [&](double T) {
+    if (w0) {
+      const double mb = sm.lane_mass_before[lane];
+      const bool last = lane == 63 || sm.lane_mass_before[lane + 1] >= T;
+      if (mb < T && last) {
+        uint32_t c = sm.lane_cnt_before[lane];
+        double m = mb, zm = sm.lane_zmass_before[lane];
+        int s = NSEG - 1 - SEG_PER_LANE * lane;
+        int found = s;
+        uint32_t fc = c;
+        double fm = m, fz = zm;
+        for (int i = 0; i < SEG_PER_LANE; ++i, --s) {
+          if (sm.seg_count[s] == 0) continue;
+          found = s;  // the last non-empty one, should rounding never reach T
+          fc = c;
+          fm = m;
+          fz = zm;
+          if (m + sm.seg_mass[s] >= T) break;
+          c += sm.seg_count[s];
+          m += sm.seg_mass[s];
+          zm += sm.seg_zmass[s];
+        }
+        sm.bu[0] = uint32_t(found);
+        sm.bu[1] = fc;
+        sm.bd[0] = fm;
+        sm.bd[1] = fz;
+      }
+    }
+    __syncthreads();
+  };
+  // Tokens / mass above segment s (s excluded).
+  auto seg_above = [&](int s) {
+    if (tid == 0) {
+      const int l = (NSEG - 1 - s) / SEG_PER_LANE;
+      uint32_t c = sm.lane_cnt_before[l];
+      double m = sm.lane_mass_before[l], zm = sm.lane_zmass_before[l];
+      for (int t = NSEG - 1 - SEG_PER_LANE * l; t > s; --t) {
+        c += sm.seg_count[t];
+        m += sm.seg_mass[t];
+        zm += sm.seg_zmass[t];
+      }
+      sm.bu[0] = uint32_t(s);
+      sm.bu[1] = c;
+      sm.bd[0] = m;
+      sm.bd[1] = zm;
+    }
+    __syncthreads();
+  };
+  // Inside the segment in bu[0] (above-values in bu[1], bd[0], bd[1]): the key
+  // at rank r (mode 0) or where the running mass reaches T (mode 1).  Results:
+  // bu[2] = key, bu[3] = tokens above it, bu[4] = its tokens, bd[2] / bd[3] =
+  // mass / z-mass above it, bd[4] = its weight.
+  auto bin_query = [&](int mode, uint32_t r, double T) {
+    fine(int(sm.bu[0]));
+    if (w0) {
+      const uint32_t s = sm.bu[0];
+      const uint32_t key = s * SEGW + uint32_t(SEGW - 1 - lane);
+      const uint32_t c = count(key);
+      const double d = c ? double(key_logit(key)) / tau - z0 : 0.0;
+      const double e = c ? exp(d) : 0.0;
+      const double m = double(c) * e;
+      const double zm = e > 0.0 ? double(c) * e * d : 0.0;
+      uint32_t ci = c;
+      double mi = m, zi = zm;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t co = __shfl_up(ci, off, 64);
+        const double mo = __shfl_up(mi, off, 64);
+        const double zo = __shfl_up(zi, off, 64);
+        if (lane >= off) {
+          ci += co;
+          mi += mo;
+          zi += zo;
+        }
+      }
+      const uint32_t cb = sm.bu[1] + ci - c;
+      const double mb = sm.bd[0] + (mi - m);
+      const double zb = sm.bd[1] + (zi - zm);
+      bool hit;
+      if (mode == 0) {
+        hit = c > 0 && r >= cb && r < cb + c;
+      } else {
+        hit = c > 0 && sm.bd[0] + mi >= T && (lane == 0 || mb < T);
+      }
+      const unsigned long long bal = __ballot(hit);
+      int src;
+      if (bal) {
+        src = __ffsll(bal) - 1;
+      } else {  // rounding kept the mass target past this segment: its last non-empty key
+        const unsigned long long ne = __ballot(c > 0);
+        src = ne ? 63 - __clzll(ne) : 0;
+      }
+      if (lane == src) {
+        sm.bu[2] = key;
+        sm.bu[3] = cb;
+        sm.bu[4] = c;
+        sm.bd[2] = mb;
+        sm.bd[3] = zb;
+        sm.bd[4] = e;
+      }
+    }
+    __syncthreads();
+  };
+
+  const uint32_t Vu = uint32_t(a.V);
+  // ---- top-k ----
+  uint32_t L_k = Vu;
+  double Z_k = total_mass;
+  if (a.kk > 0 && uint32_t(a.kk) < Vu) {
+    L_k = uint32_t(a.kk);
+    seg_of_rank(L_k - 1);
+    bin_query(0, L_k - 1, 0.0);
+    Z_k = sm.bd[2] + double(L_k - sm.bu[3]) * sm.bd[4];
+  }
+  // ---- inclusive top-p: rank j stays iff the mass before it is < top_p * Z_k ----
+  uint32_t L_p = Vu;
+  if (a.pf < 1.0f) {
+    const double T = double(a.pf) * Z_k;
+    seg_of_mass(T);
+    bin_query(1, 0, T);
+    const double e = sm.bd[4];
+    const double room = T - sm.bd[2];
+    double n = e > 0.0 ? ceil(room / e) : 1.0;
+    n = n < 1.0 ? 1.0 : n;
+    L_p = sm.bu[3] + (n >= double(sm.bu[4]) ? sm.bu[4] : uint32_t(n));
+    if (L_p > L_k) L_p = L_k;
+  }
+  // ---- min-p against the row max: the smallest key whose weight reaches min_p ----
+  uint32_t L_m = Vu;
+  if (a.mpf > 0.0f) {
+    if (tid == 0) {
+      uint32_t lo = KEY_NEG_INF + 1, hi = kmax;  // weight(kmax) = 1 >= min_p
+      const double mp = double(a.mpf);
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (key_weight(mid, tau, z0) >= mp) hi = mid;
+        else lo = mid + 1;
+      }
+      sm.bu[5] = lo;
+    }
+    __syncthreads();
+    const uint32_t km = sm.bu[5];
+    seg_above(int(km / SEGW));
+    fine(int(km / SEGW));
+    if (tid == 0) {
+      uint32_t c = sm.bu[1];
+      for (uint32_t k2 = km; k2 < (km / SEGW + 1) * SEGW; ++k2) c += count(k2);
+      sm.bu[6] = c;
+    }
+    __syncthreads();
+    L_m = sm.bu[6];
+  }
+  uint32_t L = L_k < L_p ? L_k : L_p;
+  L = L < L_m ? L : L_m;
+  if (L < 1) L = 1;
+
+  // ---- the threshold key and the support sums ----
+  seg_of_rank(L - 1);
+  bin_query(0, L - 1, 0.0);
+  const uint32_t K_L = sm.bu[2];
+  const uint32_t r_L = L - sm.bu[3];  // tokens of the threshold key inside the support
+  const double e_L = sm.bd[4];
+  const double d_L = double(key_logit(K_L)) / tau - z0;
+  const double mass_S = sm.bd[2] + double(r_L) * e_L;
+  const double zmass_S = sm.bd[3] + (e_L > 0.0 ? double(r_L) * e_L * d_L : 0.0);
+
+  // ---- target membership (ties at the threshold key resolved by token id) ----
+  const uint32_t key_y = key16(a.rowp[a.y]);
+  bool in_s = key_y > K_L;
+  if (key_y == K_L) {
+    uint32_t below = 0;
+    const int yc = int(a.y);
+    keys.each([&](uint32_t key, int col) { below += (key == K_L && col < yc) ? 1u : 0u; });
+    below = block_sum_u32(below, sm);
+    in_s = below < r_L;
+  }
+
+  // ---- dense support ids ----
+  uint8_t st = 0;
+  if (a.ids_out && a.cap > 0) {
+    const uint32_t n_out = L < uint32_t(a.cap) ? L : uint32_t(a.cap);
+    if (L > uint32_t(a.cap)) st |= kRowTruncated;
+    seg_of_rank(n_out - 1);
+    bin_query(0, n_out - 1, 0.0);
+    const uint32_t K_c = sm.bu[2];
+    const uint32_t above_c = sm.bu[3];
+    const uint32_t cnt_c = sm.bu[4];
+    const uint32_t r_c = n_out - above_c;
+    const bool with_ties = above_c + cnt_c <= uint32_t(COLLECT_MAX);
+    // candidates: every token with key > K_c, plus the tied tokens when they fit
+    uint64_t* cand = reinterpret_cast<uint64_t*>(sm.hist);
+    if (tid == 0) sm.ncand = 0;
+    __syncthreads();
+    keys.each([&](uint32_t key, int col) {
+      if (key > K_c || (with_ties && key == K_c)) {
+        const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+        cand[slot] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(col));
+      }
+    });
+    __syncthreads();
+    const uint32_t nc = sm.ncand;
+    uint32_t P = 1;
+    while (P < nc) P <<= 1;
+    for (uint32_t i = nc + tid; i < P; i += NT) cand[i] = 0;
+    __syncthreads();
+    // bitonic sort, descending: key descending, token id ascending
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        for (uint32_t i = tid; i < P; i += NT) {
+          const uint32_t pidx = i ^ stride;
+          if (pidx > i) {
+            const uint64_t x = cand[i], z = cand[pidx];
+            const bool desc = (i & size) == 0;
+            if (desc ? (x < z) : (x > z)) {
+              cand[i] = z;
+              cand[pidx] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    int64_t* out = a.ids_out + a.row * a.cap;
+    const uint32_t n_sorted = with_ties ? n_out : above_c;
+    for (uint32_t i = tid; i < n_sorted; i += NT) out[i] = int64_t(0xFFFFFFFFu - uint32_t(cand[i] & 0xFFFFFFFFu));
+    for (uint32_t i = n_out + tid; i < uint32_t(a.cap); i += NT) out[i] = -1;
+    if (!with_ties) {
+      // a very large tie group at K_c: its first r_c tokens in column order, slice by slice
+      uint32_t taken = 0;
+      keys.opaque();
+      for (int j = 0; j < keys.slices(); ++j) {
+        uint32_t mine = 0;
+        keys.slice(j, [&](uint32_t key, int) { mine += key == K_c ? 1u : 0u; });
+        uint32_t tot;
+        uint32_t pos = taken + block_excl_scan_u32(mine, tot, sm);
+        keys.slice(j, [&](uint32_t key, int col) {
+          if (key == K_c) {
+            if (pos < r_c) out[above_c + pos] = col;
+            ++pos;
+          }
+        });
+        taken += tot;
+      }
+    }
+  }
+
+  if (tid == 0) {
+    const double lms = log(mass_S);
+    if (a.entropy) a.entropy[a.row] = float(lms - zmass_S / mass_S);
+    if (in_s) {
+      a.logprob[a.row] = float((double(key_logit(key_y)) / tau - z0) - lms);
+    } else {
+      a.logprob[a.row] = kNegInf;
+      st |= kRowOutside;
+    }
+    if (a.status) a.status[a.row] = st;
+    if (a.support_len) a.support_len[a.row] = int32_t(L);
+    if (a.threshold_logit) a.threshold_logit[a.row] = key_logit(K_L);
+    if (a.threshold_ties) a.threshold_ties[a.row] = int32_t(r_L);
+    if (a.full_lse) a.full_lse[a.row] = float(z0 + log(total_mass));
+  }
+}
+
+#define VS_ROW_ARGS                                   \
+  RowArgs a;                                          \
+  a.row = blockIdx.x;                                 \
+  a.V = V;                                            \
+  a.tauf = temp ? temp[a.row] : temp_scalar;          \
+  a.kk = top_k[a.row];                                \
+  a.pf = top_p[a.row];                                \
+  a.mpf = min_p[a.row];                               \
+  a.y = targets[a.row];                               \
+  a.rowp = logits + a.row * ld;                       \
+  a.logprob = logprob;                                \
+  a.entropy = entropy;                                \
+  a.status = status;                                  \
+  a.support_len = support_len;                        \
+  a.threshold_logit = threshold_logit;                \
+  a.threshold_ties = threshold_ties;                  \
+  a.ids_out = ids_out;                                \
+  a.cap = cap;                                        \
+  a.full_lse = full_lse;
+
+#define VS_KERNEL_ARGS                                                                                       \
+  const uint16_t *__restrict__ logits, int64_t ld, int V, const float *__restrict__ temp, float temp_scalar, \
+      const int32_t *__restrict__ top_k, const float *__restrict__ top_p, const float *__restrict__ min_p,   \
+      const int64_t *__restrict__ targets, float *__restrict__ logprob, float *__restrict__ entropy,         \
+      uint8_t *__restrict__ status, int32_t *__restrict__ support_len, float *__restrict__ threshold_logit,  \
+      int32_t *__restrict__ threshold_ties, int64_t *__restrict__ ids_out, int cap,                          \
+      float *__restrict__ full_lse, uint8_t *__restrict__ handoff
+
+// Packed-counter path: one counting pass into 65536 16-bit counters.  NV > 0
+// keeps the row in registers (NV vectors of 8 tokens per thread); NV == 0
+// streams it and re-reads it for the later passes.  A row whose counts would
+// overflow 16 bits gets handoff[row] = 1 and nothing else.
+template <int NV>
+__global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) {
+  __shared__ Smem sm;
+  VS_ROW_ARGS
+  const int tid = threadIdx.x;
+  if (!params_ok(a)) {
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad(a);
+    return;
+  }
+  for (int i = tid; i < HALF; i += NT) sm.hist[i] = 0u;
+  __syncthreads();
+  using Keys = typename std::conditional<(NV > 0), RegKeys<(NV > 0 ? NV : 1)>, StreamKeys>::type;
+  Keys keys;
+  uint32_t bad, kmax, n_pad;
+  if constexpr (NV > 0) {
+    keys.load_count(a.rowp, V, sm.hist, bad, kmax);
+    n_pad = uint32_t(NV) * NT * 8u - uint32_t(V);  // padding tokens, all at key 0
+  } else {
+    keys.rowp = a.rowp;
+    keys.V = V;
+    keys.load_count(sm.hist, bad, kmax);
+    n_pad = 0;
+  }
+  kmax = block_max_u32(kmax, sm);  // (its barriers also complete the counting)
+  bad = block_max_u32(bad, sm);
+  if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad(a);
+    return;
+  }
+  // every counter stayed below 2^16 iff the packed total equals the token count
+  uint32_t part = 0;
+  for (int i = tid; i < HALF; i += NT) part += (sm.hist[i] & 0xFFFFu) + (sm.hist[i] >> 16);
+  if (block_sum_u32(part, sm) != uint32_t(V) + n_pad) {
+    if (tid == 0) handoff[a.row] = 1;
+    return;
+  }
+  if (tid == 0) handoff[a.row] = 0;
+  auto count = [&](uint32_t key) -> uint32_t {
+    const uint32_t c = (sm.hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
+    return key == 0 ? c - n_pad : c;
+  };
+  const double tau = double(a.tauf);
+  const double z0 = double(key_logit(kmax)) / tau;
+  for (int s = tid; s < NSEG; s += NT) summarize_segment(s, count, tau, z0, sm);
+  __syncthreads();
+  finish_row(a, keys, kmax, tau, z0, sm, [](int) {}, count);
+}
+
+// Stream path: the row is re-read from memory for every pass; 32-bit counts.
+// With a handoff array, only rows marked 1 are processed.
+__global__ __launch_bounds__(NT, 1) void transforms_stream_kernel(VS_KERNEL_ARGS) {
+  __shared__ Smem sm;
+  VS_ROW_ARGS
+  if (handoff && handoff[a.row] == 0) return;
+  const int tid = threadIdx.x;
+  if (!params_ok(a)) {
+    write_bad(a);
+    return;
+  }
+  StreamKeys keys{a.rowp, V};
+  uint32_t bad = 0, kmax = 0;
+  for (int c = tid; c < V; c += NT) {
+    const uint32_t h = a.rowp[c];
+    bad |= raw_bad(h) ? 1u : 0u;
+    kmax = max(kmax, key16(h));
+  }
+  kmax = block_max_u32(kmax, sm);
+  bad = block_max_u32(bad, sm);
+  if (bad || kmax <= KEY_NEG_INF) {
+    write_bad(a);
+    return;
+  }
+  const double tau = double(a.tauf);
+  const double z0 = double(key_logit(kmax)) / tau;
+  for (uint32_t h = 0; h < 2; ++h) {
+    for (int i = tid; i < HALF; i += NT) sm.hist[i] = 0u;
+    __syncthreads();
+    keys.each([&](uint32_t key, int) {
+      if ((key >> 15) == h) atomicAdd(&sm.hist[key & 0x7FFFu], 1u);
+    });
+    __syncthreads();
+    auto count_half = [&](uint32_t key) -> uint32_t { return sm.hist[key & 0x7FFFu]; };
+    for (int s = tid; s < NSEG / 2; s += NT) summarize_segment(int(h) * (NSEG / 2) + s, count_half, tau, z0, sm);
+    __syncthreads();
+  }
+  if (tid == 0) sm.fine_seg = -1;
+  __syncthreads();
+  auto fine = [&](int s) {
+    if (sm.fine_seg == s) return;
+    __syncthreads();
+    if (tid < SEGW) sm.fine[tid] = 0u;
+    __syncthreads();
+    keys.each([&](uint32_t key, int) {
+      if ((key >> 6) == uint32_t(s)) atomicAdd(&sm.fine[key & 63u], 1u);
+    });
+    __syncthreads();
+    if (tid == 0) sm.fine_seg = s;
+    __syncthreads();
+  };
+  auto count = [&](uint32_t key) -> uint32_t { return sm.fine[key & 63u]; };
+  finish_row(a, keys, kmax, tau, z0, sm, fine, count);
+}
+
+#undef VS_ROW_ARGS
+#undef VS_KERNEL_ARGS
+
+}  // namespace
+
+size_t transforms_workspace_bytes(int64_t rows) { return size_t(rows); }
+
+int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,
+                      float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
+                      const int64_t* targets, float* logprob, float* entropy, uint8_t* status,
+                      int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, int64_t* ids_out,
+                      int64_t cap, float* full_lse, uint8_t* handoff, void* stream) {
+  if (rows <= 0) return 0;
+  if (cap > kTransformsMaxCap) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int vecs = int((V + 7) / 8);
+  const int nv = (vecs + NT - 1) / NT;
+#define VS_ARGS                                                                                  \
+  logits, ld, int(V), temp, temp_scalar, top_k, top_p, min_p, targets, logprob, entropy, status, \
+      support_len, threshold_logit, threshold_ties, ids_out, int(cap), full_lse
+  if (nv <= 4) transforms_fast_kernel<4><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  else if (nv <= 10) transforms_fast_kernel<10><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  else if (nv <= 20) transforms_fast_kernel<20><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  else transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  const int rc = int(hipGetLastError());
+  if (rc) return rc;
+  transforms_stream_kernel<<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+#undef VS_ARGS
+  return int(hipGetLastError());
 }
 
 }  // namespace vs

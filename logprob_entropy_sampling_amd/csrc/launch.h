@@ -60,12 +60,18 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
 // Zero a small int32 buffer with a kernel (not a memset node).
 int launch_zero_i32(int32_t* p, int64_t n, void* stream);
 
-// Sampling transforms over bf16 logits (one workgroup per row).
+// Sampling transforms over bf16 logits (one workgroup per row).  Rows up to
+// 20 * 512 * 8 tokens are held in registers, longer ones are streamed; a row
+// that repeats one logit 65536+ times is re-done by a 32-bit-count streaming
+// kernel (flagged in `handoff`, one byte per row of workspace).  More than
+// kTransformsMaxCap dense ids: returns -1.
+constexpr int64_t kTransformsMaxCap = 4096;  // dense ids are sorted in LDS
+size_t transforms_workspace_bytes(int64_t rows);
 int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,
                       float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
                       const int64_t* targets, float* logprob, float* entropy, uint8_t* status,
                       int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, int64_t* ids_out,
-                      int64_t cap, float* full_lse, void* stream);
+                      int64_t cap, float* full_lse, uint8_t* handoff, void* stream);
 
 // Draft/target softmax L1.
 int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float* l1, float* accept,

@@ -164,7 +164,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
   switch (op) {
     case VS_OP_SCORE_FULL: return full_ws_bytes(src, src->T);
     case VS_OP_SCORE_SUPPORT: return support_ws_bytes(src);
-    case VS_OP_SCORE_TRANSFORMS: return 0;
+    case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T));
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
     default: return 0;
   }
@@ -225,18 +225,19 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
                         int32_t* support_len, float* threshold_logit, int32_t* threshold_ties,
                         int64_t* support_ids_out, int64_t support_ids_cap, float* full_lse, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = check_source(src);
   if (rc) return rc;
   if (src->kind != VS_SRC_LOGITS || src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
   if (!top_k || !top_p || !min_p || !target_ids || !logprob) return VS_E_NULL;
   if (support_ids_cap < 0 || support_ids_cap > kMaxDim) return VS_E_PARAM;
   if (support_ids_cap == 0) support_ids_out = nullptr;
+  if (support_ids_out && support_ids_cap > vs::kTransformsMaxCap) return VS_E_UNSUPPORTED;
+  rc = check_workspace(workspace, workspace_bytes, round_up(vs::transforms_workspace_bytes(src->T)));
+  if (rc) return rc;
   rc = vs::launch_transforms(static_cast<const uint16_t*>(src->logits), src->ld_logits, src->T, src->V,
                              src->temperature, src->temperature_scalar, top_k, top_p, min_p, target_ids, logprob,
                              entropy, row_status, support_len, threshold_logit, threshold_ties, support_ids_out,
-                             support_ids_cap, full_lse, stream);
+                             support_ids_cap, full_lse, static_cast<uint8_t*>(workspace), stream);
   if (rc == -1) return VS_E_UNSUPPORTED;
   return rc ? VS_E_DEVICE : VS_OK;
 }

@@ -1,0 +1,205 @@
+"""GPU parity: top-k / top-p / min-p support, descriptor, dense ids and scores vs the fp64 oracle.
+
+Support membership, support_len, threshold_logit, threshold_ties, dense ids
+and status are compared bit-exactly on every row the oracle does not flag as
+borderline (a cumulative mass within 1e-6 of top_p, or a weight within 1e-6
+of min_p); borderline rows are counted and reported separately.
+logprob / entropy / full_lse use the float tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import assert_close, bf16_tensor, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    import logprob_entropy_sampling_amd as m
+    m.lib()
+    return m
+
+
+def _run(vsa, bits, tau, k, p, mp, y, cap, ld_pad=0):
+    T, V = bits.shape
+    if ld_pad:
+        full = np.zeros((T, V + ld_pad), np.uint16)
+        full[:, :V] = bits
+        lg = bf16_tensor(full)[:, :V]
+    else:
+        lg = bf16_tensor(bits)
+    return vsa.score_transforms(to_dev(np.asarray(y, np.int64)), lg, to_dev(np.asarray(k, np.int32)),
+                                to_dev(np.asarray(p, np.float32)), to_dev(np.asarray(mp, np.float32)),
+                                temperature=to_dev(np.asarray(tau, np.float32)), cap=cap)
+
+
+def _compare(got, ref, cap, label):
+    T = len(ref["status"])
+    border = ref["borderline_top_p"] | ref["borderline_min_p"]
+    exact = ~border
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in got.items()}
+    for name in ("support_len", "threshold_ties", "status"):
+        bad = np.nonzero(exact & (g[name] != ref[name]))[0]
+        assert bad.size == 0, f"{label}: {name} differs at rows {bad[:10]}: gpu {g[name][bad[:5]]} oracle {ref[name][bad[:5]]}"
+    tl_g = g["threshold_logit"].astype(np.float64)
+    same = (tl_g == ref["threshold_logit"]) | (np.isnan(tl_g) & np.isnan(ref["threshold_logit"]))
+    bad = np.nonzero(exact & ~same)[0]
+    assert bad.size == 0, f"{label}: threshold_logit differs at rows {bad[:10]}"
+    if cap:
+        bad = np.nonzero(exact & ~(g["support_ids"] == ref["support_ids"]).all(1))[0]
+        assert bad.size == 0, f"{label}: support ids differ at rows {bad[:10]}"
+    rows = np.nonzero(exact)[0]
+    assert_close(f"{label} logprob", g["logprob"], ref["logprob"][rows], rows=rows)
+    assert_close(f"{label} entropy", g["entropy"], ref["entropy"][rows], rows=rows)
+    assert_close(f"{label} full_lse", g["full_lse"], ref["full_lse"])
+    n_b = int(border.sum())
+    mism = int(((g["support_len"] != ref["support_len"]) & border).sum())
+    say(f"  {label}: {T} rows, {n_b} borderline ({mism} of them with a different support_len)")
+    return n_b
+
+
+def _support_sample(x64, tau, k, p, mp, u):
+    """An in-support target per row: inverse CDF of the renormalised support distribution."""
+    r = oracle.score_transforms(x64, tau, k, p, mp, np.zeros(len(x64), np.int64), cap=0)
+    y = np.empty(len(x64), np.int64)
+    for t in range(len(x64)):
+        z = x64[t] / float(tau[t])
+        order = np.lexsort((np.arange(z.size), -z))
+        S = order[: int(r["support_len"][t])]
+        w = np.exp(z[S] - z[S[0]])
+        c = np.cumsum(w)
+        y[t] = S[min(int(np.searchsorted(c, u[t] * c[-1], side="right")), S.size - 1)]
+    return y
+
+
+def test_workload_rows_full_vocab(vsa):
+    say("transforms: 72 rows (two cycles of the 36 parameter combinations), V=151936, cap 64")
+    c = workloads.make(5, T=72)
+    x64 = oracle.logits_from_logits(c["logits"], "bf16")
+    y = _support_sample(x64, c["temperature"], c["top_k"], c["top_p"], c["min_p"], c["u"])
+    got = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, 64)
+    ref = oracle.score_transforms(x64, c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, cap=64)
+    assert (ref["status"] & oracle.ST_TARGET_OUTSIDE_SUPPORT == 0).all()
+    n_b = _compare(got, ref, 64, "workload")
+    assert n_b <= 8
+    again = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, 64)
+    for k in ("logprob", "entropy", "support_len", "support_ids", "full_lse"):
+        assert torch.equal(got[k], again[k]), k
+
+
+@pytest.mark.parametrize("V", [1, 5, 37, 1000, 5003, 40000, 90000])
+def test_small_and_medium_rows_with_ties(vsa, V):
+    say(f"transforms: tied rows V={V}, every parameter combination")
+    rng = np.random.default_rng(V)
+    ks = [0, 1, 2, 5, V, V + 3]
+    ps = [1.0, 0.9, 0.5, 0.1]
+    mps = [0.0, 0.1, 0.5, 1.0]
+    taus = [0.5, 1.0]
+    combos = [(k, p, mp, tau) for k in ks for p in ps for mp in mps for tau in taus]
+    T = len(combos)
+    vals = rng.integers(-6, 7, size=(T, V)).astype(np.float32) * np.float32(0.375)
+    bits = workloads.to_bf16_bits(vals)
+    k = np.array([c[0] for c in combos], np.int32)
+    p = np.array([c[1] for c in combos], np.float32)
+    mp = np.array([c[2] for c in combos], np.float32)
+    tau = np.array([c[3] for c in combos], np.float32)
+    y = rng.integers(0, V, T)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    for cap in (0, 3, 64):
+        got = _run(vsa, bits, tau, k, p, mp, y, cap)
+        ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
+        _compare(got, ref, cap, f"V={V} cap={cap}")
+
+
+def test_unaligned_rows_and_neg_inf(vsa):
+    say("transforms: unaligned rows (ld odd), -inf logits")
+    rng = np.random.default_rng(4)
+    T, V = 40, 3001
+    vals = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    vals[:, ::5] = -np.inf
+    bits = workloads.to_bf16_bits(vals)
+    k = rng.choice([0, 3, 20], T).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.5], T).astype(np.float32)
+    mp = rng.choice([0.0, 0.05], T).astype(np.float32)
+    tau = rng.choice([0.7, 1.0], T).astype(np.float32)
+    y = rng.integers(0, V, T)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    got = _run(vsa, bits, tau, k, p, mp, y, 16, ld_pad=1)
+    ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=16)
+    _compare(got, ref, 16, "unaligned")
+
+
+def test_bad_rows(vsa):
+    say("transforms: BAD rows (NaN, +inf, all -inf, tau, top_p, min_p, target)")
+    V = 100
+    vals = np.zeros((9, V), np.float32)
+    vals[0, 3] = np.nan
+    vals[1, 4] = np.inf
+    vals[2, :] = -np.inf
+    bits = workloads.to_bf16_bits(vals)
+    tau = np.array([1, 1, 1, 0, 1, 1, 1, 1, 1], np.float32)
+    p = np.array([1, 1, 1, 1, 0, np.nan, 1, 1, 1], np.float32)
+    mp = np.array([0, 0, 0, 0, 0, 0, 1.5, 0, 0], np.float32)
+    y = np.array([0, 0, 0, 0, 0, 0, 0, V, 5], np.int64)
+    k = np.zeros(9, np.int32)
+    got = _run(vsa, bits, tau, k, p, mp, y, 4)
+    ref = oracle.score_transforms(oracle.logits_from_logits(bits, "bf16"), tau, k, p, mp, y, cap=4)
+    assert list(ref["status"]) == [4] * 8 + [oracle.ST_SUPPORT_TRUNCATED]  # last row: 100 ids, cap 4
+    _compare(got, ref, 4, "bad")
+    assert (got["support_ids"][:8] == -1).all()
+
+
+def test_identity_and_singleton(vsa):
+    say("transforms: identity program == full-vocabulary scoring; top-k 1 == exact zeros")
+    c = workloads.make(5, T=8, V=30000)
+    T, V = 8, 30000
+    y = torch.from_numpy(c["targets"]).cuda()
+    lg = bf16_tensor(c["logits"])
+    tau = to_dev(c["temperature"])
+    ident = vsa.score_transforms(y, lg, to_dev(np.zeros(T, np.int32)), to_dev(np.ones(T, np.float32)),
+                                 to_dev(np.zeros(T, np.float32)), temperature=tau)
+    full = vsa.score_full(y, logits=lg, temperature=tau)
+    assert (ident["support_len"] == V).all()
+    assert_close("identity logprob", ident["logprob"].cpu().numpy(), full["logprob"].cpu().numpy().astype(np.float64))
+    assert_close("identity entropy", ident["entropy"].cpu().numpy(), full["entropy"].cpu().numpy().astype(np.float64))
+    one = vsa.score_transforms(y, lg, to_dev(np.ones(T, np.int32)), to_dev(np.ones(T, np.float32)),
+                               to_dev(np.zeros(T, np.float32)), temperature=tau, cap=2)
+    assert (one["support_len"] == 1).all()
+    assert (one["entropy"] == 0).all() and (one["logprob"] == 0).all()  # targets are the row argmax
+    assert (one["support_ids"][:, 0].cpu() == y.cpu()).all() and (one["support_ids"][:, 1] == -1).all()
+
+
+def test_all_equal_long_row_uses_32bit_counts(vsa):
+    say("transforms: 151936 equal logits (a key count beyond 16 bits), large tie groups")
+    V = 151936
+    bits = workloads.to_bf16_bits(np.full((4, V), 0.75, np.float32))
+    k = np.array([5, 0, 0, 0], np.int32)
+    p = np.array([1.0, 0.50001, 1.0, 0.25], np.float32)
+    mp = np.zeros(4, np.float32)
+    tau = np.ones(4, np.float32)
+    y = np.array([3, 75969, 151935, 40000], np.int64)
+    got = _run(vsa, bits, tau, k, p, mp, y, 64)
+    ref = oracle.score_transforms(oracle.logits_from_logits(bits, "bf16"), tau, k, p, mp, y, cap=64)
+    assert list(ref["support_len"][:3]) == [5, 75970, V]  # row 3 sits exactly on a cut (borderline)
+    _compare(got, ref, 64, "all-equal")
+    assert list(got["support_ids"][0, :6].cpu().numpy()) == [0, 1, 2, 3, 4, -1]
+    assert list(got["support_ids"][1, :64].cpu().numpy()) == list(range(64))
+
+
+def test_full_size_sampled(vsa):
+    say("transforms: full 2048-row workload; oracle on sampled rows; determinism")
+    c = workloads.make(5)
+    got = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], c["targets"], 64)
+    rows = np.array([0, 1, 2, 3, 17, 35, 36, 1000, 1500, 2047])
+    x64 = oracle.logits_from_logits(c["logits"], "bf16", rows=rows)
+    ref = oracle.score_transforms(x64, c["temperature"][rows], c["top_k"][rows], c["top_p"][rows], c["min_p"][rows],
+                                  c["targets"][rows], cap=64)
+    sub = {k: (v[rows] if v is not None else None) for k, v in got.items()}
+    _compare(sub, ref, 64, "full-size rows")
+    st = got["status"].cpu().numpy()
+    assert ((st & 0x04) == 0).all() and ((st & 0x02) == 0).all()
