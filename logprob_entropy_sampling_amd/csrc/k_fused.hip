@@ -10,8 +10,8 @@
 //     hidden state (tokens on the N axis), so every lane holds one token
 //     column and 64 vocabulary rows: the max / sum-exp / sum p*z fold is
 //     lane-local, with one cross-half and one cross-wave merge per tile;
-//   * K is swept in 32-wide slices staged through double-buffered LDS with
-//     a 16-byte-chunk XOR swizzle (conflict-free fragment reads);
+//   * K is swept in 32-wide slices staged through LDS with a 16-byte-chunk
+//     XOR swizzle (conflict-free fragment reads);
 //   * workgroup ids are remapped so each XCD walks a contiguous range of
 //     vocabulary tiles, all token tiles of one vocabulary tile back to back:
 //     a weight tile is fetched from HBM once and reused from that XCD's L2.
@@ -32,10 +32,51 @@ constexpr int CH = BK / 8;       // 16-byte chunks per row per stage (4)
 constexpr int NT = 256;          // threads (4 waves: 2 along V x 2 along T)
 constexpr int LOADS = BV * CH / NT;  // 16-byte loads per thread per operand per stage (4)
 
-__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ ((r >> 1) & 3)); }
+// 16-byte chunk c of tile row r sits at slot c ^ g(r) of that row (rows are
+// 64 bytes).  g(r) = ((r >> 1) ^ (r >> 3)) & 3 makes the fragment reads (32
+// consecutive rows, one chunk) conflict-free whether the LDS serves 8 lanes
+// over 32 banks or 16 lanes over 64 banks per cycle.
+__device__ __forceinline__ int swz_g(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ swz_g(r)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Workgroup -> tile order.  Workgroup ids are handed to the 8 XCDs round robin,
+// so id b runs on XCD b % 8.  The vocabulary tiles are cut into bands of gv
+// tiles and band g is served by XCD g % 8; inside a band the token tiles
+// advance in blocks of kBlockT, the gv x kBlockT tiles of a block back to
+// back, so one XCD's L2 holds the weight tiles of its band and the hidden
+// tiles of its block while they are reused.  The grid is
+// 8 * ceil(bands / 8) * gv * n_ttiles; ids past the last band do nothing.
+// gv = 0 (fewer than 8 vocabulary tiles): plain order, vocabulary tile fastest.
+constexpr int kBlockT = 8;
+__host__ __device__ inline int band_width(int n_vtiles) {
+  return n_vtiles < 8 ? 0 : n_vtiles < 32 ? n_vtiles / 8 : 4;
+}
+__host__ __device__ inline int64_t tile_grid(int64_t n_vtiles, int64_t n_ttiles, int gv) {
+  if (gv == 0) return n_vtiles * n_ttiles;
+  const int64_t bands = (n_vtiles + gv - 1) / gv;
+  return 8 * ((bands + 7) / 8) * gv * n_ttiles;
+}
+__device__ __forceinline__ bool map_tile(int b, int n_vtiles, int n_ttiles, int gv, int& vt, int& tt) {
+  if (gv == 0) {
+    tt = b / n_vtiles;
+    vt = b - tt * n_vtiles;
+    return tt < n_ttiles;
+  }
+  const int x = b & 7;
+  const int li = b >> 3;
+  const int per_band = gv * n_ttiles;
+  const int band_local = li / per_band;
+  const int within = li - band_local * per_band;
+  const int tb = within / (gv * kBlockT);
+  const int r = within - tb * (gv * kBlockT);
+  const int gt = n_ttiles - tb * kBlockT < kBlockT ? n_ttiles - tb * kBlockT : kBlockT;  // ragged last block
+  const int vv = r / gt;
+  vt = (band_local * 8 + x) * gv + vv;
+  tt = tb * kBlockT + (r - vv * gt);
+  return vt < n_vtiles;
+}
 
 // ---- epilogue: per token column, fold this tile's 256 vocabulary rows ----
 // acc[i][j][r] holds vocabulary row  wv*128 + 32i + 8(r/4) + 4*lh + (r%4)
@@ -158,13 +199,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
     const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
-    int n_vtiles, int n_ttiles, float4* __restrict__ partials, float* __restrict__ zy_raw) {
-  const int nb = gridDim.x;  // a multiple of 8
-  const int b = blockIdx.x;
-  const int L = (b & 7) * (nb >> 3) + (b >> 3);
-  if (L >= n_vtiles * n_ttiles) return;
-  const int vt = L / n_ttiles;
-  const int tt = L - vt * n_ttiles;
+    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+  int vt, tt;
+  if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
   const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
   const int64_t t0 = int64_t(tt) * BT;
   if (t0 >= rows_valid) return;
@@ -264,11 +301,17 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
 
 // ---------------------------------------------------------------------------
 // Pipelined sweep (H a multiple of 32): the same tile, MFMA layout, swizzle
-// and epilogue, but the K slices are brought into a 4-stage LDS ring by
+// and epilogue, but the K slices are brought into a 4-slot LDS ring by
 // direct-to-LDS 16-byte loads issued three stages ahead (no staging
-// registers).  Each stage lives in its own LDS array and the K loop is
-// unrolled by 4, so the compiler can tell a stage being filled from the one
-// being read and does not drain the loads before every LDS read.
+// registers, no VGPR round trip).
+//   * Each ring slot is its own pair of LDS arrays and the K loop is unrolled
+//     by 4, so the compiler's wait tracking tells the slot being filled from
+//     the slots being read and never drains the loads before an LDS read.
+//   * BUF: the loads are buffer loads against one resource per operand tile,
+//     with a 32-bit per-lane byte offset and the K offset in a scalar
+//     register (half the address VGPRs and VALU work of 64-bit pointers).
+//     Used when a 256-row operand tile spans less than 2 GiB and the hidden
+//     rows are not gathered; otherwise the loads take 64-bit pointers.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -277,67 +320,86 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 constexpr int NSTAGE = 4;
-
-struct Stage {
-  uint4 a[BV * CH];
-  uint4 b[BT * CH];
-};
 constexpr int DMA_PER_OP = BV * CH / NT;  // 16-byte loads per lane per operand per stage (4)
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OP;
+// dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format, no swizzle
+constexpr int kBufferFlags = 0x00020000;
 
+template <bool BUF>
 __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
     const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
-    int n_vtiles, int n_ttiles, float4* __restrict__ partials, float* __restrict__ zy_raw) {
-  const int nb = gridDim.x;  // a multiple of 8
-  const int b = blockIdx.x;
-  const int L = (b & 7) * (nb >> 3) + (b >> 3);
-  if (L >= n_vtiles * n_ttiles) return;
-  const int vt = L / n_ttiles;
-  const int tt = L - vt * n_ttiles;
+    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+  int vt, tt;
+  if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
   const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
   const int64_t t0 = int64_t(tt) * BT;
   if (t0 >= rows_valid) return;
   const int64_t v0 = int64_t(vt) * BV;
 
-  // one LDS object per ring slot (A and B tiles together): the compiler's
-  // wait tracking tells the slot being filled from the one being read
-  __shared__ Stage S0, S1, S2, S3;
+  __shared__ uint4 A0[BV * CH], A1[BV * CH], A2[BV * CH], A3[BV * CH];
+  __shared__ uint4 B0[BT * CH], B1[BT * CH], B2[BT * CH], B3[BT * CH];
+  // slot indices are compile-time constants after unrolling
+  auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : i == 1 ? A1 : i == 2 ? A2 : A3; };
+  auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : i == 1 ? B1 : i == 2 ? B2 : B3; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int wv = w & 1;
   const int wt = w >> 1;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
+  const int64_t vrows = V - v0 < BV ? V - v0 : BV;
+  const int64_t trows = rows_valid - t0 < BT ? rows_valid - t0 : BT;
 
-  // Direct-to-LDS assignment: load i of wave w fills LDS chunks (4w + i) * 64 + lane,
-  // i.e. row r = chunk / 4, physical slot chunk % 4, which holds logical K chunk
-  // slot ^ ((r >> 1) & 3) of that row (the XOR swizzle the fragment reads undo).
-  const uint16_t* ga[DMA_PER_OP];
+  // Load i of wave w fills LDS chunk p = (4w + i) * 64 + lane: tile row r = p / 4,
+  // physical slot p % 4, which holds logical K chunk (p % 4) ^ g(r) of that row.
+  // Rows past the tile's end re-read the last row (their results are masked).
+  uint32_t oa[DMA_PER_OP], ob[DMA_PER_OP];      // BUF: byte offsets inside the tile
+  const uint16_t* ga[DMA_PER_OP];               // otherwise: pointers
   const uint16_t* gb[DMA_PER_OP];
 #pragma unroll
   for (int i = 0; i < DMA_PER_OP; ++i) {
     const int p = (w * DMA_PER_OP + i) * 64 + lane;
     const int r = p >> 2;
-    const int c = (p & 3) ^ ((r >> 1) & 3);
-    int64_t v = v0 + r;
-    v = v < V ? v : V - 1;
-    int64_t t = t0 + r;
-    t = t < rows_valid ? t : rows_valid - 1;
-    const int64_t hrow = row_map ? int64_t(row_map[t]) : t;
-    ga[i] = weight + v * ld_w + c * 8;
-    gb[i] = hidden + hrow * ld_h + c * 8;
+    const int c = (p & 3) ^ swz_g(r);
+    const int64_t rv = r < vrows ? r : vrows - 1;
+    const int64_t rt = r < trows ? r : trows - 1;
+    if (BUF) {
+      oa[i] = uint32_t((rv * ld_w + c * 8) * 2);
+      ob[i] = uint32_t((rt * ld_h + c * 8) * 2);
+    } else {
+      const int64_t hrow = row_map ? int64_t(row_map[t0 + rt]) : t0 + rt;
+      ga[i] = weight + (v0 + rv) * ld_w + c * 8;
+      gb[i] = hidden + hrow * ld_h + c * 8;
+    }
   }
-  const int dma_off = w * DMA_PER_OP * 64;  // first chunk of this wave's loads
-
-#define VS_DMA(St, k0)                                                                                   \
-  do {                                                                                                   \
-    _Pragma("unroll") for (int i_ = 0; i_ < DMA_PER_OP; ++i_) {                                          \
-      __builtin_amdgcn_global_load_lds(ga[i_] + (k0), (lds_void_t*)(St.a + dma_off + i_ * 64), 16, 0, 0); \
-      __builtin_amdgcn_global_load_lds(gb[i_] + (k0), (lds_void_t*)(St.b + dma_off + i_ * 64), 16, 0, 0); \
-    }                                                                                                    \
-  } while (0)
+  // (unused, and dropped by the compiler, when !BUF)
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(weight + v0 * ld_w), (short)0, int(BUF ? vrows * ld_w * 2 : 0), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(hidden + t0 * ld_h), (short)0, int(BUF ? trows * ld_h * 2 : 0), kBufferFlags);
+  auto dma = [&](int slot, int64_t k0) {
+    if (BUF) {
+      const uint32_t so = uint32_t(k0 * 2);
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OP; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(SA(slot) + (wu * DMA_PER_OP + i) * 64), 16,
+                                                 oa[i], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_t*)(SB(slot) + (wu * DMA_PER_OP + i) * 64), 16,
+                                                 ob[i], so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OP; ++i) {
+        __builtin_amdgcn_global_load_lds(ga[i] + k0, (lds_void_t*)(SA(slot) + (wu * DMA_PER_OP + i) * 64), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds(gb[i] + k0, (lds_void_t*)(SB(slot) + (wu * DMA_PER_OP + i) * 64), 16, 0,
+                                         0);
+      }
+    }
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -347,64 +409,74 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
 
   const int lr = lane & 31;
   const int lh = lane >> 5;
+  typedef bf16x8 Frags[2][4];
+  auto read_slot = [&](int slot, Frags& fa, Frags& fb) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[kk][i] = as_bf16x8(SA(slot)[swz(wv * 128 + 32 * i + lr, 2 * kk + lh)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[kk][j] = as_bf16x8(SB(slot)[swz(wt * 128 + 32 * j + lr, 2 * kk + lh)]);
+    }
+  };
+  auto mma = [&](const Frags& fa, const Frags& fb) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+  };
+  auto mma_slot = [&](int slot) {
+    Frags fa, fb;
+    read_slot(slot, fa, fb);
+    mma(fa, fb);
+  };
+  // barrier + "LDS reads stay after it"
+  auto bar = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
   const int nk = int(H / BK);
-
-#define VS_MMA(St)                                                              \
-  do {                                                                          \
-    bf16x8 fa[2][4], fb[2][4];                                                  \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                          \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                             \
-        fa[kk][i] = as_bf16x8(St.a[swz(wv * 128 + 32 * i + lr, 2 * kk + lh)]);  \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-        fb[kk][j] = as_bf16x8(St.b[swz(wt * 128 + 32 * j + lr, 2 * kk + lh)]);  \
-    }                                                                           \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                            \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                             \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                           \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0); \
-  } while (0)
-
-  // Main loop, whole groups of 4 stages.  Stage s: wait until this wave's
-  // loads for stage s are done (the two younger stages may stay in flight),
-  // barrier (every wave's loads for s are done, and every wave has finished
-  // reading stage s-1), refill the slot of stage s-1 with stage s+3, compute
-  // stage s.  The refill is unconditional (clamped to the last stage) so the
-  // compiler's wait tracking stays exact.
-#define VS_STEP(St, Sn, s)                                                   \
-  {                                                                          \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_STAGE));                \
-    __builtin_amdgcn_s_barrier();                                            \
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");          \
-    const int pf_ = (s) + 3 < nk ? (s) + 3 : nk - 1;                         \
-    VS_DMA(Sn, int64_t(pf_) * BK);                                           \
-    VS_MMA(St);                                                              \
-  }
-
-  VS_DMA(S0, 0);
-  VS_DMA(S1, int64_t(1 < nk ? 1 : nk - 1) * BK);
-  VS_DMA(S2, int64_t(2 < nk ? 2 : nk - 1) * BK);
+  // prologue: stages 0..2 into slots 0..2 (clamped to the last stage)
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) dma(s, int64_t(s < nk ? s : nk - 1) * BK);
+  // Stage s lives in slot s % 4.  Step s: wait until this wave's loads for
+  // stage s are done (the two younger stages stay in flight), barrier (every
+  // wave's loads for s have landed and every wave has finished reading slot
+  // (s-1) % 4), read the fragments of stage s, refill slot (s-1) % 4 with
+  // stage s+3, compute stage s.  The refill is unconditional (clamped to the
+  // last stage) so the wait counts stay exact, and it follows the fragment
+  // reads so no LDS read of the step comes after a load into LDS (the
+  // compiler would otherwise drain every outstanding load before it).
   const int nk4 = nk & ~(NSTAGE - 1);
   for (int kt = 0; kt < nk4; kt += NSTAGE) {
-    VS_STEP(S0, S3, kt)
-    VS_STEP(S1, S0, kt + 1)
-    VS_STEP(S2, S1, kt + 2)
-    VS_STEP(S3, S2, kt + 3)
+#pragma unroll
+    for (int u = 0; u < NSTAGE; ++u) {
+      const int s = kt + u;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 2) * DMA_PER_STAGE));
+      bar();
+      const int pf = s + NSTAGE - 1 < nk ? s + NSTAGE - 1 : nk - 1;
+      Frags fa, fb;
+      read_slot(u, fa, fb);
+      dma((u + NSTAGE - 1) % NSTAGE, int64_t(pf) * BK);
+      mma(fa, fb);
+    }
   }
-  // leftover stages (nk % 4 of them) sit in slots 0..2 already
+  // leftover stages (nk % 4 of them) are in slots 0..2 already
   const int rem = nk - nk4;
   if (rem > 0) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    VS_MMA(S0);
-    if (rem > 1) VS_MMA(S1);
-    if (rem > 2) VS_MMA(S2);
+    bar();
+    mma_slot(0);
+    if (rem > 1) mma_slot(1);
+    if (rem > 2) mma_slot(2);
   }
-#undef VS_STEP
-#undef VS_MMA
-#undef VS_DMA
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
   __syncthreads();
-  tile_epilogue(acc, reinterpret_cast<float*>(&S0.a[0]), v0, t0, vt, rows_valid, V, temp, temp_scalar, targets,
+  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, temp, temp_scalar, targets,
                 row_map, n_vtiles, partials, zy_raw);
 }
 
@@ -430,20 +502,30 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
                           int64_t rows, int64_t H, int64_t V, const float* temp, float temp_scalar,
                           const int64_t* targets, const int32_t* row_map, const int32_t* row_count,
                           void* partials, float* zy_raw, void* stream) {
-  const int n_vtiles = int((V + BV - 1) / BV);
-  const int n_ttiles = int((rows + BT - 1) / BT);
-  const int64_t tiles = int64_t(n_vtiles) * n_ttiles;
-  if (tiles <= 0) return 0;
-  const int64_t grid = (tiles + 7) / 8 * 8;
+  const int64_t n_vtiles = (V + BV - 1) / BV;
+  const int64_t n_ttiles = (rows + BT - 1) / BT;
+  if (n_vtiles <= 0 || n_ttiles <= 0) return 0;
+  if (n_vtiles > 0x7FFFFFFF || n_ttiles > 0x7FFFFFFF) return int(hipErrorInvalidConfiguration);
+  const int gv = band_width(int(n_vtiles));
+  const int64_t grid = tile_grid(n_vtiles, n_ttiles, gv);
+  if (grid > 0x7FFFFFFF) return int(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (H % BK == 0) {
-    fused_partials_pipelined_kernel<<<dim3(unsigned(grid)), dim3(NT), 0, s>>>(
-        hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets, row_map, row_count, n_vtiles,
-        n_ttiles, static_cast<float4*>(partials), zy_raw);
+  const dim3 g{unsigned(grid)}, b{unsigned(NT)};
+  const int nv = int(n_vtiles), nt = int(n_ttiles);
+  float4* part = static_cast<float4*>(partials);
+  // buffer offsets are 32-bit: a 256-row tile of either operand must span < 2 GiB
+  const bool buf_ok = !row_map && int64_t(BV) * ld_weight * 2 <= 0x7FFFFFFF && int64_t(BT) * ld_hidden * 2 <= 0x7FFFFFFF;
+  if (H % BK == 0 && buf_ok) {
+    fused_partials_pipelined_kernel<true><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,
+                                                          temp_scalar, targets, row_map, row_count, nv, nt, gv, part,
+                                                          zy_raw);
+  } else if (H % BK == 0) {
+    fused_partials_pipelined_kernel<false><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,
+                                                           temp_scalar, targets, row_map, row_count, nv, nt, gv, part,
+                                                           zy_raw);
   } else {
-    fused_partials_kernel<<<dim3(unsigned(grid)), dim3(NT), 0, s>>>(
-        hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets, row_map, row_count, n_vtiles,
-        n_ttiles, static_cast<float4*>(partials), zy_raw);
+    fused_partials_kernel<<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar,
+                                          targets, row_map, row_count, nv, nt, gv, part, zy_raw);
   }
   return int(hipGetLastError());
 }

@@ -113,7 +113,8 @@ def test_fused_tiny_workload(vsa):
     _cmp_full(got, oracle.score_full(x, c["temperature"], c["targets"]))
 
 
-@pytest.mark.parametrize("T,H,V", [(300, 200, 5003), (257, 64, 256), (1, 8, 1), (513, 1024, 30000)])
+@pytest.mark.parametrize("T,H,V", [(300, 200, 5003), (257, 64, 256), (1, 8, 1), (513, 1024, 30000),
+                                   (2333, 160, 9000), (700, 96, 2100)])
 def test_fused_ragged(vsa, T, H, V):
     say(f"fused ragged: T={T} H={H} V={V} bf16 hidden, per-row tau")
     rng = np.random.default_rng(T + H + V)
