@@ -18,8 +18,10 @@ Prints ONE JSON line.  Besides the contract fields it carries
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -44,23 +46,61 @@ def _dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _event_times(fn, steps, warmup, flush=None):
-    """Per-call durations (ms) from HIP events on torch's current stream."""
+def _event_times(vsa, fn, steps, warmup, flush=None):
+    """Per-call durations (ms): the whole call (HIP events on torch's current
+    stream, which the call launches on) and its main sweep kernel(s) alone
+    (the library's own event bracket, recorded on the same stream)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    out = []
-    for _ in range(steps):
-        if flush is not None:
-            flush()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        e.synchronize()
-        out.append(s.elapsed_time(e))
-    return out
+    calls, sweeps = [], []
+    vsa.sweep_timer(True)
+    try:
+        for _ in range(steps):
+            if flush is not None:
+                flush()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            calls.append(s.elapsed_time(e))
+            sweeps.append(vsa.sweep_timer_ms())
+    finally:
+        vsa.sweep_timer(False)
+    return calls, sweeps
+
+
+# Kernel sources whose HBM counters are recorded in profiles/: a summary's
+# figures stand only while these files are unchanged.
+_SWEEP_SOURCES = ("logprob_entropy_sampling_amd/csrc/k_fused.hip", "logprob_entropy_sampling_amd/csrc/common.h",
+                  "logprob_entropy_sampling_amd/csrc/launch.h")
+TRAFFIC_SUMMARY = "profiles/fused_full_hbm_traffic.md"
+
+
+def sweep_source_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in _SWEEP_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _recorded_traffic():
+    """(bytes per launch, note) from the committed counter summary; None when the
+    summary is missing or was taken on kernel sources that have changed since."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h):
+        return None, "counter summary unreadable"
+    if m_h.group(1) != sweep_source_sha256():
+        return None, "kernel changed since the counters were taken"
+    return int(m_b.group(1)), TRAFFIC_SUMMARY
 
 
 def _flusher(dev):
@@ -98,10 +138,12 @@ def bench_fused(vsa, dev, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-call event timing of the same op (its kernels run on this stream)
-    ev = _event_times(step, steps, 0)
+    ev, sw = _event_times(vsa, step, steps, 0)
     med, iqr = _median_iqr(ev)
     flops = 2.0 * T * H * V
-    achieved = flops / (statistics.mean(ev) * 1e-3) / 1e12
+    sweep_ms = statistics.mean(sw)
+    achieved = flops / (sweep_ms * 1e-3) / 1e12
+    traffic, traffic_src = _recorded_traffic()
     return c, {
         "value": T * steps / wall,
         "ms_per_step": wall * 1e3 / steps,
@@ -113,9 +155,12 @@ def bench_fused(vsa, dev, steps, warmup):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "fused_partials_kernel (+ the ~1% merge kernel inside the same event bracket)",
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "kernel": "fused_partials_pipelined_kernel<true> (projection + per-tile softmax statistics)",
+            "kernel_ms_mean": round(sweep_ms, 4),
             "flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": (T * H + V * H) * 2 + T * ((V + 255) // 256) * 16 + T * 4,
         },
     }
 
@@ -141,63 +186,84 @@ def cpu_baseline(c, budget_s=15.0):
                       f"numpy float64), {el:.1f} s"}
 
 
+def _path_entry(T, ev, sw, call_bytes, sweep_bytes, **extra):
+    """One secondary path: whole-call and sweep-kernel times, algorithmic bytes, fraction of HBM peak."""
+    med, iqr = _median_iqr(ev)
+    kms = statistics.mean(sw)
+    e = {"T": T, **extra, "ms_median": round(med, 5), "ms_iqr": round(iqr, 5), "tokens_per_s": round(T / (med * 1e-3), 1),
+         "bytes": int(call_bytes), "hbm_GBs": round(call_bytes / (med * 1e-3) / 1e9, 1),
+         "hbm_frac": round(call_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "kernel_ms_mean": round(kms, 5), "kernel_bytes": int(sweep_bytes),
+         "kernel_hbm_GBs": round(sweep_bytes / (kms * 1e-3) / 1e9, 1),
+         "kernel_hbm_frac": round(sweep_bytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return e
+
+
 def bench_paths(vsa, dev, steps, warmup):
+    """The other scoring paths, each on its own workload.  A 512 MiB write
+    before every timed call leaves none of its inputs in the Infinity Cache.
+    Bytes are algorithmic: every input element read once, every output written once."""
     import torch
     import workloads
     flush = _flusher(dev)
     res = {}
 
-    # logits-input full-vocabulary scoring: T=512, V=151,936 bf16
+    # logits-input full-vocabulary scoring: T=512, V=151,936 bf16, per-row temperature
     c = workloads.make(2)
+    T, V = c["T"], c["V"]
     lg, y, tau = _bf16(c["logits"], dev), _dev(c["targets"], dev), _dev(c["temperature"], dev)
-    ev = _event_times(lambda: vsa.score_full(y, logits=lg, temperature=tau), steps, warmup, flush)
-    med, iqr = _median_iqr(ev)
-    byts = c["T"] * c["V"] * 2 + c["T"] * (8 + 4 + 4 * 3 + 1)
-    res["logits_full"] = {"T": c["T"], "V": c["V"], "ms_median": med, "ms_iqr": iqr,
-                          "tokens_per_s": c["T"] / (med * 1e-3), "bytes": byts,
-                          "hbm_GBs": byts / (med * 1e-3) / 1e9, "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ev, sw = _event_times(vsa, lambda: vsa.score_full(y, logits=lg, temperature=tau), steps, warmup, flush)
+    n_tiles = (V + 8191) // 8192
+    sweep = T * V * 2 + T * 4 + T * n_tiles * 16          # logits + tau in, partials out
+    call = sweep + T * n_tiles * 16 + T * (8 + 3 * 4 + 1)  # + partials back in, targets in, 3 floats + status out
+    res["logits_full"] = _path_entry(T, ev, sw, call, sweep, V=V)
     del lg
+
     # recorded support through selected projections: T=2048, H=7168, V=129,280, width 64
     c = workloads.make(3)
+    T, H, V = c["T"], c["H"], c["V"]
     hid, w = _bf16(c["hidden"], dev), _bf16(c["weight"], dev)
     y, ids = _dev(c["targets"], dev), _dev(c["support_ids"], dev)
-    ev = _event_times(lambda: vsa.score_support_ids(y, ids, hidden=hid, weight=w), steps, warmup, flush)
-    med, iqr = _median_iqr(ev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_support_ids(y, ids, hidden=hid, weight=w), steps, warmup, flush)
     sup = c["support_ids"][c["support_ids"] >= 0]
-    uniq = np.unique(sup).size
-    byts_u = uniq * c["H"] * 2 + c["T"] * c["H"] * 2 + c["support_ids"].nbytes + c["T"] * (8 + 9)
-    byts_p = sup.size * c["H"] * 2 + c["T"] * c["H"] * 2 + c["support_ids"].nbytes + c["T"] * (8 + 9)
-    res["support_replay"] = {"T": c["T"], "H": c["H"], "V": c["V"], "pairs": int(sup.size), "unique_rows": int(uniq),
-                             "ms_median": med, "ms_iqr": iqr, "tokens_per_s": c["T"] / (med * 1e-3),
-                             "bytes_unique": byts_u, "hbm_GBs_unique": byts_u / (med * 1e-3) / 1e9,
-                             "hbm_frac_unique": byts_u / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "bytes_pairs": byts_p, "hbm_frac_pairs": byts_p / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    uniq = int(np.unique(sup).size)
+    # unique basis: each distinct W row and each hidden row read once
+    byts = uniq * H * 2 + T * H * 2 + c["support_ids"].nbytes + T * (8 + 2 * 4 + 1)
+    res["support_replay"] = _path_entry(T, ev, sw, byts, byts, H=H, V=V, width=int(c["support_ids"].shape[1]),
+                                        pairs=int(sup.size), unique_rows=uniq,
+                                        bytes_pairs_basis=int(sup.size * H * 2 + T * H * 2 + c["support_ids"].nbytes))
     del hid, w
+
     # sampling transforms and draft/target L1: T=2048, V=151,936 bf16
     c = workloads.make(5)
+    T, V = c["T"], c["V"]
     lg, dr = _bf16(c["logits"], dev), _bf16(c["draft"], dev)
     y = _dev(c["targets"], dev)
     tk, tp, mp, tau = (_dev(c["top_k"], dev), _dev(c["top_p"], dev), _dev(c["min_p"], dev),
                        _dev(c["temperature"], dev))
-    try:
-        ev = _event_times(lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64), steps, warmup,
-                          flush)
-        med, iqr = _median_iqr(ev)
-        byts = c["T"] * c["V"] * 2
-        res["transforms"] = {"T": c["T"], "V": c["V"], "ms_median": med, "ms_iqr": iqr,
-                             "tokens_per_s": c["T"] / (med * 1e-3), "bytes": byts,
-                             "hbm_GBs": byts / (med * 1e-3) / 1e9,
-                             "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    except vsa.VsError as e:
-        res["transforms"] = {"error": str(e)}
-    ev = _event_times(lambda: vsa.l1_distance(lg, dr), steps, warmup, flush)
-    med, iqr = _median_iqr(ev)
-    byts = 2 * c["T"] * c["V"] * 2
-    res["l1_distance"] = {"T": c["T"], "V": c["V"], "ms_median": med, "ms_iqr": iqr,
-                          "tokens_per_s": c["T"] / (med * 1e-3), "bytes": byts, "hbm_GBs": byts / (med * 1e-3) / 1e9,
-                          "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64), steps,
+                          warmup, flush)
+    byts = T * V * 2 + T * (4 * 4 + 8) + T * (4 * 4 + 4 + 1 + 64 * 8 + 4)
+    res["transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, support_ids_cap=64)
+    ev, sw = _event_times(vsa, lambda: vsa.l1_distance(lg, dr), steps, warmup, flush)
+    byts = 2 * T * V * 2 + T * 8
+    res["l1_distance"] = _path_entry(T, ev, sw, byts, byts, V=V)
     torch.cuda.synchronize()
     return res
+
+
+def copy_probe(dev, mib, steps):
+    """A plain elementwise copy (out = in * 1, fp32) of `mib` MiB, run `steps`
+    times: a kernel of known traffic (mib MiB read, mib MiB written) against
+    which the HBM byte counters are scaled."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -207,6 +273,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--paths", choices=["all", "none"], default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain fp32 copy of MIB MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the op is row-local; see the sharding notes); got --gpus {args.gpus}",
@@ -216,6 +284,9 @@ def main():
     import logprob_entropy_sampling_amd as vsa
     vsa.lib()
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        print(f"bench: copy probe {args.copy_probe} MiB x {args.steps}", file=sys.stderr, flush=True)
+        copy_probe(dev, args.copy_probe, args.steps)
     print("bench: fused_full T=4096 H=4096 V=151936", file=sys.stderr, flush=True)
     c, fused = bench_fused(vsa, dev, args.steps, args.warmup)
     out = {

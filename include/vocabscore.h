@@ -199,6 +199,22 @@ int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t 
                    int64_t V, int64_t ld_target, int64_t ld_draft, float* l1, float* accept_rate,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Diagnostics (not part of the scoring contract) -------------------- */
+
+/* vs_sweep_timer(1): every later scoring call records two HIP events on its
+ * own stream, immediately before and immediately after its main sweep
+ * kernel(s) -- the MFMA sweep of the fused input, the logits sweep, the
+ * support kernel, the transforms kernels or the L1 kernel; not the merge,
+ * not the fallback rows' sweep.  vs_sweep_timer(0) stops recording.
+ * Process-wide state for the device current at enable time: one caller at a
+ * time.  Returns VS_OK, or VS_E_DEVICE when the events cannot be created. */
+int vs_sweep_timer(int32_t enable);
+
+/* Waits for the most recent bracket and writes its length in milliseconds
+ * to *ms (host pointer).  VS_E_NULL for a NULL ms, VS_E_PARAM when no bracket
+ * has been recorded since the timer was enabled, VS_E_DEVICE on a HIP error. */
+int vs_sweep_timer_ms(float* ms);
+
 /* Static text for a return code. */
 const char* vs_status_string(int32_t code);
 

@@ -43,7 +43,7 @@ class _Lazy:
 _lib = _Lazy()
 
 __all__ = ["score_full", "score_support_ids", "score_transforms", "l1_distance", "workspace_size",
-           "status_string", "VsError", "lib"]
+           "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
@@ -245,3 +245,19 @@ def l1_distance(target_logits, draft_logits):
     if rc:
         raise VsError(rc, "vs_l1_distance")
     return {"l1": l1, "accept_rate": acc}
+
+
+def sweep_timer(enable: bool) -> None:
+    """Bracket the main sweep kernel(s) of every later call with two HIP events (vs_sweep_timer)."""
+    rc = _lib.vs_sweep_timer(1 if enable else 0)
+    if rc:
+        raise VsError(rc, "vs_sweep_timer")
+
+
+def sweep_timer_ms() -> float:
+    """Length of the most recent bracket, in ms; waits for it (vs_sweep_timer_ms)."""
+    ms = ctypes.c_float()
+    rc = _lib.vs_sweep_timer_ms(ctypes.byref(ms))
+    if rc:
+        raise VsError(rc, "vs_sweep_timer_ms")
+    return float(ms.value)

@@ -53,6 +53,8 @@ _SIGS = {
                                       c_size_t, c_void_p]),
     "vs_l1_distance": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "vs_sweep_timer": (c_int32, [c_int32]),
+    "vs_sweep_timer_ms": (c_int32, [POINTER(c_float)]),
 }
 
 

@@ -101,6 +101,11 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
   const bool tail_v = vlim < 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    // the accumulators of the columns not folded yet stay in AGPRs until their turn
+#pragma unroll
+    for (int jj = j + 1; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
     const int col = wt * 128 + 32 * j + lr;
     const int64_t t = t0 + col;
     const bool tvalid = t < rows_valid;
@@ -325,7 +330,7 @@ constexpr int DMA_PER_STAGE = 2 * DMA_PER_OP;
 // dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format, no swizzle
 constexpr int kBufferFlags = 0x00020000;
 
-template <bool BUF>
+template <bool BUF, int REM>
 __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
   // prologue: stages 0..2 into slots 0..2 (clamped to the last stage)
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) dma(s, int64_t(s < nk ? s : nk - 1) * BK);
-  // Stage s lives in slot s % 4.  Step s: wait until this wave's loads for
+  // Stage s lives in slot s % 4 (REM = nk % 4, fixed at compile time).  Step s: wait until this wave's loads for
   // stage s are done (the two younger stages stay in flight), barrier (every
   // wave's loads for s have landed and every wave has finished reading slot
   // (s-1) % 4), read the fragments of stage s, refill slot (s-1) % 4 with
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
   // last stage) so the wait counts stay exact, and it follows the fragment
   // reads so no LDS read of the step comes after a load into LDS (the
   // compiler would otherwise drain every outstanding load before it).
-  const int nk4 = nk & ~(NSTAGE - 1);
+  const int nk4 = nk - REM;
   for (int kt = 0; kt < nk4; kt += NSTAGE) {
 #pragma unroll
     for (int u = 0; u < NSTAGE; ++u) {
@@ -465,19 +470,18 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
       mma(fa, fb);
     }
   }
-  // leftover stages (nk % 4 of them) are in slots 0..2 already
-  const int rem = nk - nk4;
-  if (rem > 0) {
+  // the REM = nk % 4 leftover stages sit in slots 0 .. REM-1; straight-line
+  // code (REM is a template argument) keeps the accumulators where they are
+  if (REM > 0) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     bar();
-    mma_slot(0);
-    if (rem > 1) mma_slot(1);
-    if (rem > 2) mma_slot(2);
+#pragma unroll
+    for (int u = 0; u < REM; ++u) mma_slot(u);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
   __syncthreads();
   tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, temp, temp_scalar, targets,
-                row_map, n_vtiles, partials, zy_raw);
+                BUF ? nullptr : row_map, n_vtiles, partials, zy_raw);  // BUF implies no gather
 }
 
 __global__ void round_hidden_kernel(const float* __restrict__ h, int64_t ld, int64_t rows, int64_t H,
@@ -515,14 +519,23 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
   float4* part = static_cast<float4*>(partials);
   // buffer offsets are 32-bit: a 256-row tile of either operand must span < 2 GiB
   const bool buf_ok = !row_map && int64_t(BV) * ld_weight * 2 <= 0x7FFFFFFF && int64_t(BT) * ld_hidden * 2 <= 0x7FFFFFFF;
-  if (H % BK == 0 && buf_ok) {
-    fused_partials_pipelined_kernel<true><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,
-                                                          temp_scalar, targets, row_map, row_count, nv, nt, gv, part,
-                                                          zy_raw);
-  } else if (H % BK == 0) {
-    fused_partials_pipelined_kernel<false><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,
-                                                           temp_scalar, targets, row_map, row_count, nv, nt, gv, part,
-                                                           zy_raw);
+  if (H % BK == 0) {
+    const int rem = int((H / BK) % NSTAGE);
+#define VS_LAUNCH_PIPELINED(B, R)                                                                                  \
+  fused_partials_pipelined_kernel<B, R><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,     \
+                                                        temp_scalar, targets, row_map, row_count, nv, nt, gv, part, \
+                                                        zy_raw)
+    switch (rem + (buf_ok ? 0 : 4)) {
+      case 0: VS_LAUNCH_PIPELINED(true, 0); break;
+      case 1: VS_LAUNCH_PIPELINED(true, 1); break;
+      case 2: VS_LAUNCH_PIPELINED(true, 2); break;
+      case 3: VS_LAUNCH_PIPELINED(true, 3); break;
+      case 4: VS_LAUNCH_PIPELINED(false, 0); break;
+      case 5: VS_LAUNCH_PIPELINED(false, 1); break;
+      case 6: VS_LAUNCH_PIPELINED(false, 2); break;
+      default: VS_LAUNCH_PIPELINED(false, 3); break;
+    }
+#undef VS_LAUNCH_PIPELINED
   } else {
     fused_partials_kernel<<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar,
                                           targets, row_map, row_count, nv, nt, gv, part, zy_raw);

@@ -78,4 +78,11 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
               void* workspace, void* stream);
 size_t l1_workspace_bytes(int64_t rows, int64_t V);
 
+// Timing bracket around the sweep kernel(s) of each call (diagnostics).
+// timer_enable returns 0 or 1 (event creation failed); timer_read_ms returns
+// 0, 1 (HIP error) or 2 (no bracket recorded since enabling).
+int timer_enable(int on);
+void timer_mark(int stop, void* stream);
+int timer_read_ms(float* ms);
+
 }  // namespace vs

@@ -101,15 +101,17 @@ size_t support_ws_bytes(const vs_source* s) {
 // Full-vocabulary sweep + merge over `rows` slots (row_map/row_count nullable).
 int run_full(const vs_source* s, const FullWs& w, int64_t rows, const int32_t* row_map, const int32_t* row_count,
              const int64_t* targets, int64_t vocab_chunk, float* lse, float* logprob, float* entropy,
-             uint8_t* status, int mode, void* stream) {
+             uint8_t* status, int mode, bool timed, void* stream) {
   vs::LogitsArg lg{s->logits, s->logits_dtype, s->ld_logits};
   int rc;
   if (s->kind == VS_SRC_LOGITS) {
     const int64_t nt = n_logits_tiles(s->V);
     int64_t tpc = vocab_chunk / vs::kLogitsTile;
     if (tpc < 1) tpc = 1;
+    if (timed) vs::timer_mark(0, stream);
     rc = vs::launch_logits_partials(lg, rows, s->V, s->temperature, s->temperature_scalar, row_map, row_count,
                                     w.partials, stream);
+    if (timed) vs::timer_mark(1, stream);
     if (rc) return VS_E_DEVICE;
     rc = vs::launch_merge(w.partials, int(nt), int(tpc), rows, row_map, row_count, s->temperature,
                           s->temperature_scalar, targets, s->V, lg, nullptr, lse, logprob, entropy, status, mode,
@@ -128,9 +130,11 @@ int run_full(const vs_source* s, const FullWs& w, int64_t rows, const int32_t* r
   const int64_t nt = n_fused_tiles(s->V);
   int64_t tpc = vocab_chunk / vs::kFusedTileV;
   if (tpc < 1) tpc = 1;
+  if (timed) vs::timer_mark(0, stream);
   rc = vs::launch_fused_partials(hid, ldh, static_cast<const uint16_t*>(s->weight), s->ld_weight, rows, s->H, s->V,
                                  s->temperature, s->temperature_scalar, targets, row_map, row_count, w.partials,
                                  w.zy, stream);
+  if (timed) vs::timer_mark(1, stream);
   if (rc) return VS_E_DEVICE;
   rc = vs::launch_merge(w.partials, int(nt), int(tpc), rows, row_map, row_count, s->temperature,
                         s->temperature_scalar, targets, s->V, lg, w.zy, lse, logprob, entropy, status, mode, stream);
@@ -181,7 +185,7 @@ int vs_score_full(const vs_source* src, const int64_t* target_ids, int64_t vocab
   Carver c(workspace);
   FullWs w = carve_full(c, src, src->T);
   return run_full(src, w, src->T, nullptr, nullptr, target_ids, vocab_chunk, lse, logprob, entropy, row_status,
-                  vs::kMergeFull, stream);
+                  vs::kMergeFull, true, stream);
 }
 
 int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64_t width, int64_t ld_ids,
@@ -202,6 +206,7 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
   int32_t* fb_count = static_cast<int32_t*>(c.take(4));
   FullWs w = carve_full(c, src, src->T);
   if (full_vocab_fallback && vs::launch_zero_i32(fb_count, 1, stream)) return VS_E_DEVICE;
+  vs::timer_mark(0, stream);
   if (src->kind == VS_SRC_LOGITS) {
     vs::LogitsArg lg{src->logits, src->logits_dtype, src->ld_logits};
     rc = vs::launch_support_logits(lg, src->T, src->V, src->temperature, src->temperature_scalar, support_ids,
@@ -213,11 +218,12 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
                                   src->temperature, src->temperature_scalar, support_ids, width, ld_ids, target_ids,
                                   full_vocab_fallback, logprob, entropy, row_status, fb_list, fb_count, stream);
   }
+  vs::timer_mark(1, stream);
   if (rc) return VS_E_DEVICE;
   if (!full_vocab_fallback) return VS_OK;
   // synthetic-EOS rows: full-vocabulary logprob of the listed rows
   return run_full(src, w, src->T, fb_list, fb_count, target_ids, vocab_chunk, nullptr, logprob, entropy,
-                  row_status, vs::kMergeFallback, stream);
+                  row_status, vs::kMergeFallback, false, stream);
 }
 
 int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float* top_p, const float* min_p,
@@ -234,10 +240,12 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
   if (support_ids_out && support_ids_cap > vs::kTransformsMaxCap) return VS_E_UNSUPPORTED;
   rc = check_workspace(workspace, workspace_bytes, round_up(vs::transforms_workspace_bytes(src->T)));
   if (rc) return rc;
+  vs::timer_mark(0, stream);
   rc = vs::launch_transforms(static_cast<const uint16_t*>(src->logits), src->ld_logits, src->T, src->V,
                              src->temperature, src->temperature_scalar, top_k, top_p, min_p, target_ids, logprob,
                              entropy, row_status, support_len, threshold_logit, threshold_ties, support_ids_out,
                              support_ids_cap, full_lse, static_cast<uint8_t*>(workspace), stream);
+  vs::timer_mark(1, stream);
   if (rc == -1) return VS_E_UNSUPPORTED;
   return rc ? VS_E_DEVICE : VS_OK;
 }
@@ -251,10 +259,20 @@ int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t 
   if (!aligned(target_logits, esize(dtype)) || !aligned(draft_logits, esize(dtype))) return VS_E_ALIGN;
   int rc = check_workspace(workspace, workspace_bytes, round_up(vs::l1_workspace_bytes(T, V)));
   if (rc) return rc;
+  vs::timer_mark(0, stream);
   rc = vs::launch_l1(vs::LogitsArg{target_logits, dtype, ld_target}, vs::LogitsArg{draft_logits, dtype, ld_draft}, T,
                      V, l1, accept_rate, workspace, stream);
+  vs::timer_mark(1, stream);
   if (rc == -1) return VS_E_UNSUPPORTED;
   return rc ? VS_E_DEVICE : VS_OK;
+}
+
+int vs_sweep_timer(int32_t enable) { return vs::timer_enable(enable != 0) ? VS_E_DEVICE : VS_OK; }
+
+int vs_sweep_timer_ms(float* ms) {
+  if (!ms) return VS_E_NULL;
+  const int rc = vs::timer_read_ms(ms);
+  return rc == 0 ? VS_OK : rc == 2 ? VS_E_PARAM : VS_E_DEVICE;
 }
 
 }  // extern "C"

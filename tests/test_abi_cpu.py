@@ -68,6 +68,15 @@ def test_status_strings_and_version(lib):
     assert lib.vs_version() >= 10000
 
 
+def test_sweep_timer_error_codes_without_a_bracket(lib):
+    # no HIP call is made on these paths: disabling, and reading before any bracket was recorded
+    assert lib.vs_sweep_timer(0) == 0
+    assert lib.vs_sweep_timer_ms(None) == 1  # VS_E_NULL
+    ms = ctypes.c_float(-1.0)
+    assert lib.vs_sweep_timer_ms(ctypes.byref(ms)) == 5  # VS_E_PARAM: nothing recorded
+    assert ms.value == -1.0
+
+
 FAKE = 0x10000000  # never dereferenced: every call below fails validation first
 
 

@@ -50,6 +50,27 @@ def test_tiny_workload_fused_with_fallback(vsa):
     _cmp(got2, ref2)
 
 
+@pytest.mark.parametrize("H", [96, 160, 224])
+def test_fused_fallback_rows_gathered_sweep(vsa, H):
+    say(f"support: fused source, H={H} (K not a multiple of 128), a third of the rows empty -> full-vocab fallback")
+    rng = np.random.default_rng(H)
+    T, V, W = 600, 3000, 8
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.2).astype(np.float32))
+    ids = np.argsort(rng.random((T, V)), axis=1)[:, :W].astype(np.int64)  # distinct ids per row
+    ids[rng.random((T, W)) < 0.3] = -1
+    empty = rng.random(T) < 0.33
+    ids[empty] = -1
+    y = rng.integers(0, V, T).astype(np.int64)
+    fb = empty.astype(np.uint8)
+    got = vsa.score_support_ids(to_dev(y), to_dev(ids), hidden=bf16_tensor(hb), weight=bf16_tensor(wb),
+                                fallback=to_dev(fb))
+    x = oracle.logits_from_hidden(hb, "bf16", wb)
+    ref = oracle.score_support(lambda t, cols: x[t, cols], V, ids, 1.0, y, fb)
+    assert ((ref["status"] & oracle.ST_FULL_VOCAB_FALLBACK) != 0).sum() == empty.sum()
+    _cmp(got, ref)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_logits_gather_matches_oracle(vsa, dtype):
     say(f"support over materialised logits: dtype={dtype}")
