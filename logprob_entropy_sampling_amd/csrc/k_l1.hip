@@ -16,14 +16,15 @@ namespace vs {
 
 namespace {
 
-constexpr int NT = 1024;
-constexpr int NW = NT / 64;
 
 struct Pair {
   float mx, sx, my, sy;
 };
 
-// online (max, sum 2^(u - max)) update with a block of values
+// Online (max, sum 2^((x - max) log2 e)) update with a block of raw logits.
+// m is kept in raw units (the max is taken on the logits themselves); each
+// term is one FMA and one v_exp_f32.  No floor is needed: there is no
+// e * d term, exp2(-inf) = 0, and a NaN poisons s as it should.
 __device__ __forceinline__ void online(float& m, float& s, const float* v, int n) {
   float bm = v[0];
   for (int i = 1; i < n; ++i) bm = fmaxf(bm, v[i]);
@@ -33,45 +34,52 @@ __device__ __forceinline__ void online(float& m, float& s, const float* v, int n
       if (v[i] != v[i]) s = __builtin_nanf("");
     return;
   }
-  s *= exp2_hw(floor_d(m - nm));
-  for (int i = 0; i < n; ++i) s += exp2_hw(floor_d(v[i] - nm));
+  const float c = nm * kLog2e;
+  s *= exp2_hw(m * kLog2e - c);  // exactly 1 when the max did not move; 0 from -inf
+  for (int i = 0; i < n; ++i) s += exp2_hw(__builtin_fmaf(v[i], kLog2e, -c));
   m = nm;
 }
 
-// values of element chunk q (VEC elements) of a row, in base-2 units (x * log2 e)
+// raw values of element chunk q (VEC elements) of a row
 template <int DT>
 __device__ __forceinline__ void load_chunk(const void* row, int64_t q, float* v) {
   if (DT == VS_BF16) {
     const uint4 w = reinterpret_cast<const uint4*>(row)[q];
-    v[0] = bf16_lo(w.x) * kLog2e;
-    v[1] = bf16_hi(w.x) * kLog2e;
-    v[2] = bf16_lo(w.y) * kLog2e;
-    v[3] = bf16_hi(w.y) * kLog2e;
-    v[4] = bf16_lo(w.z) * kLog2e;
-    v[5] = bf16_hi(w.z) * kLog2e;
-    v[6] = bf16_lo(w.w) * kLog2e;
-    v[7] = bf16_hi(w.w) * kLog2e;
+    v[0] = bf16_lo(w.x);
+    v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y);
+    v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z);
+    v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w);
+    v[7] = bf16_hi(w.w);
   } else {
     const float4 w = reinterpret_cast<const float4*>(row)[q];
-    v[0] = w.x * kLog2e;
-    v[1] = w.y * kLog2e;
-    v[2] = w.z * kLog2e;
-    v[3] = w.w * kLog2e;
+    v[0] = w.x;
+    v[1] = w.y;
+    v[2] = w.z;
+    v[3] = w.w;
   }
 }
 
 template <int DT>
 __device__ __forceinline__ float load_one(const void* row, int64_t i) {
-  return (DT == VS_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(row)[i]) : static_cast<const float*>(row)[i]) *
-         kLog2e;
+  return DT == VS_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(row)[i]) : static_cast<const float*>(row)[i];
 }
 
-template <int DT>
+// |p - q| of one element pair, the normalisers folded into the exponents
+__device__ __forceinline__ float absdiff(float a, float b, float lx, float ly) {
+  return fabsf(exp2_hw(__builtin_fmaf(a, kLog2e, -lx)) - exp2_hw(__builtin_fmaf(b, kLog2e, -ly)));
+}
+
+// NT threads per row; U vector chunks per thread in flight per pass step.
+template <int DT, int NT, int U>
 __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, int64_t ld_t, const void* __restrict__ dft,
                                                 int64_t ld_d, int64_t V, float* __restrict__ l1,
                                                 float* __restrict__ accept) {
   constexpr int VEC = DT == VS_BF16 ? 8 : 4;
   constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int NW = NT / 64;
   __shared__ float red[NW][4];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -83,7 +91,21 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
 
   // ---- pass 1: online max / sum-exp of both rows ----
   float mx = kNegInf, sx = 0.0f, my = kNegInf, sy = 0.0f;
-  for (int64_t q = tid; q < nvec; q += NT) {
+  int64_t q = tid;
+  for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+    float a[U][VEC], b[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_chunk<DT>(trow, q + u * NT, a[u]);
+      load_chunk<DT>(drow, q + u * NT, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      online(mx, sx, a[u], VEC);
+      online(my, sy, b[u], VEC);
+    }
+  }
+  for (; q < nvec; q += NT) {
     float a[VEC], b[VEC];
     load_chunk<DT>(trow, q, a);
     load_chunk<DT>(drow, q, b);
@@ -95,9 +117,10 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
     online(mx, sx, &a, 1);
     online(my, sy, &b, 1);
   }
-  // block merge (fixed tree): wave tree, then wave 0 over the NW wave states
-  Part px = wave_merge_to_lane0(Part{mx, sx, 0.0f});
-  Part py = wave_merge_to_lane0(Part{my, sy, 0.0f});
+  // block merge (fixed tree): wave tree, then wave 0 over the NW wave states;
+  // the merge works in base-2 units
+  Part px = wave_merge_to_lane0(Part{mx * kLog2e, sx, 0.0f});
+  Part py = wave_merge_to_lane0(Part{my * kLog2e, sy, 0.0f});
   if ((tid & 63) == 0) {
     red[tid >> 6][0] = px.m;
     red[tid >> 6][1] = px.s;
@@ -132,16 +155,29 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
 
   // ---- pass 2: sum |p - q| ----
   float acc = 0.0f;
-  for (int64_t q = tid; q < nvec; q += NT) {
+  q = tid;
+  for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+    float a[U][VEC], b[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_chunk<DT>(trow, q + u * NT, a[u]);
+      load_chunk<DT>(drow, q + u * NT, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc += absdiff(a[u][i], b[u][i], lx, ly);
+  }
+  for (; q < nvec; q += NT) {
     float a[VEC], b[VEC];
     load_chunk<DT>(trow, q, a);
     load_chunk<DT>(drow, q, b);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc += fabsf(exp2_hw(floor_d(a[i] - lx)) - exp2_hw(floor_d(b[i] - ly)));
+    for (int i = 0; i < VEC; ++i) acc += absdiff(a[i], b[i], lx, ly);
   }
   for (int64_t i = tail0 + tid; i < V; i += NT) {
     const float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
-    acc += fabsf(exp2_hw(floor_d(a - lx)) - exp2_hw(floor_d(b - ly)));
+    acc += absdiff(a, b, lx, ly);
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -166,6 +202,9 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
   }
 }
 
+constexpr int kL1Threads = 1024;
+constexpr int kL1Unroll = 4;
+
 }  // namespace
 
 size_t l1_workspace_bytes(int64_t rows, int64_t V) {
@@ -180,11 +219,11 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
   if (rows <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (target.dtype == VS_BF16) {
-    l1_kernel<VS_BF16><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V, l1,
-                                                                  accept);
+    l1_kernel<VS_BF16, kL1Threads, kL1Unroll><<<dim3(unsigned(rows)), dim3(kL1Threads), 0, s>>>(
+        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept);
   } else {
-    l1_kernel<VS_F32><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V, l1,
-                                                                 accept);
+    l1_kernel<VS_F32, kL1Threads, kL1Unroll><<<dim3(unsigned(rows)), dim3(kL1Threads), 0, s>>>(
+        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept);
   }
   return int(hipGetLastError());
 }

@@ -43,6 +43,7 @@ constexpr int NSEG = 65536 / SEGW;       // 1024
 constexpr int SEG_PER_LANE = NSEG / 64;  // 16
 constexpr int COLLECT_MAX = 4096;
 constexpr uint32_t KEY_NEG_INF = 0x007Fu;
+constexpr int kInFlight = 8;  // 16-byte loads per thread in flight in a streaming pass
 
 struct Smem {
   uint32_t hist[HALF];  // packed 16-bit counters (fast) or one half of 32-bit bins (stream); later candidates
@@ -234,12 +235,12 @@ struct StreamKeys {
     const int nvec = aligned() ? V / 8 : 0;
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
     int q = threadIdx.x;
-    for (; q + 3 * NT < nvec; q += 4 * NT) {
-      uint4 v[4];
+    for (; q + (kInFlight - 1) * NT < nvec; q += kInFlight * NT) {
+      uint4 v[kInFlight];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = pv[q + u * NT];
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * NT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kInFlight; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -263,7 +264,23 @@ struct StreamKeys {
   __device__ __forceinline__ void each(F f) const {
     const int nvec = aligned() ? V / 8 : 0;
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
-    for (int q = threadIdx.x; q < nvec; q += NT) {
+    int q = threadIdx.x;
+    for (; q + (kInFlight - 1) * NT < nvec; q += kInFlight * NT) {
+      uint4 v[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * NT];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const int c0 = 8 * (q + u * NT);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f(key16(w[e] & 0xFFFFu), c0 + 2 * e);
+          f(key16(w[e] >> 16), c0 + 2 * e + 1);
+        }
+      }
+    }
+    for (; q < nvec; q += NT) {
       const uint4 v = pv[q];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -348,6 +365,57 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
   sm.seg_count[seg] = cnt;
   sm.seg_mass[seg] = mass;
   sm.seg_zmass[seg] = zm;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+// xor butterfly: every lane ends with the same, fixed-order sum
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// All segment summaries, keys striped over the lanes of each wave: wave w
+// takes segments w, w + 8, ..., lane l key 64 s + l.  The few dense segments
+// (the keys of the bulk of the logits are contiguous) are spread over all
+// waves instead of sitting in one, and an empty segment costs one ballot.
+// Returns this thread's share of the sum of all counts.
+template <class CountFn>
+__device__ __forceinline__ uint32_t summarize_striped(CountFn count, double tau, double z0, Smem& sm) {
+  static_assert(SEGW == 64, "one key per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t total = 0;
+  for (int s = wave; s < NSEG; s += NWAVE) {
+    const uint32_t key = uint32_t(s * SEGW + lane);
+    const uint32_t c = count(key);
+    total += c;
+    uint32_t cs = 0;
+    double m = 0.0, zm = 0.0;
+    if (__ballot(c != 0)) {
+      if (c) {
+        const double d = double(key_logit(key)) / tau - z0;
+        const double e = exp(d);
+        if (e > 0.0) {
+          m = double(c) * e;
+          zm = double(c) * e * d;
+        }
+      }
+      cs = wave_sum_u32(c);
+      m = wave_sum_f64(m);
+      zm = wave_sum_f64(zm);
+    }
+    if (lane == 0) {
+      sm.seg_count[s] = cs;
+      sm.seg_mass[s] = m;
+      sm.seg_zmass[s] = zm;
+    }
+  }
+  return total;
 }
 
 // Everything after the histogram: cuts, scores, descriptor, dense ids.
@@ -545,13 +613,19 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   uint32_t L_m = Vu;
   if (a.mpf > 0.0f) {
     if (tid == 0) {
+      // bisect on z - z_max >= ln(min_p), then settle the boundary with the
+      // program's own test exp(z - z_max) >= min_p (keys are in logit order,
+      // so both predicates hold on an upper range of keys)
       uint32_t lo = KEY_NEG_INF + 1, hi = kmax;  // weight(kmax) = 1 >= min_p
       const double mp = double(a.mpf);
+      const double lmp = log(mp);
       while (lo < hi) {
         const uint32_t mid = (lo + hi) >> 1;
-        if (key_weight(mid, tau, z0) >= mp) hi = mid;
+        if (double(key_logit(mid)) / tau - z0 >= lmp) hi = mid;
         else lo = mid + 1;
       }
+      while (lo > KEY_NEG_INF + 1 && key_weight(lo - 1, tau, z0) >= mp) --lo;
+      while (lo < kmax && key_weight(lo, tau, z0) < mp) ++lo;
       sm.bu[5] = lo;
     }
     __syncthreads();
@@ -740,22 +814,20 @@ __global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) 
     write_bad(a);
     return;
   }
-  // every counter stayed below 2^16 iff the packed total equals the token count
-  uint32_t part = 0;
-  for (int i = tid; i < HALF; i += NT) part += (sm.hist[i] & 0xFFFFu) + (sm.hist[i] >> 16);
-  if (block_sum_u32(part, sm) != uint32_t(V) + n_pad) {
-    if (tid == 0) handoff[a.row] = 1;
-    return;
-  }
-  if (tid == 0) handoff[a.row] = 0;
   auto count = [&](uint32_t key) -> uint32_t {
     const uint32_t c = (sm.hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
     return key == 0 ? c - n_pad : c;
   };
   const double tau = double(a.tauf);
   const double z0 = double(key_logit(kmax)) / tau;
-  for (int s = tid; s < NSEG; s += NT) summarize_segment(s, count, tau, z0, sm);
-  __syncthreads();
+  const uint32_t part = summarize_striped(count, tau, z0, sm);
+  // every counter stayed below 2^16 iff the counts add up to the token count
+  // (a carry out of a low half, or out of a word, breaks the total)
+  if (block_sum_u32(part, sm) != uint32_t(V)) {
+    if (tid == 0) handoff[a.row] = 1;
+    return;
+  }
+  if (tid == 0) handoff[a.row] = 0;
   finish_row(a, keys, kmax, tau, z0, sm, [](int) {}, count);
 }
 
