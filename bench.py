@@ -213,10 +213,8 @@ def bench_paths(vsa, dev, steps, warmup):
     T, V = c["T"], c["V"]
     lg, y, tau = _bf16(c["logits"], dev), _dev(c["targets"], dev), _dev(c["temperature"], dev)
     ev, sw = _event_times(vsa, lambda: vsa.score_full(y, logits=lg, temperature=tau), steps, warmup, flush)
-    n_tiles = (V + 8191) // 8192
-    sweep = T * V * 2 + T * 4 + T * n_tiles * 16          # logits + tau in, partials out
-    call = sweep + T * n_tiles * 16 + T * (8 + 3 * 4 + 1)  # + partials back in, targets in, 3 floats + status out
-    res["logits_full"] = _path_entry(T, ev, sw, call, sweep, V=V)
+    byts = T * V * 2 + T * (4 + 8) + T * (3 * 4 + 1)  # logits, tau, targets in; lse, logprob, entropy, status out
+    res["logits_full"] = _path_entry(T, ev, sw, byts, byts, V=V)
     del lg
 
     # recorded support through selected projections: T=2048, H=7168, V=129,280, width 64

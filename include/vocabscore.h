@@ -119,7 +119,9 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width);
  * merged in a fixed order (tiles ascending inside each vocab_chunk-wide
  * chunk, chunks combined by a fixed tree), so results are bitwise
  * reproducible.  vocab_chunk (> 0) is rounded down to a whole number of
- * tiles (at least one); it changes only rounding.
+ * tiles (at least one); it changes only rounding.  A logits source is read
+ * once by one workgroup per row, whose per-thread states are merged by a
+ * fixed tree; vocab_chunk does not apply to it and it needs no workspace.
  *   target_ids  [T] int64, y_t in [0, V) else BAD_INPUT.
  *   lse, entropy, row_status nullable; logprob required.
  * Row status: BAD_INPUT if tau is invalid, y_t is out of range, or the row's

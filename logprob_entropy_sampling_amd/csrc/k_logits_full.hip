@@ -1,12 +1,13 @@
 // Full-vocabulary scoring over materialised logits, and the fixed-order merge
-// shared with the fused projection.
+// of the fused projection's tile partials.
 //
-// Logits-input sweep: one workgroup per (row, 8192-column tile), 16-byte
-// coalesced loads, each thread folds its 32 columns into an online state in
-// registers, the workgroup merges its 256 states with a fixed tree and writes
-// one partial.  One HBM pass over the logits; no vocabulary-sized temporary
-// (DeepSpec PR #87, Purpose: the vocabulary-sized FP32 softmax results are
-// what the page removes; xorl issue #71 section 1: chunked LSE).
+// Logits input: one workgroup per row.  Each thread folds a strided share of
+// the row (16-byte loads, kRowUnroll of them in flight) into an online
+// (max, sum 2^(u-max), sum 2^(u-max)(u-max)) state in registers; the 512
+// states are merged by a fixed tree and the row's outputs are written
+// directly.  One HBM pass over the logits, no vocabulary-sized temporary and
+// no partials (DeepSpec PR #87, Purpose: no vocabulary-sized softmax
+// results; xorl issue #71 section 1: the log-sum-exp of the row).
 #include "common.h"
 #include "launch.h"
 #include "../../include/vocabscore.h"
@@ -15,7 +16,8 @@ namespace vs {
 
 namespace {
 
-constexpr int kThreads3 = 256;
+constexpr int kRowThreads = 512;
+constexpr int kRowUnroll = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -29,136 +31,167 @@ __device__ __forceinline__ float4 stream_load(const float4* p) {
   f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
 }
-constexpr int kPerThread3 = kLogitsTile / kThreads3;  // 32 columns per thread
 
-// One row tile of bf16 logits.  Vector path when the row base is 16-byte aligned.
-__device__ __forceinline__ Part tile_state_bf16(const uint16_t* row, int64_t c0, int64_t c1, float c) {
-  float vals[kPerThread3];
-  const int tid = threadIdx.x;
-  const bool aligned = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  if (aligned && c1 - c0 == kLogitsTile) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + c0);
-#pragma unroll
-    for (int j = 0; j < kPerThread3 / 8; ++j) {
-      uint4 w = stream_load(p + j * kThreads3 + tid);
-      vals[8 * j + 0] = bf16_lo(w.x);
-      vals[8 * j + 1] = bf16_hi(w.x);
-      vals[8 * j + 2] = bf16_lo(w.y);
-      vals[8 * j + 3] = bf16_hi(w.y);
-      vals[8 * j + 4] = bf16_lo(w.z);
-      vals[8 * j + 5] = bf16_hi(w.z);
-      vals[8 * j + 6] = bf16_lo(w.w);
-      vals[8 * j + 7] = bf16_hi(w.w);
+// Fold n raw logits into the online state (base-2 units, u = x * c).  The
+// exponent of each term is one FMA; the floor is applied only inside the
+// entropy term, so a -inf logit adds exactly 0 and a NaN poisons s.
+__device__ __forceinline__ void fold_values(Part& p, const float* v, int n, float c) {
+  float bm = v[0];
+  for (int i = 1; i < n; ++i) bm = fmaxf(bm, v[i]);
+  const float nm = fmaxf(p.m, bm * c);
+  if (nm == kNegInf) {  // only -inf so far, or a NaN that fmaxf dropped
+    for (int i = 0; i < n; ++i)
+      if (v[i] != v[i]) p.s = __builtin_nanf("");
+    return;
+  }
+  if (nm > p.m) {  // move the reference to the new max, as merge() would
+    if (!(p.m == kNegInf && p.s == 0.0f)) {
+      const float d = p.m - nm;
+      const float f = exp2_hw(d);
+      p.a = f * __builtin_fmaf(p.s, d, p.a);
+      p.s *= f;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread3 / 8; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int64_t col = c0 + int64_t(j * kThreads3 + tid) * 8 + e;
-        vals[8 * j + e] = col < c1 ? bf16_to_f32(row[col]) : kNegInf;
-      }
-    }
+    p.m = nm;
   }
-  float mx = vals[0];
-#pragma unroll
-  for (int i = 1; i < kPerThread3; ++i) mx = fmaxf(mx, vals[i]);
-  Part p;
-  p.m = mx * c;
-  p.s = 0.0f;
-  p.a = 0.0f;
-  if (mx == kNegInf) {
-    p.s = empty_block_s<kPerThread3>(vals);
-    return p;
+  for (int i = 0; i < n; ++i) {
+    const float d = __builtin_fmaf(v[i], c, -nm);
+    const float e = exp2_hw(d);
+    p.s += e;
+    p.a = __builtin_fmaf(e, fmaxf(d, kDFloor), p.a);
   }
-#pragma unroll
-  for (int i = 0; i < kPerThread3; ++i) fold(__builtin_fmaf(vals[i], c, -p.m), p.s, p.a);
-  return p;
-}
-
-__device__ __forceinline__ Part tile_state_f32(const float* row, int64_t c0, int64_t c1, float c) {
-  float vals[kPerThread3];
-  const int tid = threadIdx.x;
-  const bool aligned = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  if (aligned && c1 - c0 == kLogitsTile) {
-    const float4* p = reinterpret_cast<const float4*>(row + c0);
-#pragma unroll
-    for (int j = 0; j < kPerThread3 / 4; ++j) {
-      float4 w = stream_load(p + j * kThreads3 + tid);
-      vals[4 * j + 0] = w.x;
-      vals[4 * j + 1] = w.y;
-      vals[4 * j + 2] = w.z;
-      vals[4 * j + 3] = w.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread3 / 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int64_t col = c0 + int64_t(j * kThreads3 + tid) * 4 + e;
-        vals[4 * j + e] = col < c1 ? row[col] : kNegInf;
-      }
-    }
-  }
-  float mx = vals[0];
-#pragma unroll
-  for (int i = 1; i < kPerThread3; ++i) mx = fmaxf(mx, vals[i]);
-  Part p;
-  p.m = mx * c;
-  p.s = 0.0f;
-  p.a = 0.0f;
-  if (mx == kNegInf) {
-    p.s = empty_block_s<kPerThread3>(vals);
-    return p;
-  }
-#pragma unroll
-  for (int i = 0; i < kPerThread3; ++i) fold(__builtin_fmaf(vals[i], c, -p.m), p.s, p.a);
-  return p;
-}
-
-// Workgroup merge of the 4 wave states (fixed order), result in thread 0.
-__device__ __forceinline__ Part block_merge_256(Part p) {
-  __shared__ float sm[4][3];
-  p = wave_merge_to_lane0(p);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sm[w][0] = p.m;
-    sm[w][1] = p.s;
-    sm[w][2] = p.a;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    Part q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = Part{sm[i][0], sm[i][1], sm[i][2]};
-    p = merge(merge(q[0], q[1]), merge(q[2], q[3]));
-  }
-  return p;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads3) void logits_partials_kernel(const void* __restrict__ logits, int64_t ld,
-                                                                    int64_t V, int n_tiles,
-                                                                    const float* __restrict__ temp, float temp_scalar,
-                                                                    const int32_t* __restrict__ row_map,
-                                                                    const int32_t* __restrict__ row_count,
-                                                                    float4* __restrict__ partials) {
-  const int64_t slot = int64_t(blockIdx.x) / n_tiles;
-  const int tile = int(int64_t(blockIdx.x) - slot * n_tiles);
+__device__ __forceinline__ void unpack(const uint4& w, float* v) {
+  v[0] = bf16_lo(w.x);
+  v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y);
+  v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z);
+  v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w);
+  v[7] = bf16_hi(w.w);
+}
+
+// This thread's share of one row: vectors q = tid, tid + NT, ... then a scalar tail.
+template <int DT>
+__device__ __forceinline__ Part row_state(const void* rowp, int64_t V, float c) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  Part p{kNegInf, 0.0f, 0.0f};
+  const int tid = threadIdx.x;
+  const bool aligned = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
+  const int64_t nvec = aligned ? V / VEC : 0;
+  int64_t q = tid;
+  float v[VEC];
+  if (DT == VS_BF16) {
+    const uint4* pv = static_cast<const uint4*>(rowp);
+    for (; q + int64_t(kRowUnroll - 1) * kRowThreads < nvec; q += int64_t(kRowUnroll) * kRowThreads) {
+      uint4 w[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) w[u] = stream_load(pv + q + u * kRowThreads);
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        unpack<DT>(w[u], v);
+        fold_values(p, v, VEC, c);
+      }
+    }
+    for (; q < nvec; q += kRowThreads) {
+      unpack<DT>(stream_load(pv + q), v);
+      fold_values(p, v, VEC, c);
+    }
+    for (int64_t i = nvec * VEC + tid; i < V; i += kRowThreads) {
+      v[0] = bf16_to_f32(static_cast<const uint16_t*>(rowp)[i]);
+      fold_values(p, v, 1, c);
+    }
+  } else {
+    const float4* pv = static_cast<const float4*>(rowp);
+    for (; q + int64_t(kRowUnroll - 1) * kRowThreads < nvec; q += int64_t(kRowUnroll) * kRowThreads) {
+      float4 w[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) w[u] = stream_load(pv + q + u * kRowThreads);
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        v[0] = w[u].x;
+        v[1] = w[u].y;
+        v[2] = w[u].z;
+        v[3] = w[u].w;
+        fold_values(p, v, VEC, c);
+      }
+    }
+    for (; q < nvec; q += kRowThreads) {
+      const float4 w = stream_load(pv + q);
+      v[0] = w.x;
+      v[1] = w.y;
+      v[2] = w.z;
+      v[3] = w.w;
+      fold_values(p, v, VEC, c);
+    }
+    for (int64_t i = nvec * VEC + tid; i < V; i += kRowThreads) {
+      v[0] = static_cast<const float*>(rowp)[i];
+      fold_values(p, v, 1, c);
+    }
+  }
+  return p;
+}
+
+// Row outputs from the row's merged base-2 state (shared by both input kinds).
+__device__ __forceinline__ void write_row(Part acc, int64_t row, float c, bool tau_valid, int64_t y, int64_t V,
+                                          float zy_raw, bool have_zy, float* lse, float* logprob, float* entropy,
+                                          uint8_t* status, int mode) {
+  const bool ok_in = tau_valid && y >= 0 && y < V;
+  const float l2s = log2_hw(acc.s);
+  const float lse2 = acc.m + l2s;  // base-2 LSE
+  const bool ok = ok_in && (lse2 > -__builtin_inff()) && (lse2 < __builtin_inff()) && have_zy;
+  const float zy = ok ? zy_raw * c : 0.0f;
+  const float nan = __builtin_nanf("");
+  const float lp = ok ? kLn2 * (zy - lse2) : nan;
+  if (mode == kMergeFull) {
+    if (lse) lse[row] = ok ? kLn2 * lse2 : nan;
+    logprob[row] = lp;
+    if (entropy) entropy[row] = ok ? kLn2 * (l2s - acc.a / acc.s) : nan;
+    if (status) status[row] = ok ? 0 : kRowBad;
+  } else {
+    logprob[row] = lp;
+    if (entropy) entropy[row] = ok ? 0.0f : nan;
+    if (status) status[row] = ok ? (kRowEmpty | kRowFallback) : kRowBad;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRowThreads) void logits_row_kernel(
+    const void* __restrict__ logits, int64_t ld, int64_t V, const float* __restrict__ temp, float temp_scalar,
+    const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count, const int64_t* __restrict__ targets,
+    float* __restrict__ lse, float* __restrict__ logprob, float* __restrict__ entropy, uint8_t* __restrict__ status,
+    int mode) {
+  constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int NW = kRowThreads / 64;
+  const int64_t slot = blockIdx.x;
   if (row_count && slot >= *row_count) return;
   const int64_t row = row_map ? int64_t(row_map[slot]) : slot;
   const float tau = temp ? temp[row] : temp_scalar;
   const float c = kLog2e / tau;
-  const int64_t c0 = int64_t(tile) * kLogitsTile;
-  const int64_t c1 = c0 + kLogitsTile < V ? c0 + kLogitsTile : V;
-  Part p;
-  if (DT == VS_BF16) {
-    p = tile_state_bf16(static_cast<const uint16_t*>(logits) + row * ld, c0, c1, c);
-  } else {
-    p = tile_state_f32(static_cast<const float*>(logits) + row * ld, c0, c1, c);
+  const char* rowp = static_cast<const char*>(logits) + row * ld * ES;
+  Part p = row_state<DT>(rowp, V, c);
+  // fixed tree: inside each wave, then the wave states in order
+  __shared__ float red[NW][3];
+  p = wave_merge_to_lane0(p);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[w][0] = p.m;
+    red[w][1] = p.s;
+    red[w][2] = p.a;
   }
-  p = block_merge_256(p);
-  if (threadIdx.x == 0) partials[slot * n_tiles + tile] = make_float4(p.m, p.s, p.a, 0.0f);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  Part acc = Part{red[0][0], red[0][1], red[0][2]};
+#pragma unroll
+  for (int i = 1; i < NW; ++i) acc = merge(acc, Part{red[i][0], red[i][1], red[i][2]});
+  const int64_t y = targets[row];
+  const bool yv = y >= 0 && y < V;
+  const float zraw = yv ? (DT == VS_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[y])
+                                         : reinterpret_cast<const float*>(rowp)[y])
+                        : 0.0f;
+  write_row(acc, row, c, tau_ok(tau), y, V, zraw, true, lse, logprob, entropy, status, mode);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,32 +233,18 @@ __global__ __launch_bounds__(256) void merge_kernel(const float4* __restrict__ p
   if (lane != 0) return;
 
   const int64_t y = targets[row];
-  const bool ok_in = tau_ok(tau) && y >= 0 && y < V;
-  const float l2s = log2_hw(acc.s);
-  const float lse2 = acc.m + l2s;  // base-2 LSE
-  const bool ok = ok_in && (lse2 > -__builtin_inff()) && (lse2 < __builtin_inff());
-  float zy = 0.0f;
-  if (ok) {
+  const bool yv = y >= 0 && y < V;
+  float zraw = 0.0f;
+  if (yv) {
     if (zy_raw) {
-      zy = zy_raw[slot] * c;
+      zraw = zy_raw[slot];
     } else if (lg.dtype == VS_BF16) {
-      zy = bf16_to_f32(static_cast<const uint16_t*>(lg.ptr)[row * lg.ld + y]) * c;
+      zraw = bf16_to_f32(static_cast<const uint16_t*>(lg.ptr)[row * lg.ld + y]);
     } else {
-      zy = static_cast<const float*>(lg.ptr)[row * lg.ld + y] * c;
+      zraw = static_cast<const float*>(lg.ptr)[row * lg.ld + y];
     }
   }
-  const float nan = __builtin_nanf("");
-  const float lp = ok ? kLn2 * (zy - lse2) : nan;
-  if (mode == kMergeFull) {
-    if (lse) lse[row] = ok ? kLn2 * lse2 : nan;
-    logprob[row] = lp;
-    if (entropy) entropy[row] = ok ? kLn2 * (l2s - acc.a / acc.s) : nan;
-    if (status) status[row] = ok ? 0 : kRowBad;
-  } else {
-    logprob[row] = lp;
-    if (entropy) entropy[row] = ok ? 0.0f : nan;
-    if (status) status[row] = ok ? (kRowEmpty | kRowFallback) : kRowBad;
-  }
+  write_row(acc, row, c, tau_ok(tau), y, V, zraw, true, lse, logprob, entropy, status, mode);
 }
 
 __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
@@ -235,18 +254,17 @@ __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
 
 }  // namespace
 
-int launch_logits_partials(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
-                           const int32_t* row_map, const int32_t* row_count, void* partials, void* stream) {
-  const int n_tiles = int((V + kLogitsTile - 1) / kLogitsTile);
-  const int64_t blocks = rows * n_tiles;
-  if (blocks <= 0) return 0;
+int launch_logits_rows(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
+                       const int32_t* row_map, const int32_t* row_count, const int64_t* targets, float* lse,
+                       float* logprob, float* entropy, uint8_t* status, int mode, void* stream) {
+  if (rows <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (lg.dtype == VS_BF16) {
-    logits_partials_kernel<VS_BF16><<<dim3(unsigned(blocks)), dim3(kThreads3), 0, s>>>(
-        lg.ptr, lg.ld, V, n_tiles, temp, temp_scalar, row_map, row_count, static_cast<float4*>(partials));
+    logits_row_kernel<VS_BF16><<<dim3(unsigned(rows)), dim3(kRowThreads), 0, s>>>(
+        lg.ptr, lg.ld, V, temp, temp_scalar, row_map, row_count, targets, lse, logprob, entropy, status, mode);
   } else {
-    logits_partials_kernel<VS_F32><<<dim3(unsigned(blocks)), dim3(kThreads3), 0, s>>>(
-        lg.ptr, lg.ld, V, n_tiles, temp, temp_scalar, row_map, row_count, static_cast<float4*>(partials));
+    logits_row_kernel<VS_F32><<<dim3(unsigned(rows)), dim3(kRowThreads), 0, s>>>(
+        lg.ptr, lg.ld, V, temp, temp_scalar, row_map, row_count, targets, lse, logprob, entropy, status, mode);
   }
   return int(hipGetLastError());
 }

@@ -17,13 +17,15 @@ struct LogitsArg {
 };
 
 // Tile widths of the two full-vocabulary sweeps.
-constexpr int kLogitsTile = 8192;  // columns per workgroup, logits input
 constexpr int kFusedTileV = 256;   // vocabulary rows per MFMA tile, fused input
 constexpr int kFusedTileT = 256;   // token rows per MFMA tile, fused input
 
-// Per-(row, tile) partial state for the logits input: partials[slot * n_tiles + tile].
-int launch_logits_partials(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
-                           const int32_t* row_map, const int32_t* row_count, void* partials, void* stream);
+// Full-vocabulary scoring of materialised logits, one workgroup per row slot
+// (row_map / row_count nullable); writes the row outputs directly (mode as
+// for launch_merge).
+int launch_logits_rows(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
+                       const int32_t* row_map, const int32_t* row_count, const int64_t* targets, float* lse,
+                       float* logprob, float* entropy, uint8_t* status, int mode, void* stream);
 
 // bf16 MFMA projection of hidden x weight^T with the per-tile reduction fused
 // in; writes partials[slot * n_vtiles + vtile] and zy_raw[slot] (the raw

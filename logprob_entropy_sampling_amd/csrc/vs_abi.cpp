@@ -36,7 +36,6 @@ struct Carver {
   }
 };
 
-int64_t n_logits_tiles(int64_t V) { return (V + vs::kLogitsTile - 1) / vs::kLogitsTile; }
 int64_t n_fused_tiles(int64_t V) { return (V + vs::kFusedTileV - 1) / vs::kFusedTileV; }
 
 int check_source(const vs_source* s) {
@@ -76,7 +75,7 @@ struct FullWs {
 };
 
 size_t full_ws_bytes(const vs_source* s, int64_t rows) {
-  if (s->kind == VS_SRC_LOGITS) return round_up(size_t(rows) * size_t(n_logits_tiles(s->V)) * 16);
+  if (s->kind == VS_SRC_LOGITS) return 0;  // the row kernel needs no workspace
   size_t b = round_up(size_t(rows) * size_t(n_fused_tiles(s->V)) * 16) + round_up(size_t(rows) * 4);
   if (s->hidden_dtype == VS_F32) b += round_up(size_t(s->T) * size_t(s->H) * 2);
   return b;
@@ -84,10 +83,7 @@ size_t full_ws_bytes(const vs_source* s, int64_t rows) {
 
 FullWs carve_full(Carver& c, const vs_source* s, int64_t rows) {
   FullWs w;
-  if (s->kind == VS_SRC_LOGITS) {
-    w.partials = c.take(size_t(rows) * size_t(n_logits_tiles(s->V)) * 16);
-    return w;
-  }
+  if (s->kind == VS_SRC_LOGITS) return w;
   w.partials = c.take(size_t(rows) * size_t(n_fused_tiles(s->V)) * 16);
   w.zy = static_cast<float*>(c.take(size_t(rows) * 4));
   if (s->hidden_dtype == VS_F32) w.hidden_bf16 = static_cast<uint16_t*>(c.take(size_t(s->T) * size_t(s->H) * 2));
@@ -104,18 +100,13 @@ int run_full(const vs_source* s, const FullWs& w, int64_t rows, const int32_t* r
              uint8_t* status, int mode, bool timed, void* stream) {
   vs::LogitsArg lg{s->logits, s->logits_dtype, s->ld_logits};
   int rc;
-  if (s->kind == VS_SRC_LOGITS) {
-    const int64_t nt = n_logits_tiles(s->V);
-    int64_t tpc = vocab_chunk / vs::kLogitsTile;
-    if (tpc < 1) tpc = 1;
+  if (s->kind == VS_SRC_LOGITS) {  // one pass, one kernel, no partials
+    (void)w;
+    (void)vocab_chunk;
     if (timed) vs::timer_mark(0, stream);
-    rc = vs::launch_logits_partials(lg, rows, s->V, s->temperature, s->temperature_scalar, row_map, row_count,
-                                    w.partials, stream);
+    rc = vs::launch_logits_rows(lg, rows, s->V, s->temperature, s->temperature_scalar, row_map, row_count, targets,
+                                lse, logprob, entropy, status, mode, stream);
     if (timed) vs::timer_mark(1, stream);
-    if (rc) return VS_E_DEVICE;
-    rc = vs::launch_merge(w.partials, int(nt), int(tpc), rows, row_map, row_count, s->temperature,
-                          s->temperature_scalar, targets, s->V, lg, nullptr, lse, logprob, entropy, status, mode,
-                          stream);
     return rc ? VS_E_DEVICE : VS_OK;
   }
   const uint16_t* hid = static_cast<const uint16_t*>(s->hidden);

@@ -123,12 +123,12 @@ def test_score_full_validation(lib):
     assert _full(lib, _src(temperature_scalar=0.0)) == C.VS_E_PARAM
     assert _full(lib, _src(temperature_scalar=float("nan"))) == C.VS_E_PARAM
     assert _full(lib, _src(), chunk=0) == C.VS_E_PARAM
-    assert _full(lib, _src(), ws=None) == C.VS_E_WORKSPACE
-    assert _full(lib, _src(), ws=FAKE + 16) == C.VS_E_WORKSPACE
-    need = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(_src()), 0)
+    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT)  # (a logits source needs no workspace at all)
+    assert _full(lib, _src(**hw), ws=None) == C.VS_E_WORKSPACE
+    assert _full(lib, _src(**hw), ws=FAKE + 16) == C.VS_E_WORKSPACE
+    need = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(_src(**hw)), 0)
     assert need > 0
-    assert _full(lib, _src(), nws=need - 1) == C.VS_E_WORKSPACE
-    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT)
+    assert _full(lib, _src(**hw), nws=need - 1) == C.VS_E_WORKSPACE
     assert _full(lib, _src(hidden=None, **hw)) == C.VS_E_NULL
     assert _full(lib, _src(weight_dtype=C.VS_F32, **hw)) == C.VS_E_DTYPE
     assert _full(lib, _src(H=60, ld_hidden=64, ld_weight=64, **hw)) == C.VS_E_SHAPE
@@ -180,9 +180,11 @@ def test_l1_validation(lib):
 
 def test_workspace_sizes_scale(lib):
     from logprob_entropy_sampling_amd import _capi as C
-    a = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(_src(T=100)), 0)
-    b = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(_src(T=200)), 0)
-    assert b > a > 0
+    # a logits source is scored one row per workgroup with no partials
+    assert lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(_src(T=100)), 0) == 0
+    a = lib.vs_workspace_size(C.VS_OP_SCORE_SUPPORT, ctypes.byref(_src(T=100)), 8)
+    b = lib.vs_workspace_size(C.VS_OP_SCORE_SUPPORT, ctypes.byref(_src(T=200)), 8)
+    assert b > a > 0  # the fallback row list
     hw = _src(kind=C.VS_SRC_HIDDEN_WEIGHT, T=4096, H=4096, V=151936, ld_hidden=4096, ld_weight=4096)
     n = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(hw), 0)
     assert n >= 4096 * 594 * 16  # one 16-byte partial per (row, 256-wide vocabulary tile)
