@@ -253,15 +253,23 @@ def bench_paths(vsa, dev, steps, warmup):
 def copy_probe(dev, mib, steps):
     """A plain elementwise copy (out = in * 1, fp32) of `mib` MiB, run `steps`
     times: a kernel of known traffic (mib MiB read, mib MiB written) against
-    which the HBM byte counters are scaled."""
+    which the HBM byte counters are scaled.  Also reports the copy's own
+    read+write bandwidth, the achievable-bandwidth context for the HBM paths."""
     import torch
     n = (mib << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
+    ts = []
     for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         torch.mul(src, 1.0, out=dst)
-    torch.cuda.synchronize()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
     del src, dst
+    best = min(ts)
+    return {"mib": mib, "ms_best": round(best, 4), "read_plus_write_GBs": round(2 * (mib << 20) / (best * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -282,9 +290,10 @@ def main():
     import logprob_entropy_sampling_amd as vsa
     vsa.lib()
     dev = torch.device("cuda:0")
+    probe = None
     if args.copy_probe:
         print(f"bench: copy probe {args.copy_probe} MiB x {args.steps}", file=sys.stderr, flush=True)
-        copy_probe(dev, args.copy_probe, args.steps)
+        probe = copy_probe(dev, args.copy_probe, args.steps)
     print("bench: fused_full T=4096 H=4096 V=151936", file=sys.stderr, flush=True)
     c, fused = bench_fused(vsa, dev, args.steps, args.warmup)
     out = {
@@ -309,6 +318,8 @@ def main():
     if args.paths == "all":
         print("bench: secondary paths", file=sys.stderr, flush=True)
         out["paths"] = bench_paths(vsa, dev, max(5, min(args.steps, 20)), 2)
+    if probe is not None:
+        out["copy_probe"] = probe
     if args.cpu_baseline == "on":
         print("bench: cpu oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(c)
