@@ -35,15 +35,17 @@ namespace vs {
 
 namespace {
 
-constexpr int NT = 512;
-constexpr int NWAVE = NT / 64;
+constexpr int NT = 512;          // threads of the register-resident kernels (row in registers)
+constexpr int NT_STREAM = 1024;  // threads of the streaming kernels (row re-read from memory)
+constexpr int MAX_WAVES = NT_STREAM / 64;
+
 constexpr int HALF = 32768;
 constexpr int SEGW = 64;
 constexpr int NSEG = 65536 / SEGW;       // 1024
 constexpr int SEG_PER_LANE = NSEG / 64;  // 16
 constexpr int COLLECT_MAX = 4096;
 constexpr uint32_t KEY_NEG_INF = 0x007Fu;
-constexpr int kInFlight = 8;  // 16-byte loads per thread in flight in a streaming pass
+constexpr int kInFlight = 4;  // 16-byte loads per thread in flight in a streaming pass (1024 threads)
 
 struct Smem {
   uint32_t hist[HALF];  // packed 16-bit counters (fast) or one half of 32-bit bins (stream); later candidates
@@ -53,7 +55,7 @@ struct Smem {
   uint32_t fine[SEGW];  // 32-bit counts of one segment (stream kernel)
   uint32_t lane_cnt[64], lane_cnt_before[64];
   double lane_mass[64], lane_mass_before[64], lane_zmass[64], lane_zmass_before[64];
-  uint32_t red_u[NWAVE];
+  uint32_t red_u[MAX_WAVES];
   uint32_t bu[8];  // broadcast slots (integers)
   double bd[8];    // broadcast slots (fp64)
   int fine_seg;
@@ -71,6 +73,7 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 }
 __device__ __forceinline__ bool raw_bad(uint32_t h) { return (h & 0x7FFFu) >= 0x7F80u && h != 0xFF80u; }
 
+template <int NW>
 __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -79,9 +82,10 @@ __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
   __syncthreads();
   uint32_t t = 0;
 #pragma unroll
-  for (int i = 0; i < NWAVE; ++i) t += sm.red_u[i];
+  for (int i = 0; i < NW; ++i) t += sm.red_u[i];
   return t;
 }
+template <int NW>
 __device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
@@ -90,10 +94,11 @@ __device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
   __syncthreads();
   uint32_t t = 0;
 #pragma unroll
-  for (int i = 0; i < NWAVE; ++i) t = max(t, sm.red_u[i]);
+  for (int i = 0; i < NW; ++i) t = max(t, sm.red_u[i]);
   return t;
 }
 // Exclusive prefix over threads in thread order; also returns the total.
+template <int NW>
 __device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
   const int lane = threadIdx.x & 63;
   uint32_t incl = v;
@@ -108,7 +113,7 @@ __device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
   uint32_t before = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < NWAVE; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t t = sm.red_u[i];
     if (i < int(threadIdx.x >> 6)) before += t;
     total += t;
@@ -125,6 +130,11 @@ __device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
 template <int NV>
 struct RegKeys {
   uint32_t kw[NV][4];  // two keys per word
+  static constexpr int kThreads = NT;
+  static constexpr bool kTopList = false;  // the row is in registers: a sweep is cheap
+  __device__ __forceinline__ bool listed_from(uint32_t) const { return false; }
+  template <class F>
+  __device__ __forceinline__ void each_listed(F) const {}
 
   // Loads the row, converts it to keys and counts every key into the packed
   // 16-bit counters `hist` (already zeroed); returns bad (NaN or +inf seen)
@@ -218,61 +228,107 @@ struct RegKeys {
 struct StreamKeys {
   const uint16_t* rowp;
   int V;
+  // Filled by load_count: this thread's two best 8-token vectors by their
+  // largest key (vector indices, -1 = none) and the largest key of every token
+  // outside them, so every token with a key above `dropped` is in the listed
+  // vectors.  Tail tokens (past the last whole vector) always count as dropped.
+  uint32_t vkey[2];
+  int vq[2];
+  uint32_t dropped;
+  bool have_top;
+  static constexpr int kThreads = NT_STREAM;
+  static constexpr bool kTopList = true;
   __device__ __forceinline__ void opaque() {}
   __device__ __forceinline__ bool aligned() const { return (reinterpret_cast<uintptr_t>(rowp) & 15) == 0; }
-
-  // One streaming pass: convert and count every key into the packed 16-bit
-  // counters (no padding), returning bad and this thread's max key.
-  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& bad, uint32_t& kmax) const {
-    bad = 0;
-    kmax = 0;
-    auto one = [&](uint32_t h) {
-      bad |= raw_bad(h) ? 1u : 0u;
-      const uint32_t k = key16(h);
-      kmax = max(kmax, k);
-      atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
-    };
-    const int nvec = aligned() ? V / 8 : 0;
+  // branch-free update of the two-vector list with vector q of largest key vmax
+  __device__ __forceinline__ void offer_vector(uint32_t vmax, int q) {
+    const bool in0 = vmax > vkey[0];
+    const bool in1 = vmax > vkey[1];
+    dropped = max(dropped, in1 ? vkey[1] : vmax);  // the vector that leaves (or never enters)
+    const uint32_t k1 = in0 ? vkey[0] : (in1 ? vmax : vkey[1]);
+    const int q1 = in0 ? vq[0] : (in1 ? q : vq[1]);
+    vkey[0] = in0 ? vmax : vkey[0];
+    vq[0] = in0 ? q : vq[0];
+    vkey[1] = k1;
+    vq[1] = q1;
+  }
+  // true when every token of this thread with key >= K is in the listed vectors
+  __device__ __forceinline__ bool listed_from(uint32_t K) const { return have_top && dropped < K; }
+  template <class F>
+  __device__ __forceinline__ void each_listed(F f) const {
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
-    int q = threadIdx.x;
-    for (; q + (kInFlight - 1) * NT < nvec; q += kInFlight * NT) {
-      uint4 v[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * NT];
-#pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          one(w[e] & 0xFFFFu);
-          one(w[e] >> 16);
-        }
-      }
-    }
-    for (; q < nvec; q += NT) {
-      const uint4 v = pv[q];
+    for (int i = 0; i < 2; ++i) {
+      if (vq[i] < 0) continue;
+      const uint4 v = pv[vq[i]];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        one(w[e] & 0xFFFFu);
-        one(w[e] >> 16);
+        f(key16(w[e] & 0xFFFFu), 8 * vq[i] + 2 * e);
+        f(key16(w[e] >> 16), 8 * vq[i] + 2 * e + 1);
       }
     }
-    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += NT) one(rowp[c]);
   }
-  template <class F>
-  __device__ __forceinline__ void each(F f) const {
+  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& bad, uint32_t& kmax) {
+    bad = 0;
+    kmax = 0;
+    vkey[0] = vkey[1] = 0;
+    vq[0] = vq[1] = -1;
+    dropped = 0;
+    have_top = true;
+    auto one = [&](uint32_t h) -> uint32_t {
+      bad |= raw_bad(h) ? 1u : 0u;
+      const uint32_t k = key16(h);
+      atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
+      return k;
+    };
+    constexpr int nt = kThreads;
     const int nvec = aligned() ? V / 8 : 0;
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
     int q = threadIdx.x;
-    for (; q + (kInFlight - 1) * NT < nvec; q += kInFlight * NT) {
+    for (; q + (kInFlight - 1) * nt < nvec; q += kInFlight * nt) {
       uint4 v[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * NT];
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * nt];
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        const int c0 = 8 * (q + u * NT);
+        uint32_t vmax = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vmax = max(vmax, max(one(w[e] & 0xFFFFu), one(w[e] >> 16)));
+        kmax = max(kmax, vmax);
+        offer_vector(vmax, q + u * nt);
+      }
+    }
+    for (; q < nvec; q += nt) {
+      const uint4 v = pv[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t vmax = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vmax = max(vmax, max(one(w[e] & 0xFFFFu), one(w[e] >> 16)));
+      kmax = max(kmax, vmax);
+      offer_vector(vmax, q);
+    }
+    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += nt) {
+      const uint32_t k = one(rowp[c]);
+      kmax = max(kmax, k);
+      dropped = max(dropped, k);
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+    constexpr int nt = kThreads;
+    const int nvec = aligned() ? V / 8 : 0;
+    const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    int q = threadIdx.x;
+    for (; q + (kInFlight - 1) * nt < nvec; q += kInFlight * nt) {
+      uint4 v[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * nt];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const int c0 = 8 * (q + u * nt);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           f(key16(w[e] & 0xFFFFu), c0 + 2 * e);
@@ -280,7 +336,7 @@ struct StreamKeys {
         }
       }
     }
-    for (; q < nvec; q += NT) {
+    for (; q < nvec; q += nt) {
       const uint4 v = pv[q];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -289,12 +345,12 @@ struct StreamKeys {
         f(key16(w[e] >> 16), 8 * q + 2 * e + 1);
       }
     }
-    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += NT) f(key16(rowp[c]), c);
+    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += nt) f(key16(rowp[c]), c);
   }
-  __device__ __forceinline__ int slices() const { return (V + NT - 1) / NT; }
+  __device__ __forceinline__ int slices() const { return (V + kThreads - 1) / kThreads; }
   template <class F>
   __device__ __forceinline__ void slice(int j, F f) const {
-    const int c = int(threadIdx.x) + NT * j;
+    const int c = int(threadIdx.x) + kThreads * j;
     if (c < V) f(key16(rowp[c]), c);
   }
 };
@@ -324,6 +380,7 @@ struct RowArgs {
   float* full_lse;
 };
 
+template <int NTH>
 __device__ void write_bad(const RowArgs& a) {
   const float nanf = __builtin_nanf("");
   if (threadIdx.x == 0) {
@@ -336,7 +393,7 @@ __device__ void write_bad(const RowArgs& a) {
     if (a.full_lse) a.full_lse[a.row] = nanf;
   }
   if (a.ids_out)
-    for (int i = threadIdx.x; i < a.cap; i += NT) a.ids_out[a.row * a.cap + i] = -1;
+    for (int i = threadIdx.x; i < a.cap; i += NTH) a.ids_out[a.row * a.cap + i] = -1;
 }
 
 __device__ __forceinline__ bool params_ok(const RowArgs& a) {
@@ -372,48 +429,61 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
-// xor butterfly: every lane ends with the same, fixed-order sum
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
-// All segment summaries, keys striped over the lanes of each wave: wave w
-// takes segments w, w + 8, ..., lane l key 64 s + l.  The few dense segments
-// (the keys of the bulk of the logits are contiguous) are spread over all
-// waves instead of sitting in one, and an empty segment costs one ballot.
+// All segment summaries in one pass, one thread per segment.  The thread
+// loads the segment's 32 packed count words once (starting at word t % 32, so
+// a wave's loads fall in different banks), adds up its token count and, for a
+// non-empty regular segment (2 .. 1021: finite logits only), its masses
+// sum c * exp(z - z_max) and sum c * exp(z - z_max) * (z - z_max) in fp64.
+// The 64 keys of a regular segment are equally spaced logits (one exponent,
+// consecutive mantissas), so w(key 2j) = exp(d_0) r^(2j) with r = exp(dx / tau):
+// three exp calls per segment and a multiply per key pair.  The irregular
+// segments hold only NaN and +-inf keys; in a row that passed the checks only
+// -inf (weight 0) and the register paths' padding at key 0 can be counted.
 // Returns this thread's share of the sum of all counts.
-template <class CountFn>
-__device__ __forceinline__ uint32_t summarize_striped(CountFn count, double tau, double z0, Smem& sm) {
-  static_assert(SEGW == 64, "one key per lane");
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+template <int NTH>
+__device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uint32_t n_pad, double tau, double z0,
+                                                      Smem& sm) {
   uint32_t total = 0;
-  for (int s = wave; s < NSEG; s += NWAVE) {
-    const uint32_t key = uint32_t(s * SEGW + lane);
-    const uint32_t c = count(key);
-    total += c;
-    uint32_t cs = 0;
+  const int rot = int(threadIdx.x & 31);
+  for (int s = threadIdx.x; s < NSEG; s += NTH) {
+    const uint32_t* seg = hist + s * 32;  // word j holds keys 2j (low half) and 2j + 1 (high half)
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t wd = seg[(i + rot) & 31];
+      cnt += (wd & 0xFFFFu) + (wd >> 16);
+    }
+    if (s == 0) cnt -= n_pad;
+    total += cnt;
     double m = 0.0, zm = 0.0;
-    if (__ballot(c != 0)) {
-      if (c) {
-        const double d = double(key_logit(key)) / tau - z0;
-        const double e = exp(d);
-        if (e > 0.0) {
-          m = double(c) * e;
-          zm = double(c) * e * d;
-        }
+    if (cnt != 0 && s >= 2 && s < NSEG - 2) {
+      const uint32_t k0 = uint32_t(s * SEGW);
+      const double x0 = double(key_logit(k0));
+      const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
+      const double d0 = x0 / tau - z0;
+      const double r = exp(dd);
+      const double r2 = r * r;
+      const double w_first = exp(d0);
+      double w = exp(d0 + double(2 * rot) * dd);  // weight of key 2 * rot
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const int j = (i + rot) & 31;
+        if (i > 0 && j == 0) w = w_first;  // wrapped to the segment's first key
+        const uint32_t wd = seg[j];
+        const double dl = d0 + double(2 * j) * dd;
+        const double cl = double(wd & 0xFFFFu) * w;
+        const double ch = double(wd >> 16) * (w * r);
+        m += cl;
+        m += ch;
+        zm += cl * dl;
+        zm += ch * (dl + dd);
+        w *= r2;
       }
-      cs = wave_sum_u32(c);
-      m = wave_sum_f64(m);
-      zm = wave_sum_f64(zm);
     }
-    if (lane == 0) {
-      sm.seg_count[s] = cs;
-      sm.seg_mass[s] = m;
-      sm.seg_zmass[s] = zm;
-    }
+    sm.seg_count[s] = cnt;
+    sm.seg_mass[s] = m;
+    sm.seg_zmass[s] = zm;
   }
   return total;
 }
@@ -423,6 +493,8 @@ __device__ __forceinline__ uint32_t summarize_striped(CountFn count, double tau,
 template <class Keys, class FineFn, class CountFn>
 __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double z0, Smem& sm,
                            FineFn fine, CountFn count) {
+  constexpr int NTH = Keys::kThreads;
+  constexpr int NW = NTH / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const bool w0 = tid < 64;
@@ -661,7 +733,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     uint32_t below = 0;
     const int yc = int(a.y);
     keys.each([&](uint32_t key, int col) { below += (key == K_L && col < yc) ? 1u : 0u; });
-    below = block_sum_u32(below, sm);
+    below = block_sum_u32<NW>(below, sm);
     in_s = below < r_L;
   }
 
@@ -681,22 +753,31 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     uint64_t* cand = reinterpret_cast<uint64_t*>(sm.hist);
     if (tid == 0) sm.ncand = 0;
     __syncthreads();
-    keys.each([&](uint32_t key, int col) {
+    auto take = [&](uint32_t key, int col) {
       if (key > K_c || (with_ties && key == K_c)) {
         const uint32_t slot = atomicAdd(&sm.ncand, 1u);
         cand[slot] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(col));
       }
-    });
+    };
+    // the candidates come from the per-thread lists when every thread's list
+    // holds all of its tokens with key >= K_c; otherwise from a sweep of the row
+    bool listed = false;
+    if constexpr (Keys::kTopList) listed = block_max_u32<NW>(keys.listed_from(K_c) ? 0u : 1u, sm) == 0;
+    if (listed) {
+      keys.each_listed(take);
+    } else {
+      keys.each(take);
+    }
     __syncthreads();
     const uint32_t nc = sm.ncand;
     uint32_t P = 1;
     while (P < nc) P <<= 1;
-    for (uint32_t i = nc + tid; i < P; i += NT) cand[i] = 0;
+    for (uint32_t i = nc + tid; i < P; i += NTH) cand[i] = 0;
     __syncthreads();
     // bitonic sort, descending: key descending, token id ascending
     for (uint32_t size = 2; size <= P; size <<= 1) {
       for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = tid; i < P; i += NT) {
+        for (uint32_t i = tid; i < P; i += NTH) {
           const uint32_t pidx = i ^ stride;
           if (pidx > i) {
             const uint64_t x = cand[i], z = cand[pidx];
@@ -712,8 +793,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     }
     int64_t* out = a.ids_out + a.row * a.cap;
     const uint32_t n_sorted = with_ties ? n_out : above_c;
-    for (uint32_t i = tid; i < n_sorted; i += NT) out[i] = int64_t(0xFFFFFFFFu - uint32_t(cand[i] & 0xFFFFFFFFu));
-    for (uint32_t i = n_out + tid; i < uint32_t(a.cap); i += NT) out[i] = -1;
+    for (uint32_t i = tid; i < n_sorted; i += NTH) out[i] = int64_t(0xFFFFFFFFu - uint32_t(cand[i] & 0xFFFFFFFFu));
+    for (uint32_t i = n_out + tid; i < uint32_t(a.cap); i += NTH) out[i] = -1;
     if (!with_ties) {
       // a very large tie group at K_c: its first r_c tokens in column order, slice by slice
       uint32_t taken = 0;
@@ -722,7 +803,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
         uint32_t mine = 0;
         keys.slice(j, [&](uint32_t key, int) { mine += key == K_c ? 1u : 0u; });
         uint32_t tot;
-        uint32_t pos = taken + block_excl_scan_u32(mine, tot, sm);
+        uint32_t pos = taken + block_excl_scan_u32<NW>(mine, tot, sm);
         keys.slice(j, [&](uint32_t key, int col) {
           if (key == K_c) {
             if (pos < r_c) out[above_c + pos] = col;
@@ -784,16 +865,18 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
 // streams it and re-reads it for the later passes.  A row whose counts would
 // overflow 16 bits gets handoff[row] = 1 and nothing else.
 template <int NV>
-__global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) {
+__global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) {
+  constexpr int NTH = NV > 0 ? NT : NT_STREAM;
+  constexpr int NW = NTH / 64;
   __shared__ Smem sm;
   VS_ROW_ARGS
   const int tid = threadIdx.x;
   if (!params_ok(a)) {
     if (tid == 0) handoff[a.row] = 0;
-    write_bad(a);
+    write_bad<NTH>(a);
     return;
   }
-  for (int i = tid; i < HALF; i += NT) sm.hist[i] = 0u;
+  for (int i = tid; i < HALF; i += NTH) sm.hist[i] = 0u;
   __syncthreads();
   using Keys = typename std::conditional<(NV > 0), RegKeys<(NV > 0 ? NV : 1)>, StreamKeys>::type;
   Keys keys;
@@ -807,11 +890,11 @@ __global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) 
     keys.load_count(sm.hist, bad, kmax);
     n_pad = 0;
   }
-  kmax = block_max_u32(kmax, sm);  // (its barriers also complete the counting)
-  bad = block_max_u32(bad, sm);
+  kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
+  bad = block_max_u32<NW>(bad, sm);
   if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
     if (tid == 0) handoff[a.row] = 0;
-    write_bad(a);
+    write_bad<NTH>(a);
     return;
   }
   auto count = [&](uint32_t key) -> uint32_t {
@@ -820,10 +903,11 @@ __global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) 
   };
   const double tau = double(a.tauf);
   const double z0 = double(key_logit(kmax)) / tau;
-  const uint32_t part = summarize_striped(count, tau, z0, sm);
+  const uint32_t part = summarize_segments<NTH>(sm.hist, n_pad, tau, z0, sm);
   // every counter stayed below 2^16 iff the counts add up to the token count
-  // (a carry out of a low half, or out of a word, breaks the total)
-  if (block_sum_u32(part, sm) != uint32_t(V)) {
+  // (a carry out of a low half, or out of a word, breaks the total); the sum
+  // also orders the segment summaries before the queries read them
+  if (block_sum_u32<NW>(part, sm) != uint32_t(V)) {
     if (tid == 0) handoff[a.row] = 1;
     return;
   }
@@ -833,39 +917,41 @@ __global__ __launch_bounds__(NT, 1) void transforms_fast_kernel(VS_KERNEL_ARGS) 
 
 // Stream path: the row is re-read from memory for every pass; 32-bit counts.
 // With a handoff array, only rows marked 1 are processed.
-__global__ __launch_bounds__(NT, 1) void transforms_stream_kernel(VS_KERNEL_ARGS) {
+__global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERNEL_ARGS) {
+  constexpr int NTH = NT_STREAM;
+  constexpr int NW = NTH / 64;
   __shared__ Smem sm;
   VS_ROW_ARGS
   if (handoff && handoff[a.row] == 0) return;
   const int tid = threadIdx.x;
   if (!params_ok(a)) {
-    write_bad(a);
+    write_bad<NTH>(a);
     return;
   }
   StreamKeys keys{a.rowp, V};
   uint32_t bad = 0, kmax = 0;
-  for (int c = tid; c < V; c += NT) {
+  for (int c = tid; c < V; c += NTH) {
     const uint32_t h = a.rowp[c];
     bad |= raw_bad(h) ? 1u : 0u;
     kmax = max(kmax, key16(h));
   }
-  kmax = block_max_u32(kmax, sm);
-  bad = block_max_u32(bad, sm);
+  kmax = block_max_u32<NW>(kmax, sm);
+  bad = block_max_u32<NW>(bad, sm);
   if (bad || kmax <= KEY_NEG_INF) {
-    write_bad(a);
+    write_bad<NTH>(a);
     return;
   }
   const double tau = double(a.tauf);
   const double z0 = double(key_logit(kmax)) / tau;
   for (uint32_t h = 0; h < 2; ++h) {
-    for (int i = tid; i < HALF; i += NT) sm.hist[i] = 0u;
+    for (int i = tid; i < HALF; i += NTH) sm.hist[i] = 0u;
     __syncthreads();
     keys.each([&](uint32_t key, int) {
       if ((key >> 15) == h) atomicAdd(&sm.hist[key & 0x7FFFu], 1u);
     });
     __syncthreads();
     auto count_half = [&](uint32_t key) -> uint32_t { return sm.hist[key & 0x7FFFu]; };
-    for (int s = tid; s < NSEG / 2; s += NT) summarize_segment(int(h) * (NSEG / 2) + s, count_half, tau, z0, sm);
+    for (int s = tid; s < NSEG / 2; s += NTH) summarize_segment(int(h) * (NSEG / 2) + s, count_half, tau, z0, sm);
     __syncthreads();
   }
   if (tid == 0) sm.fine_seg = -1;
@@ -909,10 +995,10 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
   if (nv <= 4) transforms_fast_kernel<4><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 10) transforms_fast_kernel<10><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 20) transforms_fast_kernel<20><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
-  else transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  else transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);
   const int rc = int(hipGetLastError());
   if (rc) return rc;
-  transforms_stream_kernel<<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
+  transforms_stream_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);
 #undef VS_ARGS
   return int(hipGetLastError());
 }
