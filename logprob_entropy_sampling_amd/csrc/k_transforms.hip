@@ -132,9 +132,11 @@ struct RegKeys {
   uint32_t kw[NV][4];  // two keys per word
   static constexpr int kThreads = NT;
   static constexpr bool kTopList = false;  // the row is in registers: a sweep is cheap
+  struct Listed {};
   __device__ __forceinline__ bool listed_from(uint32_t) const { return false; }
+  __device__ __forceinline__ Listed load_listed() const { return Listed{}; }
   template <class F>
-  __device__ __forceinline__ void each_listed(F) const {}
+  __device__ __forceinline__ void each_listed(const Listed&, F) const {}
 
   // Loads the row, converts it to keys and counts every key into the packed
   // 16-bit counters `hist` (already zeroed); returns bad (NaN or +inf seen)
@@ -254,14 +256,23 @@ struct StreamKeys {
   }
   // true when every token of this thread with key >= K is in the listed vectors
   __device__ __forceinline__ bool listed_from(uint32_t K) const { return have_top && dropped < K; }
-  template <class F>
-  __device__ __forceinline__ void each_listed(F f) const {
+  struct Listed {
+    uint4 v[2];
+  };
+  // the listed vectors' data (issued early; used by each_listed)
+  __device__ __forceinline__ Listed load_listed() const {
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    Listed l;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) l.v[i] = vq[i] >= 0 ? pv[vq[i]] : make_uint4(0, 0, 0, 0);
+    return l;
+  }
+  template <class F>
+  __device__ __forceinline__ void each_listed(const Listed& l, F f) const {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (vq[i] < 0) continue;
-      const uint4 v = pv[vq[i]];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {l.v[i].x, l.v[i].y, l.v[i].z, l.v[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         f(key16(w[e] & 0xFFFFu), 8 * vq[i] + 2 * e);
@@ -368,6 +379,7 @@ struct RowArgs {
   int kk;
   float pf, mpf;
   int64_t y;
+  uint32_t key_y;  // key of the target's logit, loaded early
   const uint16_t* rowp;
   float* logprob;
   float* entropy;
@@ -512,20 +524,27 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     sm.lane_cnt[lane] = c;
     sm.lane_mass[lane] = m;
     sm.lane_zmass[lane] = zm;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t c = 0;
-    double m = 0.0, zm = 0.0;
-    for (int l = 0; l < 64; ++l) {
-      sm.lane_cnt_before[l] = c;
-      sm.lane_mass_before[l] = m;
-      sm.lane_zmass_before[l] = zm;
-      c += sm.lane_cnt[l];
-      m += sm.lane_mass[l];
-      zm += sm.lane_zmass[l];
+    // inclusive scan over the lanes (fixed tree), then shifted by one lane
+    uint32_t ci = c;
+    double mi = m, zi = zm;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t co = __shfl_up(ci, off, 64);
+      const double mo = __shfl_up(mi, off, 64);
+      const double zo = __shfl_up(zi, off, 64);
+      if (lane >= off) {
+        ci += co;
+        mi += mo;
+        zi += zo;
+      }
     }
-    sm.bd[7] = m;  // total mass relative to the row max
+    const uint32_t ce = __shfl_up(ci, 1, 64);
+    const double me = __shfl_up(mi, 1, 64);
+    const double ze = __shfl_up(zi, 1, 64);
+    sm.lane_cnt_before[lane] = lane ? ce : 0u;
+    sm.lane_mass_before[lane] = lane ? me : 0.0;
+    sm.lane_zmass_before[lane] = lane ? ze : 0.0;
+    if (lane == 63) sm.bd[7] = mi;  // total mass relative to the row max
   }
   __syncthreads();
   const double total_mass = sm.bd[7];
@@ -704,10 +723,10 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     const uint32_t km = sm.bu[5];
     seg_above(int(km / SEGW));
     fine(int(km / SEGW));
-    if (tid == 0) {
-      uint32_t c = sm.bu[1];
-      for (uint32_t k2 = km; k2 < (km / SEGW + 1) * SEGW; ++k2) c += count(k2);
-      sm.bu[6] = c;
+    if (w0) {  // tokens of km's segment with key >= km, one key per lane
+      const uint32_t k2 = (km / SEGW) * SEGW + uint32_t(lane);
+      const uint32_t c = wave_sum_u32(k2 >= km ? count(k2) : 0u);
+      if (lane == 0) sm.bu[6] = sm.bu[1] + c;
     }
     __syncthreads();
     L_m = sm.bu[6];
@@ -727,7 +746,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   const double zmass_S = sm.bd[3] + (e_L > 0.0 ? double(r_L) * e_L * d_L : 0.0);
 
   // ---- target membership (ties at the threshold key resolved by token id) ----
-  const uint32_t key_y = key16(a.rowp[a.y]);
+  const uint32_t key_y = a.key_y;
   bool in_s = key_y > K_L;
   if (key_y == K_L) {
     uint32_t below = 0;
@@ -740,6 +759,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   // ---- dense support ids ----
   uint8_t st = 0;
   if (a.ids_out && a.cap > 0) {
+    const typename Keys::Listed listed_data = keys.load_listed();  // in flight during the rank query
     const uint32_t n_out = L < uint32_t(a.cap) ? L : uint32_t(a.cap);
     if (L > uint32_t(a.cap)) st |= kRowTruncated;
     seg_of_rank(n_out - 1);
@@ -764,7 +784,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     bool listed = false;
     if constexpr (Keys::kTopList) listed = block_max_u32<NW>(keys.listed_from(K_c) ? 0u : 1u, sm) == 0;
     if (listed) {
-      keys.each_listed(take);
+      keys.each_listed(listed_data, take);
     } else {
       keys.each(take);
     }
@@ -775,6 +795,35 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     for (uint32_t i = nc + tid; i < P; i += NTH) cand[i] = 0;
     __syncthreads();
     // bitonic sort, descending: key descending, token id ascending
+    if (P <= 128) {
+      // one wave, two elements per lane (indices lane, lane + 64), no barriers
+      if (w0) {
+        uint64_t e[2];
+        e[0] = uint32_t(lane) < P ? cand[lane] : 0ull;
+        e[1] = uint32_t(lane) + 64 < P ? cand[lane + 64] : 0ull;
+        for (uint32_t size = 2; size <= P; size <<= 1) {
+          for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride == 64) {  // partner of index lane is lane + 64: the same lane
+              const bool desc = (uint32_t(lane) & size) == 0;
+              const uint64_t hi = e[0] > e[1] ? e[0] : e[1], lo = e[0] > e[1] ? e[1] : e[0];
+              e[0] = desc ? hi : lo;
+              e[1] = desc ? lo : hi;
+            } else {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const uint32_t idx = uint32_t(lane) + 64u * uint32_t(h);
+                const uint64_t pv = __shfl_xor(e[h], int(stride), 64);
+                const bool keep_max = ((idx & stride) == 0) == ((idx & size) == 0);
+                e[h] = keep_max ? (e[h] > pv ? e[h] : pv) : (e[h] < pv ? e[h] : pv);
+              }
+            }
+          }
+        }
+        if (uint32_t(lane) < P) cand[lane] = e[0];
+        if (uint32_t(lane) + 64 < P) cand[lane + 64] = e[1];
+      }
+      __syncthreads();
+    } else {
     for (uint32_t size = 2; size <= P; size <<= 1) {
       for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
         for (uint32_t i = tid; i < P; i += NTH) {
@@ -790,6 +839,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
         }
         __syncthreads();
       }
+    }
     }
     int64_t* out = a.ids_out + a.row * a.cap;
     const uint32_t n_sorted = with_ties ? n_out : above_c;
@@ -876,6 +926,7 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
     write_bad<NTH>(a);
     return;
   }
+  a.key_y = key16(a.rowp[a.y]);  // issued now, used after the histogram
   for (int i = tid; i < HALF; i += NTH) sm.hist[i] = 0u;
   __syncthreads();
   using Keys = typename std::conditional<(NV > 0), RegKeys<(NV > 0 ? NV : 1)>, StreamKeys>::type;
@@ -928,6 +979,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
     write_bad<NTH>(a);
     return;
   }
+  a.key_y = key16(a.rowp[a.y]);
   StreamKeys keys{a.rowp, V};
   uint32_t bad = 0, kmax = 0;
   for (int c = tid; c < V; c += NTH) {
