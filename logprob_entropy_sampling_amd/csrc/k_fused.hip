@@ -86,10 +86,79 @@ __device__ __forceinline__ bool map_tile(int b, int n_vtiles, int n_ttiles, int 
 // the two half-waves and the two V-direction waves are merged, and one partial per
 // (token, vocabulary tile) is written.  The lane holding the target id stores its raw logit.
 // `red` is >= 3 KiB of LDS that no wave reads any more.
+
+// The target id and temperature of the lane's 4 token columns.  They are
+// loaded when the workgroup starts, so their latency hides behind the K loop
+// instead of stalling each column of the epilogue between its barriers.
+struct ColumnLoads {
+  int64_t y[4];
+  float tau[4];
+};
+__device__ __forceinline__ ColumnLoads load_columns(int64_t t0, int64_t rows_valid, const float* __restrict__ temp,
+                                                    float temp_scalar, const int64_t* __restrict__ targets,
+                                                    const int32_t* __restrict__ row_map) {
+  const int lane = threadIdx.x & 63;
+  const int wt = threadIdx.x >> 7;
+  ColumnLoads cl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + wt * 128 + 32 * j + (lane & 31);
+    const int64_t trow = t < rows_valid ? (row_map ? int64_t(row_map[t]) : t) : 0;
+    cl.y[j] = targets[trow];
+    cl.tau[j] = temp ? temp[trow] : temp_scalar;
+  }
+  return cl;
+}
+
+// Fold the 64 accumulator values of one token column held by this lane into
+// (max, sum 2^(u-max), sum 2^(u-max)(u-max)) in base-2 units, u = x * c.
+// TAIL: only rows r with vr(r) < vlim exist (the ragged last vocabulary tile).
+template <bool TAIL>
+__device__ __forceinline__ Part fold_column(const f32x16& x0, const f32x16& x1, const f32x16& x2, const f32x16& x3,
+                                            float c, int lh, int vlim) {
+  const f32x16* xs[4] = {&x0, &x1, &x2, &x3};
+  // opaque copy: keeps the compiler from hoisting the 64 row masks out of the
+  // (rare) ragged branch into scalar registers shared by every column
+  if (TAIL) asm volatile("" : "+v"(vlim));
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (!TAIL || vr < vlim) mx = fmaxf(mx, (*xs[i])[r]);
+    }
+  Part p;
+  p.m = mx * c;
+  p.s = 0.0f;
+  p.a = 0.0f;
+  if (mx == kNegInf) {  // every value masked or -inf, or NaN values that fmaxf dropped
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if ((!TAIL || vr < vlim) && (*xs[i])[r] != (*xs[i])[r]) p.s = __builtin_nanf("");
+      }
+    return p;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (!TAIL || vr < vlim) {
+        const float d = __builtin_fmaf((*xs[i])[r], c, -p.m);
+        const float e = exp2_hw(d);
+        p.s += e;
+        p.a = __builtin_fmaf(e, d, p.a);
+      }
+    }
+  return p;
+}
+
 __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, int64_t v0, int64_t t0, int vt,
-                                              int64_t rows_valid, int64_t V, const float* __restrict__ temp,
-                                              float temp_scalar, const int64_t* __restrict__ targets,
-                                              const int32_t* __restrict__ row_map, int n_vtiles,
+                                              int64_t rows_valid, int64_t V, const ColumnLoads& cl, int n_vtiles,
                                               float4* __restrict__ partials, float* __restrict__ zy_raw) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -100,6 +169,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
   // vocabulary rows of this wave that exist (the last tile may be ragged)
   const int vlim = int(V - v0 < BV ? V - v0 : BV) - wv * 128;  // rows r of the wave with r < vlim exist
   const bool tail_v = vlim < 128;
+  Part pj[4];  // per column, after the half-wave merge
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // the accumulators of the columns not folded yet stay in AGPRs until their turn
@@ -110,58 +180,19 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
     const int col = wt * 128 + 32 * j + lr;
     const int64_t t = t0 + col;
     const bool tvalid = t < rows_valid;
-    const int64_t trow = tvalid ? (row_map ? int64_t(row_map[t]) : t) : 0;
-    const float tau = temp ? temp[trow] : temp_scalar;
-    const float c = kLog2e / tau;
+    const float c = kLog2e / cl.tau[j];
 
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (!tail_v || vr < vlim) mx = fmaxf(mx, acc[i][j][r]);
-      }
+    // one uniform branch per wave: the unmasked fold is a plain max / exp
+    // chain; only the ragged last vocabulary tile pays for per-row masks
     Part p;
-    p.m = mx * c;
-    p.s = 0.0f;
-    p.a = 0.0f;
-    if (mx == kNegInf) {  // every value masked, or NaN values that fmaxf dropped
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (vr < vlim && acc[i][j][r] != acc[i][j][r]) p.s = __builtin_nanf("");
-        }
-    } else if (!tail_v) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float d = __builtin_fmaf(acc[i][j][r], c, -p.m);
-          const float e = exp2_hw(d);
-          p.s += e;
-          p.a = __builtin_fmaf(e, d, p.a);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vr = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (vr < vlim) {
-            const float d = __builtin_fmaf(acc[i][j][r], c, -p.m);
-            const float e = exp2_hw(d);
-            p.s += e;
-            p.a = __builtin_fmaf(e, d, p.a);
-          }
-        }
-    }
+    if (tail_v)
+      p = fold_column<true>(acc[0][j], acc[1][j], acc[2][j], acc[3][j], c, lh, vlim);
+    else
+      p = fold_column<false>(acc[0][j], acc[1][j], acc[2][j], acc[3][j], c, lh, vlim);
 
     // the target's raw logit, if this lane holds it (exactly one lane in the grid does)
     if (tvalid) {
-      const int64_t dv64 = targets[trow] - (v0 + wv * 128);
+      const int64_t dv64 = cl.y[j] - (v0 + wv * 128);
       if (dv64 >= 0 && dv64 < vlim && dv64 < 128) {
         const int dv = int(dv64);
         const int rr = dv & 31;
@@ -179,25 +210,35 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
       }
     }
 
-    // merge the two half-waves (same column, other rows), then the two V waves
+    // merge the two half-waves (same column, other rows)
     Part q;
     q.m = shfl_xor_f(p.m, 32);
     q.s = shfl_xor_f(p.s, 32);
     q.a = shfl_xor_f(p.a, 32);
-    p = merge(p, q);
-    if (wv == 1 && lh == 0) {
+    pj[j] = merge(p, q);
+  }
+  // merge the two vocabulary waves: one LDS exchange and one barrier for all
+  // four columns (no barrier between columns, so their folds overlap)
+  if (wv == 1 && lh == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       float* dst = red + (wt * 128 + 32 * j + lr) * 3;
-      dst[0] = p.m;
-      dst[1] = p.s;
-      dst[2] = p.a;
+      dst[0] = pj[j].m;
+      dst[1] = pj[j].s;
+      dst[2] = pj[j].a;
     }
-    __syncthreads();
-    if (wv == 0 && lh == 0 && tvalid) {
-      const float* src = red + (wt * 128 + 32 * j + lr) * 3;
-      p = merge(p, Part{src[0], src[1], src[2]});
-      partials[t * n_vtiles + vt] = make_float4(p.m, p.s, p.a, 0.0f);
+  }
+  __syncthreads();
+  if (wv == 0 && lh == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + wt * 128 + 32 * j + lr;
+      if (t < rows_valid) {
+        const float* src = red + (wt * 128 + 32 * j + lr) * 3;
+        const Part p = merge(pj[j], Part{src[0], src[1], src[2]});
+        partials[t * n_vtiles + vt] = make_float4(p.m, p.s, p.a, 0.0f);
+      }
     }
-    __syncthreads();
   }
 }
 
@@ -215,6 +256,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
 
   __shared__ uint4 As[2][BV * CH];
   __shared__ uint4 Bs[2][BT * CH];
+  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, row_map);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,8 +342,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     cur ^= 1;
   }
 
-  tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, temp, temp_scalar, targets,
-                row_map, n_vtiles, partials, zy_raw);
+  tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials, zy_raw);
 }
 
 
@@ -321,9 +362,14 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+// s_waitcnt immediates: "at most vm vector-memory and lgkm LDS operations
+// outstanding" (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14); }
+constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
 
 constexpr int NSTAGE = 4;
 constexpr int DMA_PER_OP = BV * CH / NT;  // 16-byte loads per lane per operand per stage (4)
@@ -346,6 +392,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
 
   __shared__ uint4 A0[BV * CH], A1[BV * CH], A2[BV * CH], A3[BV * CH];
   __shared__ uint4 B0[BT * CH], B1[BT * CH], B2[BT * CH], B3[BT * CH];
+  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
   // slot indices are compile-time constants after unrolling
   auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : i == 1 ? A1 : i == 2 ? A2 : A3; };
   auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : i == 1 ? B1 : i == 2 ? B2 : B3; };
@@ -434,11 +481,6 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   };
-  auto mma_slot = [&](int slot) {
-    Frags fa, fb;
-    read_slot(slot, fa, fb);
-    mma(fa, fb);
-  };
   // barrier + "LDS reads stay after it"
   auto bar = [&]() {
     __builtin_amdgcn_s_barrier();
@@ -446,43 +488,63 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
   };
 
   const int nk = int(H / BK);
-  // prologue: stages 0..2 into slots 0..2 (clamped to the last stage)
+  // prologue: stages 0..3 into slots 0..3 (clamped to the last stage), then
+  // the fragments of stage 0 into register set 0
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) dma(s, int64_t(s < nk ? s : nk - 1) * BK);
-  // Stage s lives in slot s % 4 (REM = nk % 4, fixed at compile time).  Step s: wait until this wave's loads for
-  // stage s are done (the two younger stages stay in flight), barrier (every
-  // wave's loads for s have landed and every wave has finished reading slot
-  // (s-1) % 4), read the fragments of stage s, refill slot (s-1) % 4 with
-  // stage s+3, compute stage s.  The refill is unconditional (clamped to the
-  // last stage) so the wait counts stay exact, and it follows the fragment
-  // reads so no LDS read of the step comes after a load into LDS (the
-  // compiler would otherwise drain every outstanding load before it).
+  for (int s = 0; s < NSTAGE; ++s) dma(s, int64_t(s < nk ? s : nk - 1) * BK);
+  Frags fa0, fb0, fa1, fb1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 1) * DMA_PER_STAGE));
+  bar();
+  read_slot(0, fa0, fb0);
+  // Stage s lives in slot s % 4, and during step s-1 its fragments move to
+  // register set s % 2.  Step s:
+  //   1. wait until this wave's loads for stage s+1 have landed (s+2 and s+3
+  //      stay in flight) and its reads of slot s % 4 are done;
+  //   2. barrier: every wave's loads for s+1 are in LDS, and no wave reads
+  //      slot s % 4 any more;
+  //   3. issue, interleaved: the 32 MFMAs of stage s from registers, the 16
+  //      fragment reads of stage s+1, and the refill of slot s % 4 with stage
+  //      s+4 (one read per MFMA pair, one load per four MFMAs).
+  // With one wave per SIMD the reads only overlap the MFMAs when they are
+  // spread among them: a burst of reads stalls issue until LDS drains it.
+  // Loads are unconditional (clamped to the last stage), so the wait counts
+  // stay exact; the refill's slot is a separate LDS array from the one being
+  // read, so the compiler's wait tracking never drains the loads before a
+  // read.  The last step's read of stage nk re-reads a clamped duplicate.
+  auto step = [&](int u, int s, Frags& fa_cur, Frags& fb_cur, Frags& fa_nxt, Frags& fb_nxt) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NSTAGE - 2) * DMA_PER_STAGE, 0));
+    bar();
+    read_slot((u + 1) % NSTAGE, fa_nxt, fb_nxt);
+    const int pf = s + NSTAGE < nk ? s + NSTAGE : nk - 1;
+    dma(u, int64_t(pf) * BK);
+    mma(fa_cur, fb_cur);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_STAGE; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   const int nk4 = nk - REM;
   for (int kt = 0; kt < nk4; kt += NSTAGE) {
-#pragma unroll
-    for (int u = 0; u < NSTAGE; ++u) {
-      const int s = kt + u;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 2) * DMA_PER_STAGE));
-      bar();
-      const int pf = s + NSTAGE - 1 < nk ? s + NSTAGE - 1 : nk - 1;
-      Frags fa, fb;
-      read_slot(u, fa, fb);
-      dma((u + NSTAGE - 1) % NSTAGE, int64_t(pf) * BK);
-      mma(fa, fb);
-    }
+    step(0, kt + 0, fa0, fb0, fa1, fb1);
+    step(1, kt + 1, fa1, fb1, fa0, fb0);
+    step(2, kt + 2, fa0, fb0, fa1, fb1);
+    step(3, kt + 3, fa1, fb1, fa0, fb0);
   }
-  // the REM = nk % 4 leftover stages sit in slots 0 .. REM-1; straight-line
-  // code (REM is a template argument) keeps the accumulators where they are
-  if (REM > 0) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    bar();
-#pragma unroll
-    for (int u = 0; u < REM; ++u) mma_slot(u);
-  }
+  // the REM = nk % 4 leftover stages: slots 0 .. REM-1, register sets 0, 1, 0
+  if (REM > 0) step(0, nk4 + 0, fa0, fb0, fa1, fb1);
+  if (REM > 1) step(1, nk4 + 1, fa1, fb1, fa0, fb0);
+  if (REM > 2) step(2, nk4 + 2, fa0, fb0, fa1, fb1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
   __syncthreads();
-  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, temp, temp_scalar, targets,
-                BUF ? nullptr : row_map, n_vtiles, partials, zy_raw);  // BUF implies no gather
+  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials,
+                zy_raw);
 }
 
 __global__ void round_hidden_kernel(const float* __restrict__ h, int64_t ld, int64_t rows, int64_t H,
