@@ -157,7 +157,7 @@ def bench_fused(vsa, dev, steps, warmup):
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
             "traffic_source": traffic_src,
-            "kernel": "fused_partials_pipelined_kernel<true, 0> (projection + per-tile softmax statistics)",
+            "kernel": "fused_partials_wide_kernel<true, 0> (projection + per-tile softmax statistics)",
             "kernel_ms_mean": round(sweep_ms, 4),
             "flop_per_launch": flops,
             "algorithmic_bytes_per_launch": (T * H + V * H) * 2 + T * ((V + 255) // 256) * 16 + T * 4,

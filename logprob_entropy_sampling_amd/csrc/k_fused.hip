@@ -547,6 +547,191 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
                 zy_raw);
 }
 
+// ---------------------------------------------------------------------------
+// Wide-stage sweep (H a multiple of 64): the same tile, MFMA layout and
+// epilogue, with the K slices staged 64 wide, so each tile row's slice is one
+// whole 128-byte line.  With 32-wide slices every refill load touches half of
+// 16 lines and the other half is fetched again one stage later; the load path
+// then costs ~20% of the loop.  Here each 16-byte-per-lane load covers 8 rows
+// x 128 bytes.
+//   * Ring: 2 slots x (A 32 KiB + B 32 KiB).  Row r of a slot is 8 chunks of
+//     16 bytes; chunk c sits at c ^ g8(r), g8(r) = (r >> 1) & 7, which keeps
+//     the fragment reads (32 rows, one chunk per half-wave; the LDS serves 16
+//     lanes per pass over its 256-byte bank row) free of bank conflicts.
+//   * Each 64-wide stage is two 32-wide sub-steps of 32 MFMAs.  Fragments of
+//     the next sub-step are read into the other register set while the
+//     current sub-step's MFMAs run, one read per MFMA pair.
+//   * One barrier per stage, at its second sub-step: the next stage has
+//     landed, and no wave reads the current slot any more, so its refill
+//     (stage S+2) is issued right there, one load per MFMA pair.
+// ---------------------------------------------------------------------------
+constexpr int BK2 = 64;
+constexpr int CH2 = BK2 / 8;                  // 16-byte chunks per row per stage (8)
+constexpr int DMA2_PER_OP = BV * CH2 / NT;    // loads per lane per operand per stage (8)
+constexpr int DMA2_PER_STAGE = 2 * DMA2_PER_OP;
+__device__ __forceinline__ int swz8(int r, int c) { return r * CH2 + (c ^ ((r >> 1) & 7)); }
+
+template <bool BUF, int REM>
+__global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
+    const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
+    int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
+    const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
+    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+  int vt, tt;
+  if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
+  const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
+  const int64_t t0 = int64_t(tt) * BT;
+  if (t0 >= rows_valid) return;
+  const int64_t v0 = int64_t(vt) * BV;
+
+  __shared__ uint4 A0[BV * CH2], A1[BV * CH2];
+  __shared__ uint4 B0[BT * CH2], B1[BT * CH2];
+  auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : A1; };
+  auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : B1; };
+  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wv = w & 1;
+  const int wt = w >> 1;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int64_t vrows = V - v0 < BV ? V - v0 : BV;
+  const int64_t trows = rows_valid - t0 < BT ? rows_valid - t0 : BT;
+
+  // Load i of wave w fills LDS chunk p = (8w + i) * 64 + lane: row r = p / 8,
+  // physical chunk p % 8, which holds logical chunk (p % 8) ^ g8(r).  Rows
+  // past the tile's end re-read the last row (their results are masked).
+  uint32_t oa[DMA2_PER_OP], ob[DMA2_PER_OP];
+  const uint16_t* ga[DMA2_PER_OP];
+  const uint16_t* gb[DMA2_PER_OP];
+#pragma unroll
+  for (int i = 0; i < DMA2_PER_OP; ++i) {
+    const int p = (w * DMA2_PER_OP + i) * 64 + lane;
+    const int r = p >> 3;
+    const int c = (p & 7) ^ ((r >> 1) & 7);
+    const int64_t rv = r < vrows ? r : vrows - 1;
+    const int64_t rt = r < trows ? r : trows - 1;
+    if (BUF) {
+      oa[i] = uint32_t((rv * ld_w + c * 8) * 2);
+      ob[i] = uint32_t((rt * ld_h + c * 8) * 2);
+    } else {
+      const int64_t hrow = row_map ? int64_t(row_map[t0 + rt]) : t0 + rt;
+      ga[i] = weight + (v0 + rv) * ld_w + c * 8;
+      gb[i] = hidden + hrow * ld_h + c * 8;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(weight + v0 * ld_w), (short)0, int(BUF ? vrows * ld_w * 2 : 0), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(hidden + t0 * ld_h), (short)0, int(BUF ? trows * ld_h * 2 : 0), kBufferFlags);
+  auto dma = [&](int slot, int64_t k0) {
+    if (BUF) {
+      const uint32_t so = uint32_t(k0 * 2);
+#pragma unroll
+      for (int i = 0; i < DMA2_PER_OP; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(SA(slot) + (wu * DMA2_PER_OP + i) * 64), 16,
+                                                 oa[i], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_t*)(SB(slot) + (wu * DMA2_PER_OP + i) * 64), 16,
+                                                 ob[i], so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA2_PER_OP; ++i) {
+        __builtin_amdgcn_global_load_lds(ga[i] + k0, (lds_void_t*)(SA(slot) + (wu * DMA2_PER_OP + i) * 64), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds(gb[i] + k0, (lds_void_t*)(SB(slot) + (wu * DMA2_PER_OP + i) * 64), 16, 0,
+                                         0);
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  typedef bf16x8 Frags[2][4];
+  // fragments of half h (K 32h .. 32h+31) of the stage in `slot`
+  auto read_half = [&](int slot, int h, Frags& fa, Frags& fb) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[kk][i] = as_bf16x8(SA(slot)[swz8(wv * 128 + 32 * i + lr, 4 * h + 2 * kk + lh)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[kk][j] = as_bf16x8(SB(slot)[swz8(wt * 128 + 32 * j + lr, 4 * h + 2 * kk + lh)]);
+    }
+  };
+  auto mma = [&](const Frags& fa, const Frags& fb) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+  };
+  auto bar = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  const int nk = int(H / BK2);
+  // prologue: stages 0 and 1 (clamped) into slots 0 and 1; half 0 of stage 0 into register set 0
+  dma(0, 0);
+  dma(1, int64_t(1 < nk ? 1 : 0) * BK2);
+  Frags fa0, fb0, fa1, fb1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA2_PER_STAGE));
+  bar();
+  read_half(0, 0, fa0, fb0);
+  // Stage S (slot S % 2), sub-step 0: read half 1 of S into set 1, MFMAs of
+  // half 0 (set 0).  Sub-step 1: wait until this wave's loads of stage S+1
+  // (the only ones in flight) and its reads of slot S % 2 are done; barrier;
+  // read half 0 of S+1 into set 0, refill slot S % 2 with stage S+2 (clamped
+  // to the last stage: unconditional loads keep the wait counts exact), MFMAs
+  // of half 1 (set 1).  The refill's slot is a separate LDS array from the one
+  // being read, so the compiler's wait tracking never drains the loads before
+  // a read.  The last stage's read of stage nk re-reads a clamped duplicate.
+  auto stage = [&](int u, int S) {
+    read_half(u, 1, fa1, fb1);
+    mma(fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    bar();
+    read_half(u ^ 1, 0, fa0, fb0);
+    const int pf = S + 2 < nk ? S + 2 : nk - 1;
+    dma(u, int64_t(pf) * BK2);
+    mma(fa1, fb1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int nk2 = nk - REM;
+  for (int S = 0; S < nk2; S += 2) {
+    stage(0, S);
+    stage(1, S + 1);
+  }
+  if (REM) stage(0, nk2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
+  __syncthreads();
+  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials,
+                zy_raw);
+}
+
 __global__ void round_hidden_kernel(const float* __restrict__ h, int64_t ld, int64_t rows, int64_t H,
                                     uint16_t* __restrict__ out) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -582,7 +767,19 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
   float4* part = static_cast<float4*>(partials);
   // buffer offsets are 32-bit: a 256-row tile of either operand must span < 2 GiB
   const bool buf_ok = !row_map && int64_t(BV) * ld_weight * 2 <= 0x7FFFFFFF && int64_t(BT) * ld_hidden * 2 <= 0x7FFFFFFF;
-  if (H % BK == 0) {
+  if (H % BK2 == 0) {
+    const int rem = int((H / BK2) % 2);
+#define VS_LAUNCH_WIDE(B, R)                                                                                     \
+  fused_partials_wide_kernel<B, R><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,        \
+                                                   temp_scalar, targets, row_map, row_count, nv, nt, gv, part, zy_raw)
+    switch (rem + (buf_ok ? 0 : 2)) {
+      case 0: VS_LAUNCH_WIDE(true, 0); break;
+      case 1: VS_LAUNCH_WIDE(true, 1); break;
+      case 2: VS_LAUNCH_WIDE(false, 0); break;
+      default: VS_LAUNCH_WIDE(false, 1); break;
+    }
+#undef VS_LAUNCH_WIDE
+  } else if (H % BK == 0) {
     const int rem = int((H / BK) % NSTAGE);
 #define VS_LAUNCH_PIPELINED(B, R)                                                                                  \
   fused_partials_pipelined_kernel<B, R><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,     \
