@@ -19,19 +19,6 @@ namespace {
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 8;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming 16-byte load: the logits are read exactly once.
-__device__ __forceinline__ uint4 stream_load(const uint4* p) {
-  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ float4 stream_load(const float4* p) {
-  f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-
 // Fold n raw logits into the online state (base-2 units, u = x * c).  The
 // exponent of each term is one FMA; the floor is applied only inside the
 // entropy term, so a -inf logit adds exactly 0 and a NaN poisons s.

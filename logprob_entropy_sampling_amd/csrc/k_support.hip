@@ -135,11 +135,11 @@ __global__ __launch_bounds__(NT) void support_kernel(
       float acc0 = 0.0f, acc1 = 0.0f;
       int64_t q = lane;
       for (; q + 64 < nch; q += 128) {
-        const uint4 w0 = wrow[q], w1 = wrow[q + 64];
+        const uint4 w0 = stream_load(wrow + q), w1 = stream_load(wrow + q + 64);
         acc0 = dot8(w0, hs[q], acc0);
         acc1 = dot8(w1, hs[q + 64], acc1);
       }
-      for (; q < nch; q += 64) acc0 = dot8(wrow[q], hs[q], acc0);
+      for (; q < nch; q += 64) acc0 = dot8(stream_load(wrow + q), hs[q], acc0);
       float acc = acc0 + acc1;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) acc += shfl_xor_f(acc, off);
