@@ -281,17 +281,30 @@ struct StreamKeys {
     }
   }
   __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& bad, uint32_t& kmax) {
-    bad = 0;
     kmax = 0;
+    uint32_t kmin = 0xFFFFu;
     vkey[0] = vkey[1] = 0;
     vq[0] = vq[1] = -1;
     dropped = 0;
     have_top = true;
-    auto one = [&](uint32_t h) -> uint32_t {
-      bad |= raw_bad(h) ? 1u : 0u;
-      const uint32_t k = key16(h);
-      atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
-      return k;
+    auto count = [&](uint32_t k) { atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u); };
+    // the keys of both bf16 halves of a word at once: sign set -> h ^ 0xFFFF,
+    // clear -> h | 0x8000 (= h ^ 0x8000); then -0 (key 0x7FFF) onto +0
+    auto pair = [&](uint32_t w) -> uint32_t {
+      const uint32_t sgn = (w >> 15) & 0x00010001u;
+      const uint32_t keys = w ^ ((sgn * 0x7FFFu) | 0x80008000u);
+      uint32_t k0 = keys & 0xFFFFu, k1 = keys >> 16;
+      k0 = k0 == 0x7FFFu ? 0x8000u : k0;
+      k1 = k1 == 0x7FFFu ? 0x8000u : k1;
+      count(k0);
+      count(k1);
+      kmin = min(kmin, min(k0, k1));
+      return max(k0, k1);
+    };
+    auto vector = [&](const uint4& v, int qv) {
+      const uint32_t vmax = max(max(pair(v.x), pair(v.y)), max(pair(v.z), pair(v.w)));
+      kmax = max(kmax, vmax);
+      offer_vector(vmax, qv);
     };
     constexpr int nt = kThreads;
     const int nvec = aligned() ? V / 8 : 0;
@@ -302,29 +315,19 @@ struct StreamKeys {
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * nt];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        uint32_t vmax = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vmax = max(vmax, max(one(w[e] & 0xFFFFu), one(w[e] >> 16)));
-        kmax = max(kmax, vmax);
-        offer_vector(vmax, q + u * nt);
-      }
+      for (int u = 0; u < kInFlight; ++u) vector(v[u], q + u * nt);
     }
-    for (; q < nvec; q += nt) {
-      const uint4 v = pv[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t vmax = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vmax = max(vmax, max(one(w[e] & 0xFFFFu), one(w[e] >> 16)));
-      kmax = max(kmax, vmax);
-      offer_vector(vmax, q);
-    }
+    for (; q < nvec; q += nt) vector(pv[q], q);
     for (int c = 8 * nvec + int(threadIdx.x); c < V; c += nt) {
-      const uint32_t k = one(rowp[c]);
+      const uint32_t k = key16(rowp[c]);
+      count(k);
+      kmin = min(kmin, k);
       kmax = max(kmax, k);
       dropped = max(dropped, k);
     }
+    // NaN and +inf map to keys >= 0xFF80, negative NaNs to keys <= 0x007E
+    // (-inf is 0x007F): the row is bad exactly when a key falls outside
+    bad = (kmax >= 0xFF80u || kmin <= 0x007Eu) ? 1u : 0u;
   }
   template <class F>
   __device__ __forceinline__ void each(F f) const {

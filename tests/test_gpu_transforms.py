@@ -154,6 +154,38 @@ def test_bad_rows(vsa):
     assert (got["support_ids"][:8] == -1).all()
 
 
+def test_streaming_rows_special_values(vsa):
+    """Rows longer than the register budget (the streaming kernel): NaN, +inf, a negative NaN, -inf,
+    -0 next to +0 (one key), a row whose maximum is -0.  V is odd, so rows alternate between
+    16-byte-vector loads (even rows) and the per-element path (odd rows)."""
+    say("transforms: streaming rows V=90001 with NaN / +inf / -NaN / -inf / signed zeros")
+    rng = np.random.default_rng(17)
+    T, V = 10, 90001
+    vals = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    bits = workloads.to_bf16_bits(vals)
+    bits[0, 7] = 0x7FC0                     # NaN
+    bits[1, V - 1] = 0x7F80                 # +inf in the last column
+    bits[2, 12345] = 0xFFC0                 # negative NaN
+    bits[3, ::3] = 0xFF80                   # -inf: legal
+    bits[4, :] = np.where(rng.random(V) < 0.5, 0x8000, 0x0000)  # only signed zeros: one tie group
+    bits[4, :50] = workloads.to_bf16_bits(np.abs(vals[4, :50]) + np.float32(0.5))
+    bits[5, :] = workloads.to_bf16_bits(-np.abs(vals[5]) - np.float32(0.25))
+    bits[5, rng.choice(V, 40, replace=False)] = 0x8000   # the row maximum is -0 (40 tokens)
+    bits[5, rng.choice(V, 40, replace=False)] = 0x0000   # ... tied with +0
+    bits[6, rng.choice(V, 300, replace=False)] = 0x8000
+    bits[6, rng.choice(V, 300, replace=False)] = 0x0000
+    k = np.array([0, 0, 0, 20, 60, 30, 0, 5, 0, 1000], np.int32)
+    p = np.array([1, 1, 1, 0.9, 1, 1, 0.95, 0.8, 0.5, 1], np.float32)
+    mp = np.array([0, 0, 0, 0.05, 0, 0, 0, 0, 0.05, 0], np.float32)
+    tau = np.array([1, 1, 1, 0.7, 1, 1, 1, 0.7, 1, 1], np.float32)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    y = _support_sample(np.where(np.isnan(x64) | (x64 == np.inf), 0.0, x64), tau, k, p, mp, rng.random(T))
+    got = _run(vsa, bits, tau, k, p, mp, y, 64)
+    ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=64)
+    assert list(ref["status"][:3] & oracle.ST_BAD_INPUT) == [oracle.ST_BAD_INPUT] * 3
+    _compare(got, ref, 64, "streaming special values")
+
+
 def test_identity_and_singleton(vsa):
     say("transforms: identity program == full-vocabulary scoring; top-k 1 == exact zeros")
     c = workloads.make(5, T=8, V=30000)
