@@ -42,7 +42,6 @@ constexpr int MAX_WAVES = NT_STREAM / 64;
 constexpr int HALF = 32768;
 constexpr int SEGW = 64;
 constexpr int NSEG = 65536 / SEGW;       // 1024
-constexpr int SEG_PER_LANE = NSEG / 64;  // 16
 constexpr int COLLECT_MAX = 4096;
 constexpr uint32_t KEY_NEG_INF = 0x007Fu;
 constexpr int kInFlight = 4;  // 16-byte loads per thread in flight in a streaming pass (1024 threads)
@@ -53,9 +52,8 @@ struct Smem {
   double seg_mass[NSEG];
   double seg_zmass[NSEG];
   uint32_t fine[SEGW];  // 32-bit counts of one segment (stream kernel)
-  uint32_t lane_cnt[64], lane_cnt_before[64];
-  double lane_mass[64], lane_mass_before[64], lane_zmass[64], lane_zmass_before[64];
   uint32_t red_u[MAX_WAVES];
+  double red_m[MAX_WAVES], red_z[MAX_WAVES];
   uint32_t bu[8];  // broadcast slots (integers)
   double bd[8];    // broadcast slots (fp64)
   int fine_seg;
@@ -514,20 +512,23 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   const int lane = tid & 63;
   const bool w0 = tid < 64;
 
-  // lane l of wave 0 owns segments 1023-16l .. 1008-16l (descending keys)
-  if (w0) {
+  // Segment prefixes in descending key order, in place: afterwards
+  // seg_count[s] / seg_mass[s] / seg_zmass[s] hold the tokens / mass / z-mass
+  // of all segments >= s.  Thread t owns descending positions SPT*t ..
+  // SPT*t + SPT-1; a wave scan and a scan over the wave totals follow, all in
+  // a fixed order (bitwise reproducible).
+  {
+    constexpr int SPT = NSEG / NTH;
+    const int wave = tid >> 6;
     uint32_t c = 0;
     double m = 0.0, zm = 0.0;
-    for (int i = 0; i < SEG_PER_LANE; ++i) {
-      const int s = NSEG - 1 - SEG_PER_LANE * lane - i;
-      c += sm.seg_count[s];
-      m += sm.seg_mass[s];
-      zm += sm.seg_zmass[s];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sg = NSEG - 1 - (SPT * tid + i);
+      c += sm.seg_count[sg];
+      m += sm.seg_mass[sg];
+      zm += sm.seg_zmass[sg];
     }
-    sm.lane_cnt[lane] = c;
-    sm.lane_mass[lane] = m;
-    sm.lane_zmass[lane] = zm;
-    // inclusive scan over the lanes (fixed tree), then shifted by one lane
     uint32_t ci = c;
     double mi = m, zi = zm;
 #pragma unroll
@@ -541,87 +542,77 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
         zi += zo;
       }
     }
-    const uint32_t ce = __shfl_up(ci, 1, 64);
-    const double me = __shfl_up(mi, 1, 64);
-    const double ze = __shfl_up(zi, 1, 64);
-    sm.lane_cnt_before[lane] = lane ? ce : 0u;
-    sm.lane_mass_before[lane] = lane ? me : 0.0;
-    sm.lane_zmass_before[lane] = lane ? ze : 0.0;
-    if (lane == 63) sm.bd[7] = mi;  // total mass relative to the row max
-  }
-  __syncthreads();
-  const double total_mass = sm.bd[7];
-
-  // Segment holding rank r (0-based): bu[0] = segment, bu[1] = tokens above it,
-  // bd[0] / bd[1] = mass / z-mass above it.
-  auto seg_of_rank = [&](uint32_t r) {
-    if (w0) {
-      const uint32_t cb = sm.lane_cnt_before[lane];
-      if (r >= cb && r < cb + sm.lane_cnt[lane]) {
-        uint32_t c = cb;
-        double m = sm.lane_mass_before[lane], zm = sm.lane_zmass_before[lane];
-        int s = NSEG - 1 - SEG_PER_LANE * lane;
-        for (int i = 0; i < SEG_PER_LANE; ++i, --s) {
-          if (r < c + sm.seg_count[s]) break;
-          c += sm.seg_count[s];
-          m += sm.seg_mass[s];
-          zm += sm.seg_zmass[s];
-        }
-        sm.bu[0] = uint32_t(s);
-        sm.bu[1] = c;
-        sm.bd[0] = m;
-        sm.bd[1] = zm;
-      }
+    if (lane == 63) {
+      sm.red_u[wave] = ci;
+      sm.red_m[wave] = mi;
+      sm.red_z[wave] = zi;
     }
     __syncthreads();
+    uint32_t cw = 0;
+    double mw = 0.0, zw = 0.0;
+    for (int i = 0; i < wave; ++i) {
+      cw += sm.red_u[i];
+      mw += sm.red_m[i];
+      zw += sm.red_z[i];
+    }
+    // exclusive start of this thread, then its own positions one by one
+    c = cw + (ci - c);
+    m = mw + (mi - m);
+    zm = zw + (zi - zm);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sg = NSEG - 1 - (SPT * tid + i);
+      c += sm.seg_count[sg];
+      m += sm.seg_mass[sg];
+      zm += sm.seg_zmass[sg];
+      sm.seg_count[sg] = c;
+      sm.seg_mass[sg] = m;
+      sm.seg_zmass[sg] = zm;
+    }
+  }
+  __syncthreads();
+  const double total_mass = sm.seg_mass[0];
+  // tokens / mass / z-mass of the segments above s (s excluded)
+  auto cnt_above = [&](int s) -> uint32_t { return s + 1 < NSEG ? sm.seg_count[s + 1] : 0u; };
+  auto mass_above = [&](int s) -> double { return s + 1 < NSEG ? sm.seg_mass[s + 1] : 0.0; };
+  auto zmass_above = [&](int s) -> double { return s + 1 < NSEG ? sm.seg_zmass[s + 1] : 0.0; };
+  auto put_seg = [&](int s) {
+    sm.bu[0] = uint32_t(s);
+    sm.bu[1] = cnt_above(s);
+    sm.bd[0] = mass_above(s);
+    sm.bd[1] = zmass_above(s);
   };
-  // First segment whose running mass (descending) reaches T, 0 < T < total.
+
+  // Segment holding rank r (0-based, r < total): bu[0] = segment, bu[1] =
+  // tokens above it, bd[0] / bd[1] = mass / z-mass above it.  One segment
+  // satisfies above <= r < above + own; every thread tests its own.
+  auto seg_of_rank = [&](uint32_t r) {
+    for (int sg = tid; sg < NSEG; sg += NTH)
+      if (r >= cnt_above(sg) && r < sm.seg_count[sg]) put_seg(sg);
+    __syncthreads();
+  };
+  // First non-empty segment (descending) whose running mass reaches T.
+  // Should rounding keep T past the total, the lowest non-empty segment.
+  // Picked by a block maximum over a score (hits outrank the rest, the first
+  // hit wins), so the answer is unique even where fp64 rounding across
+  // thread boundaries makes the prefix dip by an ulp.
   auto seg_of_mass = [&](double T) {
-    if (w0) {
-      const double mb = sm.lane_mass_before[lane];
-      const bool last = lane == 63 || sm.lane_mass_before[lane + 1] >= T;
-      if (mb < T && last) {
-        uint32_t c = sm.lane_cnt_before[lane];
-        double m = mb, zm = sm.lane_zmass_before[lane];
-        int s = NSEG - 1 - SEG_PER_LANE * lane;
-        int found = s;
-        uint32_t fc = c;
-        double fm = m, fz = zm;
-        for (int i = 0; i < SEG_PER_LANE; ++i, --s) {
-          if (sm.seg_count[s] == 0) continue;
-          found = s;  // the last non-empty one, should rounding never reach T
-          fc = c;
-          fm = m;
-          fz = zm;
-          if (m + sm.seg_mass[s] >= T) break;
-          c += sm.seg_count[s];
-          m += sm.seg_mass[s];
-          zm += sm.seg_zmass[s];
-        }
-        sm.bu[0] = uint32_t(found);
-        sm.bu[1] = fc;
-        sm.bd[0] = fm;
-        sm.bd[1] = fz;
+    uint32_t best = 0;
+    for (int sg = tid; sg < NSEG; sg += NTH) {
+      const uint32_t pos = uint32_t(NSEG - 1 - sg);  // descending position
+      if (sm.seg_count[sg] > cnt_above(sg)) {
+        const uint32_t score = sm.seg_mass[sg] >= T ? (0x80000000u | (0xFFFFu - pos)) : (pos + 1u);
+        best = max(best, score);
       }
     }
+    best = block_max_u32<NW>(best, sm);
+    const uint32_t pos = (best & 0x80000000u) ? 0xFFFFu - (best & 0xFFFFu) : best - 1u;
+    if (tid == 0) put_seg(NSEG - 1 - int(pos));
     __syncthreads();
   };
   // Tokens / mass above segment s (s excluded).
-  auto seg_above = [&](int s) {
-    if (tid == 0) {
-      const int l = (NSEG - 1 - s) / SEG_PER_LANE;
-      uint32_t c = sm.lane_cnt_before[l];
-      double m = sm.lane_mass_before[l], zm = sm.lane_zmass_before[l];
-      for (int t = NSEG - 1 - SEG_PER_LANE * l; t > s; --t) {
-        c += sm.seg_count[t];
-        m += sm.seg_mass[t];
-        zm += sm.seg_zmass[t];
-      }
-      sm.bu[0] = uint32_t(s);
-      sm.bu[1] = c;
-      sm.bd[0] = m;
-      sm.bd[1] = zm;
-    }
+  auto seg_above = [&](int sg) {
+    if (tid == 0) put_seg(sg);
     __syncthreads();
   };
   // Inside the segment in bu[0] (above-values in bu[1], bd[0], bd[1]): the key
@@ -706,21 +697,34 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   // ---- min-p against the row max: the smallest key whose weight reaches min_p ----
   uint32_t L_m = Vu;
   if (a.mpf > 0.0f) {
-    if (tid == 0) {
-      // bisect on z - z_max >= ln(min_p), then settle the boundary with the
-      // program's own test exp(z - z_max) >= min_p (keys are in logit order,
-      // so both predicates hold on an upper range of keys)
-      uint32_t lo = KEY_NEG_INF + 1, hi = kmax;  // weight(kmax) = 1 >= min_p
+    if (w0) {
+      // the smallest key with z - z_max >= ln(min_p): a 64-way search (each
+      // lane tests one key per round, ~3 rounds over 65536 keys), then the
+      // boundary is settled with the program's own test exp(z - z_max) >=
+      // min_p (keys are in logit order, so both predicates hold on an upper
+      // range of keys)
+      uint32_t lo = KEY_NEG_INF + 1, hi = kmax;  // the answer is in [lo, hi]; weight(kmax) = 1 >= min_p
       const double mp = double(a.mpf);
       const double lmp = log(mp);
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (double(key_logit(mid)) / tau - z0 >= lmp) hi = mid;
-        else lo = mid + 1;
+      while (lo < hi) {  // wave-uniform
+        const uint32_t step = (hi - lo + 63u) / 64u;
+        const uint32_t kl = lo + uint32_t(lane) * step;
+        const uint32_t k = kl < hi ? kl : hi;
+        const unsigned long long bal = __ballot(double(key_logit(k)) / tau - z0 >= lmp);
+        if (bal == 0) {
+          lo = lo + 63u * step + 1u;  // every tested key fails: the answer lies above lane 63's
+        } else {
+          const uint32_t f = uint32_t(__ffsll(bal) - 1);
+          const uint32_t kf = lo + f * step;
+          hi = kf < hi ? kf : hi;
+          lo = f == 0 ? lo : lo + (f - 1) * step + 1u;
+        }
       }
-      while (lo > KEY_NEG_INF + 1 && key_weight(lo - 1, tau, z0) >= mp) --lo;
-      while (lo < kmax && key_weight(lo, tau, z0) < mp) ++lo;
-      sm.bu[5] = lo;
+      if (lane == 0) {
+        while (lo > KEY_NEG_INF + 1 && key_weight(lo - 1, tau, z0) >= mp) --lo;
+        while (lo < kmax && key_weight(lo, tau, z0) < mp) ++lo;
+        sm.bu[5] = lo;
+      }
     }
     __syncthreads();
     const uint32_t km = sm.bu[5];
