@@ -797,60 +797,47 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     }
     __syncthreads();
     const uint32_t nc = sm.ncand;
-    uint32_t P = 1;
-    while (P < nc) P <<= 1;
-    for (uint32_t i = nc + tid; i < P; i += NTH) cand[i] = 0;
-    __syncthreads();
-    // bitonic sort, descending: key descending, token id ascending
-    if (P <= 128) {
-      // one wave, two elements per lane (indices lane, lane + 64), no barriers
-      if (w0) {
-        uint64_t e[2];
-        e[0] = uint32_t(lane) < P ? cand[lane] : 0ull;
-        e[1] = uint32_t(lane) + 64 < P ? cand[lane + 64] : 0ull;
-        for (uint32_t size = 2; size <= P; size <<= 1) {
-          for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride == 64) {  // partner of index lane is lane + 64: the same lane
-              const bool desc = (uint32_t(lane) & size) == 0;
-              const uint64_t hi = e[0] > e[1] ? e[0] : e[1], lo = e[0] > e[1] ? e[1] : e[0];
-              e[0] = desc ? hi : lo;
-              e[1] = desc ? lo : hi;
-            } else {
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const uint32_t idx = uint32_t(lane) + 64u * uint32_t(h);
-                const uint64_t pv = __shfl_xor(e[h], int(stride), 64);
-                const bool keep_max = ((idx & stride) == 0) == ((idx & size) == 0);
-                e[h] = keep_max ? (e[h] > pv ? e[h] : pv) : (e[h] < pv ? e[h] : pv);
+    int64_t* out = a.ids_out + a.row * a.cap;
+    const uint32_t n_sorted = with_ties ? n_out : above_c;
+    auto id_of = [](uint64_t e) { return int64_t(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)); };
+    if (nc <= uint32_t(NTH)) {
+      // rank placement: the candidates are distinct, so each one's position in
+      // (key desc, id asc) order is the number of larger ones (the list is
+      // read by all threads at once, LDS broadcast, no barriers)
+      if (tid < int(nc)) {
+        const uint64_t mine = cand[tid];
+        uint32_t rank = 0;
+        uint32_t j = 0;
+        for (; j + 4 <= nc; j += 4)
+          rank += uint32_t(cand[j] > mine) + uint32_t(cand[j + 1] > mine) + uint32_t(cand[j + 2] > mine) +
+                  uint32_t(cand[j + 3] > mine);
+        for (; j < nc; ++j) rank += uint32_t(cand[j] > mine);
+        if (rank < n_sorted) out[rank] = id_of(mine);
+      }
+    } else {
+      uint32_t P = 1;
+      while (P < nc) P <<= 1;
+      for (uint32_t i = nc + tid; i < P; i += NTH) cand[i] = 0;
+      __syncthreads();
+      // bitonic sort, descending: key descending, token id ascending
+      for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          for (uint32_t i = tid; i < P; i += NTH) {
+            const uint32_t pidx = i ^ stride;
+            if (pidx > i) {
+              const uint64_t x = cand[i], z = cand[pidx];
+              const bool desc = (i & size) == 0;
+              if (desc ? (x < z) : (x > z)) {
+                cand[i] = z;
+                cand[pidx] = x;
               }
             }
           }
+          __syncthreads();
         }
-        if (uint32_t(lane) < P) cand[lane] = e[0];
-        if (uint32_t(lane) + 64 < P) cand[lane + 64] = e[1];
       }
-      __syncthreads();
-    } else {
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = tid; i < P; i += NTH) {
-          const uint32_t pidx = i ^ stride;
-          if (pidx > i) {
-            const uint64_t x = cand[i], z = cand[pidx];
-            const bool desc = (i & size) == 0;
-            if (desc ? (x < z) : (x > z)) {
-              cand[i] = z;
-              cand[pidx] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
+      for (uint32_t i = tid; i < n_sorted; i += NTH) out[i] = id_of(cand[i]);
     }
-    }
-    int64_t* out = a.ids_out + a.row * a.cap;
-    const uint32_t n_sorted = with_ties ? n_out : above_c;
-    for (uint32_t i = tid; i < n_sorted; i += NTH) out[i] = int64_t(0xFFFFFFFFu - uint32_t(cand[i] & 0xFFFFFFFFu));
     for (uint32_t i = n_out + tid; i < uint32_t(a.cap); i += NTH) out[i] = -1;
     if (!with_ties) {
       // a very large tie group at K_c: its first r_c tokens in column order, slice by slice
