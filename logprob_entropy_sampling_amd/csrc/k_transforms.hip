@@ -58,6 +58,7 @@ struct Smem {
   double bd[8];    // broadcast slots (fp64)
   int fine_seg;
   uint32_t ncand;
+  uint32_t zero_overflow;  // the -0 / +0 merge of the streaming count passed 16 bits
 };
 
 // raw bf16 pattern -> order-preserving key (-0 folded onto +0)
@@ -287,20 +288,22 @@ struct StreamKeys {
     have_top = true;
     auto count = [&](uint32_t k) { atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u); };
     // the keys of both bf16 halves of a word at once: sign set -> h ^ 0xFFFF,
-    // clear -> h | 0x8000 (= h ^ 0x8000); then -0 (key 0x7FFF) onto +0
+    // clear -> h | 0x8000 (= h ^ 0x8000).  -0 keeps its key 0x7FFF here: its
+    // count is merged into +0's (0x8000) once counting is done (merge_zero),
+    // and a vector's largest key is folded below, which is all the
+    // candidate lists and the row max need.
     auto pair = [&](uint32_t w) -> uint32_t {
       const uint32_t sgn = (w >> 15) & 0x00010001u;
       const uint32_t keys = w ^ ((sgn * 0x7FFFu) | 0x80008000u);
-      uint32_t k0 = keys & 0xFFFFu, k1 = keys >> 16;
-      k0 = k0 == 0x7FFFu ? 0x8000u : k0;
-      k1 = k1 == 0x7FFFu ? 0x8000u : k1;
+      const uint32_t k0 = keys & 0xFFFFu, k1 = keys >> 16;
       count(k0);
       count(k1);
       kmin = min(kmin, min(k0, k1));
       return max(k0, k1);
     };
     auto vector = [&](const uint4& v, int qv) {
-      const uint32_t vmax = max(max(pair(v.x), pair(v.y)), max(pair(v.z), pair(v.w)));
+      uint32_t vmax = max(max(pair(v.x), pair(v.y)), max(pair(v.z), pair(v.w)));
+      vmax = vmax == 0x7FFFu ? 0x8000u : vmax;
       kmax = max(kmax, vmax);
       offer_vector(vmax, qv);
     };
@@ -326,6 +329,18 @@ struct StreamKeys {
     // NaN and +inf map to keys >= 0xFF80, negative NaNs to keys <= 0x007E
     // (-inf is 0x007F): the row is bad exactly when a key falls outside
     bad = (kmax >= 0xFF80u || kmin <= 0x007Eu) ? 1u : 0u;
+  }
+  // After counting: move the tokens counted under -0's key (0x7FFF, high half
+  // of word 0x3FFF) to +0's (0x8000, low half of word 0x4000).  Returns false
+  // when the merged count does not fit 16 bits.  One thread.
+  __device__ __forceinline__ static bool merge_zero(uint32_t* hist) {
+    const uint32_t w1 = hist[0x3FFF], w2 = hist[0x4000];
+    const uint32_t a = w1 >> 16, b = w2 & 0xFFFFu;
+    if (a == 0) return true;
+    if (a + b > 0xFFFFu) return false;
+    hist[0x3FFF] = w1 & 0xFFFFu;
+    hist[0x4000] = (w2 & 0xFFFF0000u) | (a + b);
+    return true;
   }
   template <class F>
   __device__ __forceinline__ void each(F f) const {
@@ -936,6 +951,9 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
     n_pad = 0;
   }
   kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
+  if constexpr (NV == 0) {  // (the barriers of the next block maximum publish the merge)
+    if (tid == 0) sm.zero_overflow = StreamKeys::merge_zero(sm.hist) ? 0u : 1u;
+  }
   bad = block_max_u32<NW>(bad, sm);
   if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
     if (tid == 0) handoff[a.row] = 0;
@@ -952,7 +970,7 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
   // every counter stayed below 2^16 iff the counts add up to the token count
   // (a carry out of a low half, or out of a word, breaks the total); the sum
   // also orders the segment summaries before the queries read them
-  if (block_sum_u32<NW>(part, sm) != uint32_t(V)) {
+  if (block_sum_u32<NW>(part, sm) != uint32_t(V) || (NV == 0 && sm.zero_overflow)) {
     if (tid == 0) handoff[a.row] = 1;
     return;
   }

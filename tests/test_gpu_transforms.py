@@ -156,7 +156,8 @@ def test_bad_rows(vsa):
 
 def test_streaming_rows_special_values(vsa):
     """Rows longer than the register budget (the streaming kernel): NaN, +inf, a negative NaN, -inf,
-    -0 next to +0 (one key), a row whose maximum is -0.  V is odd, so rows alternate between
+    -0 next to +0 (one key), a row whose maximum is -0, a zero key whose -0 and +0 counts only
+    together pass 16 bits.  V is odd, so rows alternate between
     16-byte-vector loads (even rows) and the per-element path (odd rows)."""
     say("transforms: streaming rows V=90001 with NaN / +inf / -NaN / -inf / signed zeros")
     rng = np.random.default_rng(17)
@@ -174,9 +175,12 @@ def test_streaming_rows_special_values(vsa):
     bits[5, rng.choice(V, 40, replace=False)] = 0x0000   # ... tied with +0
     bits[6, rng.choice(V, 300, replace=False)] = 0x8000
     bits[6, rng.choice(V, 300, replace=False)] = 0x0000
-    k = np.array([0, 0, 0, 20, 60, 30, 0, 5, 0, 1000], np.int32)
-    p = np.array([1, 1, 1, 0.9, 1, 1, 0.95, 0.8, 0.5, 1], np.float32)
-    mp = np.array([0, 0, 0, 0.05, 0, 0, 0, 0, 0.05, 0], np.float32)
+    zs = rng.permutation(V)[:89000]  # 45000 x -0 and 44000 x +0: each fits 16 bits, together they do not
+    bits[8, zs[:45000]] = 0x8000
+    bits[8, zs[45000:]] = 0x0000
+    k = np.array([0, 0, 0, 20, 60, 30, 0, 5, 600, 1000], np.int32)  # row 8: the cut falls inside the zero key
+    p = np.array([1, 1, 1, 0.9, 1, 1, 0.95, 0.8, 1, 1], np.float32)
+    mp = np.array([0, 0, 0, 0.05, 0, 0, 0, 0, 0, 0], np.float32)
     tau = np.array([1, 1, 1, 0.7, 1, 1, 1, 0.7, 1, 1], np.float32)
     x64 = oracle.logits_from_logits(bits, "bf16")
     y = _support_sample(np.where(np.isnan(x64) | (x64 == np.inf), 0.0, x64), tau, k, p, mp, rng.random(T))
