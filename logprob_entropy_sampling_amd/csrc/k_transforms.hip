@@ -72,6 +72,40 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 }
 __device__ __forceinline__ bool raw_bad(uint32_t h) { return (h & 0x7FFFu) >= 0x7F80u && h != 0xFF80u; }
 
+// Inclusive prefix sums across the 64 lanes of a wave with DPP moves (no LDS
+// traffic, unlike lane shuffles): shifts by 1, 2, 4, 8 inside each row of 16
+// lanes (lanes shifted in from outside a row read 0), then lane 15 of rows 0
+// and 2 added into rows 1 and 3, then lane 31 into rows 2 and 3.  A fixed
+// order, so results are reproducible.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xf, true));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(uint32_t(b)), hi = dpp_u32<CTRL, ROW_MASK>(uint32_t(b >> 32));
+  return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+template <class T, class Move>
+__device__ __forceinline__ T wave_scan_incl(T x, Move mv) {
+  x += mv(x, std::integral_constant<int, kRowShr1>{}, std::integral_constant<int, 0xf>{});
+  x += mv(x, std::integral_constant<int, kRowShr2>{}, std::integral_constant<int, 0xf>{});
+  x += mv(x, std::integral_constant<int, kRowShr4>{}, std::integral_constant<int, 0xf>{});
+  x += mv(x, std::integral_constant<int, kRowShr8>{}, std::integral_constant<int, 0xf>{});
+  x += mv(x, std::integral_constant<int, kRowBcast15>{}, std::integral_constant<int, 0xa>{});
+  x += mv(x, std::integral_constant<int, kRowBcast31>{}, std::integral_constant<int, 0xc>{});
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t x) {
+  return wave_scan_incl(x, [](uint32_t v, auto c, auto m) { return dpp_u32<decltype(c)::value, decltype(m)::value>(v); });
+}
+__device__ __forceinline__ double wave_scan_incl_f64(double x) {
+  return wave_scan_incl(x, [](double v, auto c, auto m) { return dpp_f64<decltype(c)::value, decltype(m)::value>(v); });
+}
+
 template <int NW>
 __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
 #pragma unroll
@@ -544,19 +578,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
       m += sm.seg_mass[sg];
       zm += sm.seg_zmass[sg];
     }
-    uint32_t ci = c;
-    double mi = m, zi = zm;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t co = __shfl_up(ci, off, 64);
-      const double mo = __shfl_up(mi, off, 64);
-      const double zo = __shfl_up(zi, off, 64);
-      if (lane >= off) {
-        ci += co;
-        mi += mo;
-        zi += zo;
-      }
-    }
+    const uint32_t ci = wave_scan_incl_u32(c);
+    const double mi = wave_scan_incl_f64(m), zi = wave_scan_incl_f64(zm);
     if (lane == 63) {
       sm.red_u[wave] = ci;
       sm.red_m[wave] = mi;
@@ -644,19 +667,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
       const double e = c ? exp(d) : 0.0;
       const double m = double(c) * e;
       const double zm = e > 0.0 ? double(c) * e * d : 0.0;
-      uint32_t ci = c;
-      double mi = m, zi = zm;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t co = __shfl_up(ci, off, 64);
-        const double mo = __shfl_up(mi, off, 64);
-        const double zo = __shfl_up(zi, off, 64);
-        if (lane >= off) {
-          ci += co;
-          mi += mo;
-          zi += zo;
-        }
-      }
+      const uint32_t ci = wave_scan_incl_u32(c);
+      const double mi = wave_scan_incl_f64(m), zi = wave_scan_incl_f64(zm);
       const uint32_t cb = sm.bu[1] + ci - c;
       const double mb = sm.bd[0] + (mi - m);
       const double zb = sm.bd[1] + (zi - zm);
