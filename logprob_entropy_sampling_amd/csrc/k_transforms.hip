@@ -89,27 +89,43 @@ __device__ __forceinline__ double dpp_f64(double v) {
 }
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-template <class T, class Move>
-__device__ __forceinline__ T wave_scan_incl(T x, Move mv) {
-  x += mv(x, std::integral_constant<int, kRowShr1>{}, std::integral_constant<int, 0xf>{});
-  x += mv(x, std::integral_constant<int, kRowShr2>{}, std::integral_constant<int, 0xf>{});
-  x += mv(x, std::integral_constant<int, kRowShr4>{}, std::integral_constant<int, 0xf>{});
-  x += mv(x, std::integral_constant<int, kRowShr8>{}, std::integral_constant<int, 0xf>{});
-  x += mv(x, std::integral_constant<int, kRowBcast15>{}, std::integral_constant<int, 0xa>{});
-  x += mv(x, std::integral_constant<int, kRowBcast31>{}, std::integral_constant<int, 0xc>{});
+template <class T, class Move, class Op>
+__device__ __forceinline__ T wave_scan_incl(T x, Move mv, Op op) {
+  x = op(x, mv(x, std::integral_constant<int, kRowShr1>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, mv(x, std::integral_constant<int, kRowShr2>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, mv(x, std::integral_constant<int, kRowShr4>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, mv(x, std::integral_constant<int, kRowShr8>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, mv(x, std::integral_constant<int, kRowBcast15>{}, std::integral_constant<int, 0xa>{}));
+  x = op(x, mv(x, std::integral_constant<int, kRowBcast31>{}, std::integral_constant<int, 0xc>{}));
   return x;
 }
+struct AddOp {
+  template <class T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
 __device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t x) {
-  return wave_scan_incl(x, [](uint32_t v, auto c, auto m) { return dpp_u32<decltype(c)::value, decltype(m)::value>(v); });
+  return wave_scan_incl(
+      x, [](uint32_t v, auto c, auto m) { return dpp_u32<decltype(c)::value, decltype(m)::value>(v); }, AddOp{});
+}
+// the wave's total / maximum (a running maximum with 0 for lanes shifted in
+// from outside a row: the identity for unsigned values), read from lane 63
+__device__ __forceinline__ uint32_t wave_total_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_readlane(int(wave_scan_incl_u32(x)), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  const uint32_t r = wave_scan_incl(
+      x, [](uint32_t v, auto c, auto m) { return dpp_u32<decltype(c)::value, decltype(m)::value>(v); },
+      [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return uint32_t(__builtin_amdgcn_readlane(int(r), 63));
 }
 __device__ __forceinline__ double wave_scan_incl_f64(double x) {
-  return wave_scan_incl(x, [](double v, auto c, auto m) { return dpp_f64<decltype(c)::value, decltype(m)::value>(v); });
+  return wave_scan_incl(
+      x, [](double v, auto c, auto m) { return dpp_f64<decltype(c)::value, decltype(m)::value>(v); }, AddOp{});
 }
 
 template <int NW>
 __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v = wave_total_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -120,8 +136,7 @@ __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
 }
 template <int NW>
 __device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+  v = wave_max_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -134,12 +149,7 @@ __device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
 template <int NW>
 __device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
   const int lane = threadIdx.x & 63;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_scan_incl_u32(v);
   __syncthreads();
   if (lane == 63) sm.red_u[threadIdx.x >> 6] = incl;
   __syncthreads();
@@ -486,11 +496,7 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
   sm.seg_zmass[seg] = zm;
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_u32(v); }
 
 // All segment summaries in one pass, one thread per segment.  The thread
 // loads the segment's 32 packed count words once (starting at word t % 32, so
