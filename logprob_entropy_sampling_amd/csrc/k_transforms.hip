@@ -72,6 +72,21 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 }
 __device__ __forceinline__ bool raw_bad(uint32_t h) { return (h & 0x7FFFu) >= 0x7F80u && h != 0xFF80u; }
 
+// Packed 16-bit helpers for the count pass (one VALU op per 32-bit word).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// the keys of both bf16 halves of a word, -0 left at 0x7FFF: a per-half
+// arithmetic shift by 15 gives 0xFFFF where the sign is set and 0 elsewhere,
+// so the xor mask is that or 0x8000 (sign set: h ^ 0xFFFF, clear: h ^ 0x8000)
+__device__ __forceinline__ uint32_t pair_keys(uint32_t w) {
+  const s16x2 smear = __builtin_bit_cast(s16x2, w) >> 15;
+  return w ^ (__builtin_bit_cast(uint32_t, smear) | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 // Inclusive prefix sums across the 64 lanes of a wave with DPP moves (no LDS
 // traffic, unlike lane shuffles): shifts by 1, 2, 4, 8 inside each row of 16
 // lanes (lanes shifted in from outside a row read 0), then lane 15 of rows 0
@@ -179,7 +194,7 @@ struct RegKeys {
   __device__ __forceinline__ bool listed_from(uint32_t) const { return false; }
   __device__ __forceinline__ Listed load_listed() const { return Listed{}; }
   template <class F>
-  __device__ __forceinline__ void each_listed(const Listed&, F) const {}
+  __device__ __forceinline__ void each_listed(const Listed&, uint32_t, F) const {}
 
   // Loads the row, converts it to keys and counts every key into the packed
   // 16-bit counters `hist` (already zeroed); returns bad (NaN or +inf seen)
@@ -273,10 +288,12 @@ struct RegKeys {
 struct StreamKeys {
   const uint16_t* rowp;
   int V;
-  // Filled by load_count: this thread's two best 8-token vectors by their
-  // largest key (vector indices, -1 = none) and the largest key of every token
-  // outside them, so every token with a key above `dropped` is in the listed
-  // vectors.  Tail tokens (past the last whole vector) always count as dropped.
+  // Filled by load_count.  The thread's 8-token vectors q and q + kThreads
+  // form a unit (the second absent past the last whole vector).  Kept: the
+  // thread's two best units by their largest key (first vector index, -1 =
+  // none) and the largest key of every token outside them, so every token
+  // with a key above `dropped` is in the listed units.  Tail tokens (past the
+  // last whole vector) always count as dropped.
   uint32_t vkey[2];
   int vq[2];
   uint32_t dropped;
@@ -285,11 +302,12 @@ struct StreamKeys {
   static constexpr bool kTopList = true;
   __device__ __forceinline__ void opaque() {}
   __device__ __forceinline__ bool aligned() const { return (reinterpret_cast<uintptr_t>(rowp) & 15) == 0; }
-  // branch-free update of the two-vector list with vector q of largest key vmax
+  __device__ __forceinline__ int nvec() const { return aligned() ? V / 8 : 0; }
+  // branch-free update of the two-unit list with unit q of largest key vmax
   __device__ __forceinline__ void offer_vector(uint32_t vmax, int q) {
     const bool in0 = vmax > vkey[0];
     const bool in1 = vmax > vkey[1];
-    dropped = max(dropped, in1 ? vkey[1] : vmax);  // the vector that leaves (or never enters)
+    dropped = max(dropped, in1 ? vkey[1] : vmax);  // the unit that leaves (or never enters)
     const uint32_t k1 = in0 ? vkey[0] : (in1 ? vmax : vkey[1]);
     const int q1 = in0 ? vq[0] : (in1 ? q : vq[1]);
     vkey[0] = in0 ? vmax : vkey[0];
@@ -297,82 +315,114 @@ struct StreamKeys {
     vkey[1] = k1;
     vq[1] = q1;
   }
-  // true when every token of this thread with key >= K is in the listed vectors
+  // true when every token of this thread with key >= K is in the listed units
   __device__ __forceinline__ bool listed_from(uint32_t K) const { return have_top && dropped < K; }
   struct Listed {
-    uint4 v[2];
+    uint4 v[4];
   };
-  // the listed vectors' data (issued early; used by each_listed)
-  __device__ __forceinline__ Listed load_listed() const {
+  // the listed units' data, loaded at the end of load_count (the loads are in
+  // flight through the segment sums and the cuts; used by each_listed)
+  Listed pre;
+  __device__ __forceinline__ Listed issue_listed() const {
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    const int nv = nvec();
     Listed l;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) l.v[i] = vq[i] >= 0 ? pv[vq[i]] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int q = vq[i];
+      l.v[2 * i] = q >= 0 ? pv[q] : make_uint4(0, 0, 0, 0);
+      l.v[2 * i + 1] = (q >= 0 && q + kThreads < nv) ? pv[q + kThreads] : make_uint4(0, 0, 0, 0);
+    }
     return l;
   }
+  __device__ __forceinline__ Listed load_listed() const { return pre; }
+  // f(key, column) for the listed tokens, possibly skipping tokens with key < K:
+  // a unit whose largest key is below K is skipped, and so is a word whose
+  // larger raw key is below K - 1 (-0 sits one below +0 before the fold)
   template <class F>
-  __device__ __forceinline__ void each_listed(const Listed& l, F f) const {
+  __device__ __forceinline__ void each_listed(const Listed& l, uint32_t K, F f) const {
+    const int nv = nvec();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (vq[i] < 0) continue;
-      const uint32_t w[4] = {l.v[i].x, l.v[i].y, l.v[i].z, l.v[i].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f(key16(w[e] & 0xFFFFu), 8 * vq[i] + 2 * e);
-        f(key16(w[e] >> 16), 8 * vq[i] + 2 * e + 1);
+      for (int h = 0; h < 2; ++h) {
+        const int q = vq[i] + h * kThreads;
+        const bool ok = vq[i] >= 0 && q < nv && vkey[i] >= K;
+        const uint4 v = l.v[2 * i + h];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t keys = pair_keys(w[e]);
+          if (ok && max(keys & 0xFFFFu, keys >> 16) + 1u >= K) {
+            f(key16(w[e] & 0xFFFFu), 8 * q + 2 * e);
+            f(key16(w[e] >> 16), 8 * q + 2 * e + 1);
+          }
+        }
       }
     }
   }
-  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& bad, uint32_t& kmax) {
+  // Count every token into the packed histogram and track the row's largest
+  // key (and, through it, NaN / +inf).  Negative NaNs (keys <= 0x7E) are found
+  // afterwards from the histogram's lowest bins (low_bad).
+  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& kmax) {
     kmax = 0;
-    uint32_t kmin = 0xFFFFu;
     vkey[0] = vkey[1] = 0;
     vq[0] = vq[1] = -1;
     dropped = 0;
     have_top = true;
-    auto count = [&](uint32_t k) { atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u); };
-    // the keys of both bf16 halves of a word at once: sign set -> h ^ 0xFFFF,
-    // clear -> h | 0x8000 (= h ^ 0x8000).  -0 keeps its key 0x7FFF here: its
-    // count is merged into +0's (0x8000) once counting is done (merge_zero),
-    // and a vector's largest key is folded below, which is all the
-    // candidate lists and the row max need.
+    // Key k counts in the 16-bit half (k & 1) of word k >> 1: byte 2 (k & ~1),
+    // increment 1 << 16 (k & 1).  Both halves' addresses and shift counts come
+    // from the packed keys with one op each (16-bit halves read by word
+    // select).  -0 keeps its key 0x7FFF here: its count is merged into +0's
+    // (0x8000) once counting is done (merge_zero), and a unit's largest key is
+    // folded below, which is all the candidate lists and the row max need.
+    char* const hb = reinterpret_cast<char*>(hist);
     auto pair = [&](uint32_t w) -> uint32_t {
-      const uint32_t sgn = (w >> 15) & 0x00010001u;
-      const uint32_t keys = w ^ ((sgn * 0x7FFFu) | 0x80008000u);
-      const uint32_t k0 = keys & 0xFFFFu, k1 = keys >> 16;
-      count(k0);
-      count(k1);
-      kmin = min(kmin, min(k0, k1));
-      return max(k0, k1);
+      const uint32_t keys = pair_keys(w);
+      const uint32_t even = keys & 0xFFFEFFFEu;
+      const uint32_t sh = (keys & 0x00010001u) << 4;
+      atomicAdd(reinterpret_cast<uint32_t*>(hb + ((even & 0xFFFFu) << 1)), 1u << (sh & 0xFFFFu));
+      atomicAdd(reinterpret_cast<uint32_t*>(hb + ((even >> 16) << 1)), 1u << (sh >> 16));
+      return keys;
     };
-    auto vector = [&](const uint4& v, int qv) {
-      uint32_t vmax = max(max(pair(v.x), pair(v.y)), max(pair(v.z), pair(v.w)));
+    auto vec_max = [&](const uint4& v) -> uint32_t {
+      return pk_max_u16(pk_max_u16(pair(v.x), pair(v.y)), pk_max_u16(pair(v.z), pair(v.w)));
+    };
+    auto unit = [&](uint32_t hi, int qv) {
+      uint32_t vmax = max(hi & 0xFFFFu, hi >> 16);
       vmax = vmax == 0x7FFFu ? 0x8000u : vmax;
       kmax = max(kmax, vmax);
       offer_vector(vmax, qv);
     };
     constexpr int nt = kThreads;
-    const int nvec = aligned() ? V / 8 : 0;
+    const int nv = nvec();
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
     int q = threadIdx.x;
-    for (; q + (kInFlight - 1) * nt < nvec; q += kInFlight * nt) {
+    static_assert(kInFlight % 2 == 0, "units are vector pairs");
+    for (; q + (kInFlight - 1) * nt < nv; q += kInFlight * nt) {
       uint4 v[kInFlight];
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * nt];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) vector(v[u], q + u * nt);
+      for (int u = 0; u < kInFlight; u += 2) unit(pk_max_u16(vec_max(v[u]), vec_max(v[u + 1])), q + u * nt);
     }
-    for (; q < nvec; q += nt) vector(pv[q], q);
-    for (int c = 8 * nvec + int(threadIdx.x); c < V; c += nt) {
+    for (; q + nt < nv; q += 2 * nt) unit(pk_max_u16(vec_max(pv[q]), vec_max(pv[q + nt])), q);
+    if (q < nv) unit(vec_max(pv[q]), q);
+    for (int c = 8 * nv + int(threadIdx.x); c < V; c += nt) {
       const uint32_t k = key16(rowp[c]);
-      count(k);
-      kmin = min(kmin, k);
+      count(hist, k);
       kmax = max(kmax, k);
       dropped = max(dropped, k);
     }
-    // NaN and +inf map to keys >= 0xFF80, negative NaNs to keys <= 0x007E
-    // (-inf is 0x007F): the row is bad exactly when a key falls outside
-    bad = (kmax >= 0xFF80u || kmin <= 0x007Eu) ? 1u : 0u;
+    pre = issue_listed();
+  }
+  __device__ __forceinline__ static void count(uint32_t* hist, uint32_t k) {
+    atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
+  }
+  // After counting: whether any key <= 0x7E (a negative NaN; -inf is 0x7F)
+  // was counted, from the 64 lowest words (one per thread of wave 0).
+  __device__ __forceinline__ static bool low_bad(const uint32_t* hist, int tid) {
+    return tid < 64 && (hist[tid] & (tid == 0x3F ? 0xFFFFu : 0xFFFFFFFFu)) != 0;
   }
   // After counting: move the tokens counted under -0's key (0x7FFF, high half
   // of word 0x3FFF) to +0's (0x8000, low half of word 0x4000).  Returns false
@@ -824,7 +874,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     bool listed = false;
     if constexpr (Keys::kTopList) listed = block_max_u32<NW>(keys.listed_from(K_c) ? 0u : 1u, sm) == 0;
     if (listed) {
-      keys.each_listed(listed_data, take);
+      keys.each_listed(listed_data, K_c, take);
     } else {
       keys.each(take);
     }
@@ -965,11 +1015,14 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
   } else {
     keys.rowp = a.rowp;
     keys.V = V;
-    keys.load_count(sm.hist, bad, kmax);
+    keys.load_count(sm.hist, kmax);
     n_pad = 0;
   }
   kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
   if constexpr (NV == 0) {  // (the barriers of the next block maximum publish the merge)
+    // NaN and +inf map to keys >= 0xFF80, negative NaNs to keys <= 0x7E (-inf
+    // is 0x7F): the row is bad exactly when its largest key or a low bin says so
+    bad = (kmax >= 0xFF80u || StreamKeys::low_bad(sm.hist, tid)) ? 1u : 0u;
     if (tid == 0) sm.zero_overflow = StreamKeys::merge_zero(sm.hist) ? 0u : 1u;
   }
   bad = block_max_u32<NW>(bad, sm);
