@@ -43,10 +43,23 @@ constexpr int HALF = 32768;
 constexpr int SEGW = 64;
 constexpr int NSEG = 65536 / SEGW;       // 1024
 constexpr int COLLECT_MAX = 4096;
+// Split path (streamed rows): a count kernel, then a finish kernel with
+// NT_FIN threads and a candidate buffer of COLLECT_SPLIT entries, so that
+// several rows share a CU.  The count kernel writes one record per row:
+//   [kRecHead]    u32 kmax, largest dropped key, stored candidates, K_cap
+//   [kRecBitmap]  u64[16]: bit l of word w = segment NSEG-1-(64w+l) non-empty
+//   [kRecCand]    u64[COLLECT_SPLIT] candidates (key << 32 | ~column)
+//   [kRecBlocks]  u32[NSEG][32]: the packed count words of each non-empty segment
+constexpr int NT_FIN = 256;
+constexpr int COLLECT_SPLIT = 2048;
+constexpr size_t kRecHead = 0, kRecBitmap = 128, kRecCand = 256;
+constexpr size_t kRecBlocks = kRecCand + size_t(COLLECT_SPLIT) * 8;
+constexpr size_t kRecBytes = kRecBlocks + size_t(NSEG) * 128;
+static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 constexpr uint32_t KEY_NEG_INF = 0x007Fu;
 constexpr int kInFlight = 4;  // 16-byte loads per thread in flight in a streaming pass (1024 threads)
 
-struct Smem {
+struct alignas(16) Smem {
   uint32_t hist[HALF];  // packed 16-bit counters (fast) or one half of 32-bit bins (stream); later candidates
   uint32_t seg_count[NSEG];
   double seg_mass[NSEG];
@@ -59,6 +72,31 @@ struct Smem {
   int fine_seg;
   uint32_t ncand;
   uint32_t zero_overflow;  // the -0 / +0 merge of the streaming count passed 16 bits
+  __device__ uint64_t* cand_area() { return reinterpret_cast<uint64_t*>(hist); }
+};
+// The finish kernel's LDS (about 39 KiB: four rows per CU).  The first
+// FIN_STAGED non-empty segments' count words are kept in LDS for the key
+// queries, in the space the dense-id candidates use afterwards.
+constexpr int FIN_STAGED = COLLECT_SPLIT * 2 / 32;  // 128 segments of 32 words
+struct alignas(16) SmemFin {
+  union {
+    uint64_t cand[COLLECT_SPLIT];
+    uint32_t blk[FIN_STAGED][32];
+  };
+  uint8_t seg_slot[NSEG];   // staging slot of a segment, 0xFF = not staged
+  uint16_t nelist[NSEG];    // the non-empty segments, ascending
+  uint32_t n_ne;
+  uint32_t seg_count[NSEG];
+  double seg_mass[NSEG];
+  double seg_zmass[NSEG];
+  uint32_t fine[SEGW];
+  uint32_t red_u[MAX_WAVES];
+  double red_m[MAX_WAVES], red_z[MAX_WAVES];
+  uint32_t bu[8];
+  double bd[8];
+  int fine_seg;
+  uint32_t ncand;
+  __device__ uint64_t* cand_area() { return cand; }
 };
 
 // raw bf16 pattern -> order-preserving key (-0 folded onto +0)
@@ -138,8 +176,8 @@ __device__ __forceinline__ double wave_scan_incl_f64(double x) {
       x, [](double v, auto c, auto m) { return dpp_f64<decltype(c)::value, decltype(m)::value>(v); }, AddOp{});
 }
 
-template <int NW>
-__device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
+template <int NW, class SM>
+__device__ uint32_t block_sum_u32(uint32_t v, SM& sm) {
   v = wave_total_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
@@ -149,8 +187,8 @@ __device__ uint32_t block_sum_u32(uint32_t v, Smem& sm) {
   for (int i = 0; i < NW; ++i) t += sm.red_u[i];
   return t;
 }
-template <int NW>
-__device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
+template <int NW, class SM>
+__device__ uint32_t block_max_u32(uint32_t v, SM& sm) {
   v = wave_max_u32(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
@@ -161,8 +199,8 @@ __device__ uint32_t block_max_u32(uint32_t v, Smem& sm) {
   return t;
 }
 // Exclusive prefix over threads in thread order; also returns the total.
-template <int NW>
-__device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, Smem& sm) {
+template <int NW, class SM>
+__device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, SM& sm) {
   const int lane = threadIdx.x & 63;
   const uint32_t incl = wave_scan_incl_u32(v);
   __syncthreads();
@@ -189,6 +227,7 @@ template <int NV>
 struct RegKeys {
   uint32_t kw[NV][4];  // two keys per word
   static constexpr int kThreads = NT;
+  static constexpr int kCollectMax = COLLECT_MAX;
   static constexpr bool kTopList = false;  // the row is in registers: a sweep is cheap
   struct Listed {};
   __device__ __forceinline__ bool listed_from(uint32_t) const { return false; }
@@ -285,9 +324,14 @@ struct RegKeys {
   }
 };
 
-struct StreamKeys {
+template <int NTH_>
+struct StreamKeysT {
   const uint16_t* rowp;
   int V;
+  // The count pass visits vector q (logical) at vector phys(q) = (q + rot) mod
+  // nvec: rows read at once start at different offsets (one contiguous stream
+  // per row, all from offset 0, camps on a subset of the memory channels).
+  int rot;
   // Filled by load_count.  The thread's 8-token vectors q and q + kThreads
   // form a unit (the second absent past the last whole vector).  Kept: the
   // thread's two best units by their largest key (first vector index, -1 =
@@ -298,11 +342,16 @@ struct StreamKeys {
   int vq[2];
   uint32_t dropped;
   bool have_top;
-  static constexpr int kThreads = NT_STREAM;
+  static constexpr int kThreads = NTH_;
+  static constexpr int kCollectMax = COLLECT_MAX;
   static constexpr bool kTopList = true;
   __device__ __forceinline__ void opaque() {}
   __device__ __forceinline__ bool aligned() const { return (reinterpret_cast<uintptr_t>(rowp) & 15) == 0; }
   __device__ __forceinline__ int nvec() const { return aligned() ? V / 8 : 0; }
+  __device__ __forceinline__ int phys(int q, int nv) const {
+    const int p = q + rot;
+    return p < nv ? p : p - nv;
+  }
   // branch-free update of the two-unit list with unit q of largest key vmax
   __device__ __forceinline__ void offer_vector(uint32_t vmax, int q) {
     const bool in0 = vmax > vkey[0];
@@ -330,8 +379,8 @@ struct StreamKeys {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = vq[i];
-      l.v[2 * i] = q >= 0 ? pv[q] : make_uint4(0, 0, 0, 0);
-      l.v[2 * i + 1] = (q >= 0 && q + kThreads < nv) ? pv[q + kThreads] : make_uint4(0, 0, 0, 0);
+      l.v[2 * i] = q >= 0 ? pv[phys(q, nv)] : make_uint4(0, 0, 0, 0);
+      l.v[2 * i + 1] = (q >= 0 && q + kThreads < nv) ? pv[phys(q + kThreads, nv)] : make_uint4(0, 0, 0, 0);
     }
     return l;
   }
@@ -348,14 +397,15 @@ struct StreamKeys {
       for (int h = 0; h < 2; ++h) {
         const int q = vq[i] + h * kThreads;
         const bool ok = vq[i] >= 0 && q < nv && vkey[i] >= K;
+        const int c0 = 8 * (ok ? phys(q, nv) : 0);
         const uint4 v = l.v[2 * i + h];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t keys = pair_keys(w[e]);
           if (ok && max(keys & 0xFFFFu, keys >> 16) + 1u >= K) {
-            f(key16(w[e] & 0xFFFFu), 8 * q + 2 * e);
-            f(key16(w[e] >> 16), 8 * q + 2 * e + 1);
+            f(key16(w[e] & 0xFFFFu), c0 + 2 * e);
+            f(key16(w[e] >> 16), c0 + 2 * e + 1);
           }
         }
       }
@@ -402,12 +452,12 @@ struct StreamKeys {
     for (; q + (kInFlight - 1) * nt < nv; q += kInFlight * nt) {
       uint4 v[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) v[u] = pv[q + u * nt];
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[phys(q + u * nt, nv)];
 #pragma unroll
       for (int u = 0; u < kInFlight; u += 2) unit(pk_max_u16(vec_max(v[u]), vec_max(v[u + 1])), q + u * nt);
     }
-    for (; q + nt < nv; q += 2 * nt) unit(pk_max_u16(vec_max(pv[q]), vec_max(pv[q + nt])), q);
-    if (q < nv) unit(vec_max(pv[q]), q);
+    for (; q + nt < nv; q += 2 * nt) unit(pk_max_u16(vec_max(pv[phys(q, nv)]), vec_max(pv[phys(q + nt, nv)])), q);
+    if (q < nv) unit(vec_max(pv[phys(q, nv)]), q);
     for (int c = 8 * nv + int(threadIdx.x); c < V; c += nt) {
       const uint32_t k = key16(rowp[c]);
       count(hist, k);
@@ -473,6 +523,31 @@ struct StreamKeys {
   __device__ __forceinline__ void slice(int j, F f) const {
     const int c = int(threadIdx.x) + kThreads * j;
     if (c < V) f(key16(rowp[c]), c);
+  }
+};
+using StreamKeys = StreamKeysT<NT_STREAM>;
+
+// The finish kernel's view of a row: sweeps re-read it with NT_FIN threads;
+// the listed candidates are the ones the count kernel stored (every token of
+// its candidate units with key >= K_cap, complete when no more than
+// COLLECT_SPLIT).  They hold every token with key >= K when K > the largest
+// key the count kernel's threads dropped from their units.
+struct SplitKeys : StreamKeysT<NT_FIN> {
+  const uint64_t* cand_g;
+  uint32_t ncand_g;
+  uint32_t maxdropped;
+  static constexpr int kCollectMax = COLLECT_SPLIT;
+  struct Listed {};
+  __device__ __forceinline__ Listed load_listed() const { return Listed{}; }
+  __device__ __forceinline__ bool listed_from(uint32_t K) const {
+    return ncand_g <= uint32_t(COLLECT_SPLIT) && maxdropped < K;
+  }
+  template <class F>
+  __device__ __forceinline__ void each_listed(const Listed&, uint32_t, F f) const {
+    for (uint32_t i = threadIdx.x; i < ncand_g; i += kThreads) {
+      const uint64_t e = cand_g[i];
+      f(uint32_t(e >> 32), int(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)));
+    }
   }
 };
 
@@ -548,6 +623,35 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_u32(v); }
 
+// The masses of regular segment s (2 .. NSEG-3) from its 32 count words
+// word(j) (keys 2j, 2j+1), visited from word rot on.
+template <class WordFn>
+__device__ __forceinline__ void segment_masses(int s, WordFn word, int rot, double tau, double z0, double& m,
+                                               double& zm) {
+  const uint32_t k0 = uint32_t(s * SEGW);
+  const double x0 = double(key_logit(k0));
+  const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
+  const double d0 = x0 / tau - z0;
+  const double r = exp(dd);
+  const double r2 = r * r;
+  const double w_first = exp(d0);
+  double w = exp(d0 + double(2 * rot) * dd);  // weight of key 2 * rot
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const int j = (i + rot) & 31;
+    if (i > 0 && j == 0) w = w_first;  // wrapped to the segment's first key
+    const uint32_t wd = word(j);
+    const double dl = d0 + double(2 * j) * dd;
+    const double cl = double(wd & 0xFFFFu) * w;
+    const double ch = double(wd >> 16) * (w * r);
+    m += cl;
+    m += ch;
+    zm += cl * dl;
+    zm += ch * (dl + dd);
+    w *= r2;
+  }
+}
+
 // All segment summaries in one pass, one thread per segment.  The thread
 // loads the segment's 32 packed count words once (starting at word t % 32, so
 // a wave's loads fall in different banks), adds up its token count and, for a
@@ -575,30 +679,7 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
     if (s == 0) cnt -= n_pad;
     total += cnt;
     double m = 0.0, zm = 0.0;
-    if (cnt != 0 && s >= 2 && s < NSEG - 2) {
-      const uint32_t k0 = uint32_t(s * SEGW);
-      const double x0 = double(key_logit(k0));
-      const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
-      const double d0 = x0 / tau - z0;
-      const double r = exp(dd);
-      const double r2 = r * r;
-      const double w_first = exp(d0);
-      double w = exp(d0 + double(2 * rot) * dd);  // weight of key 2 * rot
-#pragma unroll 8
-      for (int i = 0; i < 32; ++i) {
-        const int j = (i + rot) & 31;
-        if (i > 0 && j == 0) w = w_first;  // wrapped to the segment's first key
-        const uint32_t wd = seg[j];
-        const double dl = d0 + double(2 * j) * dd;
-        const double cl = double(wd & 0xFFFFu) * w;
-        const double ch = double(wd >> 16) * (w * r);
-        m += cl;
-        m += ch;
-        zm += cl * dl;
-        zm += ch * (dl + dd);
-        w *= r2;
-      }
-    }
+    if (cnt != 0 && s >= 2 && s < NSEG - 2) segment_masses(s, [&](int j) { return seg[j]; }, rot, tau, z0, m, zm);
     sm.seg_count[s] = cnt;
     sm.seg_mass[s] = m;
     sm.seg_zmass[s] = zm;
@@ -608,8 +689,8 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
 
 // Everything after the histogram: cuts, scores, descriptor, dense ids.
 // `fine(s)` makes the 64 key counts of segment s readable through count(key).
-template <class Keys, class FineFn, class CountFn>
-__device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double z0, Smem& sm,
+template <class Keys, class FineFn, class CountFn, class SM>
+__device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double z0, SM& sm,
                            FineFn fine, CountFn count) {
   constexpr int NTH = Keys::kThreads;
   constexpr int NW = NTH / 64;
@@ -858,9 +939,9 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     const uint32_t above_c = sm.bu[3];
     const uint32_t cnt_c = sm.bu[4];
     const uint32_t r_c = n_out - above_c;
-    const bool with_ties = above_c + cnt_c <= uint32_t(COLLECT_MAX);
+    const bool with_ties = above_c + cnt_c <= uint32_t(Keys::kCollectMax);
     // candidates: every token with key > K_c, plus the tied tokens when they fit
-    uint64_t* cand = reinterpret_cast<uint64_t*>(sm.hist);
+    uint64_t* cand = sm.cand_area();
     if (tid == 0) sm.ncand = 0;
     __syncthreads();
     auto take = [&](uint32_t key, int col) {
@@ -1015,6 +1096,7 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
   } else {
     keys.rowp = a.rowp;
     keys.V = V;
+    keys.rot = 0;
     keys.load_count(sm.hist, kmax);
     n_pad = 0;
   }
@@ -1056,7 +1138,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
   constexpr int NW = NTH / 64;
   __shared__ Smem sm;
   VS_ROW_ARGS
-  if (handoff && handoff[a.row] == 0) return;
+  if (handoff && handoff[a.row] != 1) return;
   const int tid = threadIdx.x;
   if (!params_ok(a)) {
     write_bad<NTH>(a);
@@ -1107,12 +1189,253 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
   finish_row(a, keys, kmax, tau, z0, sm, fine, count);
 }
 
+// Split path, first half: one workgroup per row (one thread per segment)
+// builds the packed histogram and checks the row as the one-kernel path does,
+// then writes the row's record: the count words of every non-empty segment
+// (the finish kernel's segment sums and key queries read them), and, for the
+// dense ids, every token with key >= K_cap, the key at rank min(cap, V) - 1
+// (the dense-id cut lies at or above it), up to COLLECT_SPLIT of them.
+// handoff[row]: 0 = done here (bad row), 1 = counter overflow (32-bit kernel),
+// 2 = the finish kernel completes the row.
+__global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNEL_ARGS,
+                                                                       uint8_t *__restrict__ recs) {
+  constexpr int NTH = NT_STREAM;
+  constexpr int NW = NTH / 64;
+  static_assert(NTH == NSEG, "one thread per segment");
+  __shared__ Smem sm;
+  VS_ROW_ARGS
+  const int tid = threadIdx.x;
+  uint8_t* rec = recs + size_t(a.row) * kRecBytes;
+  if (!params_ok(a)) {
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad<NTH>(a);
+    return;
+  }
+  for (int i = tid; i < HALF / 4; i += NTH) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+  StreamKeys keys;
+  keys.rowp = a.rowp;
+  keys.V = V;
+  {
+    const uint32_t nk = uint32_t(keys.nvec() / 64);  // 1 KiB steps
+    keys.rot = nk ? int((uint32_t(a.row) * 2654435761u) % nk) * 64 : 0;
+  }
+  uint32_t kmax;
+  keys.load_count(sm.hist, kmax);
+  kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
+  uint32_t bad = (kmax >= 0xFF80u || StreamKeys::low_bad(sm.hist, tid)) ? 1u : 0u;
+  if (tid == 0) sm.zero_overflow = StreamKeys::merge_zero(sm.hist) ? 0u : 1u;
+  bad = block_max_u32<NW>(bad, sm);
+  if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad<NTH>(a);
+    return;
+  }
+  // Thread t reads segment NSEG-1-t (descending, so the exclusive scan gives
+  // the tokens above it), starting at word t % 32 so a wave's reads fall in
+  // different banks.
+  const int sg = NSEG - 1 - tid;
+  const int rot = tid & 31;
+  const uint32_t* seg = sm.hist + sg * 32;
+  uint32_t wd[32];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    wd[i] = seg[(i + rot) & 31];
+    cnt += (wd[i] & 0xFFFFu) + (wd[i] >> 16);
+  }
+  uint32_t total;
+  const uint32_t above = block_excl_scan_u32<NW>(cnt, total, sm);
+  // every counter stayed below 2^16 iff the counts add up to the token count
+  if (total != uint32_t(V) || sm.zero_overflow) {
+    if (tid == 0) handoff[a.row] = 1;
+    return;
+  }
+  if (cnt) {
+    uint32_t* blk = reinterpret_cast<uint32_t*>(rec + kRecBlocks) + sg * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) blk[(i + rot) & 31] = wd[i];
+  }
+  const unsigned long long ne = __ballot(cnt != 0);
+  if ((tid & 63) == 0) reinterpret_cast<unsigned long long*>(rec + kRecBitmap)[tid >> 6] = ne;
+  uint32_t K_cap = 0;
+  if (a.ids_out && a.cap > 0) {
+    // K_cap, and the largest key any thread dropped from its candidate units,
+    // behind one pair of barriers
+    const uint32_t r = uint32_t((int64_t(a.cap) < int64_t(V) ? int64_t(a.cap) : int64_t(V)) - 1);
+    if (cnt && r >= above && r < above + cnt) {  // exactly one segment holds rank r
+      sm.bu[0] = uint32_t(sg);
+      sm.bu[1] = above;
+    }
+    const uint32_t dmax = wave_max_u32(keys.dropped);
+    if ((tid & 63) == 0) sm.red_u[tid >> 6] = dmax;
+    __syncthreads();
+    if (tid < 64) {  // the key inside that segment, one key per lane (descending)
+      const uint32_t key = sm.bu[0] * SEGW + uint32_t(SEGW - 1 - tid);
+      const uint32_t c = (sm.hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
+      const uint32_t cb = sm.bu[1] + wave_scan_incl_u32(c) - c;
+      const unsigned long long bal = __ballot(c > 0 && r >= cb && r < cb + c);
+      if (tid == __ffsll(bal) - 1) sm.bu[2] = key;
+      const uint32_t dm = wave_max_u32(tid < NW ? sm.red_u[tid] : 0u);
+      if (tid == 0) sm.bu[3] = dm;
+    }
+    __syncthreads();
+    K_cap = sm.bu[2];
+    // every token with key >= K_cap: from the candidate units when no thread
+    // dropped one, else from a sweep of the row
+    uint64_t* cg = reinterpret_cast<uint64_t*>(rec + kRecCand);
+    auto append = [&](uint32_t key, int col) {
+      if (key >= K_cap) {
+        const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+        if (slot < uint32_t(COLLECT_SPLIT)) cg[slot] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(col));
+      }
+    };
+    if (sm.bu[3] < K_cap) {
+      keys.each_listed(keys.load_listed(), K_cap, append);
+    } else {
+      keys.each(append);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    uint32_t* h = reinterpret_cast<uint32_t*>(rec + kRecHead);
+    h[0] = kmax;
+    h[1] = 0;  // the stored candidates hold every token with key >= K_cap
+    h[2] = sm.ncand;
+    h[3] = K_cap;
+    handoff[a.row] = 2;
+  }
+}
+
+// Split path, second half: rows marked 2.  The segment summaries come from the
+// record's count words (the same sums as the one-kernel path, keys in
+// ascending order); a key query loads one segment's words; then everything
+// after the histogram exactly as in the one-kernel path.
+__global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARGS,
+                                                                  const uint8_t *__restrict__ recs) {
+  constexpr int NTH = NT_FIN;
+  __shared__ SmemFin sm;
+  VS_ROW_ARGS
+  if (handoff[a.row] != 2) return;
+  const int tid = threadIdx.x;
+  const uint8_t* rec = recs + size_t(a.row) * kRecBytes;
+  const uint32_t* h = reinterpret_cast<const uint32_t*>(rec + kRecHead);
+  const unsigned long long* bm = reinterpret_cast<const unsigned long long*>(rec + kRecBitmap);
+  const uint32_t* blocks = reinterpret_cast<const uint32_t*>(rec + kRecBlocks);
+  a.key_y = key16(a.rowp[a.y]);
+  const uint32_t kmax = h[0];
+  const double tau = double(a.tauf);
+  const double z0 = double(key_logit(kmax)) / tau;
+  auto nonempty = [&](int s) -> bool {
+    const int t = NSEG - 1 - s;
+    return (bm[t >> 6] >> (t & 63)) & 1ull;
+  };
+  // the non-empty segments, ascending (thread t looks at segments 4t .. 4t+3);
+  // empty ones get zero summaries here
+  {
+    constexpr int SPT = NSEG / NTH;
+    uint32_t ne[SPT], n = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sg = SPT * tid + i;
+      ne[i] = nonempty(sg) ? 1u : 0u;
+      n += ne[i];
+      if (!ne[i]) {
+        sm.seg_count[sg] = 0u;
+        sm.seg_mass[sg] = 0.0;
+        sm.seg_zmass[sg] = 0.0;
+      }
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan_u32<NTH / 64>(n, tot, sm);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sg = SPT * tid + i;
+      sm.seg_slot[sg] = (ne[i] && pos < uint32_t(FIN_STAGED)) ? uint8_t(pos) : uint8_t(0xFF);
+      if (ne[i]) sm.nelist[pos++] = uint16_t(sg);
+    }
+    if (tid == 0) sm.n_ne = tot;
+    __syncthreads();
+  }
+  // stage the first FIN_STAGED non-empty segments' words in LDS (16-byte
+  // pieces, up to 4 per thread, all loads in flight together)
+  {
+    const uint32_t n_st = min(sm.n_ne, uint32_t(FIN_STAGED));
+    constexpr int PER = FIN_STAGED * 8 / NTH;
+    uint4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t idx = uint32_t(tid + u * NTH);
+      if (idx < n_st * 8u) v[u] = reinterpret_cast<const uint4*>(blocks + sm.nelist[idx >> 3] * 32)[idx & 7];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t idx = uint32_t(tid + u * NTH);
+      if (idx < n_st * 8u) reinterpret_cast<uint4*>(sm.blk[idx >> 3])[idx & 7] = v[u];
+    }
+    __syncthreads();
+  }
+  // Segment summaries, one thread per non-empty segment, with the one-kernel
+  // path's arithmetic (staged words read from word e % 32 on: no bank conflicts)
+  for (uint32_t e = uint32_t(tid); e < sm.n_ne; e += NTH) {
+    const int sg = sm.nelist[e];
+    const int rot = int(e & 31);
+    const bool st = e < uint32_t(FIN_STAGED);
+    auto word = [&](int j) -> uint32_t { return st ? sm.blk[e][j] : blocks[sg * 32 + j]; };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t wd = word((i + rot) & 31);
+      cnt += (wd & 0xFFFFu) + (wd >> 16);
+    }
+    double m = 0.0, zm = 0.0;
+    if (sg >= 2 && sg < NSEG - 2) segment_masses(sg, word, rot, tau, z0, m, zm);
+    sm.seg_count[sg] = cnt;
+    sm.seg_mass[sg] = m;
+    sm.seg_zmass[sg] = zm;
+  }
+  if (tid == 0) sm.fine_seg = -1;
+  __syncthreads();
+  SplitKeys keys;
+  keys.rot = 0;
+  keys.rowp = a.rowp;
+  keys.V = V;
+  keys.cand_g = reinterpret_cast<const uint64_t*>(rec + kRecCand);
+  keys.ncand_g = h[2];
+  keys.maxdropped = h[1];
+  // a key query's segment: staged words are read in place; others are loaded
+  auto fine = [&](int s) {
+    if (sm.seg_slot[s] != 0xFF || sm.fine_seg == s) return;
+    __syncthreads();
+    if (tid < 32) {
+      const uint32_t w = nonempty(s) ? blocks[s * 32 + tid] : 0u;
+      sm.fine[2 * tid] = w & 0xFFFFu;
+      sm.fine[2 * tid + 1] = w >> 16;
+    }
+    __syncthreads();
+    if (tid == 0) sm.fine_seg = s;
+    __syncthreads();
+  };
+  auto count = [&](uint32_t key) -> uint32_t {
+    const uint32_t slot = sm.seg_slot[key >> 6];
+    return slot != 0xFFu ? (sm.blk[slot][(key & 63u) >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu : sm.fine[key & 63u];
+  };
+  finish_row(a, keys, kmax, tau, z0, sm, fine, count);
+}
+
 #undef VS_ROW_ARGS
 #undef VS_KERNEL_ARGS
 
 }  // namespace
 
-size_t transforms_workspace_bytes(int64_t rows) { return size_t(rows); }
+// Rows longer than the register kernels hold take the split path, whose
+// records follow the handoff bytes.
+static bool split_rows(int64_t V) { return (V + 7) / 8 > int64_t(20) * NT; }
+static size_t handoff_bytes(int64_t rows) { return (size_t(rows) + 255) & ~size_t(255); }
+size_t transforms_workspace_bytes(int64_t rows, int64_t V) {
+  return split_rows(V) ? handoff_bytes(rows) + size_t(rows) * kRecBytes : size_t(rows);
+}
 
 int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,
                       float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
@@ -1130,7 +1453,13 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
   if (nv <= 4) transforms_fast_kernel<4><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 10) transforms_fast_kernel<10><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 20) transforms_fast_kernel<20><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
-  else transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);
+  else if (!ids_out || cap <= int64_t(COLLECT_SPLIT)) {
+    uint8_t* recs = handoff + handoff_bytes(rows);
+    transforms_count_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff, recs);
+    transforms_finish_kernel<<<dim3(unsigned(rows)), dim3(NT_FIN), 0, s>>>(VS_ARGS, handoff, recs);
+  } else {
+    transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);
+  }
   const int rc = int(hipGetLastError());
   if (rc) return rc;
   transforms_stream_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);

@@ -63,12 +63,14 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
 int launch_zero_i32(int32_t* p, int64_t n, void* stream);
 
 // Sampling transforms over bf16 logits (one workgroup per row).  Rows up to
-// 20 * 512 * 8 tokens are held in registers, longer ones are streamed; a row
-// that repeats one logit 65536+ times is re-done by a 32-bit-count streaming
-// kernel (flagged in `handoff`, one byte per row of workspace).  More than
-// kTransformsMaxCap dense ids: returns -1.
+// 20 * 512 * 8 tokens are held in registers; longer ones are counted by one
+// kernel and finished by another (several rows per CU), which pass a record
+// per row through the workspace (up to 2048 dense ids; more use a one-kernel
+// streaming form).  A row that repeats one logit 65536+ times is re-done by a
+// 32-bit-count streaming kernel (flagged in `handoff`, the first bytes of the
+// workspace).  More than kTransformsMaxCap dense ids: returns -1.
 constexpr int64_t kTransformsMaxCap = 4096;  // dense ids are sorted in LDS
-size_t transforms_workspace_bytes(int64_t rows);
+size_t transforms_workspace_bytes(int64_t rows, int64_t V);
 int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,
                       float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
                       const int64_t* targets, float* logprob, float* entropy, uint8_t* status,

@@ -159,7 +159,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
   switch (op) {
     case VS_OP_SCORE_FULL: return full_ws_bytes(src, src->T);
     case VS_OP_SCORE_SUPPORT: return support_ws_bytes(src);
-    case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T));
+    case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T, src->V));
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
     default: return 0;
   }
@@ -229,7 +229,7 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
   if (support_ids_cap < 0 || support_ids_cap > kMaxDim) return VS_E_PARAM;
   if (support_ids_cap == 0) support_ids_out = nullptr;
   if (support_ids_out && support_ids_cap > vs::kTransformsMaxCap) return VS_E_UNSUPPORTED;
-  rc = check_workspace(workspace, workspace_bytes, round_up(vs::transforms_workspace_bytes(src->T)));
+  rc = check_workspace(workspace, workspace_bytes, round_up(vs::transforms_workspace_bytes(src->T, src->V)));
   if (rc) return rc;
   vs::timer_mark(0, stream);
   rc = vs::launch_transforms(static_cast<const uint16_t*>(src->logits), src->ld_logits, src->T, src->V,

@@ -190,6 +190,30 @@ def test_streaming_rows_special_values(vsa):
     _compare(got, ref, 64, "streaming special values")
 
 
+def test_streamed_rows_cap_paths(vsa):
+    """Long rows at cap 2048 (count kernel + finish kernel, candidates from the
+    stored per-thread units) and cap 2049 / 4096 (one-kernel streaming form),
+    with targets on the threshold key so the id tie-break sweeps the row."""
+    say("transforms: streamed rows V=100000, caps 2048 / 2049 / 4096, targets tied at the threshold")
+    T, V = 6, 100000
+    rng = np.random.default_rng(11)
+    bits = workloads.to_bf16_bits((rng.standard_normal((T, V)) * 2.0).astype(np.float32))
+    k = np.array([0, 3000, 50, 0, 2500, 0], np.int32)
+    p = np.array([1.0, 1.0, 0.95, 0.9, 1.0, 1.0], np.float32)
+    mp = np.array([0.0, 0.0, 0.0, 0.0, 0.001, 0.0], np.float32)
+    tau = np.array([1.0, 0.7, 1.0, 1.3, 1.0, 1.0], np.float32)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    thr = oracle.score_transforms(x64, tau, k, p, mp, np.zeros(T, np.int64), cap=0)["threshold_logit"]
+    y = rng.integers(0, V, T)
+    for t in range(0, T, 2):  # every other row: a target whose logit is the threshold logit
+        tied = np.nonzero(x64[t] == thr[t])[0]
+        y[t] = tied[len(tied) // 2]
+    for cap in (2048, 2049, 4096):
+        got = _run(vsa, bits, tau, k, p, mp, y, cap)
+        ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
+        _compare(got, ref, cap, f"V={V} cap={cap}")
+
+
 def test_identity_and_singleton(vsa):
     say("transforms: identity program == full-vocabulary scoring; top-k 1 == exact zeros")
     c = workloads.make(5, T=8, V=30000)
