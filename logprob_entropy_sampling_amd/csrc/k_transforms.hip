@@ -46,13 +46,13 @@ constexpr int COLLECT_MAX = 4096;
 // Split path (streamed rows): a count kernel, then a finish kernel with
 // NT_FIN threads and a candidate buffer of COLLECT_SPLIT entries, so that
 // several rows share a CU.  The count kernel writes one record per row:
-//   [kRecHead]    u32 kmax, largest dropped key, stored candidates, K_cap
-//   [kRecBitmap]  u64[16]: bit l of word w = segment NSEG-1-(64w+l) non-empty
-//   [kRecCand]    u64[COLLECT_SPLIT] candidates (key << 32 | ~column)
-//   [kRecBlocks]  u32[NSEG][32]: the packed count words of each non-empty segment
+//   [kRecHead]   u32 kmax, candidates found, K_cap, non-empty segments n
+//   [kRecList]   u16[NSEG]: the n non-empty segments, descending
+//   [kRecCand]   u64[COLLECT_SPLIT] candidates (key << 32 | ~column)
+//   [kRecBlocks] u32[NSEG][32]: the packed count words of list entry e at e
 constexpr int NT_FIN = 256;
 constexpr int COLLECT_SPLIT = 2048;
-constexpr size_t kRecHead = 0, kRecBitmap = 128, kRecCand = 256;
+constexpr size_t kRecHead = 0, kRecList = 256, kRecCand = kRecList + size_t(NSEG) * 2;
 constexpr size_t kRecBlocks = kRecCand + size_t(COLLECT_SPLIT) * 8;
 constexpr size_t kRecBytes = kRecBlocks + size_t(NSEG) * 128;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
@@ -65,7 +65,7 @@ struct alignas(16) Smem {
   double seg_mass[NSEG];
   double seg_zmass[NSEG];
   uint32_t fine[SEGW];  // 32-bit counts of one segment (stream kernel)
-  uint32_t red_u[MAX_WAVES];
+  uint32_t red_u[MAX_WAVES], red_v[MAX_WAVES];
   double red_m[MAX_WAVES], red_z[MAX_WAVES];
   uint32_t bu[8];  // broadcast slots (integers)
   double bd[8];    // broadcast slots (fp64)
@@ -215,6 +215,34 @@ __device__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t& total, SM& sm) {
     total += t;
   }
   return before + incl - v;
+}
+
+// Two exclusive scans at once (the same barriers).
+template <int NW, class SM>
+__device__ void block_excl_scan2_u32(uint32_t v, uint32_t w, uint32_t& ev, uint32_t& ew, uint32_t& tv, uint32_t& tw,
+                                     SM& sm) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t iv = wave_scan_incl_u32(v), iw = wave_scan_incl_u32(w);
+  __syncthreads();
+  if (lane == 63) {
+    sm.red_u[threadIdx.x >> 6] = iv;
+    sm.red_v[threadIdx.x >> 6] = iw;
+  }
+  __syncthreads();
+  uint32_t bv = 0, bw = 0;
+  tv = tw = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t a = sm.red_u[i], b = sm.red_v[i];
+    if (i < int(threadIdx.x >> 6)) {
+      bv += a;
+      bw += b;
+    }
+    tv += a;
+    tw += b;
+  }
+  ev = bv + iv - v;
+  ew = bw + iw - w;
 }
 
 // ---------------------------------------------------------------------------
@@ -414,7 +442,24 @@ struct StreamKeysT {
   // Count every token into the packed histogram and track the row's largest
   // key (and, through it, NaN / +inf).  Negative NaNs (keys <= 0x7E) are found
   // afterwards from the histogram's lowest bins (low_bad).
+  // The count pass's first batch of loads (this thread's vectors q = t,
+  // t + kThreads, ...), issued ahead so they stream during other work.
+  __device__ __forceinline__ void prefetch(uint4 (&v)[kInFlight]) const {
+    const int nv = nvec();
+    const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    const int q = threadIdx.x;
+    if (q + (kInFlight - 1) * kThreads < nv) {
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) v[u] = pv[phys(q + u * kThreads, nv)];
+    }
+  }
   __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& kmax) {
+    uint4 first[kInFlight];
+    prefetch(first);
+    load_count(hist, kmax, first);
+  }
+  // `first` holds what prefetch() loaded for this row.
+  __device__ __forceinline__ void load_count(uint32_t* hist, uint32_t& kmax, const uint4 (&first)[kInFlight]) {
     kmax = 0;
     vkey[0] = vkey[1] = 0;
     vq[0] = vq[1] = -1;
@@ -449,6 +494,11 @@ struct StreamKeysT {
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
     int q = threadIdx.x;
     static_assert(kInFlight % 2 == 0, "units are vector pairs");
+    if (q + (kInFlight - 1) * nt < nv) {
+#pragma unroll
+      for (int u = 0; u < kInFlight; u += 2) unit(pk_max_u16(vec_max(first[u]), vec_max(first[u + 1])), q + u * nt);
+      q += kInFlight * nt;
+    }
     for (; q + (kInFlight - 1) * nt < nv; q += kInFlight * nt) {
       uint4 v[kInFlight];
 #pragma unroll
@@ -528,24 +578,21 @@ struct StreamKeysT {
 using StreamKeys = StreamKeysT<NT_STREAM>;
 
 // The finish kernel's view of a row: sweeps re-read it with NT_FIN threads;
-// the listed candidates are the ones the count kernel stored (every token of
-// its candidate units with key >= K_cap, complete when no more than
-// COLLECT_SPLIT).  They hold every token with key >= K when K > the largest
-// key the count kernel's threads dropped from their units.
+// the listed candidates are the ones the count kernel stored: every token with
+// key >= K_cap (the dense-id cut is never below it), when there are no more
+// than COLLECT_SPLIT of them.
 struct SplitKeys : StreamKeysT<NT_FIN> {
   const uint64_t* cand_g;
+  uint64_t cand0;  // this thread's first candidate, loaded early
   uint32_t ncand_g;
-  uint32_t maxdropped;
   static constexpr int kCollectMax = COLLECT_SPLIT;
   struct Listed {};
   __device__ __forceinline__ Listed load_listed() const { return Listed{}; }
-  __device__ __forceinline__ bool listed_from(uint32_t K) const {
-    return ncand_g <= uint32_t(COLLECT_SPLIT) && maxdropped < K;
-  }
+  __device__ __forceinline__ bool listed_from(uint32_t) const { return ncand_g <= uint32_t(COLLECT_SPLIT); }
   template <class F>
   __device__ __forceinline__ void each_listed(const Listed&, uint32_t, F f) const {
     for (uint32_t i = threadIdx.x; i < ncand_g; i += kThreads) {
-      const uint64_t e = cand_g[i];
+      const uint64_t e = i == threadIdx.x ? cand0 : cand_g[i];
       f(uint32_t(e >> 32), int(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)));
     }
   }
@@ -1040,9 +1087,10 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   }
 }
 
-#define VS_ROW_ARGS                                   \
+#define VS_ROW_ARGS VS_ROW_ARGS_AT(blockIdx.x)
+#define VS_ROW_ARGS_AT(R)                             \
   RowArgs a;                                          \
-  a.row = blockIdx.x;                                 \
+  a.row = (R);                                        \
   a.V = V;                                            \
   a.tauf = temp ? temp[a.row] : temp_scalar;          \
   a.kk = top_k[a.row];                                \
@@ -1189,76 +1237,43 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
   finish_row(a, keys, kmax, tau, z0, sm, fine, count);
 }
 
-// Split path, first half: one workgroup per row (one thread per segment)
-// builds the packed histogram and checks the row as the one-kernel path does,
-// then writes the row's record: the count words of every non-empty segment
-// (the finish kernel's segment sums and key queries read them), and, for the
-// dense ids, every token with key >= K_cap, the key at rank min(cap, V) - 1
-// (the dense-id cut lies at or above it), up to COLLECT_SPLIT of them.
-// handoff[row]: 0 = done here (bad row), 1 = counter overflow (32-bit kernel),
-// 2 = the finish kernel completes the row.
-__global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNEL_ARGS,
-                                                                       uint8_t *__restrict__ recs) {
+// The count kernel's work on a row after its histogram passed the checks.
+__device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& keys, uint32_t kmax, uint8_t* rec,
+                                               uint8_t* handoff, Smem& sm) {
   constexpr int NTH = NT_STREAM;
   constexpr int NW = NTH / 64;
-  static_assert(NTH == NSEG, "one thread per segment");
-  __shared__ Smem sm;
-  VS_ROW_ARGS
   const int tid = threadIdx.x;
-  uint8_t* rec = recs + size_t(a.row) * kRecBytes;
-  if (!params_ok(a)) {
-    if (tid == 0) handoff[a.row] = 0;
-    write_bad<NTH>(a);
-    return;
-  }
-  for (int i = tid; i < HALF / 4; i += NTH) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
-  if (tid == 0) sm.ncand = 0;
-  __syncthreads();
-  StreamKeys keys;
-  keys.rowp = a.rowp;
-  keys.V = V;
-  {
-    const uint32_t nk = uint32_t(keys.nvec() / 64);  // 1 KiB steps
-    keys.rot = nk ? int((uint32_t(a.row) * 2654435761u) % nk) * 64 : 0;
-  }
-  uint32_t kmax;
-  keys.load_count(sm.hist, kmax);
-  kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
-  uint32_t bad = (kmax >= 0xFF80u || StreamKeys::low_bad(sm.hist, tid)) ? 1u : 0u;
-  if (tid == 0) sm.zero_overflow = StreamKeys::merge_zero(sm.hist) ? 0u : 1u;
-  bad = block_max_u32<NW>(bad, sm);
-  if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
-    if (tid == 0) handoff[a.row] = 0;
-    write_bad<NTH>(a);
-    return;
-  }
+  const int V = a.V;
   // Thread t reads segment NSEG-1-t (descending, so the exclusive scan gives
   // the tokens above it), starting at word t % 32 so a wave's reads fall in
   // different banks.
   const int sg = NSEG - 1 - tid;
   const int rot = tid & 31;
   const uint32_t* seg = sm.hist + sg * 32;
-  uint32_t wd[32];
   uint32_t cnt = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    wd[i] = seg[(i + rot) & 31];
-    cnt += (wd[i] & 0xFFFFu) + (wd[i] >> 16);
+    const uint32_t wd = seg[(i + rot) & 31];
+    cnt += (wd & 0xFFFFu) + (wd >> 16);
   }
-  uint32_t total;
-  const uint32_t above = block_excl_scan_u32<NW>(cnt, total, sm);
+  uint32_t total, above, entry, n_ne;
+  block_excl_scan2_u32<NW>(cnt, cnt ? 1u : 0u, above, entry, total, n_ne, sm);
   // every counter stayed below 2^16 iff the counts add up to the token count
   if (total != uint32_t(V) || sm.zero_overflow) {
     if (tid == 0) handoff[a.row] = 1;
     return;
   }
-  if (cnt) {
-    uint32_t* blk = reinterpret_cast<uint32_t*>(rec + kRecBlocks) + sg * 32;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) blk[(i + rot) & 31] = wd[i];
+  if (cnt) {  // list entry `entry` (descending segments)
+    reinterpret_cast<uint16_t*>(rec + kRecList)[entry] = uint16_t(sg);
+    // 16-byte pieces, starting at piece t % 8 (the LDS reads spread over banks)
+    const uint4* s4 = reinterpret_cast<const uint4*>(seg);
+    uint4* b4 = reinterpret_cast<uint4*>(rec + kRecBlocks) + entry * 8;
+#pragma unroll 2
+    for (int i = 0; i < 8; ++i) {
+      const int c = (i + tid) & 7;
+      b4[c] = s4[c];
+    }
   }
-  const unsigned long long ne = __ballot(cnt != 0);
-  if ((tid & 63) == 0) reinterpret_cast<unsigned long long*>(rec + kRecBitmap)[tid >> 6] = ne;
   uint32_t K_cap = 0;
   if (a.ids_out && a.cap > 0) {
     // K_cap, and the largest key any thread dropped from its candidate units,
@@ -1299,13 +1314,58 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNE
     __syncthreads();
   }
   if (tid == 0) {
-    uint32_t* h = reinterpret_cast<uint32_t*>(rec + kRecHead);
-    h[0] = kmax;
-    h[1] = 0;  // the stored candidates hold every token with key >= K_cap
-    h[2] = sm.ncand;
-    h[3] = K_cap;
+    // (the stored candidates hold every token with key >= K_cap)
+    *reinterpret_cast<uint4*>(rec + kRecHead) = make_uint4(kmax, sm.ncand, K_cap, n_ne);
     handoff[a.row] = 2;
   }
+}
+
+// Split path, first half: one workgroup per row (one thread per segment)
+// builds the packed histogram and checks the row as the one-kernel path does,
+// then writes the row's record: the count words of every non-empty segment
+// (the finish kernel's segment sums and key queries read them), and, for the
+// dense ids, every token with key >= K_cap, the key at rank min(cap, V) - 1
+// (the dense-id cut lies at or above it), up to COLLECT_SPLIT of them.
+// handoff[row]: 0 = done here (bad row), 1 = counter overflow (32-bit kernel),
+// 2 = the finish kernel completes the row.
+__global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNEL_ARGS,
+                                                                       uint8_t *__restrict__ recs) {
+  constexpr int NTH = NT_STREAM;
+  constexpr int NW = NTH / 64;
+  static_assert(NTH == NSEG, "one thread per segment");
+  __shared__ Smem sm;
+  VS_ROW_ARGS
+  const int tid = threadIdx.x;
+  uint8_t* rec = recs + size_t(a.row) * kRecBytes;
+  if (!params_ok(a)) {
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad<NTH>(a);
+    return;
+  }
+  StreamKeys keys;
+  keys.rowp = a.rowp;
+  keys.V = V;
+  {
+    const uint32_t nk = uint32_t(keys.nvec() / 64);  // 1 KiB steps
+    keys.rot = nk ? int((uint32_t(a.row) * 2654435761u) % nk) * 64 : 0;
+  }
+  uint4 first[kInFlight];
+  keys.prefetch(first);  // streams while the histogram is cleared
+  for (int i = tid; i < HALF / 4; i += NTH) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+  uint32_t kmax;
+  keys.load_count(sm.hist, kmax, first);
+  kmax = block_max_u32<NW>(kmax, sm);  // (its barriers also complete the counting)
+  uint32_t bad = (kmax >= 0xFF80u || StreamKeys::low_bad(sm.hist, tid)) ? 1u : 0u;
+  if (tid == 0) sm.zero_overflow = StreamKeys::merge_zero(sm.hist) ? 0u : 1u;
+  bad = block_max_u32<NW>(bad, sm);
+  if (bad || kmax <= KEY_NEG_INF) {  // NaN / +inf present, or every logit is -inf
+    if (tid == 0) handoff[a.row] = 0;
+    write_bad<NTH>(a);
+    return;
+  }
+  count_row_tail(a, keys, kmax, rec, handoff, sm);
 }
 
 // Split path, second half: rows marked 2.  The segment summaries come from the
@@ -1320,80 +1380,62 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   if (handoff[a.row] != 2) return;
   const int tid = threadIdx.x;
   const uint8_t* rec = recs + size_t(a.row) * kRecBytes;
-  const uint32_t* h = reinterpret_cast<const uint32_t*>(rec + kRecHead);
-  const unsigned long long* bm = reinterpret_cast<const unsigned long long*>(rec + kRecBitmap);
   const uint32_t* blocks = reinterpret_cast<const uint32_t*>(rec + kRecBlocks);
+  // Everything the row needs first, in one round of loads: the header, the
+  // whole segment list, the first FIN_STAGED count blocks and this thread's
+  // first candidate (reads past the row's counts stay inside its record).
+  const uint4 hd = *reinterpret_cast<const uint4*>(rec + kRecHead);
+  static_assert(NSEG == 4 * NTH, "four list entries per thread");
+  const uint2 lst = reinterpret_cast<const uint2*>(rec + kRecList)[tid];
+  constexpr int PER = FIN_STAGED * 8 / NTH;
+  uint4 bv[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) bv[u] = reinterpret_cast<const uint4*>(blocks)[tid + u * NTH];
+  const uint64_t cand0 = reinterpret_cast<const uint64_t*>(rec + kRecCand)[tid];
   a.key_y = key16(a.rowp[a.y]);
-  const uint32_t kmax = h[0];
+  // meanwhile: empty summaries and no staging for every segment
+  for (int sg = tid; sg < NSEG; sg += NTH) {
+    sm.seg_count[sg] = 0u;
+    sm.seg_mass[sg] = 0.0;
+    sm.seg_zmass[sg] = 0.0;
+    sm.seg_slot[sg] = 0xFF;
+  }
+  const uint32_t kmax = hd.x;
+  const uint32_t n_ne = hd.w;
+  const uint32_t n_st = min(n_ne, uint32_t(FIN_STAGED));
   const double tau = double(a.tauf);
   const double z0 = double(key_logit(kmax)) / tau;
-  auto nonempty = [&](int s) -> bool {
-    const int t = NSEG - 1 - s;
-    return (bm[t >> 6] >> (t & 63)) & 1ull;
-  };
-  // the non-empty segments, ascending (thread t looks at segments 4t .. 4t+3);
-  // empty ones get zero summaries here
-  {
-    constexpr int SPT = NSEG / NTH;
-    uint32_t ne[SPT], n = 0;
+  reinterpret_cast<uint2*>(sm.nelist)[tid] = lst;
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int sg = SPT * tid + i;
-      ne[i] = nonempty(sg) ? 1u : 0u;
-      n += ne[i];
-      if (!ne[i]) {
-        sm.seg_count[sg] = 0u;
-        sm.seg_mass[sg] = 0.0;
-        sm.seg_zmass[sg] = 0.0;
-      }
-    }
-    uint32_t tot;
-    uint32_t pos = block_excl_scan_u32<NTH / 64>(n, tot, sm);
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int sg = SPT * tid + i;
-      sm.seg_slot[sg] = (ne[i] && pos < uint32_t(FIN_STAGED)) ? uint8_t(pos) : uint8_t(0xFF);
-      if (ne[i]) sm.nelist[pos++] = uint16_t(sg);
-    }
-    if (tid == 0) sm.n_ne = tot;
-    __syncthreads();
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t idx = uint32_t(tid + u * NTH);
+    if (idx < n_st * 8u) reinterpret_cast<uint4*>(sm.blk[idx >> 3])[idx & 7] = bv[u];
   }
-  // stage the first FIN_STAGED non-empty segments' words in LDS (16-byte
-  // pieces, up to 4 per thread, all loads in flight together)
-  {
-    const uint32_t n_st = min(sm.n_ne, uint32_t(FIN_STAGED));
-    constexpr int PER = FIN_STAGED * 8 / NTH;
-    uint4 v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t idx = uint32_t(tid + u * NTH);
-      if (idx < n_st * 8u) v[u] = reinterpret_cast<const uint4*>(blocks + sm.nelist[idx >> 3] * 32)[idx & 7];
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t idx = uint32_t(tid + u * NTH);
-      if (idx < n_st * 8u) reinterpret_cast<uint4*>(sm.blk[idx >> 3])[idx & 7] = v[u];
-    }
-    __syncthreads();
-  }
-  // Segment summaries, one thread per non-empty segment, with the one-kernel
-  // path's arithmetic (staged words read from word e % 32 on: no bank conflicts)
-  for (uint32_t e = uint32_t(tid); e < sm.n_ne; e += NTH) {
+  __syncthreads();
+  // Segment summaries, one thread per list entry, with the one-kernel path's
+  // arithmetic (staged words read from word e % 32 on: no bank conflicts)
+  for (uint32_t e = uint32_t(tid); e < n_ne; e += NTH) {
     const int sg = sm.nelist[e];
     const int rot = int(e & 31);
-    const bool st = e < uint32_t(FIN_STAGED);
-    auto word = [&](int j) -> uint32_t { return st ? sm.blk[e][j] : blocks[sg * 32 + j]; };
-    uint32_t cnt = 0;
+    auto sums = [&](auto word) {
+      uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t wd = word((i + rot) & 31);
-      cnt += (wd & 0xFFFFu) + (wd >> 16);
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t wd = word((i + rot) & 31);
+        cnt += (wd & 0xFFFFu) + (wd >> 16);
+      }
+      double m = 0.0, zm = 0.0;
+      if (sg >= 2 && sg < NSEG - 2) segment_masses(sg, word, rot, tau, z0, m, zm);
+      sm.seg_count[sg] = cnt;
+      sm.seg_mass[sg] = m;
+      sm.seg_zmass[sg] = zm;
+    };
+    if (e < uint32_t(FIN_STAGED)) {
+      sm.seg_slot[sg] = uint8_t(e);
+      sums([&](int j) -> uint32_t { return sm.blk[e][j]; });
+    } else {
+      sums([&](int j) -> uint32_t { return blocks[e * 32 + j]; });
     }
-    double m = 0.0, zm = 0.0;
-    if (sg >= 2 && sg < NSEG - 2) segment_masses(sg, word, rot, tau, z0, m, zm);
-    sm.seg_count[sg] = cnt;
-    sm.seg_mass[sg] = m;
-    sm.seg_zmass[sg] = zm;
   }
   if (tid == 0) sm.fine_seg = -1;
   __syncthreads();
@@ -1402,14 +1444,21 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   keys.rowp = a.rowp;
   keys.V = V;
   keys.cand_g = reinterpret_cast<const uint64_t*>(rec + kRecCand);
-  keys.ncand_g = h[2];
-  keys.maxdropped = h[1];
+  keys.cand0 = cand0;
+  keys.ncand_g = hd.y;
   // a key query's segment: staged words are read in place; others are loaded
+  // (list entry e >= FIN_STAGED, found in the descending list)
   auto fine = [&](int s) {
     if (sm.seg_slot[s] != 0xFF || sm.fine_seg == s) return;
     __syncthreads();
+    if (tid == 0) sm.bu[7] = 0xFFFFFFFFu;
+    __syncthreads();
+    for (uint32_t e = uint32_t(FIN_STAGED) + tid; e < n_ne; e += NTH)
+      if (sm.nelist[e] == uint16_t(s)) sm.bu[7] = e;
+    __syncthreads();
+    const uint32_t e = sm.bu[7];
     if (tid < 32) {
-      const uint32_t w = nonempty(s) ? blocks[s * 32 + tid] : 0u;
+      const uint32_t w = e != 0xFFFFFFFFu ? blocks[e * 32 + tid] : 0u;
       sm.fine[2 * tid] = w & 0xFFFFu;
       sm.fine[2 * tid + 1] = w >> 16;
     }
@@ -1425,6 +1474,7 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
 }
 
 #undef VS_ROW_ARGS
+#undef VS_ROW_ARGS_AT
 #undef VS_KERNEL_ARGS
 
 }  // namespace
