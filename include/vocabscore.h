@@ -179,7 +179,10 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  * non-NULL support_ids_out gives VS_E_UNSUPPORTED.  A target outside S_t gives
  * logprob -inf and TARGET_OUTSIDE_SUPPORT.  BAD_INPUT rows: NaN floats,
  * support_len 0, ids -1.  entropy, row_status, support_len, threshold_logit,
- * threshold_ties, full_lse nullable; logprob required.
+ * threshold_ties, full_lse nullable; logprob required.  Workspace: T bytes for
+ * V <= 81920; above that also a per-row record of 149,760 bytes (the count
+ * pass hands the finishing pass each row's non-empty key counts and dense-id
+ * candidates through it).
  */
 int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float* top_p,
                         const float* min_p, const int64_t* target_ids, float* logprob,
