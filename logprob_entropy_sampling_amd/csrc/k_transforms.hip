@@ -671,7 +671,11 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_u32(v); }
 
 // The masses of regular segment s (2 .. NSEG-3) from its 32 count words
-// word(j) (keys 2j, 2j+1), visited from word rot on.
+// word(j) (keys 2j, 2j+1), visited from word rot on.  The weights follow the
+// geometric recurrence when every weight of the segment's keys, counted or
+// not, is a normal number (-700 <= d <= 700 over the segment).  Otherwise
+// (keys so far apart that some weights underflow or, above the row max,
+// overflow) each counted key takes its own exp.
 template <class WordFn>
 __device__ __forceinline__ void segment_masses(int s, WordFn word, int rot, double tau, double z0, double& m,
                                                double& zm) {
@@ -679,6 +683,26 @@ __device__ __forceinline__ void segment_masses(int s, WordFn word, int rot, doub
   const double x0 = double(key_logit(k0));
   const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
   const double d0 = x0 / tau - z0;
+  const double d_last = d0 + double(SEGW - 1) * dd;
+  if (d_last < -746.0) return;  // every weight is 0 in fp64
+  if (d0 < -700.0 || d_last > 700.0) {
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t wd = word(j);
+      const uint32_t lo = wd & 0xFFFFu, hi = wd >> 16;
+      const double dl = d0 + double(2 * j) * dd;
+      if (lo) {
+        const double cl = double(lo) * exp(dl);
+        m += cl;
+        zm += cl > 0.0 ? cl * dl : 0.0;
+      }
+      if (hi) {
+        const double ch = double(hi) * exp(dl + dd);
+        m += ch;
+        zm += ch > 0.0 ? ch * (dl + dd) : 0.0;
+      }
+    }
+    return;
+  }
   const double r = exp(dd);
   const double r2 = r * r;
   const double w_first = exp(d0);

@@ -214,6 +214,35 @@ def test_streamed_rows_cap_paths(vsa):
         _compare(got, ref, cap, f"V={V} cap={cap}")
 
 
+def test_streamed_rows_spread_over_many_segments(vsa):
+    """Long rows whose keys spread over most of the 1024 key segments (random
+    finite bf16 patterns): more non-empty segments than the finish kernel keeps
+    in LDS, so its sums and key queries also read segments from the record;
+    and segments whose weights cannot follow one geometric recurrence."""
+    say("transforms: V=100000 rows of random bf16 patterns, |x| < 2^20 (~590 non-empty segments), caps 0 / 64 / 2048")
+    T, V = 6, 100000
+    rng = np.random.default_rng(12)
+    sign = rng.integers(0, 2, size=(T, V)) << 15
+    # biased exponents 0 .. 146: zero, subnormals, up to 2^19.  (Larger logits
+    # leave fp64 too few fraction bits for the oracle's z - LSE; here the top
+    # segments' key spacing / tau is still large enough that weights inside
+    # one segment span underflow to overflow.)
+    expo = rng.integers(0, 147, size=(T, V)) << 7
+    mant = rng.integers(0, 128, size=(T, V))
+    bits = (sign | expo | mant).astype(np.uint16)
+    bits[1] = np.where(np.arange(V) % 3 == 0, bits[1], bits[1] & 0x80FF)  # a third spread, the rest tiny
+    k = np.array([0, 0, 40, 1000, 0, 5], np.int32)
+    p = np.array([1.0, 0.9, 1.0, 0.5, 1.0, 1.0], np.float32)
+    mp = np.array([0.0, 0.0, 0.0, 0.0, 1e-30, 0.0], np.float32)
+    tau = np.array([1.0, 1.0, 0.5, 2.0, 1.0, 1e-3], np.float32)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    y = rng.integers(0, V, T)
+    for cap in (0, 64, 2048):
+        got = _run(vsa, bits, tau, k, p, mp, y, cap)
+        ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
+        _compare(got, ref, cap, f"spread V={V} cap={cap}")
+
+
 def test_identity_and_singleton(vsa):
     say("transforms: identity program == full-vocabulary scoring; top-k 1 == exact zeros")
     c = workloads.make(5, T=8, V=30000)
