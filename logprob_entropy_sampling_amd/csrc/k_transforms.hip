@@ -397,22 +397,23 @@ struct StreamKeysT {
   struct Listed {
     uint4 v[4];
   };
-  // the listed units' data, loaded at the end of load_count (the loads are in
-  // flight through the segment sums and the cuts; used by each_listed)
-  Listed pre;
-  __device__ __forceinline__ Listed issue_listed() const {
+  // The data of the listed units whose largest key is >= K (the others are
+  // not loaded: by the end of the count their lines have left the caches,
+  // and a scattered 16-byte piece costs a whole line from memory).
+  __device__ __forceinline__ Listed issue_listed(uint32_t K) const {
     const uint4* pv = reinterpret_cast<const uint4*>(rowp);
     const int nv = nvec();
     Listed l;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = vq[i];
-      l.v[2 * i] = q >= 0 ? pv[phys(q, nv)] : make_uint4(0, 0, 0, 0);
-      l.v[2 * i + 1] = (q >= 0 && q + kThreads < nv) ? pv[phys(q + kThreads, nv)] : make_uint4(0, 0, 0, 0);
+      const bool use = q >= 0 && vkey[i] >= K;
+      l.v[2 * i] = use ? pv[phys(q, nv)] : make_uint4(0, 0, 0, 0);
+      l.v[2 * i + 1] = (use && q + kThreads < nv) ? pv[phys(q + kThreads, nv)] : make_uint4(0, 0, 0, 0);
     }
     return l;
   }
-  __device__ __forceinline__ Listed load_listed() const { return pre; }
+  __device__ __forceinline__ Listed load_listed() const { return issue_listed(0); }
   // f(key, column) for the listed tokens, possibly skipping tokens with key < K:
   // a unit whose largest key is below K is skipped, and so is a word whose
   // larger raw key is below K - 1 (-0 sits one below +0 before the fold)
@@ -514,7 +515,6 @@ struct StreamKeysT {
       kmax = max(kmax, k);
       dropped = max(dropped, k);
     }
-    pre = issue_listed();
   }
   __device__ __forceinline__ static void count(uint32_t* hist, uint32_t k) {
     atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
@@ -670,39 +670,23 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_u32(v); }
 
-// The masses of regular segment s (2 .. NSEG-3) from its 32 count words
-// word(j) (keys 2j, 2j+1), visited from word rot on.  The weights follow the
-// geometric recurrence when every weight of the segment's keys, counted or
-// not, is a normal number (-700 <= d <= 700 over the segment).  Otherwise
-// (keys so far apart that some weights underflow or, above the row max,
-// overflow) each counted key takes its own exp.
+// The masses of regular segment s (2 .. NSEG-3, at least one key counted)
+// from its 32 count words word(j) (keys 2j, 2j+1), visited from word rot on:
+// the weights follow the geometric recurrence upwards from exp(d0).  That
+// holds when every weight of the segment's keys, counted or not, is a normal
+// number (-700 <= d <= 700 over the segment); otherwise (keys so far apart
+// that the low weights underflow or, above the row max, overflow) nothing is
+// added and false is returned: the caller then runs segment_masses_down.
 template <class WordFn>
-__device__ __forceinline__ void segment_masses(int s, WordFn word, int rot, double tau, double z0, double& m,
+__device__ __forceinline__ bool segment_masses(int s, WordFn word, int rot, double tau, double z0, double& m,
                                                double& zm) {
   const uint32_t k0 = uint32_t(s * SEGW);
   const double x0 = double(key_logit(k0));
   const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
   const double d0 = x0 / tau - z0;
   const double d_last = d0 + double(SEGW - 1) * dd;
-  if (d_last < -746.0) return;  // every weight is 0 in fp64
-  if (d0 < -700.0 || d_last > 700.0) {
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t wd = word(j);
-      const uint32_t lo = wd & 0xFFFFu, hi = wd >> 16;
-      const double dl = d0 + double(2 * j) * dd;
-      if (lo) {
-        const double cl = double(lo) * exp(dl);
-        m += cl;
-        zm += cl > 0.0 ? cl * dl : 0.0;
-      }
-      if (hi) {
-        const double ch = double(hi) * exp(dl + dd);
-        m += ch;
-        zm += ch > 0.0 ? ch * (dl + dd) : 0.0;
-      }
-    }
-    return;
-  }
+  if (d_last < -746.0) return true;  // every weight is 0 in fp64
+  if (d0 < -700.0 || d_last > 700.0) return false;
   const double r = exp(dd);
   const double r2 = r * r;
   const double w_first = exp(d0);
@@ -720,6 +704,32 @@ __device__ __forceinline__ void segment_masses(int s, WordFn word, int rot, doub
     zm += cl * dl;
     zm += ch * (dl + dd);
     w *= r2;
+  }
+  return true;
+}
+// The same masses for the segments segment_masses declines: the recurrence
+// runs downwards from the highest counted key, whose weight is at most 1 (it
+// is not above the row max), so nothing overflows; what underflows is below
+// the fp64 resolution of the row's mass, which is at least 1.
+template <class WordFn>
+__device__ __forceinline__ void segment_masses_down(int s, WordFn word, double tau, double z0, double& m,
+                                                 double& zm) {
+  const uint32_t k0 = uint32_t(s * SEGW);
+  const double x0 = double(key_logit(k0));
+  const double dd = (double(key_logit(k0 + 1)) - x0) / tau;
+  const double d0 = x0 / tau - z0;
+  int kt = SEGW - 1;  // the highest counted key
+  while (kt > 0 && ((word(kt >> 1) >> ((kt & 1) * 16)) & 0xFFFFu) == 0) --kt;
+  double w = exp(d0 + double(kt) * dd);
+  const double r_down = exp(-dd);  // 0 when the keys are that far apart: only key kt has weight
+  for (int k = kt; k >= 0 && w > 0.0; --k) {
+    const uint32_t c = (word(k >> 1) >> ((k & 1) * 16)) & 0xFFFFu;
+    if (c) {
+      const double ck = double(c) * w;
+      m += ck;
+      zm += ck * (d0 + double(k) * dd);
+    }
+    w *= r_down;
   }
 }
 
@@ -739,7 +749,9 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
                                                       Smem& sm) {
   uint32_t total = 0;
   const int rot = int(threadIdx.x & 31);
-  for (int s = threadIdx.x; s < NSEG; s += NTH) {
+  uint32_t down = 0;  // bit i: this thread's i-th segment needs segment_masses_down
+  int i = 0;
+  for (int s = threadIdx.x; s < NSEG; s += NTH, ++i) {
     const uint32_t* seg = hist + s * 32;  // word j holds keys 2j (low half) and 2j + 1 (high half)
     uint32_t cnt = 0;
 #pragma unroll
@@ -750,10 +762,22 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
     if (s == 0) cnt -= n_pad;
     total += cnt;
     double m = 0.0, zm = 0.0;
-    if (cnt != 0 && s >= 2 && s < NSEG - 2) segment_masses(s, [&](int j) { return seg[j]; }, rot, tau, z0, m, zm);
+    if (cnt != 0 && s >= 2 && s < NSEG - 2 && !segment_masses(s, [&](int j) { return seg[j]; }, rot, tau, z0, m, zm))
+      down |= 1u << i;
     sm.seg_count[s] = cnt;
     sm.seg_mass[s] = m;
     sm.seg_zmass[s] = zm;
+  }
+  if (down) {
+    i = 0;
+    for (int s = threadIdx.x; s < NSEG; s += NTH, ++i) {
+      if (!((down >> i) & 1u)) continue;
+      const uint32_t* seg = hist + s * 32;
+      double m = 0.0, zm = 0.0;
+      segment_masses_down(s, [&](int j) { return seg[j]; }, tau, z0, m, zm);
+      sm.seg_mass[s] = m;
+      sm.seg_zmass[s] = zm;
+    }
   }
   return total;
 }
@@ -1331,7 +1355,7 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
       }
     };
     if (sm.bu[3] < K_cap) {
-      keys.each_listed(keys.load_listed(), K_cap, append);
+      keys.each_listed(keys.issue_listed(K_cap), K_cap, append);
     } else {
       keys.each(append);
     }
@@ -1438,7 +1462,9 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   __syncthreads();
   // Segment summaries, one thread per list entry, with the one-kernel path's
   // arithmetic (staged words read from word e % 32 on: no bank conflicts)
-  for (uint32_t e = uint32_t(tid); e < n_ne; e += NTH) {
+  uint32_t down = 0;  // bit i: this thread's i-th entry needs segment_masses_down
+  int i_e = 0;
+  for (uint32_t e = uint32_t(tid); e < n_ne; e += NTH, ++i_e) {
     const int sg = sm.nelist[e];
     const int rot = int(e & 31);
     auto sums = [&](auto word) {
@@ -1449,7 +1475,7 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
         cnt += (wd & 0xFFFFu) + (wd >> 16);
       }
       double m = 0.0, zm = 0.0;
-      if (sg >= 2 && sg < NSEG - 2) segment_masses(sg, word, rot, tau, z0, m, zm);
+      if (sg >= 2 && sg < NSEG - 2 && !segment_masses(sg, word, rot, tau, z0, m, zm)) down |= 1u << i_e;
       sm.seg_count[sg] = cnt;
       sm.seg_mass[sg] = m;
       sm.seg_zmass[sg] = zm;
@@ -1459,6 +1485,17 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
       sums([&](int j) -> uint32_t { return sm.blk[e][j]; });
     } else {
       sums([&](int j) -> uint32_t { return blocks[e * 32 + j]; });
+    }
+  }
+  if (down) {  // rare: segments whose weights leave the normal range
+    i_e = 0;
+    for (uint32_t e = uint32_t(tid); e < n_ne; e += NTH, ++i_e) {
+      if (!((down >> i_e) & 1u)) continue;
+      const int sg = sm.nelist[e];
+      double m = 0.0, zm = 0.0;
+      segment_masses_down(sg, [&](int j) -> uint32_t { return blocks[e * 32 + j]; }, tau, z0, m, zm);
+      sm.seg_mass[sg] = m;
+      sm.seg_zmass[sg] = zm;
     }
   }
   if (tid == 0) sm.fine_seg = -1;
