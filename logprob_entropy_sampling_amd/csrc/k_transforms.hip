@@ -46,13 +46,17 @@ constexpr int COLLECT_MAX = 4096;
 // Split path (streamed rows): a count kernel, then a finish kernel with
 // NT_FIN threads and a candidate buffer of COLLECT_SPLIT entries, so that
 // several rows share a CU.  The count kernel writes one record per row:
-//   [kRecHead]   u32 kmax, candidates found, K_cap, non-empty segments n
+//   [kRecHead]   u32 kmax, candidate entries, K_cap, non-empty segments n;
+//                then u32 candidate kind (kCandTokens / kCandUnits)
 //   [kRecList]   u16[NSEG]: the n non-empty segments, descending
-//   [kRecCand]   u64[COLLECT_SPLIT] candidates (key << 32 | ~column)
+//   [kRecCand]   u64[COLLECT_SPLIT] candidate entries: tokens (key << 32 |
+//                ~column), or units (vector index of the first 8 tokens |
+//                vector index of the second 8, or ~0, << 32)
 //   [kRecBlocks] u32[NSEG][32]: the packed count words of list entry e at e
 constexpr int NT_FIN = 256;
 constexpr int COLLECT_SPLIT = 2048;
 constexpr size_t kRecHead = 0, kRecList = 256, kRecCand = kRecList + size_t(NSEG) * 2;
+constexpr uint32_t kCandTokens = 1, kCandUnits = 2;
 constexpr size_t kRecBlocks = kRecCand + size_t(COLLECT_SPLIT) * 8;
 constexpr size_t kRecBytes = kRecBlocks + size_t(NSEG) * 128;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
@@ -583,17 +587,47 @@ using StreamKeys = StreamKeysT<NT_STREAM>;
 // than COLLECT_SPLIT of them.
 struct SplitKeys : StreamKeysT<NT_FIN> {
   const uint64_t* cand_g;
-  uint64_t cand0;  // this thread's first candidate, loaded early
+  uint64_t cand0;  // this thread's first candidate entry, loaded early
+  uint4 unit0[2];  // its data when the entries are units (loaded early too)
   uint32_t ncand_g;
+  uint32_t kind;   // kCandTokens or kCandUnits
   static constexpr int kCollectMax = COLLECT_SPLIT;
   struct Listed {};
   __device__ __forceinline__ Listed load_listed() const { return Listed{}; }
   __device__ __forceinline__ bool listed_from(uint32_t) const { return ncand_g <= uint32_t(COLLECT_SPLIT); }
+  // the two 8-token vectors of unit entry e (the second absent: zeros)
+  __device__ __forceinline__ void load_unit(uint64_t e, uint4 (&u)[2]) const {
+    const uint4* pv = reinterpret_cast<const uint4*>(rowp);
+    const uint32_t v0 = uint32_t(e & 0xFFFFFFFFu), v1 = uint32_t(e >> 32);
+    u[0] = pv[v0];
+    u[1] = v1 != 0xFFFFFFFFu ? pv[v1] : make_uint4(0, 0, 0, 0);
+  }
   template <class F>
   __device__ __forceinline__ void each_listed(const Listed&, uint32_t, F f) const {
     for (uint32_t i = threadIdx.x; i < ncand_g; i += kThreads) {
       const uint64_t e = i == threadIdx.x ? cand0 : cand_g[i];
-      f(uint32_t(e >> 32), int(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)));
+      if (kind == kCandTokens) {
+        f(uint32_t(e >> 32), int(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)));
+        continue;
+      }
+      uint4 u[2];
+      if (i == threadIdx.x) {
+        u[0] = unit0[0];
+        u[1] = unit0[1];
+      } else {
+        load_unit(e, u);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t v = h == 0 ? uint32_t(e & 0xFFFFFFFFu) : uint32_t(e >> 32);
+        if (v == 0xFFFFFFFFu) continue;
+        const uint32_t w[4] = {u[h].x, u[h].y, u[h].z, u[h].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f(key16(w[k] & 0xFFFFu), int(8 * v + 2 * k));
+          f(key16(w[k] >> 16), int(8 * v + 2 * k + 1));
+        }
+      }
     }
   }
 };
@@ -1323,6 +1357,7 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
     }
   }
   uint32_t K_cap = 0;
+  uint32_t cand_kind = kCandTokens;
   if (a.ids_out && a.cap > 0) {
     // K_cap, and the largest key any thread dropped from its candidate units,
     // behind one pair of barriers
@@ -1345,25 +1380,36 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
     }
     __syncthreads();
     K_cap = sm.bu[2];
-    // every token with key >= K_cap: from the candidate units when no thread
-    // dropped one, else from a sweep of the row
+    // Every token with key >= K_cap is in the candidate units reaching K_cap
+    // unless some thread dropped such a token: then the row is swept here and
+    // the tokens themselves are stored.  Units are stored by position (the
+    // finish kernel loads them while it does the segment sums and cuts).
     uint64_t* cg = reinterpret_cast<uint64_t*>(rec + kRecCand);
-    auto append = [&](uint32_t key, int col) {
-      if (key >= K_cap) {
-        const uint32_t slot = atomicAdd(&sm.ncand, 1u);
-        if (slot < uint32_t(COLLECT_SPLIT)) cg[slot] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(col));
+    cand_kind = sm.bu[3] < K_cap ? kCandUnits : kCandTokens;
+    if (cand_kind == kCandUnits) {
+      const int nv = keys.nvec();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = keys.vq[i];
+        if (q >= 0 && keys.vkey[i] >= K_cap) {
+          const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+          const uint32_t v1 = q + NTH < nv ? uint32_t(keys.phys(q + NTH, nv)) : 0xFFFFFFFFu;
+          if (slot < uint32_t(COLLECT_SPLIT)) cg[slot] = uint64_t(uint32_t(keys.phys(q, nv))) | (uint64_t(v1) << 32);
+        }
       }
-    };
-    if (sm.bu[3] < K_cap) {
-      keys.each_listed(keys.issue_listed(K_cap), K_cap, append);
     } else {
-      keys.each(append);
+      keys.each([&](uint32_t key, int col) {
+        if (key >= K_cap) {
+          const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+          if (slot < uint32_t(COLLECT_SPLIT)) cg[slot] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(col));
+        }
+      });
     }
     __syncthreads();
   }
   if (tid == 0) {
-    // (the stored candidates hold every token with key >= K_cap)
     *reinterpret_cast<uint4*>(rec + kRecHead) = make_uint4(kmax, sm.ncand, K_cap, n_ne);
+    reinterpret_cast<uint32_t*>(rec + kRecHead)[4] = cand_kind;
     handoff[a.row] = 2;
   }
 }
@@ -1433,6 +1479,7 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   // whole segment list, the first FIN_STAGED count blocks and this thread's
   // first candidate (reads past the row's counts stay inside its record).
   const uint4 hd = *reinterpret_cast<const uint4*>(rec + kRecHead);
+  const uint32_t cand_kind = reinterpret_cast<const uint32_t*>(rec + kRecHead)[4];
   static_assert(NSEG == 4 * NTH, "four list entries per thread");
   const uint2 lst = reinterpret_cast<const uint2*>(rec + kRecList)[tid];
   constexpr int PER = FIN_STAGED * 8 / NTH;
@@ -1458,6 +1505,14 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   for (int u = 0; u < PER; ++u) {
     const uint32_t idx = uint32_t(tid + u * NTH);
     if (idx < n_st * 8u) reinterpret_cast<uint4*>(sm.blk[idx >> 3])[idx & 7] = bv[u];
+  }
+  // this thread's first candidate unit: loaded now, used at the dense ids
+  uint4 unit0[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if (cand_kind == kCandUnits && uint32_t(tid) < hd.y) {
+    const uint4* pv = reinterpret_cast<const uint4*>(a.rowp);
+    const uint32_t v0 = uint32_t(cand0 & 0xFFFFFFFFu), v1 = uint32_t(cand0 >> 32);
+    unit0[0] = pv[v0];
+    if (v1 != 0xFFFFFFFFu) unit0[1] = pv[v1];
   }
   __syncthreads();
   // Segment summaries, one thread per list entry, with the one-kernel path's
@@ -1507,6 +1562,9 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   keys.cand_g = reinterpret_cast<const uint64_t*>(rec + kRecCand);
   keys.cand0 = cand0;
   keys.ncand_g = hd.y;
+  keys.kind = cand_kind;
+  keys.unit0[0] = unit0[0];
+  keys.unit0[1] = unit0[1];
   // a key query's segment: staged words are read in place; others are loaded
   // (list entry e >= FIN_STAGED, found in the descending list)
   auto fine = [&](int s) {
