@@ -585,6 +585,11 @@ using StreamKeys = StreamKeysT<NT_STREAM>;
 // the listed candidates are the ones the count kernel stored: every token with
 // key >= K_cap (the dense-id cut is never below it), when there are no more
 // than COLLECT_SPLIT of them.
+// The finish kernel's first candidate entry of thread t: consecutive entries
+// go to different waves, so a row's few candidates spread over all four.
+__device__ __forceinline__ uint32_t fin_entry(int t) { return uint32_t(((t & 63) << 2) | (t >> 6)); }
+static_assert(NT_FIN == 256, "fin_entry spreads entries over four waves");
+
 struct SplitKeys : StreamKeysT<NT_FIN> {
   const uint64_t* cand_g;
   uint64_t cand0;  // this thread's first candidate entry, loaded early
@@ -604,14 +609,15 @@ struct SplitKeys : StreamKeysT<NT_FIN> {
   }
   template <class F>
   __device__ __forceinline__ void each_listed(const Listed&, uint32_t, F f) const {
-    for (uint32_t i = threadIdx.x; i < ncand_g; i += kThreads) {
-      const uint64_t e = i == threadIdx.x ? cand0 : cand_g[i];
+    const uint32_t first = fin_entry(threadIdx.x);
+    for (uint32_t i = first; i < ncand_g; i += kThreads) {
+      const uint64_t e = i == first ? cand0 : cand_g[i];
       if (kind == kCandTokens) {
         f(uint32_t(e >> 32), int(0xFFFFFFFFu - uint32_t(e & 0xFFFFFFFFu)));
         continue;
       }
       uint4 u[2];
-      if (i == threadIdx.x) {
+      if (i == first) {
         u[0] = unit0[0];
         u[1] = unit0[1];
       } else {
@@ -1466,7 +1472,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNE
 // record's count words (the same sums as the one-kernel path, keys in
 // ascending order); a key query loads one segment's words; then everything
 // after the histogram exactly as in the one-kernel path.
-__global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARGS,
+__global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_ARGS,
                                                                   const uint8_t *__restrict__ recs) {
   constexpr int NTH = NT_FIN;
   __shared__ SmemFin sm;
@@ -1486,7 +1492,7 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   uint4 bv[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) bv[u] = reinterpret_cast<const uint4*>(blocks)[tid + u * NTH];
-  const uint64_t cand0 = reinterpret_cast<const uint64_t*>(rec + kRecCand)[tid];
+  const uint64_t cand0 = reinterpret_cast<const uint64_t*>(rec + kRecCand)[fin_entry(tid)];
   a.key_y = key16(a.rowp[a.y]);
   // meanwhile: empty summaries and no staging for every segment
   for (int sg = tid; sg < NSEG; sg += NTH) {
@@ -1508,7 +1514,7 @@ __global__ __launch_bounds__(NT_FIN) void transforms_finish_kernel(VS_KERNEL_ARG
   }
   // this thread's first candidate unit: loaded now, used at the dense ids
   uint4 unit0[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  if (cand_kind == kCandUnits && uint32_t(tid) < hd.y) {
+  if (cand_kind == kCandUnits && fin_entry(tid) < hd.y) {
     const uint4* pv = reinterpret_cast<const uint4*>(a.rowp);
     const uint32_t v0 = uint32_t(cand0 & 0xFFFFFFFFu), v1 = uint32_t(cand0 >> 32);
     unit0[0] = pv[v0];
