@@ -6,26 +6,32 @@
 // each filter keeps a prefix of it, so the support is the shortest prefix
 // pi[0:L].  Its scores follow SkyRL PR #2004 (renormalise over the support).
 //
-// One 512-thread workgroup per row.  Tokens are compared through 16-bit
-// order-preserving keys (a larger key is a larger logit; -0 is folded onto
-// +0).  Every token with the same key has the same probability, so every cut
-// position and every support sum follows exactly from the histogram of key
-// counts:
+// Tokens are compared through 16-bit order-preserving keys (a larger key is a
+// larger logit; -0 is folded onto +0).  Every token with the same key has the
+// same probability, so every cut position and every support sum follows
+// exactly from the histogram of key counts:
 //   * 1024 segments of 64 keys, each with its token count, its mass
 //     sum c * exp(z - z_max) and sum c * exp(z - z_max) * (z - z_max) in fp64
-//     (one exp per distinct key, not per token);
+//     (a segment's weights form a geometric sequence: three exp calls);
 //   * rank and mass queries walk the segments in descending key order, then
 //     the 64 keys of one segment;
 //   * inside the threshold key, ties go by token id: the support holds its
 //     first r tokens.
-// Fast kernel: the row is held in registers and counted once into 65536
-// 16-bit counters packed two per LDS word (one branch-free atomic per token).
-// A counter that would pass 65535 (a key repeated that often) is detected from
-// the exact total and the row is handed to the stream kernel, which re-reads
-// the row from memory for every pass and counts with 32-bit bins in two
-// halves; it also serves rows too long for registers.  Dense support ids (at
-// most 4096) come from sorting the few candidate tokens in LDS.  All sums run
-// in a fixed order, so results are bitwise reproducible.
+// The histogram is 65536 16-bit counters packed two per LDS word (one
+// branch-free atomic per token).  A counter that would pass 65535 (a key
+// repeated that often) is detected from the exact total and the row is handed
+// to the stream kernel, which re-reads the row for every pass and counts with
+// 32-bit bins in two halves.
+// Kernels:
+//   * rows up to 20 * 512 * 8 tokens: one 512-thread workgroup per row with
+//     the row in registers (transforms_fast_kernel<NV>);
+//   * longer rows: a count kernel (1024 threads per row: histogram, checks,
+//     per-row record of the non-empty counts and the dense-id candidates) and
+//     a finish kernel (256 threads per row, four rows per CU: sums, cuts,
+//     descriptor, dense ids, scores), or, above 2048 dense ids, one
+//     1024-thread workgroup per row (transforms_fast_kernel<0>).
+// Dense support ids come from ranking the few candidate tokens in LDS.  All
+// sums run in a fixed order, so results are bitwise reproducible.
 #include <type_traits>
 
 #include "common.h"
