@@ -76,3 +76,67 @@ def test_full_size_sampled(vsa):
                              oracle.logits_from_logits(c["draft"], "bf16", rows=rows))
     assert_close("l1", got["l1"].cpu().numpy(), ref["l1"], rows=rows)
     assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"], rows=rows)
+
+
+def _l1_case(vsa, a, b, ld_pad=0):
+    ab, bb = workloads.to_bf16_bits(a), workloads.to_bf16_bits(b)
+    if ld_pad:
+        T, V = ab.shape
+        ab = np.concatenate([ab, np.zeros((T, ld_pad), ab.dtype)], axis=1)
+        bb = np.concatenate([bb, np.zeros((T, ld_pad), bb.dtype)], axis=1)
+        ta, tb = bf16_tensor(ab)[:, :V], bf16_tensor(bb)[:, :V]
+        ab, bb = ab[:, :V], bb[:, :V]
+    else:
+        ta, tb = bf16_tensor(ab), bf16_tensor(bb)
+    got = vsa.l1_distance(ta, tb)
+    ref = oracle.l1_distance(oracle.logits_from_logits(ab, "bf16"), oracle.logits_from_logits(bb, "bf16"))
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"])
+    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"])
+    return got
+
+
+def test_resident_rows_more_than_cus(vsa):
+    # one workgroup per CU walks several rows: a NaN row and an all -inf draft
+    # row must not disturb the rows the same workgroup takes after them
+    T, V = 300, 100003
+    say(f"l1 resident form: T={T} V={V} bf16 (tail of 3), bad rows 5 and 6, identical row 7")
+    rng = np.random.default_rng(11)
+    a = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    b = (a + rng.standard_normal((T, V)) * rng.uniform(0, 4, (T, 1))).astype(np.float32)
+    a[5, 77] = np.nan
+    b[6] = -np.inf
+    b[7] = a[7]
+    b[8] = -20.0
+    b[8, V - 1] = 20.0  # all the draft mass on the last (tail) element
+    got = _l1_case(vsa, a, b)
+    l1 = got["l1"].cpu().numpy()
+    assert np.isnan(l1[5]) and np.isnan(l1[6]) and l1[7] == 0.0
+    assert np.isfinite(l1[np.r_[0:5, 8:T]]).all()
+
+
+@pytest.mark.parametrize("V", [65537, 131072, 155648, 155655, 155656])
+def test_resident_bounds(vsa, V):
+    # the smallest and largest rows of the resident form, and the first row
+    # length past it (two-pass form)
+    say(f"l1 resident bounds: T=5 V={V} bf16")
+    rng = np.random.default_rng(V)
+    a = (rng.standard_normal((5, V)) * 3).astype(np.float32)
+    b = (a + rng.standard_normal((5, V))).astype(np.float32)
+    b[1] = a[1]
+    a[2, :] = -np.inf
+    a[2, V // 2] = 1.0  # a one-hot target
+    a[3] = np.float32(0.25)  # a uniform target
+    got = _l1_case(vsa, a, b)
+    assert float(got["l1"][1]) == 0.0
+
+
+@pytest.mark.parametrize("pad", [8, 5])
+def test_resident_leading_dimension(vsa, pad):
+    # ld = V + 8 keeps rows 16-byte aligned (resident form); ld = V + 5 does not
+    # (two-pass form)
+    T, V = 40, 151936
+    say(f"l1 leading dimension: T={T} V={V} ld=V+{pad}")
+    rng = np.random.default_rng(pad)
+    a = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    b = (a + rng.standard_normal((T, V)) * 0.5).astype(np.float32)
+    _l1_case(vsa, a, b, ld_pad=pad)
