@@ -19,33 +19,53 @@ namespace {
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 8;
 
-// Fold n raw logits into the online state (base-2 units, u = x * c).  The
-// exponent of each term is one FMA; the floor is applied only inside the
-// entropy term, so a -inf logit adds exactly 0 and a NaN poisons s.
-__device__ __forceinline__ void fold_values(Part& p, const float* v, int n, float c) {
-  float bm = v[0];
-  for (int i = 1; i < n; ++i) bm = fmaxf(bm, v[i]);
-  const float nm = fmaxf(p.m, bm * c);
-  if (nm == kNegInf) {  // only -inf so far, or a NaN that fmaxf dropped
-    for (int i = 0; i < n; ++i)
-      if (v[i] != v[i]) p.s = __builtin_nanf("");
-    return;
-  }
-  if (nm > p.m) {  // move the reference to the new max, as merge() would
-    if (!(p.m == kNegInf && p.s == 0.0f)) {
-      const float d = p.m - nm;
-      const float f = exp2_hw(d);
-      p.a = f * __builtin_fmaf(p.s, d, p.a);
-      p.s *= f;
-    }
-    p.m = nm;
-  }
+// Fold n raw logits into the state (base-2 units, u = x * c) against its
+// reference m, which moves only when it must: a block whose terms sum to 2^32
+// or more (a logit more than 32 above m, the initial m = -inf, or a NaN) is
+// folded again after m moves to the block's largest logit, as merge() would.
+// The reference then stays within 32 of the running maximum: the entropy sum
+// sum 2^d d (d = u - m <= 32) loses about 32 ulps (relative) to cancellation
+// when the states are merged, and the common block costs no maximum and no
+// rescale.  (A trigger at 2^8 fired in some lane of most waves on N(0, 2)
+// logits, and the wave then took the slow path.)  The floor is
+// applied only inside the entropy term, so a -inf logit adds exactly 0 and a
+// NaN poisons s.
+__device__ __forceinline__ void fold_terms(float m, const float* v, int n, float c, float& cs, float& ca) {
+  cs = 0.0f;
+  ca = 0.0f;
   for (int i = 0; i < n; ++i) {
-    const float d = __builtin_fmaf(v[i], c, -nm);
+    const float d = __builtin_fmaf(v[i], c, -m);
     const float e = exp2_hw(d);
-    p.s += e;
-    p.a = __builtin_fmaf(e, fmaxf(d, kDFloor), p.a);
+    cs += e;
+    ca = __builtin_fmaf(e, fmaxf(d, kDFloor), ca);
   }
+}
+
+__device__ __forceinline__ void fold_values(Part& p, const float* v, int n, float c) {
+  float cs, ca;
+  fold_terms(p.m, v, n, c, cs, ca);
+  if (!(cs < 0x1p32f)) {
+    float bm = v[0];
+    for (int i = 1; i < n; ++i) bm = fmaxf(bm, v[i]);
+    const float nm = fmaxf(p.m, bm * c);
+    if (nm == kNegInf) {  // only -inf so far, or a NaN that fmaxf dropped
+      for (int i = 0; i < n; ++i)
+        if (v[i] != v[i]) p.s = __builtin_nanf("");
+      return;
+    }
+    if (nm > p.m) {
+      if (!(p.m == kNegInf && p.s == 0.0f)) {
+        const float d = p.m - nm;
+        const float f = exp2_hw(d);
+        p.a = f * __builtin_fmaf(p.s, d, p.a);
+        p.s *= f;
+      }
+      p.m = nm;
+    }
+    fold_terms(p.m, v, n, c, cs, ca);
+  }
+  p.s += cs;
+  p.a += ca;
 }
 
 template <int DT>
