@@ -24,7 +24,6 @@ namespace vs {
 namespace {
 
 constexpr int NT = 256;
-constexpr int kMaxWidth = 1024;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -47,9 +46,14 @@ __global__ __launch_bounds__(NT) void support_kernel(
   // No contraction in this kernel: u = x * c is rounded before u - max, so
   // the maximum's own term is exactly 2^0 = 1 with d = 0.
 #pragma clang fp contract(off)
-  extern __shared__ uint4 hs[];  // hidden row as bf16, H/8 chunks (fused source only)
-  __shared__ int64_t sid[kMaxWidth];
-  __shared__ float sx[kMaxWidth];
+  // dynamic LDS, sized by the launch: the hidden row as bf16 (H/8 chunks,
+  // fused source only), then the row's ids and their logits.  Sizing the id
+  // arrays by the width instead of its maximum keeps a 64-wide support at
+  // 15 KiB per workgroup at H = 7168, so eight workgroups share a CU.
+  extern __shared__ uint4 dyn[];
+  uint4* hs = dyn;
+  int64_t* sid = reinterpret_cast<int64_t*>(dyn + (FUSED ? H / 8 : 0));
+  float* sx = reinterpret_cast<float*>(sid + width);
   __shared__ int s_bad, s_count;
 
   const int64_t row = blockIdx.x;
@@ -206,6 +210,11 @@ __global__ __launch_bounds__(NT) void support_kernel(
   }
 }
 
+// dynamic LDS of one workgroup: [bf16 hidden row][ids int64][logits fp32]
+size_t support_lds_bytes(bool fused, int64_t H, int64_t width) {
+  return (fused ? size_t(H / 8) * 16 : 0) + size_t(width) * 8 + size_t(width) * 4;
+}
+
 }  // namespace
 
 int launch_support_logits(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
@@ -213,7 +222,8 @@ int launch_support_logits(LogitsArg lg, int64_t rows, int64_t V, const float* te
                           const uint8_t* fallback, float* logprob, float* entropy, uint8_t* status,
                           int32_t* fb_list, int32_t* fb_count, void* stream) {
   if (rows <= 0) return 0;
-  support_kernel<false><<<dim3(unsigned(rows)), dim3(NT), 0, static_cast<hipStream_t>(stream)>>>(
+  const size_t lds = support_lds_bytes(false, 0, width);
+  support_kernel<false><<<dim3(unsigned(rows)), dim3(NT), lds, static_cast<hipStream_t>(stream)>>>(
       lg.ptr, lg.dtype, lg.ld, nullptr, 0, 0, V, temp, temp_scalar, ids, int(width), ld_ids, targets, fallback,
       logprob, entropy, status, fb_list, fb_count);
   return int(hipGetLastError());
@@ -225,7 +235,7 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
                          const int64_t* targets, const uint8_t* fallback, float* logprob, float* entropy,
                          uint8_t* status, int32_t* fb_list, int32_t* fb_count, void* stream) {
   if (rows <= 0) return 0;
-  const size_t lds = size_t(H) * 2;  // bf16 hidden row
+  const size_t lds = support_lds_bytes(true, H, width);
   support_kernel<true><<<dim3(unsigned(rows)), dim3(NT), lds, static_cast<hipStream_t>(stream)>>>(
       hidden, hidden_dtype, ld_hidden, weight, ld_weight, H, V, temp, temp_scalar, ids, int(width), ld_ids,
       targets, fallback, logprob, entropy, status, fb_list, fb_count);
