@@ -91,20 +91,44 @@ __device__ __forceinline__ Part row_state(const void* rowp, int64_t V, float c) 
   int64_t q = tid;
   float v[VEC];
   if (DT == VS_BF16) {
-    const uint4* pv = static_cast<const uint4*>(rowp);
-    for (; q + int64_t(kRowUnroll - 1) * kRowThreads < nvec; q += int64_t(kRowUnroll) * kRowThreads) {
-      uint4 w[kRowUnroll];
+    // a ring of kRowUnroll loads: chunk k's slot is refilled with chunk
+    // k + kRowUnroll as soon as k is taken, so the loads stay in flight while
+    // the thread folds (chunks in ascending order, as a plain loop would)
+    const uint4* pv = static_cast<const uint4*>(rowp) + tid;
+    const int64_t n = nvec > tid ? (nvec - 1 - tid) / kRowThreads + 1 : 0;  // this thread's chunks
+    constexpr int U = kRowUnroll;
+    if (n >= U) {
+      uint4 w[U];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) w[u] = stream_load(pv + q + u * kRowThreads);
+      for (int u = 0; u < U; ++u) w[u] = stream_load(pv + int64_t(u) * kRowThreads);
+      int64_t i = 0;
+      for (; i + 2 * U <= n; i += U) {
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
-        unpack<DT>(w[u], v);
+        for (int u = 0; u < U; ++u) {
+          const uint4 cur = w[u];
+          w[u] = stream_load(pv + (i + U + u) * kRowThreads);
+          unpack<DT>(cur, v);
+          fold_values(p, v, VEC, c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // chunks i .. i+U-1; refills only inside the row
+        const uint4 cur = w[u];
+        if (i + U + u < n) w[u] = stream_load(pv + (i + U + u) * kRowThreads);
+        unpack<DT>(cur, v);
         fold_values(p, v, VEC, c);
       }
-    }
-    for (; q < nvec; q += kRowThreads) {
-      unpack<DT>(stream_load(pv + q), v);
-      fold_values(p, v, VEC, c);
+#pragma unroll
+      for (int u = 0; u < U; ++u)  // the last n - i - U < U chunks
+        if (i + U + u < n) {
+          unpack<DT>(w[u], v);
+          fold_values(p, v, VEC, c);
+        }
+    } else {
+      for (int64_t k = 0; k < n; ++k) {
+        unpack<DT>(stream_load(pv + k * kRowThreads), v);
+        fold_values(p, v, VEC, c);
+      }
     }
     for (int64_t i = nvec * VEC + tid; i < V; i += kRowThreads) {
       v[0] = bf16_to_f32(static_cast<const uint16_t*>(rowp)[i]);
