@@ -482,10 +482,17 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
   const bool aligned = ((reinterpret_cast<uintptr_t>(target.ptr) | reinterpret_cast<uintptr_t>(draft.ptr)) & 15) == 0 &&
                        (target.ld & 7) == 0 && (draft.ld & 7) == 0;
   if (target.dtype == VS_BF16 && aligned && V >= kResMinV && V <= kResMaxVec * 8 + 7) {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || ncu <= 0)
-      return int(hipErrorInvalidDevice);
+    // CU count of the current device, cached per device (a benign race: every
+    // writer stores the same value)
+    static int cu_count[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return int(hipErrorInvalidDevice);
+    int ncu = dev < 64 ? cu_count[dev] : 0;
+    if (ncu <= 0) {
+      if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        return int(hipErrorInvalidDevice);
+      if (dev < 64) cu_count[dev] = ncu;
+    }
     const int64_t grid = rows < ncu ? rows : ncu;
     l1_resident_kernel<<<dim3(unsigned(grid)), dim3(RES_NT), 0, s>>>(
         static_cast<const uint16_t*>(target.ptr), target.ld, static_cast<const uint16_t*>(draft.ptr), draft.ld, rows, V,
