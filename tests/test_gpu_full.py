@@ -128,6 +128,25 @@ def test_fused_ragged(vsa, T, H, V):
     _cmp_full(got, oracle.score_full(x, tau, y))
 
 
+def test_fused_many_tiles_ragged(vsa):
+    # more tiles than CUs at an even stage count (H = 128, 64-wide stages), so
+    # CUs run several tiles back to back; the last vocabulary and token tiles
+    # are ragged (136 and 184 rows)
+    T, H, V = 3000, 128, 5000
+    say(f"fused, many tiles: T={T} H={H} V={V}, ragged last tiles")
+    rng = np.random.default_rng(31)
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.2).astype(np.float32))
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    y[:4] = [0, V - 1, 4863, 4864]  # ids in the first, the ragged last and its neighbouring tile
+    got = vsa.score_full(to_dev(y), hidden=bf16_tensor(hb), weight=bf16_tensor(wb), temperature=to_dev(tau))
+    x = oracle.logits_from_hidden(hb, "bf16", wb)
+    _cmp_full(got, oracle.score_full(x, tau, y))
+    again = vsa.score_full(to_dev(y), hidden=bf16_tensor(hb), weight=bf16_tensor(wb), temperature=to_dev(tau))
+    assert all(torch.equal(got[k], again[k]) for k in ("lse", "logprob", "entropy"))
+
+
 def test_fused_strided_weight(vsa):
     say("fused: padded leading dims (ld_hidden=136, ld_weight=264)")
     rng = np.random.default_rng(5)
