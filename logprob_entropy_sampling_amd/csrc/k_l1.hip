@@ -366,10 +366,12 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
     uint4 tb[RES_U];
 #pragma unroll
     for (int u = 0; u < RES_U; ++u) tb[u] = res_load(rt, voff, u);
-    float ta = 0.0f, da = 0.0f;  // this thread's tail element, if any
+    // this thread's tail element, if any; kept raw until the end of pass 1, so
+    // the wait for it does not also wait for every load issued before it
+    uint16_t ta_raw = 0, da_raw = 0;
     if (tid < ntail) {
-      ta = bf16_to_f32(tgt[row * ld_t + nvec * 8 + tid]);
-      da = bf16_to_f32(dft[row * ld_d + nvec * 8 + tid]);
+      ta_raw = tgt[row * ld_t + nvec * 8 + tid];
+      da_raw = dft[row * ld_d + nvec * 8 + tid];
     }
 
     // ---- pass 1: sums of both rows against lazily moved references; target
@@ -388,6 +390,9 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
         lazy_add<8>(cy, sy, v);
       }
     }
+    uint32_t tr = ta_raw, dr = da_raw;
+    asm volatile("" : "+v"(tr), "+v"(dr));  // keeps the conversion (and its wait) here
+    const float ta = __uint_as_float(tr << 16), da = __uint_as_float(dr << 16);
     if (tid < ntail) {
       lazy_add<1>(cx, sx, &ta);
       lazy_add<1>(cy, sy, &da);
