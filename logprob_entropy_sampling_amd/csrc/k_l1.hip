@@ -303,19 +303,31 @@ __device__ __forceinline__ void lazy_add(float& c, float& s, const float* v) {
 // weight of a state with reference c inside a merge whose reference is M >= c
 __device__ __forceinline__ float ref_scale(float c, float M) { return c == M ? 1.0f : exp2_hw(c - M); }
 
-__device__ __forceinline__ float wave_max_all(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// Wave maximum and sum with DPP moves (no LDS round trips): shifts by 1, 2,
+// 4, 8 inside each row of 16 lanes, then lane 15 of rows 0 and 2 into rows 1
+// and 3, then lane 31 into rows 2 and 3; lanes with no source take the
+// operation's identity.  Lane 63 ends with the result, read into a scalar
+// register.  A fixed order, so the sums are reproducible.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v, float identity) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
-
-__device__ __forceinline__ float wave_sum_lane0(float v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = shfl_down_f(v, off);
-    if ((lane & ((off << 1) - 1)) == 0) v += o;
-  }
-  return v;
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, float identity, Op op) {
+  x = op(x, dpp_f32<0x111, 0xf>(x, identity));  // row_shr:1
+  x = op(x, dpp_f32<0x112, 0xf>(x, identity));  // row_shr:2
+  x = op(x, dpp_f32<0x114, 0xf>(x, identity));  // row_shr:4
+  x = op(x, dpp_f32<0x118, 0xf>(x, identity));  // row_shr:8
+  x = op(x, dpp_f32<0x142, 0xa>(x, identity));  // row_bcast:15 into rows 1, 3
+  x = op(x, dpp_f32<0x143, 0xc>(x, identity));  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+  return wave_reduce(v, kNegInf, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_sum_all(float v) {
+  return wave_reduce(v, 0.0f, [](float a, float b) { return a + b; });
 }
 
 __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __restrict__ tgt, int64_t ld_t,
@@ -406,8 +418,8 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
     // then every wave combines the NW wave states itself in a fixed order
     {
       const float Mx = wave_max_all(cx), My = wave_max_all(cy);
-      const float wx = wave_sum_lane0(sx * ref_scale(cx, Mx), lane);
-      const float wy = wave_sum_lane0(sy * ref_scale(cy, My), lane);
+      const float wx = wave_sum_all(sx * ref_scale(cx, Mx));
+      const float wy = wave_sum_all(sy * ref_scale(cy, My));
       if (lane == 0) {
         red_a[b][wave][0] = Mx;
         red_a[b][wave][1] = wx;
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
       d[j] = res_load(rn, voff, j);
     }
     if (tid < ntail) acc += absdiff(ta, da, lx, ly);
-    acc = wave_sum_lane0(acc, lane);
+    acc = wave_sum_all(acc);
     if (lane == 0) red_b[b][wave] = acc;  // summed after the next row's barrier
     prev_ok = ok;
   }
