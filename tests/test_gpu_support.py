@@ -165,3 +165,33 @@ def test_replay_workload_full_size_sampled(vsa):
         return oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=[rows[t]], cols=cols)[0]
     ref = oracle.score_support(fn, c["V"], c["support_ids"][rows], 1.0, c["targets"][rows])
     _cmp(got, ref, rows=rows)
+
+
+def test_fused_max_width_duplicates_far_apart(vsa):
+    # the widest support (1024 ids, sized LDS arrays at their largest) on the
+    # fused source: distinct ids with padding anywhere, a repeated id far
+    # from its first use (BAD_INPUT), an id >= V, an empty row
+    T, H, V, W = 12, 256, 4000, 1024
+    say(f"support: fused source, width {W} (maximum), duplicates far apart, id >= V, empty row")
+    rng = np.random.default_rng(41)
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.1).astype(np.float32))
+    ids = np.full((T, W), -1, np.int64)
+    y = np.empty(T, np.int64)
+    for t in range(T):
+        w = int(rng.integers(W // 2, W + 1))
+        row = rng.choice(V, w, replace=False)
+        ids[t, rng.choice(W, w, replace=False)] = row
+        y[t] = row[int(rng.integers(0, w))]
+    used = np.nonzero(ids[2] >= 0)[0]
+    ids[2, used[-1]] = ids[2, used[0]]  # a repeat, hundreds of positions after the first use
+    ids[4, 1000] = V  # out of range
+    ids[7] = -1  # empty
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    got = vsa.score_support_ids(to_dev(y), to_dev(ids), hidden=bf16_tensor(hb), weight=bf16_tensor(wb),
+                                temperature=to_dev(tau))
+    x = oracle.logits_from_hidden(hb, "bf16", wb)
+    ref = oracle.score_support(lambda t, cols: x[t, cols], V, ids, tau, y)
+    st = ref["status"]
+    assert st[2] == oracle.ST_BAD_INPUT and st[4] == oracle.ST_BAD_INPUT, st
+    _cmp(got, ref)
