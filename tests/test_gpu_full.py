@@ -59,6 +59,28 @@ def test_logits_ragged_and_strided(vsa, dtype, ld_pad):
     _cmp_full(got, oracle.score_full(x64, tau, y))
 
 
+@pytest.mark.parametrize("V", [4096 * 8 - 1, 4096 * 8, 4096 * 8 + 5, 512 * 8 * 9 + 3, 512 * 8 * 15 + 7, 512 * 8 * 16,
+                               512 * 8 * 17 + 1])
+def test_logits_load_ring_lengths(vsa, V):
+    # bf16 rows whose threads hold fewer than 8 vectors, exactly 8, between 9
+    # and 15, 16, and 17 or more (the load ring's plain, drain-only, drain and
+    # tail, one-pass and steady paths), each with a ragged scalar tail
+    say(f"logits load ring: T=6 V={V} bf16, NaN and -inf rows")
+    rng = np.random.default_rng(V)
+    T = 6
+    x = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    x[1, V - 1] = 30.0  # the row's mass on its last (tail) logit
+    x[2, :] = -np.inf
+    x[2, V // 3] = 0.5
+    x[3, V - 2] = np.nan
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    y[1] = V - 1
+    bits = workloads.to_bf16_bits(x)
+    got = vsa.score_full(to_dev(y), logits=bf16_tensor(bits), temperature=to_dev(tau))
+    _cmp_full(got, oracle.score_full(oracle.logits_from_logits(bits, "bf16"), tau, y))
+
+
 def test_vocab_chunk_and_determinism(vsa):
     say("vocab_chunk variants + bitwise run-to-run equality")
     c = workloads.make(2, T=16)
