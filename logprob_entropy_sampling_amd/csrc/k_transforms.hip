@@ -1051,7 +1051,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   seg_of_rank(L - 1);
   bin_query(0, L - 1, 0.0);
   const uint32_t K_L = sm.bu[2];
-  const uint32_t r_L = L - sm.bu[3];  // tokens of the threshold key inside the support
+  const uint32_t above_L = sm.bu[3], cnt_L = sm.bu[4];
+  const uint32_t r_L = L - above_L;  // tokens of the threshold key inside the support
   const double e_L = sm.bd[4];
   const double d_L = double(key_logit(K_L)) / tau - z0;
   const double mass_S = sm.bd[2] + double(r_L) * e_L;
@@ -1074,11 +1075,16 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     const typename Keys::Listed listed_data = keys.load_listed();  // in flight during the rank query
     const uint32_t n_out = L < uint32_t(a.cap) ? L : uint32_t(a.cap);
     if (L > uint32_t(a.cap)) st |= kRowTruncated;
-    seg_of_rank(n_out - 1);
-    bin_query(0, n_out - 1, 0.0);
-    const uint32_t K_c = sm.bu[2];
-    const uint32_t above_c = sm.bu[3];
-    const uint32_t cnt_c = sm.bu[4];
+    // the key at rank n_out - 1: the support's own threshold query when the
+    // whole support fits the cap
+    uint32_t K_c = K_L, above_c = above_L, cnt_c = cnt_L;
+    if (n_out != L) {
+      seg_of_rank(n_out - 1);
+      bin_query(0, n_out - 1, 0.0);
+      K_c = sm.bu[2];
+      above_c = sm.bu[3];
+      cnt_c = sm.bu[4];
+    }
     const uint32_t r_c = n_out - above_c;
     const bool with_ties = above_c + cnt_c <= uint32_t(Keys::kCollectMax);
     // candidates: every token with key > K_c, plus the tied tokens when they fit
