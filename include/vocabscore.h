@@ -199,6 +199,7 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
  * or draft LSE is not finite gives NaN for both.
  *   target_logits [T, ld_target], draft_logits [T, ld_draft], both of `dtype`
  *   (VS_BF16 or VS_F32), ld >= V.  accept_rate nullable; l1 required.
+ *   No workspace: workspace may be null and workspace_bytes 0.
  */
 int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T,
                    int64_t V, int64_t ld_target, int64_t ld_draft, float* l1, float* accept_rate,
