@@ -126,25 +126,33 @@ def _valid_tau(tau) -> bool:
     return bool(np.isfinite(tau) and tau > 0.0)
 
 
-def _lse_and_entropy(z: np.ndarray):
-    """Log-sum-exp and entropy of softmax(z) for one row (two-pass max shift).
+def _log_softmax(x: np.ndarray, tau: float = 1.0):
+    """Log-softmax, log-sum-exp and entropy of softmax(x / tau) for one row.
 
-    ``LSE = m + ln sum_v exp(z_v - m)`` with ``m = max_v z_v``;
-    ``H = -sum_v p_v ln p_v`` with ``p_v = exp(z_v - LSE)`` and
-    ``ln p_v = z_v - LSE``; a zero-probability entry (z = -inf) adds 0.
-    Returns ``(nan, nan)`` when the row holds a NaN or +inf or is all -inf.
+    The plain definition, evaluated from shifted values so that no term is
+    lost at any magnitude: with ``x_max = max_v x_v``,
+    ``d_v = (x_v - x_max) / tau`` (the difference of two widened inputs is
+    exact; the division rounds once), ``ln s = ln sum_v exp(d_v)``,
+    ``ln p_v = d_v - ln s``, ``LSE = x_max / tau + ln s`` and
+    ``H = -sum_v p_v ln p_v``.  (Forming ``z_v - LSE`` from the unshifted
+    ``z = x / tau`` instead drops ``ln s`` below one float64 ulp of ``z``
+    once ``|z|`` passes about 2^42.)  Since ``tau > 0``, ``x_max / tau`` is
+    the maximum of ``z``.  A zero-probability entry (``x = -inf``) adds 0.
+    Returns ``(lse, lnp, h)``; ``(nan, None, nan)`` when the row is empty,
+    holds a NaN or +inf, or is all -inf.
     """
-    if z.size == 0 or np.isnan(z).any():
-        return np.nan, np.nan
-    m = z.max()
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0 or np.isnan(x).any():
+        return np.nan, None, np.nan
+    m = x.max()
     if not np.isfinite(m):
-        return np.nan, np.nan
-    s = np.sum(np.exp(z - m))
-    lse = m + np.log(s)
-    lnp = z - lse
+        return np.nan, None, np.nan
+    d = (x - m) / tau
+    ln_s = np.log(np.sum(np.exp(d)))
+    lnp = d - ln_s
     p = np.exp(lnp)
     h = -np.sum(np.where(p > 0.0, p * np.where(np.isfinite(lnp), lnp, 0.0), 0.0))
-    return lse, h
+    return m / tau + ln_s, lnp, h
 
 
 # ---------------------------------------------------------------------------
@@ -178,13 +186,12 @@ def score_full(x, tau, targets) -> dict:
         if not _valid_tau(tau[t]) or not (0 <= y < V):
             status[t] = ST_BAD_INPUT
             continue
-        z = x[t] / tau[t]
-        l, h = _lse_and_entropy(z)
+        l, lnp, h = _log_softmax(x[t], tau[t])
         if not np.isfinite(l):
             status[t] = ST_BAD_INPUT
             continue
         lse[t] = l
-        logprob[t] = z[y] - l
+        logprob[t] = lnp[y]
         entropy[t] = h
     return {"lse": lse, "logprob": logprob, "entropy": entropy, "status": status}
 
@@ -244,15 +251,14 @@ def score_support(logit_fn, V: int, ids, tau, targets, fallback=None) -> dict:
         if not (0 <= y < V):
             status[t] = ST_BAD_INPUT
             continue
-        z = logit_fn(t, sup) / tau[t]
-        l, h = _lse_and_entropy(z)
+        l, lnp, h = _log_softmax(logit_fn(t, sup), tau[t])
         if not np.isfinite(l):
             status[t] = ST_BAD_INPUT
             continue
         entropy[t] = h
         hit = np.nonzero(sup == y)[0]
         if hit.size:
-            logprob[t] = z[hit[0]] - l
+            logprob[t] = lnp[hit[0]]
         else:
             logprob[t] = -np.inf
             status[t] = ST_TARGET_OUTSIDE_SUPPORT
@@ -263,10 +269,10 @@ def score_support(logit_fn, V: int, ids, tau, targets, fallback=None) -> dict:
 # O3: sampling transforms (temperature -> top-k -> top-p -> min-p)
 # ---------------------------------------------------------------------------
 
-def _rank_order(z: np.ndarray) -> np.ndarray:
-    """Token ids sorted by tempered logit descending, ties by ascending id."""
-    ids = np.arange(z.size)
-    return np.lexsort((ids, -z))
+def _rank_order(x: np.ndarray) -> np.ndarray:
+    """Token ids sorted by logit descending, ties by ascending id."""
+    ids = np.arange(x.size)
+    return np.lexsort((ids, -x))
 
 
 def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict:
@@ -328,20 +334,21 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
                 or np.isnan(p_min) or p_min > 1.0 or not (0 <= y < V)):
             out["status"][t] = ST_BAD_INPUT
             continue
-        z = x[t] / tau[t]
-        full_lse, _ = _lse_and_entropy(z)
+        full_lse, _, _ = _log_softmax(x[t], tau[t])
         if not np.isfinite(full_lse):
             out["status"][t] = ST_BAD_INPUT
             continue
         out["full_lse"][t] = full_lse
 
-        order = _rank_order(z)
-        zs = z[order]
+        # tau > 0 keeps the order of x, so ranking x ranks z = x / tau exactly
+        order = _rank_order(x[t])
+        xs = x[t, order]
+        d = (xs - xs[0]) / tau[t]  # z - z_max from the exact input difference
         k = int(top_k[t])
         L_k = V if (k <= 0 or k >= V) else k
 
         # inclusive top-p on the top-k renormalised masses
-        e = np.exp(zs[:L_k] - zs[0])
+        e = np.exp(d[:L_k])
         mass = e / np.sum(e)
         excl = np.concatenate(([0.0], np.cumsum(mass)))  # excl[j] = E_j, excl[L_k] = total
         if p_top >= 1.0:
@@ -354,7 +361,7 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
         if p_min <= 0.0:
             L_m = V
         else:
-            rel = np.exp(zs - zs[0])
+            rel = np.exp(d)
             L_m = int(np.count_nonzero(rel >= p_min))
             out["borderline_min_p"][t] = bool(np.any(np.abs(rel - p_min) <= BORDERLINE))
 
@@ -370,7 +377,7 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
             if L > cap:
                 out["status"][t] |= ST_SUPPORT_TRUNCATED
 
-        lse_s, h_s = _lse_and_entropy(zs[:L])
+        lse_s, lnp_s, h_s = _log_softmax(xs[:L], tau[t])
         if not np.isfinite(lse_s):
             out["status"][t] = ST_BAD_INPUT
             out["support_len"][t] = 0
@@ -382,7 +389,7 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
         out["entropy"][t] = h_s
         rank_y = int(np.nonzero(order == y)[0][0])
         if rank_y < L:
-            out["logprob"][t] = z[y] - lse_s
+            out["logprob"][t] = lnp_s[rank_y]
         else:
             out["logprob"][t] = -np.inf
             out["status"][t] |= ST_TARGET_OUTSIDE_SUPPORT
@@ -407,12 +414,12 @@ def l1_distance(x_target, x_draft) -> dict:
     l1 = np.full(R, np.nan)
     acc = np.full(R, np.nan)
     for t in range(R):
-        la, _ = _lse_and_entropy(a[t])
-        lb, _ = _lse_and_entropy(b[t])
+        la, lnp_a, _ = _log_softmax(a[t])
+        lb, lnq_b, _ = _log_softmax(b[t])
         if not (np.isfinite(la) and np.isfinite(lb)):
             continue
-        p = np.exp(a[t] - la)
-        q = np.exp(b[t] - lb)
+        p = np.exp(lnp_a)
+        q = np.exp(lnq_b)
         d = np.sum(np.abs(p - q))
         l1[t] = d
         acc[t] = min(1.0, max(0.0, 1.0 - 0.5 * d))

@@ -101,6 +101,44 @@ def test_shift_and_temperature_relations():
             np.testing.assert_array_equal(a[k], b[k])
 
 
+@pytest.mark.parametrize("shift_exp,unit_exp", [(40, 0), (60, 8), (100, 48), (1000, 948)])
+def test_huge_shift_invariance(shift_exp, unit_exp):
+    # logits c + 2^u * k_v with tau = 2^u: every value is exact in float64
+    # (the spacing at c = 2^e is 2^(e-52) <= 2^u) and z = c / tau + k_v, so
+    # logprob and entropy must equal those of the small integers k_v with
+    # tau = 1 (a shift changes neither), and LSE moves by exactly c / tau.
+    rng = np.random.default_rng(shift_exp)
+    k = rng.integers(-12, 13, size=(5, 300)).astype(np.float64)
+    y = rng.integers(0, 300, size=5)
+    c, unit = 2.0 ** shift_exp, 2.0 ** unit_exp
+    base = oracle.score_full(k, 1.0, y)
+    for sign in (1.0, -1.0):
+        x = sign * c + unit * k
+        assert np.array_equal((x - sign * c) / unit, k)  # exactly representable
+        r = oracle.score_full(x, unit, y)
+        np.testing.assert_allclose(r["logprob"], base["logprob"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["entropy"], base["entropy"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["lse"] - sign * c / unit, base["lse"], rtol=0, atol=1e-12 * c / unit)
+
+
+@pytest.mark.parametrize("mag", [2.0 ** 43, 2.0 ** 50, 2.0 ** 60, 3.0e38])
+@pytest.mark.parametrize("n_tied", [2, 4, 7])
+def test_k_way_tie_at_large_magnitude(mag, n_tied):
+    # n_tied equal maxima far above every other logit: softmax puts 1/n_tied
+    # on each, so entropy = ln n_tied and a tied target has logprob -ln n_tied,
+    # whatever the magnitude (and for maxima at -mag above -2 mag as well)
+    V = 64
+    for top, rest in ((mag, 0.0), (-mag, -2.0 * mag)):
+        x = np.full((1, V), rest)
+        x[0, 5:5 + n_tied] = top
+        r = oracle.score_full(x, 1.0, [5 + n_tied - 1])
+        assert abs(r["entropy"][0] - math.log(n_tied)) < 1e-12, (top, r["entropy"][0])
+        assert abs(r["logprob"][0] + math.log(n_tied)) < 1e-12, (top, r["logprob"][0])
+        assert r["status"][0] == 0
+        r = oracle.score_full(x, 1.0, [0])  # a target far below the maxima
+        assert r["logprob"][0] < -1e10 and abs(r["entropy"][0] - math.log(n_tied)) < 1e-12
+
+
 def test_bounds():
     rng = np.random.default_rng(4)
     x = rng.normal(0, 5, size=(16, 300))

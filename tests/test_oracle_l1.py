@@ -67,3 +67,16 @@ def test_nonfinite_rows():
     b[1, :] = -np.inf
     r = oracle.l1_distance(a, b)
     assert np.isnan(r["l1"]).all() and np.isnan(r["accept_rate"]).all()
+
+
+def test_ties_at_large_magnitude():
+    # target mass split over 2 tied maxima, draft mass over 4 (a superset):
+    # |1/2 - 1/4| twice plus 1/4 twice = 1, at any magnitude of the logits
+    for mag in (2.0 ** 45, 2.0 ** 60, -(2.0 ** 60), 3.0e38):
+        a = np.full((1, 30), mag - abs(mag))
+        b = a.copy()
+        a[0, [2, 7]] = mag
+        b[0, [2, 7, 11, 12]] = mag
+        r = oracle.l1_distance(a, b)
+        assert abs(r["l1"][0] - 1.0) < 1e-12, mag
+        assert abs(r["accept_rate"][0] - 0.5) < 1e-12

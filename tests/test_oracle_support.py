@@ -128,3 +128,19 @@ def test_brute_force_python_floats():
         r = oracle.score_support(_fn(xs[None, :]), V, ids, 1.0, [y])
         assert abs(r["logprob"][0] - math.log(wts[y] / tot)) < 1e-12
         assert abs(r["entropy"][0] + sum(q / tot * math.log(q / tot) for q in wts.values())) < 1e-12
+
+
+def test_ties_at_large_magnitude():
+    # a support of n equal logits far from zero: renormalised uniform, so
+    # entropy ln n and logprob -ln n at any magnitude; one id far below the
+    # others adds nothing
+    for mag in (2.0 ** 45, 2.0 ** 60, -(2.0 ** 60), 3.0e38):
+        x = np.zeros((1, 50))
+        x[0, [3, 9, 20]] = mag
+        x[0, 30] = mag - abs(mag) * 0.5
+        ids = np.array([[20, 3, 30, 9, -1]])
+        r = oracle.score_support(lambda t, cols: x[t, cols], 50, ids, 1.0, [9])
+        assert abs(r["entropy"][0] - math.log(3)) < 1e-12, mag
+        assert abs(r["logprob"][0] + math.log(3)) < 1e-12, mag
+        r = oracle.score_support(lambda t, cols: x[t, cols], 50, ids[:, 1:2], 1.0, [3])
+        assert r["entropy"][0] == 0.0 and r["logprob"][0] == 0.0

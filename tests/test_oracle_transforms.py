@@ -224,3 +224,22 @@ def test_every_combination_small():
             continue
         L = int(r["support_len"][0])
         assert list(r["support_ids"][0][:L]) == _brute(list(x), tau, k, p, mp)
+
+
+@pytest.mark.parametrize("mag", [2.0 ** 45, 2.0 ** 60, -(2.0 ** 60), 3.0e38])
+def test_tied_maxima_at_large_magnitude(mag):
+    # four equal maxima far above the rest: each carries 1/4 of the mass, so
+    # top-p 0.6 keeps three of them (exclusive prefixes 0, 1/4, 1/2 < 0.6),
+    # the three lowest ids; the support entropy is ln 3 and a kept target
+    # scores -ln 3, at any magnitude
+    V = 40
+    x = np.full((1, V), mag - abs(mag))
+    x[0, [31, 4, 17, 8]] = mag
+    r = oracle.score_transforms(x, 1.0, 0, 0.6, 0.0, [8], cap=5)
+    assert r["support_len"][0] == 3 and list(r["support_ids"][0]) == [4, 8, 17, -1, -1]
+    assert r["threshold_logit"][0] == mag and r["threshold_ties"][0] == 3
+    assert abs(r["entropy"][0] - math.log(3)) < 1e-12
+    assert abs(r["logprob"][0] + math.log(3)) < 1e-12
+    assert not r["borderline_top_p"][0]
+    # the full-vocabulary LSE: four equal maxima
+    assert abs(r["full_lse"][0] - (mag + math.log(4))) <= 1e-12 * max(1.0, abs(mag))
