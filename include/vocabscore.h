@@ -16,9 +16,12 @@
  *
  * Conventions for every entry point:
  *   - Every array argument is a DEVICE pointer (hipMalloc'ed or a torch CUDA
- *     tensor), row-major, owned by the caller.  The library allocates nothing
- *     and keeps no mutable global state; concurrent calls on different
- *     streams with different buffers are safe.
+ *     tensor), row-major, owned by the caller.  The scoring entry points
+ *     allocate nothing and keep no per-call state outside the caller's
+ *     buffers; concurrent calls on different streams with different buffers
+ *     are safe.  The library's only process-wide state is a per-device cache
+ *     of the compute-unit count (atomic; every writer stores the same value)
+ *     and the diagnostic timer below (one caller at a time).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
  *     is enqueued on it; returning VS_OK means "enqueued", not "finished".
  *   - `workspace` is caller-owned device scratch of at least
@@ -32,6 +35,16 @@
  *     host never synchronises.
  *   - Pointers marked "nullable" may be NULL: that output is not written (and,
  *     where stated, not computed).
+ *   - Range: the full-vocabulary, recorded-support and L1 kernels work in fp32
+ *     base-2 units u = x * log2(e) / tau.  A row whose largest logit has
+ *     |x| * log2(e) / tau above the fp32 range (about 3.4e38) is BAD_INPUT,
+ *     and a log-probability below about -2.3e38 comes out as -inf.  With fp32
+ *     logits (or the projection's fp32 sums) each term's exponent carries the
+ *     fp32 rounding of u, about |u| * 2^-24: the results keep 1e-3 accuracy
+ *     for |x / tau| up to about 2^12.  bf16 logits are exact in u at any
+ *     magnitude.  The sampling transforms compute their masses in fp64 and
+ *     take every finite bf16 logit; their fp32 outputs are the fp64 results
+ *     rounded (a logprob beyond the fp32 range is -inf).
  */
 #ifndef VOCABSCORE_H
 #define VOCABSCORE_H
@@ -82,7 +95,9 @@ enum { VS_OP_SCORE_FULL = 0, VS_OP_SCORE_SUPPORT = 1, VS_OP_SCORE_TRANSFORMS = 2
  *                multiples of 8; hidden and weight 16-byte aligned.
  * temperature    [T] fp32 per-row tau (nullable: then temperature_scalar is
  *                used for every row).  tau <= 0 or non-finite => BAD_INPUT row.
- * Limits: 1 <= T < 2^31, 1 <= V < 2^31, H < 2^24.
+ * Limits: 1 <= T < 2^31, 1 <= V < 2^31, H < 2^24 (vs_score_support_ids with
+ * a hidden/weight source: H <= 16384, the hidden row it stages in LDS; larger
+ * H returns VS_E_UNSUPPORTED).
  */
 typedef struct vs_source {
   int32_t kind;
@@ -149,6 +164,7 @@ int vs_score_full(const vs_source* src, const int64_t* target_ids, int64_t vocab
  *   entropy, row_status  nullable; logprob required.
  * BAD_INPUT: tau invalid, an id >= V, a repeated id, or (on a scored row) a
  * target outside [0, V) or a support whose LSE is not finite.
+ * VS_E_UNSUPPORTED: a hidden/weight source with H > 16384.
  */
 int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64_t width,
                          int64_t ld_ids, const int64_t* target_ids,

@@ -44,5 +44,6 @@ from .scoring import (  # noqa: F401
     score_full,
     score_support,
     score_transforms,
+    score_prefix_support,
     l1_distance,
 )

@@ -275,6 +275,80 @@ def _rank_order(x: np.ndarray) -> np.ndarray:
     return np.lexsort((ids, -x))
 
 
+def _transform_outputs(R: int, cap: int) -> dict:
+    return {
+        "logprob": np.full(R, np.nan),
+        "entropy": np.full(R, np.nan),
+        "status": np.zeros(R, dtype=np.uint8),
+        "support_len": np.zeros(R, dtype=np.int32),
+        "threshold_logit": np.full(R, np.nan),
+        "threshold_ties": np.zeros(R, dtype=np.int32),
+        "support_ids": np.full((R, max(cap, 0)), -1, dtype=np.int64),
+    }
+
+
+def _prefix_outputs(out: dict, t: int, x_row: np.ndarray, order: np.ndarray, L: int, tau: float, y: int,
+                    cap: int) -> None:
+    """Descriptor, dense ids and scores of the support ``pi[0:L]`` of row t.
+
+    ``support_len = L``, ``threshold_logit = x_pi(L-1)``,
+    ``threshold_ties = #{j < L : x_pi(j) == x_pi(L-1)}``, dense ids
+    ``pi[0:min(L, cap)]`` padded with -1 (``ST_SUPPORT_TRUNCATED`` past the
+    capacity), and the logprob / entropy renormalised over the support as in
+    ``score_support`` (the support always holds the row maximum).
+    """
+    sup = order[:L]
+    out["support_len"][t] = L
+    thr = x_row[order[L - 1]]
+    out["threshold_logit"][t] = thr
+    out["threshold_ties"][t] = int(np.count_nonzero(x_row[sup] == thr))
+    if cap > 0:
+        n = min(L, cap)
+        out["support_ids"][t, :n] = sup[:n]
+        if L > cap:
+            out["status"][t] |= ST_SUPPORT_TRUNCATED
+    lse_s, lnp_s, h_s = _log_softmax(x_row[sup], tau)
+    if not np.isfinite(lse_s):
+        out["status"][t] = ST_BAD_INPUT
+        out["support_len"][t] = 0
+        out["threshold_logit"][t] = np.nan
+        out["threshold_ties"][t] = 0
+        out["support_ids"][t, :] = -1
+        if "full_lse" in out:
+            out["full_lse"][t] = np.nan
+        return
+    out["entropy"][t] = h_s
+    rank_y = int(np.nonzero(order == y)[0][0])
+    if rank_y < L:
+        out["logprob"][t] = lnp_s[rank_y]
+    else:
+        out["logprob"][t] = -np.inf
+        out["status"][t] |= ST_TARGET_OUTSIDE_SUPPORT
+
+
+def score_prefix_support(x, tau, support_len, targets, cap: int = 0) -> dict:
+    """Descriptor, dense ids and scores of a given support length per row.
+
+    The last steps of the transform program (support = the first
+    ``support_len[t]`` ranks of ``pi``, ids by logit descending, ties by
+    ascending id; xorl issue #71 section 3) for a cut chosen by the caller.
+    It serves rows whose top-p or min-p cut lies within the borderline band,
+    where several cuts are equally correct: given the cut the kernel chose,
+    everything else is fixed.  ``support_len[t]`` must lie in [1, V].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, V = x.shape
+    tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (R,))
+    targets = np.asarray(targets, dtype=np.int64)
+    out = _transform_outputs(R, cap)
+    for t in range(R):
+        L = int(support_len[t])
+        if not 1 <= L <= V:
+            raise ValueError(f"row {t}: support_len {L} outside [1, {V}]")
+        _prefix_outputs(out, t, x[t], _rank_order(x[t]), L, tau[t], int(targets[t]), cap)
+    return out
+
+
 def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict:
     """Scores over the top-k / top-p / min-p support of softmax(x / tau).
 
@@ -301,8 +375,10 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
     ``pi[0:min(L, cap)]`` padded with -1 (``ST_SUPPORT_TRUNCATED`` if
     ``cap > 0`` and ``L > cap``), and ``full_lse`` (the full-vocabulary LSE).
     Oracle-only extras: ``borderline_top_p`` (``top_p < 1`` and some
-    ``E_j``, j <= L_k, within 1e-6 of top_p) and ``borderline_min_p``
-    (``min_p > 0`` and some ``exp(z - z_max)`` within 1e-6 of min_p).
+    ``E_j``, j <= L_k, within 1e-6 of top_p), ``borderline_min_p``
+    (``min_p > 0`` and some ``exp(z - z_max)`` within 1e-6 of min_p), and the
+    band ``support_len_lo .. support_len_hi`` of the cut when top_p and min_p
+    move by up to 1e-6 (a single value on a row that is not borderline).
 
     ``ST_BAD_INPUT`` (NaN floats, support_len 0, ids -1): tau invalid,
     top_p NaN or <= 0, min_p NaN or > 1, target outside [0, V), or a row
@@ -315,18 +391,14 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
     top_p = np.broadcast_to(np.asarray(top_p, dtype=np.float64), (R,))
     min_p = np.broadcast_to(np.asarray(min_p, dtype=np.float64), (R,))
     targets = np.asarray(targets, dtype=np.int64)
-    out = {
-        "logprob": np.full(R, np.nan),
-        "entropy": np.full(R, np.nan),
-        "status": np.zeros(R, dtype=np.uint8),
-        "support_len": np.zeros(R, dtype=np.int32),
-        "threshold_logit": np.full(R, np.nan),
-        "threshold_ties": np.zeros(R, dtype=np.int32),
-        "support_ids": np.full((R, max(cap, 0)), -1, dtype=np.int64),
+    out = _transform_outputs(R, cap)
+    out.update({
         "full_lse": np.full(R, np.nan),
         "borderline_top_p": np.zeros(R, dtype=bool),
         "borderline_min_p": np.zeros(R, dtype=bool),
-    }
+        "support_len_lo": np.zeros(R, dtype=np.int32),
+        "support_len_hi": np.zeros(R, dtype=np.int32),
+    })
     for t in range(R):
         y = int(targets[t])
         p_top, p_min = top_p[t], min_p[t]
@@ -366,33 +438,22 @@ def score_transforms(x, tau, top_k, top_p, min_p, targets, cap: int = 0) -> dict
             out["borderline_min_p"][t] = bool(np.any(np.abs(rel - p_min) <= BORDERLINE))
 
         L = min(L_k, L_p, L_m)
-        sup = order[:L]
-        out["support_len"][t] = L
-        thr = x[t, order[L - 1]]
-        out["threshold_logit"][t] = thr
-        out["threshold_ties"][t] = int(np.count_nonzero(x[t, sup] == thr))
-        if cap > 0:
-            n = min(L, cap)
-            out["support_ids"][t, :n] = sup[:n]
-            if L > cap:
-                out["status"][t] |= ST_SUPPORT_TRUNCATED
+        _prefix_outputs(out, t, x[t], order, L, tau[t], y, cap)
 
-        lse_s, lnp_s, h_s = _log_softmax(xs[:L], tau[t])
-        if not np.isfinite(lse_s):
-            out["status"][t] = ST_BAD_INPUT
-            out["support_len"][t] = 0
-            out["threshold_logit"][t] = np.nan
-            out["threshold_ties"][t] = 0
-            out["support_ids"][t, :] = -1
-            out["full_lse"][t] = np.nan
+        # the cut band: L when top_p and min_p move by up to BORDERLINE (one
+        # value on every row that is not borderline)
+        lo_p = hi_p = L_k
+        if p_top < 1.0:
+            lo_p = int(np.count_nonzero(excl[:L_k] < p_top - BORDERLINE))
+            hi_p = int(np.count_nonzero(excl[:L_k] < p_top + BORDERLINE))
+        lo_m = hi_m = V
+        if p_min > 0.0:
+            lo_m = int(np.count_nonzero(rel >= p_min + BORDERLINE))
+            hi_m = int(np.count_nonzero(rel >= p_min - BORDERLINE))
+        if out["status"][t] & ST_BAD_INPUT:
             continue
-        out["entropy"][t] = h_s
-        rank_y = int(np.nonzero(order == y)[0][0])
-        if rank_y < L:
-            out["logprob"][t] = lnp_s[rank_y]
-        else:
-            out["logprob"][t] = -np.inf
-            out["status"][t] |= ST_TARGET_OUTSIDE_SUPPORT
+        out["support_len_lo"][t] = max(1, min(L_k, lo_p, lo_m))
+        out["support_len_hi"][t] = min(L_k, hi_p, hi_m)
     return out
 
 

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, bf16_tensor, dev, say, to_dev
+from tests.gpu_common import assert_close, bf16_tensor, dev, oracle_by_rows, say, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -29,12 +29,16 @@ def _cmp_full(got, ref, rows=None):
         assert_close(k, got[k].cpu().numpy(), ref[k], rows=rows)
 
 
-def test_logits_bf16_full_vocab_workload_rows(vsa):
-    say("logits_full: T=40 of the 512-row workload recipe, V=151936 bf16, per-row tau")
-    c = workloads.make(2, T=40)
+def test_logits_bf16_full_vocab_workload_all_rows(vsa):
+    say("logits_full: the full workload T=512 V=151936 bf16, per-row tau, every row vs the oracle")
+    c = workload(2)
     lg = bf16_tensor(c["logits"])
-    got = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=to_dev(c["temperature"]))
-    ref = oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16"), c["temperature"], c["targets"])
+    tau = to_dev(c["temperature"])
+    got = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=tau)
+    again = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=tau)
+    assert all(torch.equal(got[k], again[k]) for k in ("lse", "logprob", "entropy", "status"))
+    ref = oracle_by_rows(lambda r: oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
+                                                     c["temperature"][r], c["targets"][r]), c["T"])
     _cmp_full(got, ref)
 
 
@@ -82,19 +86,33 @@ def test_logits_load_ring_lengths(vsa, V):
 
 
 def test_vocab_chunk_and_determinism(vsa):
-    say("vocab_chunk variants + bitwise run-to-run equality")
-    c = workloads.make(2, T=16)
-    lg = bf16_tensor(c["logits"])
-    y = to_dev(c["targets"])
-    tau = to_dev(c["temperature"])
-    ref = oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16"), c["temperature"], c["targets"])
+    # vocab_chunk groups the fused sweep's 256-wide tile partials before the
+    # groups are merged: every grouping gives the same values up to rounding,
+    # and each one is bitwise reproducible
+    T, H, V = 96, 256, 40000
+    say(f"fused vocab_chunk 1 / 256 / 512 / 8192 / 65536 / V + bitwise run-to-run equality, T={T} H={H} V={V}")
+    rng = np.random.default_rng(77)
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.15).astype(np.float32))
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    hid, w, yd, td = bf16_tensor(hb), bf16_tensor(wb), to_dev(y), to_dev(tau)
+    ref = oracle.score_full(oracle.logits_from_hidden(hb, "bf16", wb), tau, y)
     outs = {}
-    for chunk in (1, 8192, 65536, 151936):
-        outs[chunk] = vsa.score_full(y, logits=lg, temperature=tau, vocab_chunk=chunk)
+    for chunk in (1, 256, 512, 8192, 65536, V):
+        outs[chunk] = vsa.score_full(yd, hidden=hid, weight=w, temperature=td, vocab_chunk=chunk)
         _cmp_full(outs[chunk], ref)
-    again = vsa.score_full(y, logits=lg, temperature=tau, vocab_chunk=8192)
-    for k in ("lse", "logprob", "entropy"):
-        assert torch.equal(again[k], outs[8192][k])
+        again = vsa.score_full(yd, hidden=hid, weight=w, temperature=td, vocab_chunk=chunk)
+        for k in ("lse", "logprob", "entropy"):
+            assert torch.equal(again[k], outs[chunk][k]), (chunk, k)
+    # the chunk rounds down to whole tiles: 1 and 256 are the same grouping
+    assert all(torch.equal(outs[1][k], outs[256][k]) for k in ("lse", "logprob", "entropy"))
+    # a logits source ignores vocab_chunk (one workgroup folds the whole row)
+    c = workloads.make(2, T=8)
+    lg = bf16_tensor(c["logits"])
+    a = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=to_dev(c["temperature"]), vocab_chunk=1)
+    b = vsa.score_full(to_dev(c["targets"]), logits=lg, temperature=to_dev(c["temperature"]), vocab_chunk=151936)
+    assert all(torch.equal(a[k], b[k]) for k in ("lse", "logprob", "entropy"))
 
 
 def test_edge_rows(vsa):
@@ -181,9 +199,9 @@ def test_fused_strided_weight(vsa):
     _cmp_full(got, oracle.score_full(x, 1.0, y))
 
 
-def test_fused_full_size_sampled_rows(vsa):
-    say("fused: full LM-head workload T=4096 H=4096 V=151936; oracle on sampled rows")
-    c = workloads.make(4)
+def test_fused_full_size_rows_in_every_tile(vsa):
+    say("fused: full LM-head workload T=4096 H=4096 V=151936; 256 rows (16 in each token tile) vs the oracle")
+    c = workload(4)
     hid = bf16_tensor(c["hidden"])
     w = bf16_tensor(c["weight"])
     y = to_dev(c["targets"])
@@ -197,7 +215,44 @@ def test_fused_full_size_sampled_rows(vsa):
     assert (st == 0).all()
     assert np.isfinite(ent).all() and (ent >= 0).all() and (ent <= math.log(151936) + 1e-3).all()
     assert (lp <= 1e-6).all()
-    rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3333, 4094, 4095])
+    # 16 rows of each 256-row token tile, first and last row of every tile included;
+    # every row's 594 vocabulary tiles (the last one ragged) are in its sums
+    rows = (np.arange(16)[:, None] * 256 + np.arange(0, 256, 17)[None, :]).ravel()
     x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
     ref = oracle.score_full(x, 1.0, c["targets"][rows])
     _cmp_full(got, ref, rows=rows)
+    # another vocab_chunk groups the same tile partials differently: same values up to rounding
+    for chunk in (256, 65536, 151936):
+        other = vsa.score_full(y, hidden=hid, weight=w, vocab_chunk=chunk)
+        _cmp_full(other, ref, rows=rows)
+
+
+def test_fp32_range_of_the_tempered_logits(vsa):
+    # The kernels work in fp32 base-2 units u = x * log2(e) / tau.  A row whose
+    # largest logit has |x| * log2(e) / tau beyond the fp32 range is
+    # BAD_INPUT (documented limit); below it, huge logits score like any
+    # others, and a logit that falls below -FLT_MAX in those units has
+    # probability 0 (its true weight underflows anyway).
+    say("fp32 range: rows at 3e38 with tau 0.5 / 1 / 2, all at -3e38, one id at -3e38")
+    V = 5000
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, V)).astype(np.float32)
+    x[0, [10, 20]] = 3.0e38   # tau 0.5: u overflows -> BAD
+    x[1, [10, 20]] = 3.0e38   # tau 1: 4.3e38 overflows -> BAD
+    x[2, [10, 20]] = 3.0e38   # tau 2: 2.2e38 fits: two tied maxima
+    x[3, :] = -3.0e38         # tau 0.5: every u is -inf -> BAD
+    x[4, 30] = -3.0e38        # tau 0.5: that id has probability 0
+    x[5, 40] = 1.0e38         # tau 1: one maximum far above the rest
+    tau = np.array([0.5, 1.0, 2.0, 0.5, 0.5, 1.0], np.float32)
+    y = np.array([10, 10, 20, 0, 30, 40], np.int64)
+    bits = workloads.to_bf16_bits(x)
+    got = vsa.score_full(to_dev(y), logits=bf16_tensor(bits), temperature=to_dev(tau))
+    st = got["status"].cpu().numpy()
+    assert list(st) == [4, 4, 0, 4, 0, 0], st
+    ok = np.array([2, 4, 5])
+    ref = oracle.score_full(oracle.logits_from_logits(bits[ok], "bf16"), tau[ok], y[ok])
+    with np.errstate(over="ignore"):  # fp32 outputs: the oracle's values rounded to fp32
+        for k in ("lse", "logprob", "entropy"):
+            assert_close(k, got[k].cpu().numpy()[ok], ref[k].astype(np.float32).astype(np.float64))
+    assert abs(float(got["entropy"][2]) - math.log(2)) < 1e-6 and abs(float(got["logprob"][2]) + math.log(2)) < 1e-6
+    assert float(got["logprob"][4]) == -math.inf and float(got["logprob"][5]) == 0.0

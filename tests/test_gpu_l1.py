@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, bf16_tensor, say, to_dev
+from tests.gpu_common import assert_close, bf16_tensor, oracle_by_rows, say, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -67,15 +67,16 @@ def test_ragged_and_bounds(vsa, dtype):
     assert torch.allclose(sym["l1"][fin], got["l1"][fin], atol=2e-6)
 
 
-def test_full_size_sampled(vsa):
-    say("l1: full 2048-row workload; oracle on sampled rows")
-    c = workloads.make(5)
+def test_full_size_all_rows(vsa):
+    say("l1: full workload T=2048 V=151936 bf16, every row vs the oracle; determinism")
+    c = workload(5)
     got = vsa.l1_distance(bf16_tensor(c["logits"]), bf16_tensor(c["draft"]))
-    rows = np.array([0, 1, 35, 1024, 2047])
-    ref = oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16", rows=rows),
-                             oracle.logits_from_logits(c["draft"], "bf16", rows=rows))
-    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"], rows=rows)
-    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"], rows=rows)
+    again = vsa.l1_distance(bf16_tensor(c["logits"]), bf16_tensor(c["draft"]))
+    assert torch.equal(got["l1"], again["l1"]) and torch.equal(got["accept_rate"], again["accept_rate"])
+    ref = oracle_by_rows(lambda r: oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
+                                                      oracle.logits_from_logits(c["draft"], "bf16", rows=r)), c["T"])
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"])
+    assert_close("accept_rate", got["accept_rate"].cpu().numpy(), ref["accept_rate"])
 
 
 def _l1_case(vsa, a, b, ld_pad=0):

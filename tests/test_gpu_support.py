@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, bf16_tensor, say, to_dev
+from tests.gpu_common import assert_close, bf16_tensor, oracle_by_rows, say, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -147,9 +147,10 @@ def test_replay_workload_reduced(vsa):
     _cmp(got, ref)
 
 
-def test_replay_workload_full_size_sampled(vsa):
-    say("support replay full size T=2048; oracle on sampled rows; determinism")
-    c = workloads.make(3)
+def test_replay_workload_full_size_all_rows(vsa):
+    say("support replay full size T=2048 H=7168 V=129280 width 64: every row vs the oracle; determinism")
+    c = workload(3)
+    T = c["T"]
     hid, w = bf16_tensor(c["hidden"]), bf16_tensor(c["weight"])
     y, ids = to_dev(c["targets"]), to_dev(c["support_ids"])
     got = vsa.score_support_ids(y, ids, hidden=hid, weight=w)
@@ -158,13 +159,15 @@ def test_replay_workload_full_size_sampled(vsa):
     widths = (c["support_ids"] >= 0).sum(1)
     st = got["status"].cpu().numpy()
     assert np.array_equal(st, np.where(widths == 0, 1, 0).astype(np.uint8))
-    rows = np.concatenate([np.nonzero(widths == 1)[0][:3], np.nonzero(widths == 0)[0][:2],
-                           np.array([0, 777, 2047])])
 
-    def fn(t, cols):
-        return oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=[rows[t]], cols=cols)[0]
-    ref = oracle.score_support(fn, c["V"], c["support_ids"][rows], 1.0, c["targets"][rows])
-    _cmp(got, ref, rows=rows)
+    def ref_rows(rows):
+        def fn(t, cols):
+            return oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=[rows[t]], cols=cols)[0]
+        return oracle.score_support(fn, c["V"], c["support_ids"][rows], 1.0, c["targets"][rows])
+    _cmp(got, oracle_by_rows(ref_rows, T))
+    single = np.nonzero(widths == 1)[0]
+    assert single.size and (got["logprob"].cpu().numpy()[single] == 0).all()
+    assert (got["entropy"].cpu().numpy()[single] == 0).all()
 
 
 def test_fused_max_width_duplicates_far_apart(vsa):

@@ -1,10 +1,9 @@
 """GPU parity sweep: seeded random shapes, dtypes, strides, value mixes and
 parameters for every entry point, against the fp64 oracle.
 
-Each case prints its seed and shape before running.  Logit magnitudes stay
-where fp32 accumulation meets the float tolerance (|x / tau| up to a few
-hundred); the sampling transforms, whose masses are fp64, also get wide
-exponent spreads.
+Each case prints its seed and shape before running.  Magnitudes: see
+``_values`` (every finite bf16 value for the transforms, bf16 up to 2^123 for
+the fp32 kernels, |x| < 2^7 for fp32 logits).
 """
 
 import numpy as np
@@ -27,8 +26,18 @@ def vsa():
     return m
 
 
-def _values(rng, kind, shape, wide=False):
-    """fp32 logits of one of several mixes."""
+def _values(rng, kind, shape, wide=False, dtype="bf16"):
+    """fp32 logits of one of several mixes.
+
+    Magnitudes: the sampling transforms (fp64 masses, ``wide``) take every
+    finite value; the fp32 kernels take bf16 logits up to 2^123, where every
+    difference |x_u - x_v| * log2(e) / tau of two logits of a row stays inside
+    the fp32 range for every tau >= 0.3 used here; fp32 logits stay within |x| < 2^7, the range where the fp32
+    rounding of x * log2(e) / tau (about |x / tau| * 2^-24 per term) meets the
+    float tolerance.
+    """
+    if kind == "huge" and dtype != "bf16":
+        kind = "ties"
     if kind == "normal":
         x = rng.standard_normal(shape) * rng.choice([0.05, 1.0, 4.0])
     elif kind == "ties":
@@ -42,16 +51,19 @@ def _values(rng, kind, shape, wide=False):
         x[rng.random(shape) < 0.3] = -np.inf
     elif kind == "zeros":
         x = rng.choice([-0.0, 0.0, 1.0, -1.0], size=shape, p=[0.3, 0.3, 0.2, 0.2])
-    elif kind == "spread":  # random exponents: tiny to large magnitudes in one row
-        top = 15 if wide else 7
-        e = rng.integers(-40, top, size=shape).astype(np.float64)
-        x = np.sign(rng.standard_normal(shape)) * rng.uniform(1.0, 2.0, shape) * np.exp2(e)
+    elif kind == "spread":  # random exponents: subnormal to large magnitudes in one row
+        lo, hi = (-133, 127) if wide else ((-133, 123) if dtype == "bf16" else (-40, 7))
+        e = rng.integers(lo, hi, size=shape).astype(np.float64)
+        x = np.sign(rng.standard_normal(shape)) * rng.uniform(1.0, 1.99, shape) * np.exp2(e)
+    elif kind == "huge":  # small integers times 2^E, E up to 121: tied maxima far from zero
+        E = float(rng.integers(20, 122 if not wide else 125))
+        x = rng.integers(-3, 4, size=shape) * np.exp2(E)
     else:
         raise ValueError(kind)
     return np.asarray(x, dtype=np.float32)
 
 
-KINDS = ["normal", "ties", "peaked", "neg_inf", "zeros", "spread"]
+KINDS = ["normal", "ties", "peaked", "neg_inf", "zeros", "spread", "huge"]
 
 
 @pytest.mark.parametrize("seed", range(32))
@@ -63,7 +75,7 @@ def test_sweep_logits_full(vsa, seed):
     pad = int(rng.choice([0, 1, 8]))
     kind = str(rng.choice(KINDS))
     say(f"sweep logits_full seed={seed}: T={T} V={V} {dtype} ld_pad={pad} values={kind}")
-    x = _values(rng, kind, (T, V + pad))
+    x = _values(rng, kind, (T, V + pad), dtype=dtype)
     tau = rng.uniform(0.3, 2.0, T).astype(np.float32)
     y = rng.integers(0, V, T).astype(np.int64)
     y[0] = V - 1
@@ -133,10 +145,10 @@ def test_sweep_l1(vsa, seed):
     T = int(rng.integers(1, 8))
     V = int(rng.choice([1, 2, 9, 1000, 65537, 151936]))
     dtype = str(rng.choice(["bf16", "f32"]))
-    kind = str(rng.choice(["normal", "ties", "peaked", "zeros", "spread"]))
+    kind = str(rng.choice(["normal", "ties", "peaked", "zeros", "spread", "huge"]))
     noise = float(rng.choice([0.0, 0.01, 1.0, 10.0]))
     say(f"sweep l1 seed={seed}: T={T} V={V} {dtype} values={kind} noise={noise}")
-    a = _values(rng, kind, (T, V))
+    a = _values(rng, kind, (T, V), dtype=dtype)
     b = (a + rng.standard_normal((T, V)) * noise).astype(np.float32)
     b[0] = a[0]  # one identical row: exactly 0
     if dtype == "bf16":
@@ -162,7 +174,7 @@ def test_sweep_support_logits(vsa, seed):
     dtype = str(rng.choice(["bf16", "f32"]))
     kind = str(rng.choice(KINDS))
     say(f"sweep support seed={seed}: T={T} V={V} width={W} {dtype} values={kind}")
-    x = _values(rng, kind, (T, V))
+    x = _values(rng, kind, (T, V), dtype=dtype)
     if dtype == "bf16":
         bits = workloads.to_bf16_bits(x)
         lg = bf16_tensor(bits)

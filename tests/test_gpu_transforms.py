@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, bf16_tensor, say, to_dev
+from tests.gpu_common import assert_close, bf16_tensor, oracle_by_rows, say, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,12 @@ def _run(vsa, bits, tau, k, p, mp, y, cap, ld_pad=0):
                                 temperature=to_dev(np.asarray(tau, np.float32)), cap=cap)
 
 
-def _compare(got, ref, cap, label):
+def _compare(got, ref, cap, label, x64=None, tau=None, y=None):
+    """Bit-exact descriptor, ids and status on every row that is not
+    borderline; float scores within the tolerance.  On a borderline row the
+    kernel's cut must lie in the oracle's band (top_p / min_p moved by up to
+    1e-6); given x64 / tau / y, that row's descriptor, ids, status and scores
+    are then checked against the oracle's outputs for the kernel's own cut."""
     T = len(ref["status"])
     border = ref["borderline_top_p"] | ref["borderline_min_p"]
     exact = ~border
@@ -54,12 +59,34 @@ def _compare(got, ref, cap, label):
         bad = np.nonzero(exact & ~(g["support_ids"] == ref["support_ids"]).all(1))[0]
         assert bad.size == 0, f"{label}: support ids differ at rows {bad[:10]}"
     rows = np.nonzero(exact)[0]
-    assert_close(f"{label} logprob", g["logprob"], ref["logprob"][rows], rows=rows)
-    assert_close(f"{label} entropy", g["entropy"], ref["entropy"][rows], rows=rows)
-    assert_close(f"{label} full_lse", g["full_lse"], ref["full_lse"])
-    n_b = int(border.sum())
+    # the outputs are fp32: the expected value is the oracle's rounded to fp32
+    # (a logprob beyond the fp32 range is -inf there too)
+    f32 = lambda a: np.asarray(a, np.float64).astype(np.float32).astype(np.float64)  # noqa: E731
+    with np.errstate(over="ignore"):
+        assert_close(f"{label} logprob", g["logprob"], f32(ref["logprob"][rows]), rows=rows)
+        assert_close(f"{label} entropy", g["entropy"], f32(ref["entropy"][rows]), rows=rows)
+        assert_close(f"{label} full_lse", g["full_lse"], f32(ref["full_lse"]))
+    brow = np.nonzero(border)[0]
+    n_b = int(brow.size)
+    if n_b:
+        L = g["support_len"][brow]
+        lo, hi = ref["support_len_lo"][brow], ref["support_len_hi"][brow]
+        out = np.nonzero((L < lo) | (L > hi))[0]
+        assert out.size == 0, f"{label}: borderline rows {brow[out][:10]} cut {L[out][:5]} outside [{lo[out][:5]}, {hi[out][:5]}]"
+        if x64 is not None:
+            tau_b = np.broadcast_to(np.asarray(tau, np.float64), (T,))[brow]
+            forced = oracle.score_prefix_support(x64[brow], tau_b, L, np.asarray(y)[brow], cap=cap)
+            for name in ("threshold_ties", "status"):
+                assert np.array_equal(g[name][brow], forced[name]), f"{label}: borderline {name}"
+            assert np.array_equal(g["threshold_logit"][brow].astype(np.float64), forced["threshold_logit"])
+            if cap:
+                assert np.array_equal(g["support_ids"][brow], forced["support_ids"]), f"{label}: borderline ids"
+            with np.errstate(over="ignore"):
+                assert_close(f"{label} borderline logprob", g["logprob"][brow], f32(forced["logprob"]))
+                assert_close(f"{label} borderline entropy", g["entropy"][brow], f32(forced["entropy"]))
     mism = int(((g["support_len"] != ref["support_len"]) & border).sum())
-    say(f"  {label}: {T} rows, {n_b} borderline ({mism} of them with a different support_len)")
+    say(f"  {label}: {T} rows, {n_b} borderline ({mism} of them cut on the other side of the band, "
+        f"{'all checked against that cut' if x64 is not None else 'cut inside the band'})")
     return n_b
 
 
@@ -85,7 +112,7 @@ def test_workload_rows_full_vocab(vsa):
     got = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, 64)
     ref = oracle.score_transforms(x64, c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, cap=64)
     assert (ref["status"] & oracle.ST_TARGET_OUTSIDE_SUPPORT == 0).all()
-    n_b = _compare(got, ref, 64, "workload")
+    n_b = _compare(got, ref, 64, "workload", x64, c["temperature"], y)
     assert n_b <= 8
     again = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], y, 64)
     for k in ("logprob", "entropy", "support_len", "support_ids", "full_lse"):
@@ -113,7 +140,7 @@ def test_small_and_medium_rows_with_ties(vsa, V):
     for cap in (0, 3, 64):
         got = _run(vsa, bits, tau, k, p, mp, y, cap)
         ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
-        _compare(got, ref, cap, f"V={V} cap={cap}")
+        _compare(got, ref, cap, f"V={V} cap={cap}", x64, tau, y)
 
 
 def test_unaligned_rows_and_neg_inf(vsa):
@@ -131,7 +158,7 @@ def test_unaligned_rows_and_neg_inf(vsa):
     x64 = oracle.logits_from_logits(bits, "bf16")
     got = _run(vsa, bits, tau, k, p, mp, y, 16, ld_pad=1)
     ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=16)
-    _compare(got, ref, 16, "unaligned")
+    _compare(got, ref, 16, "unaligned", x64, tau, y)
 
 
 def test_bad_rows(vsa):
@@ -187,7 +214,7 @@ def test_streaming_rows_special_values(vsa):
     got = _run(vsa, bits, tau, k, p, mp, y, 64)
     ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=64)
     assert list(ref["status"][:3] & oracle.ST_BAD_INPUT) == [oracle.ST_BAD_INPUT] * 3
-    _compare(got, ref, 64, "streaming special values")
+    _compare(got, ref, 64, "streaming special values", x64, tau, y)
 
 
 def test_streamed_rows_cap_paths(vsa):
@@ -211,36 +238,42 @@ def test_streamed_rows_cap_paths(vsa):
     for cap in (2048, 2049, 4096):
         got = _run(vsa, bits, tau, k, p, mp, y, cap)
         ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
-        _compare(got, ref, cap, f"V={V} cap={cap}")
+        _compare(got, ref, cap, f"V={V} cap={cap}", x64, tau, y)
 
 
 def test_streamed_rows_spread_over_many_segments(vsa):
     """Long rows whose keys spread over most of the 1024 key segments (random
-    finite bf16 patterns): more non-empty segments than the finish kernel keeps
-    in LDS, so its sums and key queries also read segments from the record;
-    and segments whose weights cannot follow one geometric recurrence."""
-    say("transforms: V=100000 rows of random bf16 patterns, |x| < 2^20 (~590 non-empty segments), caps 0 / 64 / 2048")
-    T, V = 6, 100000
+    finite bf16 patterns over the whole finite range, subnormals to 2^127):
+    more non-empty segments than the finish kernel keeps in LDS, so its sums
+    and key queries also read segments from the record; segments whose
+    weights cannot follow one geometric recurrence; and ties at the largest
+    magnitudes.  The masses are fp64, so no tempered logit overflows."""
+    say("transforms: V=100000 rows of random finite bf16 patterns (|x| < 2^128), caps 0 / 64 / 2048")
+    T, V = 8, 100000
     rng = np.random.default_rng(12)
     sign = rng.integers(0, 2, size=(T, V)) << 15
-    # biased exponents 0 .. 146: zero, subnormals, up to 2^19.  (Larger logits
-    # leave fp64 too few fraction bits for the oracle's z - LSE; here the top
-    # segments' key spacing / tau is still large enough that weights inside
-    # one segment span underflow to overflow.)
-    expo = rng.integers(0, 147, size=(T, V)) << 7
+    expo = rng.integers(0, 255, size=(T, V)) << 7  # biased exponents 0 .. 254: every finite bf16
     mant = rng.integers(0, 128, size=(T, V))
     bits = (sign | expo | mant).astype(np.uint16)
     bits[1] = np.where(np.arange(V) % 3 == 0, bits[1], bits[1] & 0x80FF)  # a third spread, the rest tiny
-    k = np.array([0, 0, 40, 1000, 0, 5], np.int32)
-    p = np.array([1.0, 0.9, 1.0, 0.5, 1.0, 1.0], np.float32)
-    mp = np.array([0.0, 0.0, 0.0, 0.0, 1e-30, 0.0], np.float32)
-    tau = np.array([1.0, 1.0, 0.5, 2.0, 1.0, 1e-3], np.float32)
+    bits[6, rng.choice(V, 5, replace=False)] = 0x7F7F  # more tied maxima at the largest finite bf16
+    bits[7, rng.choice(V, 3, replace=False)] = 0x5D80  # tied maxima at 2^60 ...
+    bits[7] = np.where(bits[7] == 0x5D80, bits[7], bits[7] & 0x5CFF)  # ... the rest below 2^58
+    k = np.array([0, 0, 40, 1000, 0, 5, 0, 0], np.int32)
+    p = np.array([1.0, 0.9, 1.0, 0.5, 1.0, 1.0, 0.6, 0.9], np.float32)
+    mp = np.array([0.0, 0.0, 0.0, 0.0, 1e-30, 0.0, 0.0, 0.0], np.float32)
+    tau = np.array([1.0, 1.0, 0.5, 2.0, 1.0, 1e-3, 1.0, 1.0], np.float32)
     x64 = oracle.logits_from_logits(bits, "bf16")
     y = rng.integers(0, V, T)
+    y[6] = int(np.nonzero(bits[6] == 0x7F7F)[0][1])
+    y[7] = int(np.nonzero(bits[7] == 0x5D80)[0][2])
     for cap in (0, 64, 2048):
         got = _run(vsa, bits, tau, k, p, mp, y, cap)
         ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
-        _compare(got, ref, cap, f"spread V={V} cap={cap}")
+        for t in (6, 7):  # top-p keeps some of the tied maxima: a uniform support
+            assert ref["support_len"][t] >= 2 and not ref["borderline_top_p"][t]
+            assert abs(ref["entropy"][t] - np.log(ref["support_len"][t])) < 1e-12
+        _compare(got, ref, cap, f"spread V={V} cap={cap}", x64, tau, y)
 
 
 def test_identity_and_singleton(vsa):
@@ -273,22 +306,36 @@ def test_all_equal_long_row_uses_32bit_counts(vsa):
     tau = np.ones(4, np.float32)
     y = np.array([3, 75969, 151935, 40000], np.int64)
     got = _run(vsa, bits, tau, k, p, mp, y, 64)
-    ref = oracle.score_transforms(oracle.logits_from_logits(bits, "bf16"), tau, k, p, mp, y, cap=64)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=64)
     assert list(ref["support_len"][:3]) == [5, 75970, V]  # row 3 sits exactly on a cut (borderline)
-    _compare(got, ref, 64, "all-equal")
+    _compare(got, ref, 64, "all-equal", x64, tau, y)
     assert list(got["support_ids"][0, :6].cpu().numpy()) == [0, 1, 2, 3, 4, -1]
     assert list(got["support_ids"][1, :64].cpu().numpy()) == list(range(64))
 
 
-def test_full_size_sampled(vsa):
-    say("transforms: full 2048-row workload; oracle on sampled rows; determinism")
-    c = workloads.make(5)
-    got = _run(vsa, c["logits"], c["temperature"], c["top_k"], c["top_p"], c["min_p"], c["targets"], 64)
-    rows = np.array([0, 1, 2, 3, 17, 35, 36, 1000, 1500, 2047])
-    x64 = oracle.logits_from_logits(c["logits"], "bf16", rows=rows)
-    ref = oracle.score_transforms(x64, c["temperature"][rows], c["top_k"][rows], c["top_p"][rows], c["min_p"][rows],
-                                  c["targets"][rows], cap=64)
-    sub = {k: (v[rows] if v is not None else None) for k, v in got.items()}
-    _compare(sub, ref, 64, "full-size rows")
-    st = got["status"].cpu().numpy()
-    assert ((st & 0x04) == 0).all() and ((st & 0x02) == 0).all()
+class _WidenedRows:
+    """x64[rows] of a bf16 logits array, widened only for the rows asked for."""
+
+    def __init__(self, bits):
+        self.bits = bits
+
+    def __getitem__(self, rows):
+        return oracle.logits_from_logits(self.bits, "bf16", rows=np.atleast_1d(rows))
+
+
+def test_full_size_all_rows(vsa):
+    say("transforms: full workload T=2048 V=151936 cap 64, every row vs the oracle, in-support sampled targets")
+    c = workload(5)
+    T = c["T"]
+    k, p, mp, tau = c["top_k"], c["top_p"], c["min_p"], c["temperature"]
+    xr = _WidenedRows(c["logits"])
+    y = oracle_by_rows(lambda r: {"y": _support_sample(xr[r], tau[r], k[r], p[r], mp[r], c["u"][r])}, T)["y"]
+    got = _run(vsa, c["logits"], tau, k, p, mp, y, 64)
+    again = _run(vsa, c["logits"], tau, k, p, mp, y, 64)
+    for key in got:
+        assert torch.equal(got[key], again[key]), key
+    ref = oracle_by_rows(lambda r: oracle.score_transforms(xr[r], tau[r], k[r], p[r], mp[r], y[r], cap=64), T)
+    assert (ref["status"] & (oracle.ST_TARGET_OUTSIDE_SUPPORT | oracle.ST_BAD_INPUT) == 0).all()
+    n_b = _compare(got, ref, 64, "full size", xr, tau, y)
+    assert n_b < T // 10

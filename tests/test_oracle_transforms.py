@@ -243,3 +243,33 @@ def test_tied_maxima_at_large_magnitude(mag):
     assert not r["borderline_top_p"][0]
     # the full-vocabulary LSE: four equal maxima
     assert abs(r["full_lse"][0] - (mag + math.log(4))) <= 1e-12 * max(1.0, abs(mag))
+
+
+def test_cut_band_and_forced_length():
+    # a row whose top-p cut lies exactly on a prefix mass: masses 1/2, 1/4,
+    # 1/8, 1/8 (logits ln 4, ln 2, 0, 0); with top_p = 0.75 the exclusive
+    # prefix before rank 2 is 0.75 up to rounding, so whether rank 2 is kept
+    # (L = 3) or dropped (L = 2) turns on the last bit; the band is [2, 3]
+    x = np.array([[0.0, math.log(4.0), 0.0, math.log(2.0)]])
+    r = oracle.score_transforms(x, 1.0, 0, 0.75, 0.0, [1], cap=4)
+    assert r["borderline_top_p"][0]
+    assert r["support_len"][0] in (2, 3) and r["support_len_lo"][0] == 2 and r["support_len_hi"][0] == 3
+    # forcing each cut of the band reproduces the program's outputs for that cut
+    for L, ids in ((2, [1, 3, -1, -1]), (3, [1, 3, 0, -1]), (4, [1, 3, 0, 2])):
+        f = oracle.score_prefix_support(x, 1.0, [L], [1], cap=4)
+        assert f["support_len"][0] == L and list(f["support_ids"][0]) == ids
+        w = np.array([4.0, 2.0, 1.0, 1.0])[:L]
+        assert abs(f["logprob"][0] - math.log(4.0 / w.sum())) < 1e-12
+        q = w / w.sum()
+        assert abs(f["entropy"][0] + np.sum(q * np.log(q))) < 1e-12
+    assert oracle.score_prefix_support(x, 1.0, [3], [1], cap=4)["threshold_ties"][0] == 1
+    g = oracle.score_prefix_support(x, 1.0, r["support_len"], [1], cap=4)
+    for k in ("support_len", "threshold_logit", "threshold_ties", "support_ids", "logprob", "entropy", "status"):
+        np.testing.assert_array_equal(g[k], r[k])
+    # a row that is not borderline has a one-value band
+    r = oracle.score_transforms(x, 1.0, 0, 0.6, 0.0, [1], cap=4)
+    assert not r["borderline_top_p"][0] and r["support_len_lo"][0] == r["support_len_hi"][0] == r["support_len"][0]
+    # min-p band: weights 1, 1/2, 1/4, 1/4 relative to the max; min_p = 0.25 sits on the last two
+    r = oracle.score_transforms(x, 1.0, 0, 1.0, 0.25, [1], cap=4)
+    assert r["borderline_min_p"][0] and r["support_len"][0] == 4
+    assert r["support_len_lo"][0] == 2 and r["support_len_hi"][0] == 4
