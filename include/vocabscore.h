@@ -41,8 +41,10 @@
  *     and a log-probability below about -2.3e38 comes out as -inf.  With fp32
  *     logits (or the projection's fp32 sums) each term's exponent carries the
  *     fp32 rounding of u, about |u| * 2^-24: the results keep 1e-3 accuracy
- *     for |x / tau| up to about 2^12.  bf16 logits are exact in u at any
- *     magnitude.  The sampling transforms compute their masses in fp64 and
+ *     for |x / tau| up to about 2^12.  For bf16 logits the scale log2(e)/tau
+ *     is rounded to 16 significant bits (a 2^-17 relative change of 1/tau),
+ *     which makes every product x * scale exact, so that accuracy holds at
+ *     any magnitude.  The sampling transforms compute their masses in fp64 and
  *     take every finite bf16 logit; their fp32 outputs are the fp64 results
  *     rounded (a logprob beyond the fp32 range is -inf).
  */

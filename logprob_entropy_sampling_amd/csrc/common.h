@@ -17,6 +17,9 @@
 namespace vs {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// log2(e) rounded to 16 significant bits (see scale16): the base-2 scale of
+// the bf16 inputs of the softmax L1, which takes no temperature.
+constexpr float kLog2eBf16 = 1.44268798828125f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 // Exponent floor: 2^-256 is 0 in fp32, and keeps e * d finite when d = -inf.
@@ -33,6 +36,18 @@ struct Part {
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The base-2 scale c = log2(e) / tau rounded to 16 significant bits (nearest,
+// ties away from zero).  Its product with a bf16 value (8 significant bits)
+// is exact in fp32, so for bf16 logits the fused form fma(x, c, -m), with m
+// the product of the running maximum and c, is exactly 0 at the maximum and
+// one rounding of the exact difference elsewhere - at any magnitude.  (With
+// c unrounded, fma(x_max, c, -round(x_max * c)) is the product's rounding
+// error, about |u| * 2^-24, which at |u| near 2^127 is itself huge.)  The
+// rounding moves 1/tau by at most 2^-17 relative.
+__device__ __forceinline__ float scale16(float c) {
+  return __uint_as_float((__float_as_uint(c) + 0x80u) & 0xFFFFFF00u);
+}
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
 // Streaming 16-byte loads (non-temporal): for data read once, or whose
@@ -81,7 +96,9 @@ __device__ __forceinline__ Part merge(Part p, Part q) {
   Part r;
   r.m = p.m;
   r.s = p.s + q.s * f;
-  r.a = p.a + f * __builtin_fmaf(q.s, d, q.a);
+  // f = 0 (q's maximum far below p's): q adds nothing; q.s * d may
+  // overflow to -inf there, and 0 * -inf would be NaN
+  r.a = f == 0.0f ? p.a : p.a + f * __builtin_fmaf(q.s, d, q.a);
   return r;
 }
 

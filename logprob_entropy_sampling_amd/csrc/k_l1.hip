@@ -12,6 +12,8 @@
 // LDS, so HBM is read 1.25 times instead of twice (described below).
 // No probability vector is stored anywhere.  Identical rows give exactly 0:
 // both sides run the same instructions on the same bits.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "../../include/vocabscore.h"
@@ -29,7 +31,7 @@ struct Pair {
 // m is kept in raw units (the max is taken on the logits themselves); each
 // term is one FMA and one v_exp_f32.  No floor is needed: there is no
 // e * d term, exp2(-inf) = 0, and a NaN poisons s as it should.
-__device__ __forceinline__ void online(float& m, float& s, const float* v, int n) {
+__device__ __forceinline__ void online(float& m, float& s, const float* v, int n, float l2e) {
   float bm = v[0];
   for (int i = 1; i < n; ++i) bm = fmaxf(bm, v[i]);
   const float nm = fmaxf(m, bm);
@@ -38,9 +40,9 @@ __device__ __forceinline__ void online(float& m, float& s, const float* v, int n
       if (v[i] != v[i]) s = __builtin_nanf("");
     return;
   }
-  const float c = nm * kLog2e;
-  s *= exp2_hw(m * kLog2e - c);  // exactly 1 when the max did not move; 0 from -inf
-  for (int i = 0; i < n; ++i) s += exp2_hw(__builtin_fmaf(v[i], kLog2e, -c));
+  const float c = nm * l2e;
+  s *= exp2_hw(m * l2e - c);  // exactly 1 when the max did not move; 0 from -inf
+  for (int i = 0; i < n; ++i) s += exp2_hw(__builtin_fmaf(v[i], l2e, -c));
   m = nm;
 }
 
@@ -75,21 +77,50 @@ __device__ __forceinline__ float load_one(const void* row, int64_t i) {
   return DT == VS_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(row)[i]) : static_cast<const float*>(row)[i];
 }
 
-// |p - q| of one element pair, the normalisers folded into the exponents
-__device__ __forceinline__ float absdiff(float a, float b, float lx, float ly) {
-  return fabsf(exp2_hw(__builtin_fmaf(a, kLog2e, -lx)) - exp2_hw(__builtin_fmaf(b, kLog2e, -ly)));
+// A row's base-2 normaliser: p_v = 2^(u_v - m - l2s), l2s = log2 of the sum
+// against the maximum m.  The fast form subtracts l = m + l2s in the same FMA
+// as the scale; once |m| reaches 2^13 the rounding of l (up to 2^-12 in the
+// exponent, the same for every element of the row) would show, and the
+// accurate form subtracts m and l2s one after the other (one more operation
+// per element, on such rows only).
+struct Norm {
+  float m, l2s, l;
+};
+constexpr float kBigRef = 0x1p13f;
+// l1 marker of a row the resident kernel leaves to the redo kernel (no L1 is negative)
+constexpr float kL1Redo = -1.0f;
+
+__device__ __forceinline__ Norm make_norm(float m, float s) {
+  const float l2s = log2_hw(s);
+  return Norm{m, l2s, m + l2s};
+}
+__device__ __forceinline__ bool norm_ok(const Norm& n) { return n.l > -__builtin_inff() && n.l < __builtin_inff(); }
+// row-uniform choice of the accurate form (a scalar value: the branch does not diverge)
+__device__ __forceinline__ bool norms_big(const Norm& x, const Norm& y) {
+  return __builtin_amdgcn_readfirstlane(int(!(fabsf(x.m) < kBigRef && fabsf(y.m) < kBigRef))) != 0;
 }
 
-// NT threads per row; U vector chunks per thread in flight per pass step.
+// |p - q| of one element pair, the normalisers folded into the exponents
+template <bool ACC>
+__device__ __forceinline__ float absdiff(float a, float b, const Norm& x, const Norm& y, float l2e) {
+  if (ACC)
+    return fabsf(exp2_hw(__builtin_fmaf(a, l2e, -x.m) - x.l2s) - exp2_hw(__builtin_fmaf(b, l2e, -y.m) - y.l2s));
+  return fabsf(exp2_hw(__builtin_fmaf(a, l2e, -x.l)) - exp2_hw(__builtin_fmaf(b, l2e, -y.l)));
+}
+
+// One row pair by one workgroup of NT threads, U vector chunks per thread in
+// flight per pass step: pass 1 (online max / sum-exp of both rows), merge,
+// pass 2 (sum |p - q|).
 template <int DT, int NT, int U>
-__global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, int64_t ld_t, const void* __restrict__ dft,
-                                                int64_t ld_d, int64_t V, float* __restrict__ l1,
-                                                float* __restrict__ accept) {
+__device__ __forceinline__ void l1_row(const void* __restrict__ tgt, int64_t ld_t, const void* __restrict__ dft,
+                                       int64_t ld_d, int64_t V, int64_t row, float* __restrict__ l1,
+                                       float* __restrict__ accept) {
   constexpr int VEC = DT == VS_BF16 ? 8 : 4;
   constexpr int ES = DT == VS_BF16 ? 2 : 4;
   constexpr int NW = NT / 64;
+  // base-2 scale: log2(e), rounded to 16 bits for bf16 rows (exact products)
+  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
   __shared__ float red[NW][4];
-  const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
   const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
@@ -109,26 +140,26 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      online(mx, sx, a[u], VEC);
-      online(my, sy, b[u], VEC);
+      online(mx, sx, a[u], VEC, l2e);
+      online(my, sy, b[u], VEC, l2e);
     }
   }
   for (; q < nvec; q += NT) {
     float a[VEC], b[VEC];
     load_chunk<DT>(trow, q, a);
     load_chunk<DT>(drow, q, b);
-    online(mx, sx, a, VEC);
-    online(my, sy, b, VEC);
+    online(mx, sx, a, VEC, l2e);
+    online(my, sy, b, VEC, l2e);
   }
   for (int64_t i = tail0 + tid; i < V; i += NT) {
     float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
-    online(mx, sx, &a, 1);
-    online(my, sy, &b, 1);
+    online(mx, sx, &a, 1, l2e);
+    online(my, sy, &b, 1, l2e);
   }
   // block merge (fixed tree): wave tree, then wave 0 over the NW wave states;
   // the merge works in base-2 units
-  Part px = wave_merge_to_lane0(Part{mx * kLog2e, sx, 0.0f});
-  Part py = wave_merge_to_lane0(Part{my * kLog2e, sy, 0.0f});
+  Part px = wave_merge_to_lane0(Part{mx * l2e, sx, 0.0f});
+  Part py = wave_merge_to_lane0(Part{my * l2e, sy, 0.0f});
   if ((tid & 63) == 0) {
     red[tid >> 6][0] = px.m;
     red[tid >> 6][1] = px.s;
@@ -146,13 +177,15 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
     qx = wave_merge_to_lane0(qx);
     qy = wave_merge_to_lane0(qy);
     if (tid == 0) {
-      fin[0] = qx.m + log2_hw(qx.s);  // base-2 LSE of the target row
-      fin[1] = qy.m + log2_hw(qy.s);
+      fin[0] = qx.m;  // base-2 maximum and sum of the target row
+      fin[1] = qx.s;
+      fin[2] = qy.m;
+      fin[3] = qy.s;
     }
   }
   __syncthreads();
-  const float lx = fin[0], ly = fin[1];
-  const bool ok = lx > -__builtin_inff() && lx < __builtin_inff() && ly > -__builtin_inff() && ly < __builtin_inff();
+  const Norm nx = make_norm(fin[0], fin[1]), ny = make_norm(fin[2], fin[3]);
+  const bool ok = norm_ok(nx) && norm_ok(ny);
   if (!ok) {
     if (tid == 0) {
       l1[row] = __builtin_nanf("");
@@ -162,31 +195,36 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
   }
 
   // ---- pass 2: sum |p - q| ----
-  float acc = 0.0f;
-  q = tid;
-  for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
-    float a[U][VEC], b[U][VEC];
+  auto pass2 = [&](auto acc_form) {
+    constexpr bool ACC = decltype(acc_form)::value;
+    float acc = 0.0f;
+    int64_t q = tid;
+    for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+      float a[U][VEC], b[U][VEC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      load_chunk<DT>(trow, q + u * NT, a[u]);
-      load_chunk<DT>(drow, q + u * NT, b[u]);
+      for (int u = 0; u < U; ++u) {
+        load_chunk<DT>(trow, q + u * NT, a[u]);
+        load_chunk<DT>(drow, q + u * NT, b[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc += absdiff<ACC>(a[u][i], b[u][i], nx, ny, l2e);
     }
+    for (; q < nvec; q += NT) {
+      float a[VEC], b[VEC];
+      load_chunk<DT>(trow, q, a);
+      load_chunk<DT>(drow, q, b);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc += absdiff(a[u][i], b[u][i], lx, ly);
-  }
-  for (; q < nvec; q += NT) {
-    float a[VEC], b[VEC];
-    load_chunk<DT>(trow, q, a);
-    load_chunk<DT>(drow, q, b);
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc += absdiff(a[i], b[i], lx, ly);
-  }
-  for (int64_t i = tail0 + tid; i < V; i += NT) {
-    const float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
-    acc += absdiff(a, b, lx, ly);
-  }
+      for (int i = 0; i < VEC; ++i) acc += absdiff<ACC>(a[i], b[i], nx, ny, l2e);
+    }
+    for (int64_t i = tail0 + tid; i < V; i += NT) {
+      const float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
+      acc += absdiff<ACC>(a, b, nx, ny, l2e);
+    }
+    return acc;
+  };
+  float acc = norms_big(nx, ny) ? pass2(std::true_type{}) : pass2(std::false_type{});
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float o = shfl_down_f(acc, off);
@@ -207,6 +245,27 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
       l1[row] = d;
       if (accept) accept[row] = fminf(fmaxf(1.0f - 0.5f * d, 0.0f), 1.0f);
     }
+  }
+}
+
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, int64_t ld_t, const void* __restrict__ dft,
+                                                int64_t ld_d, int64_t V, float* __restrict__ l1,
+                                                float* __restrict__ accept) {
+  l1_row<DT, NT, U>(tgt, ld_t, dft, ld_d, V, blockIdx.x, l1, accept);
+}
+
+// The rows the resident kernel below marked kL1Redo (maxima past 2^13 in
+// base-2 units), done again by the two-pass form, which takes the accurate
+// exponent form on such rows.  Workgroups stride over the rows; every other
+// row costs one load of its l1 entry.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void l1_redo_kernel(const void* __restrict__ tgt, int64_t ld_t,
+                                                     const void* __restrict__ dft, int64_t ld_d, int64_t rows,
+                                                     int64_t V, float* __restrict__ l1, float* __restrict__ accept) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    if (l1[r] == kL1Redo) l1_row<VS_BF16, NT, U>(tgt, ld_t, dft, ld_d, V, r, l1, accept);
+    __syncthreads();  // the row's last LDS reads come before the next row's writes
   }
 }
 
@@ -279,12 +338,12 @@ template <int N>
 __device__ __forceinline__ void lazy_add(float& c, float& s, const float* v) {
   float cs = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) cs += exp2_hw(__builtin_fmaf(v[i], kLog2e, -c));
+  for (int i = 0; i < N; ++i) cs += exp2_hw(__builtin_fmaf(v[i], kLog2eBf16, -c));
   if (!(cs < 0x1p64f)) {
     float bm = v[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) bm = fmaxf(bm, v[i]);
-    const float nc = fmaxf(c, bm * kLog2e);
+    const float nc = fmaxf(c, bm * kLog2eBf16);
     cs = 0.0f;
     if (nc == kNegInf) {  // only -inf so far (or NaNs that fmaxf dropped)
 #pragma unroll
@@ -294,7 +353,7 @@ __device__ __forceinline__ void lazy_add(float& c, float& s, const float* v) {
       s *= exp2_hw(c - nc);  // 0 from the initial -inf
       c = nc;
 #pragma unroll
-      for (int i = 0; i < N; ++i) cs += exp2_hw(__builtin_fmaf(v[i], kLog2e, -c));
+      for (int i = 0; i < N; ++i) cs += exp2_hw(__builtin_fmaf(v[i], kLog2eBf16, -c));
     }
   }
   s += cs;
@@ -353,14 +412,17 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (live ? r : 0) * ld), (short)0, live ? nbytes : 0,
                                              kBufFlags);
   };
-  // row r's L1 from the pass-2 partials of buffer b (thread 0)
-  auto finish = [&](int64_t r, int b, bool ok) {
+  // row r's L1 from the pass-2 partials of buffer b (thread 0); state 0: a
+  // non-finite normaliser (NaN), 1: done, 2: the maxima need the accurate
+  // form, left to l1_redo_kernel (the kL1Redo marker)
+  auto finish = [&](int64_t r, int b, int state) {
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red_b[b][w];
-    const float dd = ok ? fminf(fmaxf(v, 0.0f), 2.0f) : __builtin_nanf("");
+    const float nan = __builtin_nanf("");
+    const float dd = state == 1 ? fminf(fmaxf(v, 0.0f), 2.0f) : state == 2 ? kL1Redo : nan;
     l1[r] = dd;
-    if (accept) accept[r] = ok ? fminf(fmaxf(1.0f - 0.5f * dd, 0.0f), 1.0f) : __builtin_nanf("");
+    if (accept) accept[r] = state == 1 ? fminf(fmaxf(1.0f - 0.5f * dd, 0.0f), 1.0f) : nan;
   };
 
   int64_t row = blockIdx.x;
@@ -370,7 +432,7 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < RES_JD; ++j) d[j] = res_load(rd, voff, j);
   }
-  bool prev_ok = false;
+  int prev_state = 0;
   int it = 0;
   for (; row < rows; row += gridDim.x, ++it) {
     const int b = it & 1;
@@ -428,7 +490,7 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
       }
     }
     __syncthreads();
-    if (tid == 0 && it > 0) finish(row - gridDim.x, b ^ 1, prev_ok);
+    if (tid == 0 && it > 0) finish(row - gridDim.x, b ^ 1, prev_state);
     float Mx = red_a[b][0][0], My = red_a[b][0][2];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
@@ -441,9 +503,8 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
       Sx += red_a[b][w][1] * ref_scale(red_a[b][w][0], Mx);
       Sy += red_a[b][w][3] * ref_scale(red_a[b][w][2], My);
     }
-    const float lx = Mx + log2_hw(Sx);  // base-2 log-sum-exp of each row
-    const float ly = My + log2_hw(Sy);
-    const bool ok = lx > -__builtin_inff() && lx < __builtin_inff() && ly > -__builtin_inff() && ly < __builtin_inff();
+    const Norm nx = make_norm(Mx, Sx), ny = make_norm(My, Sy);  // base-2 normalisers of each row
+    const bool ok = norm_ok(nx) && norm_ok(ny);
 
     // ---- pass 2: sum |p - q|; the next row's draft chunks replace the used ones ----
     // (a row with a non-finite normaliser runs it too, to keep the next row's
@@ -464,17 +525,17 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
         unpack8(w, a);
         unpack8(d[j], c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += absdiff(a[i], c[i], lx, ly);
+        for (int i = 0; i < 8; ++i) acc += absdiff<false>(a[i], c[i], nx, ny, kLog2eBf16);
       }
       d[j] = res_load(rn, voff, j);
     }
-    if (tid < ntail) acc += absdiff(ta, da, lx, ly);
+    if (tid < ntail) acc += absdiff<false>(ta, da, nx, ny, kLog2eBf16);
     acc = wave_sum_all(acc);
     if (lane == 0) red_b[b][wave] = acc;  // summed after the next row's barrier
-    prev_ok = ok;
+    prev_state = !ok ? 0 : (fabsf(nx.m) < kBigRef && fabsf(ny.m) < kBigRef) ? 1 : 2;
   }
   __syncthreads();
-  if (tid == 0 && it > 0) finish(row - gridDim.x, (it - 1) & 1, prev_ok);
+  if (tid == 0 && it > 0) finish(row - gridDim.x, (it - 1) & 1, prev_state);
 }
 
 // 256 threads x 8 loads in flight: several rows per CU overlap their passes
@@ -505,6 +566,9 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
     l1_resident_kernel<<<dim3(unsigned(grid)), dim3(RES_NT), 0, s>>>(
         static_cast<const uint16_t*>(target.ptr), target.ld, static_cast<const uint16_t*>(draft.ptr), draft.ld, rows, V,
         l1, accept);
+    const int64_t redo_grid = rows < 512 ? rows : 512;
+    l1_redo_kernel<kL1Threads, kL1Unroll><<<dim3(unsigned(redo_grid)), dim3(kL1Threads), 0, s>>>(
+        target.ptr, target.ld, draft.ptr, draft.ld, rows, V, l1, accept);
     return int(hipGetLastError());
   }
   if (target.dtype == VS_BF16) {

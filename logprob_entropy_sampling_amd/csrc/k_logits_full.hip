@@ -57,7 +57,7 @@ __device__ __forceinline__ void fold_values(Part& p, const float* v, int n, floa
       if (!(p.m == kNegInf && p.s == 0.0f)) {
         const float d = p.m - nm;
         const float f = exp2_hw(d);
-        p.a = f * __builtin_fmaf(p.s, d, p.a);
+        p.a = f == 0.0f ? 0.0f : f * __builtin_fmaf(p.s, d, p.a);  // (p.s * d may overflow when f = 0)
         p.s *= f;
       }
       p.m = nm;
@@ -175,7 +175,9 @@ __device__ __forceinline__ void write_row(Part acc, int64_t row, float c, bool t
   const bool ok = ok_in && (lse2 > -__builtin_inff()) && (lse2 < __builtin_inff()) && have_zy;
   const float zy = ok ? zy_raw * c : 0.0f;
   const float nan = __builtin_nanf("");
-  const float lp = ok ? kLn2 * (zy - lse2) : nan;
+  // (u_y - m) - log2 s: forming u_y - (m + log2 s) would drop log2 s below
+  // one ulp of m at large magnitudes
+  const float lp = ok ? kLn2 * ((zy - acc.m) - l2s) : nan;
   if (mode == kMergeFull) {
     if (lse) lse[row] = ok ? kLn2 * lse2 : nan;
     logprob[row] = lp;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kRowThreads) void logits_row_kernel(
   if (row_count && slot >= *row_count) return;
   const int64_t row = row_map ? int64_t(row_map[slot]) : slot;
   const float tau = temp ? temp[row] : temp_scalar;
-  const float c = kLog2e / tau;
+  const float c = DT == VS_BF16 ? scale16(kLog2e / tau) : kLog2e / tau;
   const char* rowp = static_cast<const char*>(logits) + row * ld * ES;
   Part p = row_state<DT>(rowp, V, c);
   // fixed tree: inside each wave, then the wave states in order

@@ -644,10 +644,17 @@ struct SplitKeys : StreamKeysT<NT_FIN> {
   }
 };
 
-// fp64 weight of a key relative to the row max: exp(x / tau - z_max), the
-// quantity the program compares with min_p and sums for the masses.
-__device__ __forceinline__ double key_weight(uint32_t k, double tau, double z0) {
-  return exp(double(key_logit(k)) / tau - z0);
+// z - z_max of key k in fp64, from the exact difference of the two logits
+// (bf16 values are exact in fp64), divided by tau once.  Forming x / tau - z_max
+// instead would carry a rounding error of about |x / tau| * 2^-53, which at
+// large magnitudes is far from small once exponentiated.
+__device__ __forceinline__ double key_d(uint32_t k, double tau, double xmax) {
+  return (double(key_logit(k)) - xmax) / tau;
+}
+// fp64 weight of a key relative to the row max: exp(z - z_max), the quantity
+// the program compares with min_p and sums for the masses.
+__device__ __forceinline__ double key_weight(uint32_t k, double tau, double xmax) {
+  return exp(key_d(k, tau, xmax));
 }
 
 struct RowArgs {
@@ -693,7 +700,7 @@ __device__ __forceinline__ bool params_ok(const RowArgs& a) {
 
 // Segment summary from the counts of its 64 keys (ascending key order).
 template <class CountFn>
-__device__ __forceinline__ void summarize_segment(int seg, CountFn count, double tau, double z0, Smem& sm) {
+__device__ __forceinline__ void summarize_segment(int seg, CountFn count, double tau, double xmax, Smem& sm) {
   uint32_t cnt = 0;
   double mass = 0.0, zm = 0.0;
   for (int b = 0; b < SEGW; ++b) {
@@ -701,7 +708,7 @@ __device__ __forceinline__ void summarize_segment(int seg, CountFn count, double
     const uint32_t c = count(key);
     if (c) {
       cnt += c;
-      const double d = double(key_logit(key)) / tau - z0;
+      const double d = key_d(key, tau, xmax);
       const double e = exp(d);
       if (e > 0.0) {
         mass += double(c) * e;
@@ -724,13 +731,15 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total
 // that the low weights underflow or, above the row max, overflow) nothing is
 // added and false is returned: the caller then runs segment_masses_down.
 template <class WordFn>
-__device__ __forceinline__ bool segment_masses(int s, WordFn word, int rot, double tau, double z0, double& m,
+__device__ __forceinline__ bool segment_masses(int s, WordFn word, int rot, double tau, double xmax, double& m,
                                                double& zm) {
   const uint32_t k0 = uint32_t(s * SEGW);
   const double x0 = double(key_logit(k0));
   const double dd = (double(key_logit(k0 + 1)) - x0) / tau;  // exact spacing / tau
-  const double d0 = x0 / tau - z0;
-  const double d_last = d0 + double(SEGW - 1) * dd;
+  const double d0 = (x0 - xmax) / tau;
+  // the last key's offset from its own logit, not d0 + 63 dd: with huge
+  // spacings that sum would carry the rounding of two huge terms
+  const double d_last = key_d(k0 + uint32_t(SEGW - 1), tau, xmax);
   if (d_last < -746.0) return true;  // every weight is 0 in fp64
   if (d0 < -700.0 || d_last > 700.0) return false;
   const double r = exp(dd);
@@ -753,29 +762,26 @@ __device__ __forceinline__ bool segment_masses(int s, WordFn word, int rot, doub
   }
   return true;
 }
-// The same masses for the segments segment_masses declines: the recurrence
-// runs downwards from the highest counted key, whose weight is at most 1 (it
-// is not above the row max), so nothing overflows; what underflows is below
-// the fp64 resolution of the row's mass, which is at least 1.
+// The same masses for the segments segment_masses declines (keys so far
+// apart that a recurrence over them would overflow, underflow or carry the
+// rounding of huge offsets): one exponential per counted key, from the top
+// counted key down, each exponent taken from the key's own logit (key_d), so
+// the row maximum has exactly weight 1 and z - z_max = 0.  Weights fall with
+// the key, so the walk stops at the first weight that is 0; what it leaves out
+// is below the fp64 resolution of the row's mass, which is at least 1.
 template <class WordFn>
-__device__ __forceinline__ void segment_masses_down(int s, WordFn word, double tau, double z0, double& m,
+__device__ __forceinline__ void segment_masses_down(int s, WordFn word, double tau, double xmax, double& m,
                                                  double& zm) {
   const uint32_t k0 = uint32_t(s * SEGW);
-  const double x0 = double(key_logit(k0));
-  const double dd = (double(key_logit(k0 + 1)) - x0) / tau;
-  const double d0 = x0 / tau - z0;
-  int kt = SEGW - 1;  // the highest counted key
-  while (kt > 0 && ((word(kt >> 1) >> ((kt & 1) * 16)) & 0xFFFFu) == 0) --kt;
-  double w = exp(d0 + double(kt) * dd);
-  const double r_down = exp(-dd);  // 0 when the keys are that far apart: only key kt has weight
-  for (int k = kt; k >= 0 && w > 0.0; --k) {
+  for (int k = SEGW - 1; k >= 0; --k) {
     const uint32_t c = (word(k >> 1) >> ((k & 1) * 16)) & 0xFFFFu;
-    if (c) {
-      const double ck = double(c) * w;
-      m += ck;
-      zm += ck * (d0 + double(k) * dd);
-    }
-    w *= r_down;
+    if (!c) continue;
+    const double d = key_d(k0 + uint32_t(k), tau, xmax);
+    const double w = exp(d);
+    if (w == 0.0) break;
+    const double ck = double(c) * w;
+    m += ck;
+    zm += ck * d;
   }
 }
 
@@ -791,7 +797,7 @@ __device__ __forceinline__ void segment_masses_down(int s, WordFn word, double t
 // -inf (weight 0) and the register paths' padding at key 0 can be counted.
 // Returns this thread's share of the sum of all counts.
 template <int NTH>
-__device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uint32_t n_pad, double tau, double z0,
+__device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uint32_t n_pad, double tau, double xmax,
                                                       Smem& sm) {
   uint32_t total = 0;
   const int rot = int(threadIdx.x & 31);
@@ -808,7 +814,7 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
     if (s == 0) cnt -= n_pad;
     total += cnt;
     double m = 0.0, zm = 0.0;
-    if (cnt != 0 && s >= 2 && s < NSEG - 2 && !segment_masses(s, [&](int j) { return seg[j]; }, rot, tau, z0, m, zm))
+    if (cnt != 0 && s >= 2 && s < NSEG - 2 && !segment_masses(s, [&](int j) { return seg[j]; }, rot, tau, xmax, m, zm))
       down |= 1u << i;
     sm.seg_count[s] = cnt;
     sm.seg_mass[s] = m;
@@ -820,7 +826,7 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
       if (!((down >> i) & 1u)) continue;
       const uint32_t* seg = hist + s * 32;
       double m = 0.0, zm = 0.0;
-      segment_masses_down(s, [&](int j) { return seg[j]; }, tau, z0, m, zm);
+      segment_masses_down(s, [&](int j) { return seg[j]; }, tau, xmax, m, zm);
       sm.seg_mass[s] = m;
       sm.seg_zmass[s] = zm;
     }
@@ -831,7 +837,7 @@ __device__ __forceinline__ uint32_t summarize_segments(const uint32_t* hist, uin
 // Everything after the histogram: cuts, scores, descriptor, dense ids.
 // `fine(s)` makes the 64 key counts of segment s readable through count(key).
 template <class Keys, class FineFn, class CountFn, class SM>
-__device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double z0, SM& sm,
+__device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double tau, double xmax, SM& sm,
                            FineFn fine, CountFn count) {
   constexpr int NTH = Keys::kThreads;
   constexpr int NW = NTH / 64;
@@ -941,7 +947,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
       const uint32_t s = sm.bu[0];
       const uint32_t key = s * SEGW + uint32_t(SEGW - 1 - lane);
       const uint32_t c = count(key);
-      const double d = c ? double(key_logit(key)) / tau - z0 : 0.0;
+      const double d = c ? key_d(key, tau, xmax) : 0.0;
       const double e = c ? exp(d) : 0.0;
       const double m = double(c) * e;
       const double zm = e > 0.0 ? double(c) * e * d : 0.0;
@@ -1015,7 +1021,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
         const uint32_t step = (hi - lo + 63u) / 64u;
         const uint32_t kl = lo + uint32_t(lane) * step;
         const uint32_t k = kl < hi ? kl : hi;
-        const unsigned long long bal = __ballot(double(key_logit(k)) / tau - z0 >= lmp);
+        const unsigned long long bal = __ballot(key_d(k, tau, xmax) >= lmp);
         if (bal == 0) {
           lo = lo + 63u * step + 1u;  // every tested key fails: the answer lies above lane 63's
         } else {
@@ -1026,8 +1032,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
         }
       }
       if (lane == 0) {
-        while (lo > KEY_NEG_INF + 1 && key_weight(lo - 1, tau, z0) >= mp) --lo;
-        while (lo < kmax && key_weight(lo, tau, z0) < mp) ++lo;
+        while (lo > KEY_NEG_INF + 1 && key_weight(lo - 1, tau, xmax) >= mp) --lo;
+        while (lo < kmax && key_weight(lo, tau, xmax) < mp) ++lo;
         sm.bu[5] = lo;
       }
     }
@@ -1054,7 +1060,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   const uint32_t above_L = sm.bu[3], cnt_L = sm.bu[4];
   const uint32_t r_L = L - above_L;  // tokens of the threshold key inside the support
   const double e_L = sm.bd[4];
-  const double d_L = double(key_logit(K_L)) / tau - z0;
+  const double d_L = key_d(K_L, tau, xmax);
   const double mass_S = sm.bd[2] + double(r_L) * e_L;
   const double zmass_S = sm.bd[3] + (e_L > 0.0 ? double(r_L) * e_L * d_L : 0.0);
 
@@ -1174,7 +1180,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     const double lms = log(mass_S);
     if (a.entropy) a.entropy[a.row] = float(lms - zmass_S / mass_S);
     if (in_s) {
-      a.logprob[a.row] = float((double(key_logit(key_y)) / tau - z0) - lms);
+      a.logprob[a.row] = float(key_d(key_y, tau, xmax) - lms);
     } else {
       a.logprob[a.row] = kNegInf;
       st |= kRowOutside;
@@ -1183,7 +1189,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     if (a.support_len) a.support_len[a.row] = int32_t(L);
     if (a.threshold_logit) a.threshold_logit[a.row] = key_logit(K_L);
     if (a.threshold_ties) a.threshold_ties[a.row] = int32_t(r_L);
-    if (a.full_lse) a.full_lse[a.row] = float(z0 + log(total_mass));
+    if (a.full_lse) a.full_lse[a.row] = float(xmax / tau + log(total_mass));
   }
 }
 
@@ -1266,8 +1272,8 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
     return key == 0 ? c - n_pad : c;
   };
   const double tau = double(a.tauf);
-  const double z0 = double(key_logit(kmax)) / tau;
-  const uint32_t part = summarize_segments<NTH>(sm.hist, n_pad, tau, z0, sm);
+  const double xmax = double(key_logit(kmax));  // the row maximum (z_max = xmax / tau)
+  const uint32_t part = summarize_segments<NTH>(sm.hist, n_pad, tau, xmax, sm);
   // every counter stayed below 2^16 iff the counts add up to the token count
   // (a carry out of a low half, or out of a word, breaks the total); the sum
   // also orders the segment summaries before the queries read them
@@ -1276,7 +1282,7 @@ __global__ __launch_bounds__(NV > 0 ? NT : NT_STREAM, 1) void transforms_fast_ke
     return;
   }
   if (tid == 0) handoff[a.row] = 0;
-  finish_row(a, keys, kmax, tau, z0, sm, [](int) {}, count);
+  finish_row(a, keys, kmax, tau, xmax, sm, [](int) {}, count);
 }
 
 // Stream path: the row is re-read from memory for every pass; 32-bit counts.
@@ -1307,7 +1313,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
     return;
   }
   const double tau = double(a.tauf);
-  const double z0 = double(key_logit(kmax)) / tau;
+  const double xmax = double(key_logit(kmax));  // the row maximum (z_max = xmax / tau)
   for (uint32_t h = 0; h < 2; ++h) {
     for (int i = tid; i < HALF; i += NTH) sm.hist[i] = 0u;
     __syncthreads();
@@ -1316,7 +1322,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
     });
     __syncthreads();
     auto count_half = [&](uint32_t key) -> uint32_t { return sm.hist[key & 0x7FFFu]; };
-    for (int s = tid; s < NSEG / 2; s += NTH) summarize_segment(int(h) * (NSEG / 2) + s, count_half, tau, z0, sm);
+    for (int s = tid; s < NSEG / 2; s += NTH) summarize_segment(int(h) * (NSEG / 2) + s, count_half, tau, xmax, sm);
     __syncthreads();
   }
   if (tid == 0) sm.fine_seg = -1;
@@ -1334,7 +1340,7 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_stream_kernel(VS_KERN
     __syncthreads();
   };
   auto count = [&](uint32_t key) -> uint32_t { return sm.fine[key & 63u]; };
-  finish_row(a, keys, kmax, tau, z0, sm, fine, count);
+  finish_row(a, keys, kmax, tau, xmax, sm, fine, count);
 }
 
 // The count kernel's work on a row after its histogram passed the checks.
@@ -1517,7 +1523,7 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
   const uint32_t n_ne = hd.w;
   const uint32_t n_st = min(n_ne, uint32_t(FIN_STAGED));
   const double tau = double(a.tauf);
-  const double z0 = double(key_logit(kmax)) / tau;
+  const double xmax = double(key_logit(kmax));  // the row maximum (z_max = xmax / tau)
   reinterpret_cast<uint2*>(sm.nelist)[tid] = lst;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -1548,7 +1554,7 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
         cnt += (wd & 0xFFFFu) + (wd >> 16);
       }
       double m = 0.0, zm = 0.0;
-      if (sg >= 2 && sg < NSEG - 2 && !segment_masses(sg, word, rot, tau, z0, m, zm)) down |= 1u << i_e;
+      if (sg >= 2 && sg < NSEG - 2 && !segment_masses(sg, word, rot, tau, xmax, m, zm)) down |= 1u << i_e;
       sm.seg_count[sg] = cnt;
       sm.seg_mass[sg] = m;
       sm.seg_zmass[sg] = zm;
@@ -1566,7 +1572,7 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
       if (!((down >> i_e) & 1u)) continue;
       const int sg = sm.nelist[e];
       double m = 0.0, zm = 0.0;
-      segment_masses_down(sg, [&](int j) -> uint32_t { return blocks[e * 32 + j]; }, tau, z0, m, zm);
+      segment_masses_down(sg, [&](int j) -> uint32_t { return blocks[e * 32 + j]; }, tau, xmax, m, zm);
       sm.seg_mass[sg] = m;
       sm.seg_zmass[sg] = zm;
     }
@@ -1607,7 +1613,7 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
     const uint32_t slot = sm.seg_slot[key >> 6];
     return slot != 0xFFu ? (sm.blk[slot][(key & 63u) >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu : sm.fine[key & 63u];
   };
-  finish_row(a, keys, kmax, tau, z0, sm, fine, count);
+  finish_row(a, keys, kmax, tau, xmax, sm, fine, count);
 }
 
 #undef VS_ROW_ARGS

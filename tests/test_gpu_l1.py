@@ -141,3 +141,27 @@ def test_resident_leading_dimension(vsa, pad):
     a = (rng.standard_normal((T, V)) * 2).astype(np.float32)
     b = (a + rng.standard_normal((T, V)) * 0.5).astype(np.float32)
     _l1_case(vsa, a, b, ld_pad=pad)
+
+
+@pytest.mark.parametrize("V", [1000, 100003, 151936])
+def test_ties_at_large_magnitude(vsa, V):
+    # tied maxima far from zero: the target's mass split over 2 ids, the
+    # draft's over 4 (a superset) gives L1 = 1 at any magnitude.  Maxima past
+    # 2^13 in base-2 units take the accurate exponent form (the resident form
+    # hands such rows to the redo kernel); row 0 stays small for contrast.
+    say(f"l1: tied maxima at 2^12 .. 2^120 (bf16), V={V}")
+    mags = [4.0, 2.0 ** 12, 2.0 ** 20, 2.0 ** 60, 2.0 ** 100, 2.0 ** 120, -(2.0 ** 100)]
+    T = len(mags)
+    rng = np.random.default_rng(V)
+    a = np.zeros((T, V), np.float32)
+    b = np.zeros((T, V), np.float32)
+    for t, mag in enumerate(mags):
+        base = mag - abs(mag) * 0.5 if mag > 0 else 2.0 * mag
+        a[t] = base
+        b[t] = base
+        ids = rng.choice(V, 4, replace=False)
+        a[t, ids[:2]] = mag
+        b[t, ids] = mag
+    got = _l1_case(vsa, a, b)
+    l1 = got["l1"].cpu().numpy()
+    assert np.all(np.abs(l1[1:] - 1.0) < 2e-3), l1
