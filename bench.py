@@ -165,25 +165,64 @@ def bench_fused(vsa, dev, steps, warmup):
     }
 
 
+def _oracle_threads():
+    """(threads the oracle runs on, CPUs in this process's affinity set): every
+    CPU the process may use, at most 16 (one GPU's share of the host)."""
+    n_aff = len(os.sched_getaffinity(0))
+    return max(1, min(16, n_aff)), n_aff
+
+
+def _timed_oracle(fn, n_rows, budget_s, block=16):
+    """Run ``fn(rows)`` over consecutive row blocks on a pool of threads (numpy
+    releases the GIL in the oracle's array work) until every row is done or the
+    time budget is spent; BLAS threads are set to the same count.  Returns
+    (rows done, seconds, threads, affinity CPUs)."""
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+    import threadpoolctl
+    threads, n_aff = _oracle_threads()
+    blocks = [np.arange(r0, min(n_rows, r0 + block)) for r0 in range(0, n_rows, block)]
+    done = 0
+    with threadpoolctl.threadpool_limits(threads):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            pending = set()
+            nxt = 0
+            while nxt < len(blocks) or pending:
+                while nxt < len(blocks) and len(pending) < threads and time.perf_counter() - t0 < budget_s:
+                    pending.add(ex.submit(lambda b=blocks[nxt]: (fn(b), len(b))[1]))
+                    nxt += 1
+                if not pending:
+                    break
+                fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+                done += sum(f.result() for f in fin)
+        el = time.perf_counter() - t0
+    return done, el, threads, n_aff
+
+
+def _cpu_entry(done, el, threads, n_aff, what):
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(threads), "affinity_cpus": int(n_aff),
+            "kind": "oracle", "sample": f"{what}: {done} rows in {el:.1f} s (numpy float64, {threads} threads)"}
+
+
 def cpu_baseline(c, budget_s=15.0):
-    """fp64 oracle on the first rows of the same workload, batches of 32 rows until the budget is spent."""
+    """fp64 oracle on the first rows of the fused workload: blocks of 32 rows in
+    order (the projection's matmul uses every BLAS thread) until the budget is spent."""
     import threadpoolctl
     import oracle
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
-        if threadpoolctl.threadpool_info() else 1
+    threads, n_aff = _oracle_threads()
     rows_done = 0
-    t0 = time.perf_counter()
-    while True:
-        rows = np.arange(rows_done, rows_done + 32)
-        x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
-        oracle.score_full(x, 1.0, c["targets"][rows])
-        rows_done += 32
-        if time.perf_counter() - t0 > budget_s or rows_done >= c["T"]:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(rows_done / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows_done} of {c['T']} rows of fused_full (projection + LSE/logprob/entropy, "
-                      f"numpy float64), {el:.1f} s"}
+    with threadpoolctl.threadpool_limits(threads):
+        t0 = time.perf_counter()
+        while True:
+            rows = np.arange(rows_done, rows_done + 32)
+            x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
+            oracle.score_full(x, 1.0, c["targets"][rows])
+            rows_done += 32
+            if time.perf_counter() - t0 > budget_s or rows_done >= c["T"]:
+                break
+        el = time.perf_counter() - t0
+    return _cpu_entry(rows_done, el, threads, n_aff,
+                      f"first rows of fused_full of {c['T']} (projection + LSE/logprob/entropy)")
 
 
 def _path_entry(T, ev, sw, call_bytes, sweep_bytes, **extra):
@@ -199,30 +238,44 @@ def _path_entry(T, ev, sw, call_bytes, sweep_bytes, **extra):
     return e
 
 
-def bench_paths(vsa, dev, steps, warmup):
+def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     """The other scoring paths, each on its own workload.  A 512 MiB write
     before every timed call leaves none of its inputs in the Infinity Cache.
-    Bytes are algorithmic: every input element read once, every output written once."""
+    Outputs and workspace are allocated once, so the timed calls allocate
+    nothing.  Bytes are algorithmic: every input element read once, every
+    output written once.  With ``cpu``, each path also times the fp64 oracle
+    on the same inputs (all rows, or as many as the budget allows)."""
     import torch
     import workloads
     flush = _flusher(dev)
     res = {}
+    if cpu:
+        import oracle
 
     # logits-input full-vocabulary scoring: T=512, V=151,936 bf16, per-row temperature
     c = workloads.make(2)
     T, V = c["T"], c["V"]
     lg, y, tau = _bf16(c["logits"], dev), _dev(c["targets"], dev), _dev(c["temperature"], dev)
-    ev, sw = _event_times(vsa, lambda: vsa.score_full(y, logits=lg, temperature=tau), steps, warmup, flush)
+    o = vsa.score_full(y, logits=lg, temperature=tau)
+    ev, sw = _event_times(vsa, lambda: vsa.score_full(y, logits=lg, temperature=tau, out=o), steps, warmup, flush)
     byts = T * V * 2 + T * (4 + 8) + T * (3 * 4 + 1)  # logits, tau, targets in; lse, logprob, entropy, status out
     res["logits_full"] = _path_entry(T, ev, sw, byts, byts, V=V)
-    del lg
+    if cpu:
+        res["logits_full"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
+            lambda r: oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16", rows=r), c["temperature"][r],
+                                        c["targets"][r]), T, cpu_budget_s), "logits_full rows (LSE/logprob/entropy)")
+    del lg, o
 
     # recorded support through selected projections: T=2048, H=7168, V=129,280, width 64
     c = workloads.make(3)
     T, H, V = c["T"], c["H"], c["V"]
     hid, w = _bf16(c["hidden"], dev), _bf16(c["weight"], dev)
     y, ids = _dev(c["targets"], dev), _dev(c["support_ids"], dev)
-    ev, sw = _event_times(vsa, lambda: vsa.score_support_ids(y, ids, hidden=hid, weight=w), steps, warmup, flush)
+    o = vsa.score_support_ids(y, ids, hidden=hid, weight=w)
+    wsp = torch.empty(max(1, vsa.workspace_bytes("score_support_ids", hidden=hid, weight=w, width=ids.shape[1])),
+                      dtype=torch.uint8, device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_support_ids(y, ids, hidden=hid, weight=w, out=o, workspace=wsp),
+                          steps, warmup, flush)
     sup = c["support_ids"][c["support_ids"] >= 0]
     uniq = int(np.unique(sup).size)
     # unique basis: each distinct W row and each hidden row read once
@@ -230,7 +283,14 @@ def bench_paths(vsa, dev, steps, warmup):
     res["support_replay"] = _path_entry(T, ev, sw, byts, byts, H=H, V=V, width=int(c["support_ids"].shape[1]),
                                         pairs=int(sup.size), unique_rows=uniq,
                                         bytes_pairs_basis=int(sup.size * H * 2 + T * H * 2 + c["support_ids"].nbytes))
-    del hid, w
+    if cpu:
+        def support_rows(r):
+            def fn(t, cols):
+                return oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=[r[t]], cols=cols)[0]
+            return oracle.score_support(fn, V, c["support_ids"][r], 1.0, c["targets"][r])
+        res["support_replay"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(support_rows, T, cpu_budget_s),
+                                                           "support_replay rows (selected projections + scores)")
+    del hid, w, o, wsp
 
     # sampling transforms and draft/target L1: T=2048, V=151,936 bf16
     c = workloads.make(5)
@@ -239,13 +299,28 @@ def bench_paths(vsa, dev, steps, warmup):
     y = _dev(c["targets"], dev)
     tk, tp, mp, tau = (_dev(c["top_k"], dev), _dev(c["top_p"], dev), _dev(c["min_p"], dev),
                        _dev(c["temperature"], dev))
-    ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64), steps,
-                          warmup, flush)
+    o = vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64)
+    wsp = torch.empty(max(1, vsa.workspace_bytes("score_transforms", logits=lg)), dtype=torch.uint8, device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64, out=o,
+                                                            workspace=wsp), steps, warmup, flush)
     byts = T * V * 2 + T * (4 * 4 + 8) + T * (4 * 4 + 4 + 1 + 64 * 8 + 4)
     res["transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, support_ids_cap=64)
-    ev, sw = _event_times(vsa, lambda: vsa.l1_distance(lg, dr), steps, warmup, flush)
+    if cpu:
+        res["transforms"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
+            lambda r: oracle.score_transforms(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
+                                              c["temperature"][r], c["top_k"][r], c["top_p"][r], c["min_p"][r],
+                                              c["targets"][r], cap=64), T, cpu_budget_s),
+            "transforms_l1 rows (sort, top-k/top-p/min-p, support scores)")
+    del o, wsp
+    o = vsa.l1_distance(lg, dr)
+    ev, sw = _event_times(vsa, lambda: vsa.l1_distance(lg, dr, out=o), steps, warmup, flush)
     byts = 2 * T * V * 2 + T * 8
     res["l1_distance"] = _path_entry(T, ev, sw, byts, byts, V=V)
+    if cpu:
+        res["l1_distance"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
+            lambda r: oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
+                                         oracle.logits_from_logits(c["draft"], "bf16", rows=r)), T, cpu_budget_s),
+            "transforms_l1 rows (two softmaxes, L1, accept_rate)")
     torch.cuda.synchronize()
     return res
 
@@ -317,7 +392,7 @@ def main():
     }
     if args.paths == "all":
         print("bench: secondary paths", file=sys.stderr, flush=True)
-        out["paths"] = bench_paths(vsa, dev, max(5, min(args.steps, 20)), 2)
+        out["paths"] = bench_paths(vsa, dev, max(5, min(args.steps, 20)), 2, cpu=args.cpu_baseline == "on")
     if probe is not None:
         out["copy_probe"] = probe
     if args.cpu_baseline == "on":

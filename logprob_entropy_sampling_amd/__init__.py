@@ -42,7 +42,7 @@ class _Lazy:
 
 _lib = _Lazy()
 
-__all__ = ["score_full", "score_support_ids", "score_transforms", "l1_distance", "workspace_size",
+__all__ = ["score_full", "score_support_ids", "score_transforms", "l1_distance", "workspace_size", "workspace_bytes",
            "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
@@ -133,9 +133,45 @@ def workspace_size(op: int, src: VsSource, width: int = 0) -> int:
     return int(_lib.vs_workspace_size(op, ctypes.byref(src), int(width)))
 
 
-def _workspace(op, src, dev, width=0):
+def _workspace(op, src, dev, width=0, given=None):
+    """The call's workspace: the caller's uint8 tensor when given (checked for
+    size), else a new one."""
     n = workspace_size(op, src, width)
+    if given is not None:
+        _check_cuda("workspace", given, {torch.uint8}, 1)
+        if given.numel() < n or not given.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {n} bytes")
+        return given, given.numel()
     return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
+
+
+def _outputs(spec, dev, out):
+    """Output tensors: the caller's (``out``, a dict, checked against
+    ``spec`` = {name: (shape, dtype) or None}) or new ones."""
+    res = {}
+    for name, sd in spec.items():
+        if sd is None:
+            res[name] = None
+            continue
+        shape, dtype = sd
+        t = None if out is None else out.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        else:
+            _check_cuda(f"out[{name!r}]", t, {dtype})
+            if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+                raise ValueError(f"out[{name!r}] must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+        res[name] = t
+    return res
+
+
+def workspace_bytes(op: str, *, logits=None, hidden=None, weight=None, width: int = 0) -> int:
+    """Bytes of workspace an entry point needs for these inputs (vs_workspace_size);
+    op is one of "score_full", "score_support_ids", "score_transforms", "l1_distance"."""
+    ops = {"score_full": _capi.VS_OP_SCORE_FULL, "score_support_ids": _capi.VS_OP_SCORE_SUPPORT,
+           "score_transforms": _capi.VS_OP_SCORE_TRANSFORMS, "l1_distance": _capi.VS_OP_L1_DISTANCE}
+    src, _, _ = _make_source(logits, hidden, weight, 1.0)
+    return workspace_size(ops[op], src, width)
 
 
 def _stream(dev):
@@ -149,26 +185,30 @@ def _ids(name, t, T):
 
 
 def score_full(targets, *, logits=None, hidden=None, weight=None, temperature=1.0, vocab_chunk=8192,
-               with_entropy=True, with_lse=True):
-    """Full-vocabulary LSE, selected logprob and entropy (vs_score_full)."""
+               with_entropy=True, with_lse=True, out=None, workspace=None):
+    """Full-vocabulary LSE, selected logprob and entropy (vs_score_full).
+
+    ``out`` (dict of preallocated outputs) and ``workspace`` (uint8 tensor of
+    at least workspace_bytes("score_full", ...) bytes) are optional: with
+    both, the call allocates nothing."""
     src, dev, _keep = _make_source(logits, hidden, weight, temperature)
     _ids("targets", targets, src.T)
     T = src.T
-    lse = torch.empty(T, dtype=torch.float32, device=dev) if with_lse else None
-    logprob = torch.empty(T, dtype=torch.float32, device=dev)
-    entropy = torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None
-    status = torch.empty(T, dtype=torch.uint8, device=dev)
-    ws, n = _workspace(_capi.VS_OP_SCORE_FULL, src, dev)
-    rc = _lib.vs_score_full(ctypes.byref(src), _ptr(targets), int(vocab_chunk), _ptr(lse), _ptr(logprob),
-                            _ptr(entropy), _ptr(status), _ptr(ws), n, _stream(dev))
+    o = _outputs({"lse": ((T,), torch.float32) if with_lse else None, "logprob": ((T,), torch.float32),
+                  "entropy": ((T,), torch.float32) if with_entropy else None, "status": ((T,), torch.uint8)},
+                 dev, out)
+    ws, n = _workspace(_capi.VS_OP_SCORE_FULL, src, dev, given=workspace)
+    rc = _lib.vs_score_full(ctypes.byref(src), _ptr(targets), int(vocab_chunk), _ptr(o["lse"]), _ptr(o["logprob"]),
+                            _ptr(o["entropy"]), _ptr(o["status"]), _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_score_full")
-    return {"lse": lse, "logprob": logprob, "entropy": entropy, "status": status}
+    return o
 
 
 def score_support_ids(targets, support_ids, *, logits=None, hidden=None, weight=None, temperature=1.0,
-                      fallback=None, vocab_chunk=8192, with_entropy=True):
-    """Recorded-support logprob and entropy (vs_score_support_ids)."""
+                      fallback=None, vocab_chunk=8192, with_entropy=True, out=None, workspace=None):
+    """Recorded-support logprob and entropy (vs_score_support_ids); ``out`` and
+    ``workspace`` as for score_full."""
     src, dev, _keep = _make_source(logits, hidden, weight, temperature)
     _ids("targets", targets, src.T)
     _check_cuda("support_ids", support_ids, {torch.int64}, 2)
@@ -183,20 +223,21 @@ def score_support_ids(targets, support_ids, *, logits=None, hidden=None, weight=
         if fallback.dtype == torch.bool:
             fallback = fallback.to(torch.uint8)
     T = src.T
-    logprob = torch.empty(T, dtype=torch.float32, device=dev)
-    entropy = torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None
-    status = torch.empty(T, dtype=torch.uint8, device=dev)
-    ws, n = _workspace(_capi.VS_OP_SCORE_SUPPORT, src, dev, width)
+    o = _outputs({"logprob": ((T,), torch.float32), "entropy": ((T,), torch.float32) if with_entropy else None,
+                  "status": ((T,), torch.uint8)}, dev, out)
+    ws, n = _workspace(_capi.VS_OP_SCORE_SUPPORT, src, dev, width, given=workspace)
     rc = _lib.vs_score_support_ids(ctypes.byref(src), _ptr(support_ids) if width else None, width, ld_ids,
-                                   _ptr(targets), _ptr(fallback), int(vocab_chunk), _ptr(logprob), _ptr(entropy),
-                                   _ptr(status), _ptr(ws), n, _stream(dev))
+                                   _ptr(targets), _ptr(fallback), int(vocab_chunk), _ptr(o["logprob"]),
+                                   _ptr(o["entropy"]), _ptr(o["status"]), _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_score_support_ids")
-    return {"logprob": logprob, "entropy": entropy, "status": status}
+    return o
 
 
-def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, cap=0, with_full_lse=True):
-    """Top-k / top-p / min-p support scores and support descriptor (vs_score_transforms)."""
+def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, cap=0, with_full_lse=True, out=None,
+                     workspace=None):
+    """Top-k / top-p / min-p support scores and support descriptor
+    (vs_score_transforms); ``out`` and ``workspace`` as for score_full."""
     src, dev, _keep = _make_source(logits=logits, temperature=temperature)
     T = src.T
     _ids("targets", targets, T)
@@ -205,17 +246,17 @@ def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, c
         _check_cuda(name, t, {dt}, 1)
         if t.numel() != T or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [T] tensor")
-    out = {
-        "logprob": torch.empty(T, dtype=torch.float32, device=dev),
-        "entropy": torch.empty(T, dtype=torch.float32, device=dev),
-        "status": torch.empty(T, dtype=torch.uint8, device=dev),
-        "support_len": torch.empty(T, dtype=torch.int32, device=dev),
-        "threshold_logit": torch.empty(T, dtype=torch.float32, device=dev),
-        "threshold_ties": torch.empty(T, dtype=torch.int32, device=dev),
-        "support_ids": torch.empty((T, cap), dtype=torch.int64, device=dev) if cap > 0 else None,
-        "full_lse": torch.empty(T, dtype=torch.float32, device=dev) if with_full_lse else None,
-    }
-    ws, n = _workspace(_capi.VS_OP_SCORE_TRANSFORMS, src, dev)
+    out = _outputs({
+        "logprob": ((T,), torch.float32),
+        "entropy": ((T,), torch.float32),
+        "status": ((T,), torch.uint8),
+        "support_len": ((T,), torch.int32),
+        "threshold_logit": ((T,), torch.float32),
+        "threshold_ties": ((T,), torch.int32),
+        "support_ids": ((T, cap), torch.int64) if cap > 0 else None,
+        "full_lse": ((T,), torch.float32) if with_full_lse else None,
+    }, dev, out)
+    ws, n = _workspace(_capi.VS_OP_SCORE_TRANSFORMS, src, dev, given=workspace)
     rc = _lib.vs_score_transforms(ctypes.byref(src), _ptr(top_k), _ptr(top_p), _ptr(min_p), _ptr(targets),
                                   _ptr(out["logprob"]), _ptr(out["entropy"]), _ptr(out["status"]),
                                   _ptr(out["support_len"]), _ptr(out["threshold_logit"]), _ptr(out["threshold_ties"]),
@@ -226,25 +267,26 @@ def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, c
     return out
 
 
-def l1_distance(target_logits, draft_logits):
-    """Per-row softmax L1 distance and accept_rate (vs_l1_distance)."""
+def l1_distance(target_logits, draft_logits, *, out=None):
+    """Per-row softmax L1 distance and accept_rate (vs_l1_distance); ``out`` as
+    for score_full (this call needs no workspace)."""
     _check_cuda("target_logits", target_logits, _DT, 2)
     _check_cuda("draft_logits", draft_logits, _DT, 2)
     if target_logits.shape != draft_logits.shape or target_logits.dtype != draft_logits.dtype:
         raise ValueError("target and draft logits must have the same shape and dtype")
     T, V = target_logits.shape
     dev = target_logits.device
-    l1 = torch.empty(T, dtype=torch.float32, device=dev)
-    acc = torch.empty(T, dtype=torch.float32, device=dev)
+    o = _outputs({"l1": ((T,), torch.float32), "accept_rate": ((T,), torch.float32)}, dev, out)
     src = VsSource()
     src.T, src.V = T, V
-    ws, n = _workspace(_capi.VS_OP_L1_DISTANCE, src, dev)
+    n = workspace_size(_capi.VS_OP_L1_DISTANCE, src, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
     rc = _lib.vs_l1_distance(_ptr(target_logits), _ptr(draft_logits), _DT[target_logits.dtype], T, V,
                              _rowmajor("target_logits", target_logits), _rowmajor("draft_logits", draft_logits),
-                             _ptr(l1), _ptr(acc), _ptr(ws), n, _stream(dev))
+                             _ptr(o["l1"]), _ptr(o["accept_rate"]), _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_l1_distance")
-    return {"l1": l1, "accept_rate": acc}
+    return o
 
 
 def sweep_timer(enable: bool) -> None:
