@@ -68,7 +68,9 @@ enum {
   VS_E_PARAM = 5,       /* a scalar parameter is out of range                  */
   VS_E_WORKSPACE = 6,   /* workspace NULL, misaligned or smaller than needed   */
   VS_E_UNSUPPORTED = 7, /* valid request this version does not implement       */
-  VS_E_DEVICE = 8       /* a HIP launch failed                                 */
+  VS_E_DEVICE = 8,      /* a HIP launch failed                                 */
+  VS_E_SCRATCH = 9      /* the call needs more scratch than the allocation-free
+                           entry point holds (vs_noalloc_scratch_bytes)         */
 };
 
 /* ---- dtypes and source kinds ------------------------------------------- */
@@ -222,6 +224,28 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
 int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T,
                    int64_t V, int64_t ld_target, int64_t ld_draft, float* l1, float* accept_rate,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vs_score_full without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, outputs and row status as vs_score_full,
+ * minus workspace and workspace_bytes; the same kernels and results.  The
+ * scratch the hidden/weight source needs sits in one device array of
+ * vs_noalloc_scratch_bytes() bytes (64 MiB) per GPU, held from the library's
+ * load until the process ends: enough for the per-tile partials of 4096 rows
+ * over a vocabulary of 151,936 (38.9 MB; fp32 hidden states add T * H * 2
+ * bytes).  vs_workspace_size(VS_OP_SCORE_FULL, ...) above that limit returns
+ * VS_E_SCRATCH before anything is enqueued.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  All calls on one GPU
+ * share its array: calls that overlap on one GPU (on two streams, or from two
+ * threads) race and must be ordered by the caller.  Its contents carry over
+ * between calls; nothing in it needs to start at zero.
+ */
+int vs_score_full_noalloc(const vs_source* src, const int64_t* target_ids, int64_t vocab_chunk, float* lse,
+                          float* logprob, float* entropy, uint8_t* row_status, void* stream);
+
+/* Bytes of the allocation-free entry point's scratch array on each GPU. */
+size_t vs_noalloc_scratch_bytes(void);
 
 /* ---- Diagnostics (not part of the scoring contract) -------------------- */
 

@@ -42,7 +42,7 @@ class _Lazy:
 
 _lib = _Lazy()
 
-__all__ = ["score_full", "score_support_ids", "score_transforms", "l1_distance", "workspace_size", "workspace_bytes",
+__all__ = ["score_full", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms", "l1_distance", "workspace_size", "workspace_bytes",
            "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
@@ -203,6 +203,29 @@ def score_full(targets, *, logits=None, hidden=None, weight=None, temperature=1.
     if rc:
         raise VsError(rc, "vs_score_full")
     return o
+
+
+def score_full_noalloc(targets, *, logits=None, hidden=None, weight=None, temperature=1.0, vocab_chunk=8192,
+                       with_entropy=True, with_lse=True, out=None):
+    """score_full through vs_score_full_noalloc: no workspace; the library's
+    per-GPU scratch array serves the hidden/weight source (calls that overlap
+    on one GPU race on it).  With ``out`` the call allocates nothing."""
+    src, dev, _keep = _make_source(logits, hidden, weight, temperature)
+    _ids("targets", targets, src.T)
+    T = src.T
+    o = _outputs({"lse": ((T,), torch.float32) if with_lse else None, "logprob": ((T,), torch.float32),
+                  "entropy": ((T,), torch.float32) if with_entropy else None, "status": ((T,), torch.uint8)},
+                 dev, out)
+    rc = _lib.vs_score_full_noalloc(ctypes.byref(src), _ptr(targets), int(vocab_chunk), _ptr(o["lse"]),
+                                    _ptr(o["logprob"]), _ptr(o["entropy"]), _ptr(o["status"]), _stream(dev))
+    if rc:
+        raise VsError(rc, "vs_score_full_noalloc")
+    return o
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the per-GPU scratch array of score_full_noalloc (vs_noalloc_scratch_bytes)."""
+    return int(_lib.vs_noalloc_scratch_bytes())
 
 
 def score_support_ids(targets, support_ids, *, logits=None, hidden=None, weight=None, temperature=1.0,

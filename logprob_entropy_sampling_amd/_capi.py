@@ -8,7 +8,8 @@ from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_voi
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocabscore.so")
 
-VS_OK, VS_E_NULL, VS_E_SHAPE, VS_E_DTYPE, VS_E_ALIGN, VS_E_PARAM, VS_E_WORKSPACE, VS_E_UNSUPPORTED, VS_E_DEVICE = range(9)
+(VS_OK, VS_E_NULL, VS_E_SHAPE, VS_E_DTYPE, VS_E_ALIGN, VS_E_PARAM, VS_E_WORKSPACE, VS_E_UNSUPPORTED, VS_E_DEVICE,
+ VS_E_SCRATCH) = range(10)
 VS_F32, VS_BF16 = 0, 1
 VS_SRC_LOGITS, VS_SRC_HIDDEN_WEIGHT = 0, 1
 VS_OP_SCORE_FULL, VS_OP_SCORE_SUPPORT, VS_OP_SCORE_TRANSFORMS, VS_OP_L1_DISTANCE = range(4)
@@ -53,6 +54,9 @@ _SIGS = {
                                       c_size_t, c_void_p]),
     "vs_l1_distance": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "vs_score_full_noalloc": (c_int32, [POINTER(VsSource), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
+    "vs_noalloc_scratch_bytes": (c_size_t, []),
     "vs_sweep_timer": (c_int32, [c_int32]),
     "vs_sweep_timer_ms": (c_int32, [POINTER(c_float)]),
 }

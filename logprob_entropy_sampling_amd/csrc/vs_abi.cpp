@@ -149,6 +149,7 @@ const char* vs_status_string(int32_t code) {
     case VS_E_WORKSPACE: return "workspace is NULL, not 256-byte aligned, or smaller than vs_workspace_size()";
     case VS_E_UNSUPPORTED: return "this request is valid but not implemented for this source kind";
     case VS_E_DEVICE: return "a HIP kernel launch failed";
+    case VS_E_SCRATCH: return "the call needs more scratch than vs_score_full_noalloc holds (vs_noalloc_scratch_bytes)";
     default: return "unknown status code";
   }
 }

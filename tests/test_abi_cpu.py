@@ -61,7 +61,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.vs_status_string(code).decode()
         assert s and s != "unknown status code"
     assert lib.vs_status_string(99).decode() == "unknown status code"
@@ -189,3 +189,20 @@ def test_workspace_sizes_scale(lib):
     n = lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(hw), 0)
     assert n >= 4096 * 594 * 16  # one 16-byte partial per (row, 256-wide vocabulary tile)
     assert lib.vs_workspace_size(C.VS_OP_SCORE_FULL, None, 0) == 0
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    from logprob_entropy_sampling_amd import _capi as C
+    assert lib.vs_noalloc_scratch_bytes() == 64 << 20
+
+    def call(src, targets=FAKE, logprob=FAKE):
+        return lib.vs_score_full_noalloc(ctypes.byref(src) if src is not None else None, targets, 8192, FAKE,
+                                         logprob, FAKE, FAKE, None)
+    assert call(None) == C.VS_E_NULL
+    assert call(_src(), targets=None) == C.VS_E_NULL  # a logits source needs no scratch
+    assert call(_src(T=0)) == C.VS_E_SHAPE
+    # the fused source's partials of 32768 rows over 151,936 ids (311 MB) exceed the 64 MiB array
+    big = _src(kind=C.VS_SRC_HIDDEN_WEIGHT, T=32768, H=4096, V=151936, ld_hidden=4096, ld_weight=4096)
+    assert lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(big), 0) > 64 << 20
+    assert call(big) == C.VS_E_SCRATCH
+    assert "scratch" in lib.vs_status_string(C.VS_E_SCRATCH).decode()
