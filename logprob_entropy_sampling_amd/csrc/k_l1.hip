@@ -87,7 +87,7 @@ struct Norm {
   float m, l2s, l;
 };
 constexpr float kBigRef = 0x1p13f;
-// l1 marker of a row the resident kernel leaves to the redo kernel (no L1 is negative)
+// l1 marker of a row the resident kernel redoes in the accurate form after its row loop (no L1 is negative)
 constexpr float kL1Redo = -1.0f;
 
 __device__ __forceinline__ Norm make_norm(float m, float s) {
@@ -255,20 +255,6 @@ __global__ __launch_bounds__(NT) void l1_kernel(const void* __restrict__ tgt, in
   l1_row<DT, NT, U>(tgt, ld_t, dft, ld_d, V, blockIdx.x, l1, accept);
 }
 
-// The rows the resident kernel below marked kL1Redo (maxima past 2^13 in
-// base-2 units), done again by the two-pass form, which takes the accurate
-// exponent form on such rows.  Workgroups stride over the rows; every other
-// row costs one load of its l1 entry.
-template <int NT, int U>
-__global__ __launch_bounds__(NT) void l1_redo_kernel(const void* __restrict__ tgt, int64_t ld_t,
-                                                     const void* __restrict__ dft, int64_t ld_d, int64_t rows,
-                                                     int64_t V, float* __restrict__ l1, float* __restrict__ accept) {
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    if (l1[r] == kL1Redo) l1_row<VS_BF16, NT, U>(tgt, ld_t, dft, ld_d, V, r, l1, accept);
-    __syncthreads();  // the row's last LDS reads come before the next row's writes
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Resident form (bf16 rows, 65,536 < V <= 155,655, 16-byte aligned rows).
 //
@@ -414,7 +400,7 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
   };
   // row r's L1 from the pass-2 partials of buffer b (thread 0); state 0: a
   // non-finite normaliser (NaN), 1: done, 2: the maxima need the accurate
-  // form, left to l1_redo_kernel (the kL1Redo marker)
+  // form, redone after the row loop (the kL1Redo marker until then)
   auto finish = [&](int64_t r, int b, int state) {
     float v = 0.0f;
 #pragma unroll
@@ -433,6 +419,10 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
     for (int j = 0; j < RES_JD; ++j) d[j] = res_load(rd, voff, j);
   }
   int prev_state = 0;
+  // rows this workgroup leaves to the accurate form (state 2): bit k for its
+  // k-th row (k < 64), else the kL1Redo marker in l1 (rows past 64 x grid)
+  uint64_t redo = 0;
+  bool redo_far = false;
   int it = 0;
   for (; row < rows; row += gridDim.x, ++it) {
     const int b = it & 1;
@@ -533,9 +523,26 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
     acc = wave_sum_all(acc);
     if (lane == 0) red_b[b][wave] = acc;  // summed after the next row's barrier
     prev_state = !ok ? 0 : (fabsf(nx.m) < kBigRef && fabsf(ny.m) < kBigRef) ? 1 : 2;
+    if (prev_state == 2) {
+      if (it < 64)
+        redo |= uint64_t(1) << it;
+      else
+        redo_far = true;
+    }
   }
   __syncthreads();
   if (tid == 0 && it > 0) finish(row - gridDim.x, (it - 1) & 1, prev_state);
+  if (redo == 0 && !redo_far) return;  // (the same for every thread of the workgroup)
+  // rows whose maxima passed 2^13: done again here by the two-pass form,
+  // which takes the accurate exponent form on them
+  __syncthreads();  // thread 0's markers are visible to the whole workgroup
+  int k = 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, ++k) {
+    const bool mine = k < 64 ? ((redo >> k) & 1) != 0 : l1[r] == kL1Redo;
+    if (!mine) continue;
+    l1_row<VS_BF16, RES_NT, 4>(tgt, ld_t, dft, ld_d, V, r, l1, accept);
+    __syncthreads();  // this row's last LDS reads come before the next row's writes
+  }
 }
 
 // 256 threads x 8 loads in flight: several rows per CU overlap their passes
@@ -566,9 +573,6 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
     l1_resident_kernel<<<dim3(unsigned(grid)), dim3(RES_NT), 0, s>>>(
         static_cast<const uint16_t*>(target.ptr), target.ld, static_cast<const uint16_t*>(draft.ptr), draft.ld, rows, V,
         l1, accept);
-    const int64_t redo_grid = rows < 512 ? rows : 512;
-    l1_redo_kernel<kL1Threads, kL1Unroll><<<dim3(unsigned(redo_grid)), dim3(kL1Threads), 0, s>>>(
-        target.ptr, target.ld, draft.ptr, draft.ld, rows, V, l1, accept);
     return int(hipGetLastError());
   }
   if (target.dtype == VS_BF16) {
