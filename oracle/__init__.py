@@ -26,10 +26,14 @@ what the method computes, written from these pages:
 
 Pinned by ``tests/test_oracle_*.py`` against closed forms, library routines
 (scipy, torch CPU), brute force on tiny inputs and hand-derived fixtures in
-``tests/golden/``.  The seeded Gumbel sampler that ends the transform program
-is not implemented here (parity unpinned: the pages do not define its RNG).
+``tests/golden/``.  ``sampling`` holds the seeded Gumbel draw that ends the
+transform program; the pages name it without defining its generator, so it
+follows a stated reading (Philox4x32-10 from its published definition, pinned
+by that generator's known-answer vectors, and the Gumbel-max draw, pinned by
+the softmax frequencies it must produce).
 """
 
+from . import sampling  # noqa: F401
 from .scoring import (  # noqa: F401
     ST_OK,
     ST_EMPTY_SUPPORT,
