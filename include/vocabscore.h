@@ -76,7 +76,13 @@ enum {
 /* ---- dtypes and source kinds ------------------------------------------- */
 enum { VS_F32 = 0, VS_BF16 = 1 };
 enum { VS_SRC_LOGITS = 0, VS_SRC_HIDDEN_WEIGHT = 1 };
-enum { VS_OP_SCORE_FULL = 0, VS_OP_SCORE_SUPPORT = 1, VS_OP_SCORE_TRANSFORMS = 2, VS_OP_L1_DISTANCE = 3 };
+enum {
+  VS_OP_SCORE_FULL = 0,
+  VS_OP_SCORE_SUPPORT = 1,
+  VS_OP_SCORE_TRANSFORMS = 2,
+  VS_OP_L1_DISTANCE = 3,
+  VS_OP_SAMPLE_TRANSFORMS = 4
+};
 
 /* ---- per-row status bits (uint8 per row) -------------------------------- */
 #define VS_ROW_EMPTY_SUPPORT 0x01u          /* recorded support has no id >= 0         */
@@ -210,6 +216,32 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
                         float* threshold_logit, int32_t* threshold_ties, int64_t* support_ids_out,
                         int64_t support_ids_cap, float* full_lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * The seeded Gumbel draw that ends the transform program (xorl issue #71,
+ * section 3: temperature -> stable token-id top-k -> inclusive top-p -> min-p
+ * -> seeded Gumbel; the pages name the last stage without defining its
+ * generator).  For every row t: the support S_t of vs_score_transforms, then
+ *   sampled_ids[t] = argmax over v in S_t of (x_v - x_max)/tau - ln(-ln u_v)
+ * (the lower id on equal scores; computed in fp64), with
+ *   u_v = (r_v + 1/2) 2^-32, r_v = word (v mod 4) of Philox4x32-10 (Salmon et
+ *   al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) of the counter
+ *   (v div 4, t, offset mod 2^32, offset div 2^32) under the key
+ *   (seed mod 2^32, seed div 2^32).
+ * A (seed, offset) pair gives a fixed draw on every run; distinct offsets
+ * give independent draws.  Parameters and source rules as for
+ * vs_score_transforms (bf16 logits only).  Outputs:
+ *   sampled_ids [T] int64 (-1 on a BAD_INPUT row)
+ *   row_status, support_len, threshold_logit, threshold_ties  (nullable) the
+ *                row's BAD_INPUT bit and support descriptor.
+ * The support-conditioned logprob and entropy of the drawn tokens come from
+ * vs_score_transforms with target_ids = sampled_ids.  Workspace:
+ * vs_workspace_size(VS_OP_SAMPLE_TRANSFORMS, src, 0).
+ */
+int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float* top_p, const float* min_p,
+                         uint64_t seed, uint64_t offset, int64_t* sampled_ids, uint8_t* row_status,
+                         int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Draft/target softmax L1 distance (DeepSpec PR #87, section Purpose):

@@ -8,6 +8,7 @@ path: importing this package fails if the library has not been built.
     score_full(...)          full-vocabulary LSE / selected logprob / entropy
     score_support_ids(...)   recorded-support logprob / entropy (+ synthetic-EOS fallback)
     score_transforms(...)    top-k / top-p / min-p support scores and descriptor
+    sample_transforms(...)   seeded Gumbel draw from the top-k / top-p / min-p support
     l1_distance(...)         draft/target softmax L1 and accept_rate
 """
 
@@ -42,7 +43,8 @@ class _Lazy:
 
 _lib = _Lazy()
 
-__all__ = ["score_full", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms", "l1_distance", "workspace_size", "workspace_bytes",
+__all__ = ["score_full", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms",
+           "sample_transforms", "l1_distance", "workspace_size", "workspace_bytes",
            "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
@@ -169,7 +171,8 @@ def workspace_bytes(op: str, *, logits=None, hidden=None, weight=None, width: in
     """Bytes of workspace an entry point needs for these inputs (vs_workspace_size);
     op is one of "score_full", "score_support_ids", "score_transforms", "l1_distance"."""
     ops = {"score_full": _capi.VS_OP_SCORE_FULL, "score_support_ids": _capi.VS_OP_SCORE_SUPPORT,
-           "score_transforms": _capi.VS_OP_SCORE_TRANSFORMS, "l1_distance": _capi.VS_OP_L1_DISTANCE}
+           "score_transforms": _capi.VS_OP_SCORE_TRANSFORMS, "l1_distance": _capi.VS_OP_L1_DISTANCE,
+           "sample_transforms": _capi.VS_OP_SAMPLE_TRANSFORMS}
     src, _, _ = _make_source(logits, hidden, weight, 1.0)
     return workspace_size(ops[op], src, width)
 
@@ -288,6 +291,31 @@ def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, c
     if rc:
         raise VsError(rc, "vs_score_transforms")
     return out
+
+
+def sample_transforms(logits, top_k, top_p, min_p, *, seed, offset=0, temperature=1.0, out=None, workspace=None):
+    """Seeded Gumbel draw of one token per row from the top-k / top-p / min-p
+    support (vs_sample_transforms).  Returns ``sampled`` (int64, -1 on a
+    BAD_INPUT row), ``status`` and the support descriptor; ``out`` and
+    ``workspace`` as for score_full."""
+    src, dev, _keep = _make_source(logits=logits, temperature=temperature)
+    T = src.T
+    for name, t, dt in (("top_k", top_k, torch.int32), ("top_p", top_p, torch.float32),
+                        ("min_p", min_p, torch.float32)):
+        _check_cuda(name, t, {dt}, 1)
+        if t.numel() != T or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T] tensor")
+    o = _outputs({"sampled": ((T,), torch.int64), "status": ((T,), torch.uint8),
+                  "support_len": ((T,), torch.int32), "threshold_logit": ((T,), torch.float32),
+                  "threshold_ties": ((T,), torch.int32)}, dev, out)
+    ws, n = _workspace(_capi.VS_OP_SAMPLE_TRANSFORMS, src, dev, given=workspace)
+    rc = _lib.vs_sample_transforms(ctypes.byref(src), _ptr(top_k), _ptr(top_p), _ptr(min_p),
+                                   int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), _ptr(o["sampled"]),
+                                   _ptr(o["status"]), _ptr(o["support_len"]), _ptr(o["threshold_logit"]),
+                                   _ptr(o["threshold_ties"]), _ptr(ws), n, _stream(dev))
+    if rc:
+        raise VsError(rc, "vs_sample_transforms")
+    return o
 
 
 def l1_distance(target_logits, draft_logits, *, out=None):

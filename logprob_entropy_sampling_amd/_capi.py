@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocabscore.so")
 
@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocabsco
  VS_E_SCRATCH) = range(10)
 VS_F32, VS_BF16 = 0, 1
 VS_SRC_LOGITS, VS_SRC_HIDDEN_WEIGHT = 0, 1
-VS_OP_SCORE_FULL, VS_OP_SCORE_SUPPORT, VS_OP_SCORE_TRANSFORMS, VS_OP_L1_DISTANCE = range(4)
+VS_OP_SCORE_FULL, VS_OP_SCORE_SUPPORT, VS_OP_SCORE_TRANSFORMS, VS_OP_L1_DISTANCE, VS_OP_SAMPLE_TRANSFORMS = range(5)
 
 ROW_EMPTY_SUPPORT = 0x01
 ROW_TARGET_OUTSIDE_SUPPORT = 0x02
@@ -52,6 +52,8 @@ _SIGS = {
     "vs_score_transforms": (c_int32, [POINTER(VsSource), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                       c_size_t, c_void_p]),
+    "vs_sample_transforms": (c_int32, [POINTER(VsSource), c_void_p, c_void_p, c_void_p, c_uint64, c_uint64, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "vs_l1_distance": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
     "vs_score_full_noalloc": (c_int32, [POINTER(VsSource), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,

@@ -1,0 +1,275 @@
+// The seeded Gumbel draw that ends the transform program (xorl issue #71,
+// section 3: temperature -> stable token-id top-k -> inclusive top-p -> min-p
+// -> seeded Gumbel).  The pages name the stage without defining its
+// generator; the draw here:
+//   r_v   = word (v mod 4) of Philox4x32-10(counter = (v div 4, row, offset
+//           low, offset high), key = (seed low, seed high)) - the generator of
+//           Salmon, Moraes, Dror and Shaw ("Parallel random numbers: as easy as
+//           1, 2, 3", SC 2011), written from its definition;
+//   u_v   = (r_v + 1/2) 2^-32, strictly inside (0, 1);
+//   draw  = the support token with the largest (x_v - x_max) / tau - ln(-ln u_v)
+//           in fp64, the lower id on equal scores.
+// The support is the transforms' descriptor: every token with x above the
+// threshold logit, and the first threshold_ties tokens (by id) equal to it.
+//
+// One workgroup per row streams the row once.  Every token at or above the
+// threshold is scored (its Philox block computed once per 4 tokens); tokens
+// equal to the threshold are tracked apart.  When the row holds more
+// threshold-equal tokens than the support takes, a second pass ranks them by
+// id (a block scan per round of chunks, ending once the support's ties are
+// passed) and keeps the best of the first threshold_ties.
+#include "common.h"
+#include "launch.h"
+
+namespace vs {
+
+namespace {
+
+constexpr int kSampleThreads = 1024;
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct Ctr {
+  uint32_t c0, c1, c2, c3;
+};
+
+// Ten Philox rounds: words 0 and 2 are multiplied into 64-bit products, the
+// high halves are mixed with words 1 and 3 and the key, the key grows by the
+// Weyl increments after every round.
+__device__ __forceinline__ Ctr philox4x32_10(Ctr c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint64_t p0 = uint64_t(kPhiloxM0) * c.c0;
+    const uint64_t p1 = uint64_t(kPhiloxM1) * c.c2;
+    Ctr n;
+    n.c0 = uint32_t(p1 >> 32) ^ c.c1 ^ k0;
+    n.c1 = uint32_t(p1);
+    n.c2 = uint32_t(p0 >> 32) ^ c.c3 ^ k1;
+    n.c3 = uint32_t(p0);
+    c = n;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return c;
+}
+
+__device__ __forceinline__ uint32_t ctr_word(const Ctr& c, int j) {
+  return j == 0 ? c.c0 : j == 1 ? c.c1 : j == 2 ? c.c2 : c.c3;
+}
+
+struct Best {
+  double s;
+  int64_t id;
+};
+
+__device__ __forceinline__ bool better(const Best& a, const Best& b) { return a.s > b.s || (a.s == b.s && a.id < b.id); }
+
+__device__ __forceinline__ Best wave_best(Best b) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Best o;
+    o.s = __shfl_xor(b.s, off, 64);
+    o.id = __shfl_xor(b.id, off, 64);
+    if (better(o, b)) b = o;
+  }
+  return b;
+}
+
+struct SampleSmem {
+  double best_s[kSampleThreads / 64];
+  int64_t best_id[kSampleThreads / 64];
+  uint32_t wcount[2][kSampleThreads / 64];
+};
+
+// The workgroup's best of every thread's candidate, in every thread.
+__device__ __forceinline__ Best block_best(Best b, SampleSmem& sm) {
+  constexpr int NW = kSampleThreads / 64;
+  b = wave_best(b);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    sm.best_s[w] = b.s;
+    sm.best_id[w] = b.id;
+  }
+  __syncthreads();
+  Best r{sm.best_s[0], sm.best_id[0]};
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    const Best o{sm.best_s[i], sm.best_id[i]};
+    if (better(o, r)) r = o;
+  }
+  return r;
+}
+
+// Exclusive prefix of c over the workgroup's threads and the total (every
+// thread); `buf` alternates between two LDS slots so consecutive calls need
+// one barrier each.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t c, uint32_t& total, SampleSmem& sm, int buf) {
+  constexpr int NW = kSampleThreads / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t inc = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) sm.wcount[buf][w] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t t = sm.wcount[buf][i];
+    before += i < w ? t : 0u;
+    total += t;
+  }
+  return before + inc - c;
+}
+
+// Chunk q of a row: tokens 8q .. 8q+7; past V a NaN, which compares false with
+// any threshold (a -inf threshold included).
+__device__ __forceinline__ void load_chunk(const uint16_t* rowp, bool vec, int64_t q, int V, float* x) {
+  const int64_t v0 = 8 * q;
+  if (vec && v0 + 8 <= V) {
+    const uint4 w = *reinterpret_cast<const uint4*>(rowp + v0);
+    x[0] = bf16_lo(w.x);
+    x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y);
+    x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z);
+    x[5] = bf16_hi(w.z);
+    x[6] = bf16_lo(w.w);
+    x[7] = bf16_hi(w.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = v0 + i < V ? bf16_to_f32(rowp[v0 + i]) : __builtin_nanf("");
+  }
+}
+
+struct DrawArgs {
+  int64_t row;
+  double tau, xmax;
+  uint32_t k0, k1, off_lo, off_hi;
+};
+
+// The Gumbel score of token v from its 32-bit number r.
+__device__ __forceinline__ double gumbel_score(float x, uint32_t r, const DrawArgs& d) {
+  const double u = (double(r) + 0.5) * 0x1p-32;
+  const double g = -log(-log(u));
+  return (double(x) - d.xmax) / d.tau + g;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(
+    const uint16_t* __restrict__ logits, int64_t ld, int V, const float* __restrict__ temp, float temp_scalar,
+    const uint8_t* __restrict__ status, const float* __restrict__ threshold_logit,
+    const int32_t* __restrict__ threshold_ties, const float* __restrict__ row_max, uint64_t seed, uint64_t offset,
+    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status) {
+  __shared__ SampleSmem sm;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0 && out_status) out_status[row] = status[row] & kRowBad;
+  if (status[row] & kRowBad) {
+    if (tid == 0) sampled[row] = -1;
+    return;
+  }
+  DrawArgs d;
+  d.row = row;
+  d.tau = double(temp ? temp[row] : temp_scalar);
+  d.xmax = double(row_max[row]);
+  d.k0 = uint32_t(seed);
+  d.k1 = uint32_t(seed >> 32);
+  d.off_lo = uint32_t(offset);
+  d.off_hi = uint32_t(offset >> 32);
+  const float thr = threshold_logit[row];
+  const uint32_t ties = uint32_t(threshold_ties[row]);
+  const uint16_t* rowp = logits + row * ld;
+  const bool vec = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
+  const int64_t nchunk = (int64_t(V) + 7) / 8;
+
+  // ---- pass 1: every token at or above the threshold ----
+  Best gt{-__builtin_inf(), int64_t(V)}, eq{-__builtin_inf(), int64_t(V)};
+  uint32_t n_eq = 0;
+  for (int64_t q = tid; q < nchunk; q += kSampleThreads) {
+    float x[8];
+    load_chunk(rowp, vec, q, V, x);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) any |= x[4 * b + i] >= thr;
+      if (!any) continue;
+      const Ctr r = philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xv = x[4 * b + i];
+        if (!(xv >= thr)) continue;
+        const Best c{gumbel_score(xv, ctr_word(r, i), d), 8 * q + 4 * b + i};
+        if (xv == thr) {
+          ++n_eq;
+          if (better(c, eq)) eq = c;
+        } else if (better(c, gt)) {
+          gt = c;
+        }
+      }
+    }
+  }
+  uint32_t n_eq_total;
+  (void)block_excl_scan(n_eq, n_eq_total, sm, 0);
+  gt = block_best(gt, sm);
+  if (n_eq_total > ties) {
+    // ---- pass 2: the support takes only the first `ties` threshold-equal tokens by id ----
+    eq = Best{-__builtin_inf(), int64_t(V)};
+    uint32_t base = 0;
+    int buf = 1;
+    for (int64_t q0 = 0; q0 < nchunk && base < ties; q0 += kSampleThreads, buf ^= 1) {
+      const int64_t q = q0 + tid;
+      float x[8];
+      uint32_t m = 0;
+      if (q < nchunk) {
+        load_chunk(rowp, vec, q, V, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m |= (x[i] == thr ? 1u : 0u) << i;
+      }
+      uint32_t total;
+      const uint32_t before = base + block_excl_scan(__builtin_popcount(m), total, sm, buf);
+      if (m) {
+        uint32_t rank = before;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t mb = (m >> (4 * b)) & 0xFu;
+          if (!mb) continue;
+          const Ctr r = philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!((mb >> i) & 1u)) continue;
+            if (rank < ties) {
+              const Best c{gumbel_score(x[4 * b + i], ctr_word(r, i), d), 8 * q + 4 * b + i};
+              if (better(c, eq)) eq = c;
+            }
+            ++rank;
+          }
+        }
+      }
+      base += total;
+    }
+  }
+  eq = block_best(eq, sm);
+  if (tid == 0) sampled[row] = better(eq, gt) ? eq.id : gt.id;
+}
+
+}  // namespace
+
+int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
+                  const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
+                  const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
+                  void* stream) {
+  if (rows <= 0) return 0;
+  sample_kernel<<<dim3(unsigned(rows)), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream)>>>(
+      logits, ld, int(V), temp, temp_scalar, status, threshold_logit, threshold_ties, row_max, seed, offset, sampled,
+      out_status);
+  return int(hipGetLastError());
+}
+
+}  // namespace vs

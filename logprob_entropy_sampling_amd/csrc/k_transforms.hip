@@ -675,6 +675,7 @@ struct RowArgs {
   int64_t* ids_out;
   int cap;
   float* full_lse;
+  float* row_max;  // the row's largest logit (nullable; the sampler's shift)
 };
 
 template <int NTH>
@@ -688,6 +689,7 @@ __device__ void write_bad(const RowArgs& a) {
     if (a.threshold_logit) a.threshold_logit[a.row] = nanf;
     if (a.threshold_ties) a.threshold_ties[a.row] = 0;
     if (a.full_lse) a.full_lse[a.row] = nanf;
+    if (a.row_max) a.row_max[a.row] = nanf;
   }
   if (a.ids_out)
     for (int i = threadIdx.x; i < a.cap; i += NTH) a.ids_out[a.row * a.cap + i] = -1;
@@ -1190,6 +1192,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
     if (a.threshold_logit) a.threshold_logit[a.row] = key_logit(K_L);
     if (a.threshold_ties) a.threshold_ties[a.row] = int32_t(r_L);
     if (a.full_lse) a.full_lse[a.row] = float(xmax / tau + log(total_mass));
+    if (a.row_max) a.row_max[a.row] = key_logit(kmax);
   }
 }
 
@@ -1212,7 +1215,8 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   a.threshold_ties = threshold_ties;                  \
   a.ids_out = ids_out;                                \
   a.cap = cap;                                        \
-  a.full_lse = full_lse;
+  a.full_lse = full_lse;                              \
+  a.row_max = row_max;
 
 #define VS_KERNEL_ARGS                                                                                       \
   const uint16_t *__restrict__ logits, int64_t ld, int V, const float *__restrict__ temp, float temp_scalar, \
@@ -1220,7 +1224,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
       const int64_t *__restrict__ targets, float *__restrict__ logprob, float *__restrict__ entropy,         \
       uint8_t *__restrict__ status, int32_t *__restrict__ support_len, float *__restrict__ threshold_logit,  \
       int32_t *__restrict__ threshold_ties, int64_t *__restrict__ ids_out, int cap,                          \
-      float *__restrict__ full_lse, uint8_t *__restrict__ handoff
+      float *__restrict__ full_lse, float *__restrict__ row_max, uint8_t *__restrict__ handoff
 
 // Packed-counter path: one counting pass into 65536 16-bit counters.  NV > 0
 // keeps the row in registers (NV vectors of 8 tokens per thread); NV == 0
@@ -1634,7 +1638,7 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
                       float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
                       const int64_t* targets, float* logprob, float* entropy, uint8_t* status,
                       int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, int64_t* ids_out,
-                      int64_t cap, float* full_lse, uint8_t* handoff, void* stream) {
+                      int64_t cap, float* full_lse, float* row_max, uint8_t* handoff, void* stream) {
   if (rows <= 0) return 0;
   if (cap > kTransformsMaxCap) return -1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1642,7 +1646,7 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
   const int nv = (vecs + NT - 1) / NT;
 #define VS_ARGS                                                                                  \
   logits, ld, int(V), temp, temp_scalar, top_k, top_p, min_p, targets, logprob, entropy, status, \
-      support_len, threshold_logit, threshold_ties, ids_out, int(cap), full_lse
+      support_len, threshold_logit, threshold_ties, ids_out, int(cap), full_lse, row_max
   if (nv <= 4) transforms_fast_kernel<4><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 10) transforms_fast_kernel<10><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (nv <= 20) transforms_fast_kernel<20><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);

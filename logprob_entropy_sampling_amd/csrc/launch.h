@@ -75,7 +75,15 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
                       float temp_scalar, const int32_t* top_k, const float* top_p, const float* min_p,
                       const int64_t* targets, float* logprob, float* entropy, uint8_t* status,
                       int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, int64_t* ids_out,
-                      int64_t cap, float* full_lse, uint8_t* handoff, void* stream);
+                      int64_t cap, float* full_lse, float* row_max, uint8_t* handoff, void* stream);
+
+// Seeded Gumbel draw over the transforms' support descriptor (status and
+// descriptor from launch_transforms, row_max its largest logit per row);
+// out_status (nullable) gets the BAD_INPUT bit.
+int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
+                  const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
+                  const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
+                  void* stream);
 
 // Draft/target softmax L1.
 int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float* l1, float* accept,

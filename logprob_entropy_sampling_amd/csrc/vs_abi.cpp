@@ -90,6 +90,14 @@ FullWs carve_full(Carver& c, const vs_source* s, int64_t rows) {
   return w;
 }
 
+// the sampler: dummy targets, logprob, status, row maxima, threshold logit and
+// ties (when the caller passes none), then the transforms' own workspace
+size_t sample_ws_bytes(const vs_source* s) {
+  const size_t T = size_t(s->T);
+  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 3 * round_up(T * 4) +
+         round_up(vs::transforms_workspace_bytes(s->T, s->V));
+}
+
 size_t support_ws_bytes(const vs_source* s) {
   return round_up(size_t(s->T) * 4) + round_up(4) + full_ws_bytes(s, s->T);
 }
@@ -162,6 +170,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
     case VS_OP_SCORE_SUPPORT: return support_ws_bytes(src);
     case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T, src->V));
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
+    case VS_OP_SAMPLE_TRANSFORMS: return sample_ws_bytes(src);
     default: return 0;
   }
 }
@@ -236,9 +245,42 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
   rc = vs::launch_transforms(static_cast<const uint16_t*>(src->logits), src->ld_logits, src->T, src->V,
                              src->temperature, src->temperature_scalar, top_k, top_p, min_p, target_ids, logprob,
                              entropy, row_status, support_len, threshold_logit, threshold_ties, support_ids_out,
-                             support_ids_cap, full_lse, static_cast<uint8_t*>(workspace), stream);
+                             support_ids_cap, full_lse, nullptr, static_cast<uint8_t*>(workspace), stream);
   vs::timer_mark(1, stream);
   if (rc == -1) return VS_E_UNSUPPORTED;
+  return rc ? VS_E_DEVICE : VS_OK;
+}
+
+int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float* top_p, const float* min_p,
+                         uint64_t seed, uint64_t offset, int64_t* sampled_ids, uint8_t* row_status,
+                         int32_t* support_len, float* threshold_logit, int32_t* threshold_ties, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int rc = check_source(src);
+  if (rc) return rc;
+  if (src->kind != VS_SRC_LOGITS || src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
+  if (!top_k || !top_p || !min_p || !sampled_ids) return VS_E_NULL;
+  rc = check_workspace(workspace, workspace_bytes, sample_ws_bytes(src));
+  if (rc) return rc;
+  const int64_t T = src->T;
+  Carver c(workspace);
+  int64_t* dummy_targets = static_cast<int64_t*>(c.take(size_t(T) * 8));
+  float* lp = static_cast<float*>(c.take(size_t(T) * 4));
+  uint8_t* st = static_cast<uint8_t*>(c.take(size_t(T)));
+  float* row_max = static_cast<float*>(c.take(size_t(T) * 4));
+  float* thr = threshold_logit ? threshold_logit : static_cast<float*>(c.take(size_t(T) * 4));
+  int32_t* ties = threshold_ties ? threshold_ties : static_cast<int32_t*>(c.take(size_t(T) * 4));
+  uint8_t* tws = static_cast<uint8_t*>(c.take(vs::transforms_workspace_bytes(T, src->V)));
+  // the transforms need a target per row: token 0 (its score is discarded)
+  if (vs::launch_zero_i32(reinterpret_cast<int32_t*>(dummy_targets), 2 * T, stream)) return VS_E_DEVICE;
+  vs::timer_mark(0, stream);
+  const uint16_t* lg = static_cast<const uint16_t*>(src->logits);
+  rc = vs::launch_transforms(lg, src->ld_logits, T, src->V, src->temperature, src->temperature_scalar, top_k, top_p,
+                             min_p, dummy_targets, lp, nullptr, st, support_len, thr, ties, nullptr, 0, nullptr,
+                             row_max, tws, stream);
+  if (rc) return rc == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
+  rc = vs::launch_sample(lg, src->ld_logits, T, src->V, src->temperature, src->temperature_scalar, st, thr, ties,
+                         row_max, seed, offset, sampled_ids, row_status, stream);
+  vs::timer_mark(1, stream);
   return rc ? VS_E_DEVICE : VS_OK;
 }
 

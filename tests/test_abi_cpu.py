@@ -206,3 +206,20 @@ def test_noalloc_rejects_before_any_device_call(lib):
     assert lib.vs_workspace_size(C.VS_OP_SCORE_FULL, ctypes.byref(big), 0) > 64 << 20
     assert call(big) == C.VS_E_SCRATCH
     assert "scratch" in lib.vs_status_string(C.VS_E_SCRATCH).decode()
+
+
+def test_sample_validation(lib):
+    from logprob_entropy_sampling_amd import _capi as C
+
+    def call(src, topk=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
+        return lib.vs_sample_transforms(ctypes.byref(src), topk, FAKE, FAKE, 1, 0, out, None, None, None, None, ws,
+                                        nws, None)
+    assert call(_src(kind=C.VS_SRC_HIDDEN_WEIGHT)) == C.VS_E_UNSUPPORTED
+    assert call(_src(logits_dtype=C.VS_F32)) == C.VS_E_UNSUPPORTED
+    assert call(_src(), topk=None) == C.VS_E_NULL
+    assert call(_src(), out=None) == C.VS_E_NULL
+    assert call(_src(), ws=None) == C.VS_E_WORKSPACE
+    need = lib.vs_workspace_size(C.VS_OP_SAMPLE_TRANSFORMS, ctypes.byref(_src(T=100, V=151936, ld_logits=151936)), 0)
+    t = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS, ctypes.byref(_src(T=100, V=151936, ld_logits=151936)), 0)
+    assert need > t > 0
+    assert call(_src(T=100, V=151936, ld_logits=151936), nws=need - 1) == C.VS_E_WORKSPACE
