@@ -11,8 +11,9 @@ timing starts.
 Prints ONE JSON line.  Besides the contract fields it carries
     roofline      the fused sweep kernel vs bf16 dense MFMA peak (2.5 PFLOP/s)
     cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
-    paths         the other scoring paths, each on its own workload, with an
-                  Infinity-Cache flush between timed calls, vs HBM peak (8 TB/s)
+    paths         the other scoring paths (and the seeded sampler), each on its
+                  own workload, with an Infinity-Cache flush between timed
+                  calls, vs HBM peak (8 TB/s)
 """
 
 from __future__ import annotations
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 METRIC = "scored tokens/sec at V=151,936 (fused LM head); % MFMA / HBM peak"
+SAMPLE_SEED = 20260101  # seed of the transforms workload's sampled targets
 
 
 def _bf16(bits, dev):
@@ -296,9 +298,18 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     c = workloads.make(5)
     T, V = c["T"], c["V"]
     lg, dr = _bf16(c["logits"], dev), _bf16(c["draft"], dev)
-    y = _dev(c["targets"], dev)
     tk, tp, mp, tau = (_dev(c["top_k"], dev), _dev(c["top_p"], dev), _dev(c["min_p"], dev),
                        _dev(c["temperature"], dev))
+    # the seeded Gumbel draw from each row's transformed support: the sampled in-support
+    # target of the transforms workload (drawn once, outside the timed calls), and a path of its own
+    smp = vsa.sample_transforms(lg, tk, tp, mp, temperature=tau, seed=SAMPLE_SEED)
+    y = smp["sampled"].clone()
+    wsp = torch.empty(max(1, vsa.workspace_bytes("sample_transforms", logits=lg)), dtype=torch.uint8, device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.sample_transforms(lg, tk, tp, mp, temperature=tau, seed=SAMPLE_SEED,
+                                                             out=smp, workspace=wsp), steps, warmup, flush)
+    byts = T * V * 2 + T * (4 * 4 + 8 + 4 + 4 + 4 + 1)
+    res["sample_transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, seed=SAMPLE_SEED)
+    del wsp
     o = vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64)
     wsp = torch.empty(max(1, vsa.workspace_bytes("score_transforms", logits=lg)), dtype=torch.uint8, device=dev)
     ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64, out=o,
@@ -306,11 +317,18 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     byts = T * V * 2 + T * (4 * 4 + 8) + T * (4 * 4 + 4 + 1 + 64 * 8 + 4)
     res["transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, support_ids_cap=64)
     if cpu:
+        # (the oracle takes its own inputs: the workload's row-argmax targets, which lie in every
+        # support; a target changes no step of the program's cost)
         res["transforms"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
             lambda r: oracle.score_transforms(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
                                               c["temperature"][r], c["top_k"][r], c["top_p"][r], c["min_p"][r],
                                               c["targets"][r], cap=64), T, cpu_budget_s),
             "transforms_l1 rows (sort, top-k/top-p/min-p, support scores)")
+        res["sample_transforms"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
+            lambda r: oracle.sampling.sample_transforms(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
+                                                        c["temperature"][r], c["top_k"][r], c["top_p"][r],
+                                                        c["min_p"][r], seed=SAMPLE_SEED, rows=r), T, cpu_budget_s),
+            "transforms_l1 rows (support, Philox numbers, Gumbel-max draw)")
     del o, wsp
     o = vsa.l1_distance(lg, dr)
     ev, sw = _event_times(vsa, lambda: vsa.l1_distance(lg, dr, out=o), steps, warmup, flush)
