@@ -20,9 +20,10 @@ what the method computes, written from these pages:
   program name): chunked projection -> log-sum-exp -> sampling support ->
   selected logprob; temperature, then stable token-id top-k, inclusive
   top-p, min-p against the original row max.
-* DeepSpec PR #87 "[Perf] Reuse DSpark probability distance" (section
-  Purpose): per-token L1 distance between draft and target softmaxes and
-  accept_rate = clamp(1 - 0.5 * L1, 0, 1).
+* DeepSpec PR #87 "[Perf] Reuse DSpark probability distance" (sections
+  Purpose and Test Plan): per-token L1 distance between draft and target
+  softmaxes, accept_rate = clamp(1 - 0.5 * L1, 0, 1), and the weighted L1
+  distillation loss with its draft-logit gradient.
 
 Pinned by ``tests/test_oracle_*.py`` against closed forms, library routines
 (scipy, torch CPU), brute force on tiny inputs and hand-derived fixtures in
@@ -50,4 +51,5 @@ from .scoring import (  # noqa: F401
     score_transforms,
     score_prefix_support,
     l1_distance,
+    weighted_l1_loss,
 )

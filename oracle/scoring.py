@@ -485,3 +485,54 @@ def l1_distance(x_target, x_draft) -> dict:
         l1[t] = d
         acc[t] = min(1.0, max(0.0, 1.0 - 0.5 * d))
     return {"l1": l1, "accept_rate": acc}
+
+
+# ---------------------------------------------------------------------------
+# O5: weighted L1 distillation loss and its draft-logit gradient
+# ---------------------------------------------------------------------------
+
+def weighted_l1_loss(x_target, x_draft, weights=None, grad_scale: float = 1.0) -> dict:
+    """The weighted L1 distillation loss built on the shared distance.
+
+    DeepSpec PR #87 (Purpose; Test Plan): the per-token L1 distance, computed
+    once, gives both ``accept_rate = clamp(1 - 0.5 * L1, 0, 1)`` and the
+    weighted L1 loss, whose numerator and denominator are
+    ``num = sum_t w_t L1_t`` and ``den = sum_t w_t``; the loss is
+    ``num / den`` and its gradient flows into the draft logits (the target is
+    a fixed reference).  With ``q = softmax(x_draft)``, ``p =
+    softmax(x_target)`` and ``s_u = sign(q_u - p_u)`` (sign 0 where they are
+    equal, as the subgradient of |.| is taken at 0):
+
+        d L1_t / d x_draft[t, v] = q_v (s_v - sum_u s_u q_u)
+        grad[t, v] = grad_scale * (w_t / den) * q_v (s_v - sum_u s_u q_u)
+
+    Reading where the page is silent: a row of weight 0 adds nothing to num
+    and has zero gradient even when its distance is NaN (a loss mask); a
+    weight must be finite and >= 0.  ``weights`` None means 1 for every row.
+    Returns ``l1``, ``accept_rate`` (per row, as ``l1_distance``), ``num``,
+    ``den``, ``loss`` and ``grad`` (float64 [R, V]).
+    """
+    a = np.asarray(x_target, dtype=np.float64)
+    b = np.asarray(x_draft, dtype=np.float64)
+    R, V = a.shape
+    w = np.ones(R) if weights is None else np.asarray(weights, dtype=np.float64)
+    base = l1_distance(a, b)
+    num = 0.0
+    for t in range(R):
+        if w[t] != 0.0:
+            num += w[t] * base["l1"][t]
+    den = float(np.sum(w))
+    grad = np.zeros((R, V))
+    for t in range(R):
+        if w[t] == 0.0:
+            continue
+        la, lnp, _ = _log_softmax(a[t])
+        lb, lnq, _ = _log_softmax(b[t])
+        if not (np.isfinite(la) and np.isfinite(lb)):
+            grad[t] = np.nan
+            continue
+        p, q = np.exp(lnp), np.exp(lnq)
+        s = np.sign(q - p)
+        grad[t] = grad_scale * (w[t] / den) * q * (s - np.sum(s * q))
+    return {"l1": base["l1"], "accept_rate": base["accept_rate"], "num": num, "den": den,
+            "loss": num / den if den != 0.0 else np.nan, "grad": grad}

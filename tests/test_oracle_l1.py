@@ -80,3 +80,47 @@ def test_ties_at_large_magnitude():
         r = oracle.l1_distance(a, b)
         assert abs(r["l1"][0] - 1.0) < 1e-12, mag
         assert abs(r["accept_rate"][0] - 0.5) < 1e-12
+
+
+def test_weighted_loss_num_den_and_finite_differences():
+    # the loss is sum w L1 / sum w; its draft-logit gradient matches central
+    # differences of that loss (where no p_v - q_v changes sign in the step)
+    rng = np.random.default_rng(11)
+    R, V = 4, 7
+    a = rng.normal(0, 1.5, (R, V))
+    b = a + rng.normal(0, 0.8, (R, V))
+    w = np.array([1.0, 0.5, 0.0, 2.0])
+    r = oracle.weighted_l1_loss(a, b, w, grad_scale=3.0)
+    l1 = oracle.l1_distance(a, b)["l1"]
+    assert abs(r["num"] - float(np.sum(w * l1))) < 1e-14 and r["den"] == 3.5
+    assert abs(r["loss"] - r["num"] / 3.5) < 1e-15
+    h = 1e-6
+    for t in range(R):
+        for v in range(V):
+            bp, bm = b.copy(), b.copy()
+            bp[t, v] += h
+            bm[t, v] -= h
+            fd = 3.0 * (oracle.weighted_l1_loss(a, bp, w)["loss"] - oracle.weighted_l1_loss(a, bm, w)["loss"]) / (2 * h)
+            assert abs(fd - r["grad"][t, v]) < 1e-7, (t, v, fd, r["grad"][t, v])
+    assert (r["grad"][2] == 0).all()  # weight 0: no gradient
+    np.testing.assert_allclose(r["grad"].sum(axis=1), 0.0, atol=1e-15)  # softmax gradients sum to 0
+
+
+def test_weighted_loss_closed_forms():
+    # two tokens: L1 = 2 |sigma(a0 - a1) - sigma(b0 - b1)|, and dL1/db0 = 2 sign(q0 - p0) q0 (1 - q0)
+    a, b = np.array([[0.3, -0.4]]), np.array([[1.1, 0.2]])
+    r = oracle.weighted_l1_loss(a, b)
+    p0 = 1.0 / (1.0 + math.exp(-(0.3 + 0.4)))
+    q0 = 1.0 / (1.0 + math.exp(-(1.1 - 0.2)))
+    assert abs(r["loss"] - 2 * abs(q0 - p0)) < 1e-14
+    assert abs(r["grad"][0, 0] - 2 * np.sign(q0 - p0) * q0 * (1 - q0)) < 1e-14
+    assert abs(r["grad"][0, 1] + r["grad"][0, 0]) < 1e-15
+    # identical rows: zero distance and exactly zero gradient (every sign is 0)
+    x = np.random.default_rng(2).normal(0, 2, (3, 50))
+    z = oracle.weighted_l1_loss(x, x.copy())
+    assert z["loss"] == 0.0 and (z["grad"] == 0.0).all()
+    # a masked NaN row adds nothing
+    y = x.copy()
+    y[1, 4] = np.nan
+    m = oracle.weighted_l1_loss(x, y, [1.0, 0.0, 1.0])
+    assert np.isnan(m["l1"][1]) and np.isfinite(m["loss"]) and (m["grad"][1] == 0).all()
