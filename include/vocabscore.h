@@ -81,7 +81,8 @@ enum {
   VS_OP_SCORE_SUPPORT = 1,
   VS_OP_SCORE_TRANSFORMS = 2,
   VS_OP_L1_DISTANCE = 3,
-  VS_OP_SAMPLE_TRANSFORMS = 4
+  VS_OP_SAMPLE_TRANSFORMS = 4,
+  VS_OP_L1_LOSS = 5
 };
 
 /* ---- per-row status bits (uint8 per row) -------------------------------- */
@@ -278,6 +279,34 @@ int vs_score_full_noalloc(const vs_source* src, const int64_t* target_ids, int64
 
 /* Bytes of the allocation-free entry point's scratch array on each GPU. */
 size_t vs_noalloc_scratch_bytes(void);
+
+/*
+ * The weighted L1 distillation loss on the shared distance, and its gradient
+ * with respect to the draft logits (DeepSpec PR #87, Purpose: the per-token
+ * distance is computed once and reused for accept_rate and for the weighted
+ * L1 loss; Test Plan: its numerator, denominator and draft-logit gradients):
+ *   l1[t], accept_rate[t]   as vs_l1_distance
+ *   loss[0] = num = sum_t w_t l1[t] over rows with w_t != 0
+ *   loss[1] = den = sum_t w_t,   loss[2] = num / den          (device, fp32)
+ *   grad_draft[t, v] = grad_scale * (w_t / den) * q_v (s_v - sum_u s_u q_u),
+ *     p = softmax(target[t]), q = softmax(draft[t]), s = sign(q - p) (0 where
+ *     equal): the gradient of grad_scale * loss[2].  The target is a fixed
+ *     reference (no gradient).
+ * A row of weight 0 adds nothing to num and gets a zero gradient row, even if
+ * its distance is NaN (a loss mask); a row whose target or draft LSE is not
+ * finite and whose weight is not 0 makes num, the loss and its gradient row
+ * NaN.  Weights are read as given (finite and >= 0 is the caller's part).
+ *   target_logits, draft_logits, dtype, T, V, ld_*   as vs_l1_distance
+ *   weights     [T] fp32, nullable (every weight 1)
+ *   grad_draft  [T, ld_grad] of grad_dtype (VS_F32 or VS_BF16, the latter
+ *               rounded to nearest even), nullable: no gradient computed
+ *   accept_rate nullable; l1 and loss required.
+ * Workspace: vs_workspace_size(VS_OP_L1_LOSS, src with T, 0) bytes.
+ */
+int vs_l1_loss(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T, int64_t V,
+               int64_t ld_target, int64_t ld_draft, const float* weights, float grad_scale, float* l1,
+               float* accept_rate, float* loss, void* grad_draft, int32_t grad_dtype, int64_t ld_grad,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Diagnostics (not part of the scoring contract) -------------------- */
 

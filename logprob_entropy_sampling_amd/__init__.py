@@ -10,6 +10,7 @@ path: importing this package fails if the library has not been built.
     score_transforms(...)    top-k / top-p / min-p support scores and descriptor
     sample_transforms(...)   seeded Gumbel draw from the top-k / top-p / min-p support
     l1_distance(...)         draft/target softmax L1 and accept_rate
+    l1_loss(...)             weighted L1 distillation loss and its draft-logit gradient
 """
 
 from __future__ import annotations
@@ -44,7 +45,7 @@ class _Lazy:
 _lib = _Lazy()
 
 __all__ = ["score_full", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms",
-           "sample_transforms", "l1_distance", "workspace_size", "workspace_bytes",
+           "sample_transforms", "l1_distance", "l1_loss", "workspace_size", "workspace_bytes",
            "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
@@ -337,6 +338,38 @@ def l1_distance(target_logits, draft_logits, *, out=None):
                              _ptr(o["l1"]), _ptr(o["accept_rate"]), _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_l1_distance")
+    return o
+
+
+def l1_loss(target_logits, draft_logits, *, weights=None, grad_scale=1.0, with_grad=True, grad_dtype=None,
+            out=None, workspace=None):
+    """Weighted L1 distillation loss and its draft-logit gradient (vs_l1_loss).
+
+    Returns ``l1``, ``accept_rate``, ``loss`` (a [3] tensor: num, den,
+    num / den) and ``grad`` (the gradient of grad_scale * loss with respect to
+    the draft logits, in ``grad_dtype``, default the logits' dtype)."""
+    _check_cuda("target_logits", target_logits, _DT, 2)
+    _check_cuda("draft_logits", draft_logits, _DT, 2)
+    if target_logits.shape != draft_logits.shape or target_logits.dtype != draft_logits.dtype:
+        raise ValueError("target and draft logits must have the same shape and dtype")
+    T, V = target_logits.shape
+    dev = target_logits.device
+    if weights is not None:
+        _check_cuda("weights", weights, {torch.float32}, 1)
+        if weights.numel() != T or not weights.is_contiguous():
+            raise ValueError("weights must be a contiguous [T] float32 tensor")
+    gdt = grad_dtype or draft_logits.dtype
+    o = _outputs({"l1": ((T,), torch.float32), "accept_rate": ((T,), torch.float32), "loss": ((3,), torch.float32),
+                  "grad": ((T, V), gdt) if with_grad else None}, dev, out)
+    src = VsSource()
+    src.T, src.V = T, V
+    ws, n = _workspace(_capi.VS_OP_L1_LOSS, src, dev, given=workspace)
+    rc = _lib.vs_l1_loss(_ptr(target_logits), _ptr(draft_logits), _DT[target_logits.dtype], T, V,
+                         _rowmajor("target_logits", target_logits), _rowmajor("draft_logits", draft_logits),
+                         _ptr(weights), float(grad_scale), _ptr(o["l1"]), _ptr(o["accept_rate"]), _ptr(o["loss"]),
+                         _ptr(o["grad"]), _DT[gdt], V if with_grad else 0, _ptr(ws), n, _stream(dev))
+    if rc:
+        raise VsError(rc, "vs_l1_loss")
     return o
 
 

@@ -551,6 +551,311 @@ __global__ __launch_bounds__(RES_NT) void l1_resident_kernel(const uint16_t* __r
 constexpr int kL1Threads = 256;
 constexpr int kL1Unroll = 8;
 
+// ---------------------------------------------------------------------------
+// The weighted L1 distillation loss and its draft-logit gradient (DeepSpec PR
+// #87, Purpose and Test Plan: the distance is computed once and feeds both
+// accept_rate and the weighted L1 loss num / den, num = sum_t w_t L1_t,
+// den = sum_t w_t; the loss's gradient goes to the draft logits):
+//   d L1_t / d b_v = q_v (s_v - S_t),  s_v = sign(q_v - p_v),  S_t = sum_u s_u q_u.
+// l1_stats_kernel: one workgroup per row, two passes (the L1 kernel's), the
+//   second also sums S_t; writes l1, accept and the row's normalisers and S_t.
+// l1_loss_kernel: one workgroup, num and den in a fixed order.
+// l1_grad_kernel: one workgroup per row, one pass: recomputes p_v, q_v and
+//   their sign with the same instructions as the stats pass, and writes
+//   grad_scale (w_t / den) q_v (s_v - S_t).
+// A row of weight 0 adds nothing to num and gets a zero gradient (a loss
+// mask), even if its distance is NaN.
+// ---------------------------------------------------------------------------
+constexpr int kLossThreads = 256;
+constexpr int kLossUnroll = 8;
+
+struct RowStats {
+  float mx, l2sx, my, l2sy, S;  // normalisers of both rows (base 2), sum s q; mx = NaN on a bad row
+};
+
+template <bool ACC>
+__device__ __forceinline__ void pq_pair(float a, float b, const Norm& x, const Norm& y, float l2e, float& p, float& q) {
+  if (ACC) {
+    p = exp2_hw(__builtin_fmaf(a, l2e, -x.m) - x.l2s);
+    q = exp2_hw(__builtin_fmaf(b, l2e, -y.m) - y.l2s);
+  } else {
+    p = exp2_hw(__builtin_fmaf(a, l2e, -x.l));
+    q = exp2_hw(__builtin_fmaf(b, l2e, -y.l));
+  }
+}
+__device__ __forceinline__ float sgn(float d) { return d > 0.0f ? 1.0f : d < 0.0f ? -1.0f : 0.0f; }
+
+// Calls f(a, b, n) on this thread's share of a row pair: U 16-byte chunks per
+// step in flight (n = VEC values each), then the remaining chunks, then the
+// scalar tail (n = 1).
+template <int DT, int NT, int U, class F>
+__device__ __forceinline__ void row_pairs(const char* trow, const char* drow, int64_t nvec, int64_t V, F f) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  const int tid = threadIdx.x;
+  int64_t q = tid;
+  for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+    float a[U][VEC], b[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_chunk<DT>(trow, q + u * NT, a[u]);
+      load_chunk<DT>(drow, q + u * NT, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(a[u], b[u], VEC);
+  }
+  for (; q < nvec; q += NT) {
+    float a[VEC], b[VEC];
+    load_chunk<DT>(trow, q, a);
+    load_chunk<DT>(drow, q, b);
+    f(a, b, VEC);
+  }
+  for (int64_t i = nvec * VEC + tid; i < V; i += NT) {
+    float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
+    f(&a, &b, 1);
+  }
+}
+
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void l1_stats_kernel(const void* __restrict__ tgt, int64_t ld_t,
+                                                      const void* __restrict__ dft, int64_t ld_d, int64_t V,
+                                                      float* __restrict__ l1, float* __restrict__ accept,
+                                                      RowStats* __restrict__ stats) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int NW = NT / 64;
+  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
+  __shared__ float red[NW][4];
+  __shared__ float fin[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
+  const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
+  const int64_t nvec = vec_ok ? V / VEC : 0;
+
+  // ---- pass 1: online max / sum-exp of both rows ----
+  float mx = kNegInf, sx = 0.0f, my = kNegInf, sy = 0.0f;
+  row_pairs<DT, NT, U>(trow, drow, nvec, V, [&](const float* a, const float* b, int n) {
+    online(mx, sx, a, n, l2e);
+    online(my, sy, b, n, l2e);
+  });
+  Part px = wave_merge_to_lane0(Part{mx * l2e, sx, 0.0f});
+  Part py = wave_merge_to_lane0(Part{my * l2e, sy, 0.0f});
+  if ((tid & 63) == 0) {
+    red[tid >> 6][0] = px.m;
+    red[tid >> 6][1] = px.s;
+    red[tid >> 6][2] = py.m;
+    red[tid >> 6][3] = py.s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    Part qx{kNegInf, 0.0f, 0.0f}, qy{kNegInf, 0.0f, 0.0f};
+    if (tid < NW) {
+      qx = Part{red[tid][0], red[tid][1], 0.0f};
+      qy = Part{red[tid][2], red[tid][3], 0.0f};
+    }
+    qx = wave_merge_to_lane0(qx);
+    qy = wave_merge_to_lane0(qy);
+    if (tid == 0) {
+      fin[0] = qx.m;
+      fin[1] = qx.s;
+      fin[2] = qy.m;
+      fin[3] = qy.s;
+    }
+  }
+  __syncthreads();
+  const Norm nx = make_norm(fin[0], fin[1]), ny = make_norm(fin[2], fin[3]);
+  if (!(norm_ok(nx) && norm_ok(ny))) {
+    if (tid == 0) {
+      const float nan = __builtin_nanf("");
+      l1[row] = nan;
+      if (accept) accept[row] = nan;
+      stats[row] = RowStats{nan, nan, nan, nan, nan};
+    }
+    return;
+  }
+
+  // ---- pass 2: sum |p - q| and sum sign(q - p) q ----
+  float d1 = 0.0f, ds = 0.0f;
+  auto pass2 = [&](auto acc_form) {
+    constexpr bool ACC = decltype(acc_form)::value;
+    row_pairs<DT, NT, U>(trow, drow, nvec, V, [&](const float* a, const float* b, int n) {
+      for (int i = 0; i < n; ++i) {
+        float pp, qq;
+        pq_pair<ACC>(a[i], b[i], nx, ny, l2e, pp, qq);
+        d1 += fabsf(pp - qq);
+        ds = __builtin_fmaf(sgn(qq - pp), qq, ds);
+      }
+    });
+  };
+  if (norms_big(nx, ny))
+    pass2(std::true_type{});
+  else
+    pass2(std::false_type{});
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o1 = shfl_down_f(d1, off), o2 = shfl_down_f(ds, off);
+    if ((tid & ((off << 1) - 1)) == 0) {
+      d1 += o1;
+      ds += o2;
+    }
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    red[tid >> 6][0] = d1;
+    red[tid >> 6][1] = ds;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = 0.0f, S = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      v += red[w][0];
+      S += red[w][1];
+    }
+    const float d = fminf(fmaxf(v, 0.0f), 2.0f);
+    l1[row] = d;
+    if (accept) accept[row] = fminf(fmaxf(1.0f - 0.5f * d, 0.0f), 1.0f);
+    stats[row] = RowStats{nx.m, nx.l2s, ny.m, ny.l2s, S};
+  }
+}
+
+// num = sum_t w_t l1_t over rows of nonzero weight, den = sum_t w_t: thread i
+// takes rows i, i + 256, ... in order, then a fixed tree.  out = {num, den, num / den}.
+__global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(const float* __restrict__ l1,
+                                                               const float* __restrict__ weights, int64_t rows,
+                                                               float* __restrict__ out) {
+  __shared__ float sn[kLossThreads], sd[kLossThreads];
+  const int tid = threadIdx.x;
+  float n = 0.0f, d = 0.0f;
+  for (int64_t t = tid; t < rows; t += kLossThreads) {
+    const float w = weights ? weights[t] : 1.0f;
+    if (w != 0.0f) n = __builtin_fmaf(w, l1[t], n);
+    d += w;
+  }
+  sn[tid] = n;
+  sd[tid] = d;
+  __syncthreads();
+  for (int h = kLossThreads / 2; h > 0; h >>= 1) {
+    if (tid < h) {
+      sn[tid] += sn[tid + h];
+      sd[tid] += sd[tid + h];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out[0] = sn[0];
+    out[1] = sd[0];
+    out[2] = sn[0] / sd[0];
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  // round to nearest even (NaN kept quiet)
+  const uint32_t u = __float_as_uint(v);
+  return (v != v) ? ((u >> 16) | 0x40u) : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int GDT>
+__device__ __forceinline__ void store_one(void* g, int64_t i, float v) {
+  if (GDT == VS_BF16)
+    static_cast<uint16_t*>(g)[i] = uint16_t(bf16_rne(v));
+  else
+    static_cast<float*>(g)[i] = v;
+}
+
+// n gradient values of consecutive elements starting at element i (16-byte
+// aligned when n > 1)
+template <int GDT>
+__device__ __forceinline__ void store_run(void* g, int64_t i, const float* v, int n) {
+  if (n == 8 && GDT == VS_BF16) {
+    uint4 w;
+    w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+    w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+    w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g) + i) = w;
+  } else if (n % 4 == 0 && GDT == VS_F32) {
+    for (int k = 0; k < n; k += 4)
+      *reinterpret_cast<float4*>(static_cast<float*>(g) + i + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  } else {
+    for (int k = 0; k < n; ++k) store_one<GDT>(g, i + k, v[k]);
+  }
+}
+
+template <int DT, int GDT, int NT>
+__global__ __launch_bounds__(NT) void l1_grad_kernel(const void* __restrict__ tgt, int64_t ld_t,
+                                                     const void* __restrict__ dft, int64_t ld_d, int64_t V,
+                                                     const float* __restrict__ weights, float grad_scale,
+                                                     const RowStats* __restrict__ stats,
+                                                     const float* __restrict__ loss_out, void* __restrict__ grad,
+                                                     int64_t ld_g) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int GS = GDT == VS_BF16 ? 2 : 4;
+  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float w = weights ? weights[row] : 1.0f;
+  const RowStats st = stats[row];
+  const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
+  const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
+  const int64_t g0 = row * ld_g;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow) |
+                        (reinterpret_cast<uintptr_t>(grad) + uintptr_t(g0) * GS)) & 15) == 0;
+  const int64_t nvec = vec_ok ? V / VEC : 0;
+  if (w == 0.0f || !(st.mx == st.mx)) {  // masked row: zeros; a bad row: NaN
+    const float v = w == 0.0f ? 0.0f : __builtin_nanf("");
+    for (int64_t i = tid; i < V; i += NT) store_one<GDT>(grad, g0 + i, v);
+    return;
+  }
+  const float scale = grad_scale * (w / loss_out[1]);
+  const Norm nx{st.mx, st.l2sx, st.mx + st.l2sx}, ny{st.my, st.l2sy, st.my + st.l2sy};
+  auto run = [&](auto acc_form) {
+    constexpr bool ACC = decltype(acc_form)::value;
+    auto grads = [&](const float* a, const float* b, int n, float* g) {
+      for (int i = 0; i < n; ++i) {
+        float pp, qq;
+        pq_pair<ACC>(a[i], b[i], nx, ny, l2e, pp, qq);
+        g[i] = scale * (qq * (sgn(qq - pp) - st.S));
+      }
+    };
+    int64_t q = tid;
+    constexpr int U = 4;
+    for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+      float a[U][VEC], b[U][VEC];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        load_chunk<DT>(trow, q + u * NT, a[u]);
+        load_chunk<DT>(drow, q + u * NT, b[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float g[VEC];
+        grads(a[u], b[u], VEC, g);
+        store_run<GDT>(grad, g0 + (q + u * NT) * VEC, g, VEC);
+      }
+    }
+    for (; q < nvec; q += NT) {
+      float a[VEC], b[VEC], g[VEC];
+      load_chunk<DT>(trow, q, a);
+      load_chunk<DT>(drow, q, b);
+      grads(a, b, VEC, g);
+      store_run<GDT>(grad, g0 + q * VEC, g, VEC);
+    }
+    for (int64_t i = nvec * VEC + tid; i < V; i += NT) {
+      const float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
+      float g;
+      grads(&a, &b, 1, &g);
+      store_one<GDT>(grad, g0 + i, g);
+    }
+  };
+  if (norms_big(nx, ny))
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+}
+
 }  // namespace
 
 size_t l1_workspace_bytes(int64_t rows, int64_t V) {
@@ -581,6 +886,43 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
   } else {
     l1_kernel<VS_F32, kL1Threads, kL1Unroll><<<dim3(unsigned(rows)), dim3(kL1Threads), 0, s>>>(
         target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept);
+  }
+  return int(hipGetLastError());
+}
+
+size_t l1_loss_workspace_bytes(int64_t rows) { return size_t(rows) * sizeof(RowStats) + 256 + 16; }
+
+int launch_l1_loss(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, const float* weights,
+                   float grad_scale, float* l1, float* accept, float* loss_out, void* grad, int grad_dtype,
+                   int64_t ld_grad, void* workspace, void* stream) {
+  if (rows <= 0) return 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RowStats* stats = static_cast<RowStats*>(workspace);
+  if (target.dtype == VS_BF16)
+    l1_stats_kernel<VS_BF16, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
+        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
+  else
+    l1_stats_kernel<VS_F32, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
+        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
+  l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, weights, rows, loss_out);
+  if (grad) {
+    const dim3 g{unsigned(rows)}, b{unsigned(kLossThreads)};
+    if (target.dtype == VS_BF16 && grad_dtype == VS_BF16)
+      l1_grad_kernel<VS_BF16, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                     weights, grad_scale, stats, loss_out, grad,
+                                                                     ld_grad);
+    else if (target.dtype == VS_BF16)
+      l1_grad_kernel<VS_BF16, VS_F32, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                    weights, grad_scale, stats, loss_out, grad,
+                                                                    ld_grad);
+    else if (grad_dtype == VS_BF16)
+      l1_grad_kernel<VS_F32, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                    weights, grad_scale, stats, loss_out, grad,
+                                                                    ld_grad);
+    else
+      l1_grad_kernel<VS_F32, VS_F32, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                   weights, grad_scale, stats, loss_out, grad,
+                                                                   ld_grad);
   }
   return int(hipGetLastError());
 }

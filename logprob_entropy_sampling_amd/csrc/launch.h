@@ -94,6 +94,14 @@ size_t l1_workspace_bytes(int64_t rows, int64_t V);
 // hipError_t value.
 int device_cu_count(int* ncu);
 
+// Weighted L1 distillation loss: per-row l1 / accept, loss_out = {num, den,
+// num / den}, and (grad non-NULL) the draft-logit gradient [rows, ld_grad] of
+// grad_dtype.  Workspace: l1_loss_workspace_bytes(rows).
+size_t l1_loss_workspace_bytes(int64_t rows);
+int launch_l1_loss(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, const float* weights,
+                   float grad_scale, float* l1, float* accept, float* loss_out, void* grad, int grad_dtype,
+                   int64_t ld_grad, void* workspace, void* stream);
+
 // Timing bracket around the sweep kernel(s) of each call (diagnostics).
 // timer_enable returns 0 or 1 (event creation failed); timer_read_ms returns
 // 0, 1 (HIP error) or 2 (no bracket recorded since enabling).

@@ -171,6 +171,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
     case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T, src->V));
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
     case VS_OP_SAMPLE_TRANSFORMS: return sample_ws_bytes(src);
+    case VS_OP_L1_LOSS: return round_up(vs::l1_loss_workspace_bytes(src->T));
     default: return 0;
   }
 }
@@ -298,6 +299,27 @@ int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t 
                      V, l1, accept_rate, workspace, stream);
   vs::timer_mark(1, stream);
   if (rc == -1) return VS_E_UNSUPPORTED;
+  return rc ? VS_E_DEVICE : VS_OK;
+}
+
+int vs_l1_loss(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T, int64_t V,
+               int64_t ld_target, int64_t ld_draft, const float* weights, float grad_scale, float* l1,
+               float* accept_rate, float* loss, void* grad_draft, int32_t grad_dtype, int64_t ld_grad,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !l1 || !loss) return VS_E_NULL;
+  if (!dtype_ok(dtype) || (grad_draft && !dtype_ok(grad_dtype))) return VS_E_DTYPE;
+  if (T < 1 || T > kMaxDim || V < 1 || V > kMaxDim || ld_target < V || ld_draft < V) return VS_E_SHAPE;
+  if (grad_draft && ld_grad < V) return VS_E_SHAPE;
+  if (!aligned(target_logits, esize(dtype)) || !aligned(draft_logits, esize(dtype))) return VS_E_ALIGN;
+  if (grad_draft && !aligned(grad_draft, esize(grad_dtype))) return VS_E_ALIGN;
+  if (!std::isfinite(grad_scale)) return VS_E_PARAM;
+  int rc = check_workspace(workspace, workspace_bytes, round_up(vs::l1_loss_workspace_bytes(T)));
+  if (rc) return rc;
+  vs::timer_mark(0, stream);
+  rc = vs::launch_l1_loss(vs::LogitsArg{target_logits, dtype, ld_target}, vs::LogitsArg{draft_logits, dtype, ld_draft},
+                          T, V, weights, grad_scale, l1, accept_rate, loss, grad_draft, grad_dtype, ld_grad, workspace,
+                          stream);
+  vs::timer_mark(1, stream);
   return rc ? VS_E_DEVICE : VS_OK;
 }
 

@@ -223,3 +223,19 @@ def test_sample_validation(lib):
     t = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS, ctypes.byref(_src(T=100, V=151936, ld_logits=151936)), 0)
     assert need > t > 0
     assert call(_src(T=100, V=151936, ld_logits=151936), nws=need - 1) == C.VS_E_WORKSPACE
+
+
+def test_l1_loss_validation(lib):
+    from logprob_entropy_sampling_amd import _capi as C
+
+    def call(t=FAKE, d=FAKE, dt=C.VS_BF16, T=4, V=100, l1=FAKE, loss=FAKE, grad=FAKE, gdt=C.VS_F32, ldg=100,
+             scale=1.0, ws=FAKE, nws=1 << 40):
+        return lib.vs_l1_loss(t, d, dt, T, V, V, V, None, scale, l1, None, loss, grad, gdt, ldg, ws, nws, None)
+    assert call(loss=None) == C.VS_E_NULL
+    assert call(l1=None) == C.VS_E_NULL
+    assert call(gdt=7) == C.VS_E_DTYPE
+    assert call(ldg=99) == C.VS_E_SHAPE
+    assert call(grad=FAKE + 2) == C.VS_E_ALIGN
+    assert call(scale=float("inf")) == C.VS_E_PARAM
+    assert call(ws=None) == C.VS_E_WORKSPACE
+    assert call(grad=None, ldg=0, gdt=7, ws=None) == C.VS_E_WORKSPACE  # no gradient: its dtype is not read
