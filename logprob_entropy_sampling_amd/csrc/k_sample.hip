@@ -13,11 +13,15 @@
 // threshold logit, and the first threshold_ties tokens (by id) equal to it.
 //
 // One workgroup per row streams the row once.  Every token at or above the
-// threshold is scored (its Philox block computed once per 4 tokens); tokens
-// equal to the threshold are tracked apart.  When the row holds more
+// threshold gets an fp32 score with a bound on its error (its Philox block
+// computed once per 4 tokens); each thread keeps its two best by the upper
+// end of that interval, so the fp64 score - the decision - is taken only for
+// the few tokens that can still be the best, without divergent fp64 work in
+// the loop.  Tokens equal to the threshold are tracked apart.  When the row holds more
 // threshold-equal tokens than the support takes, a second pass ranks them by
-// id (a block scan per round of chunks, ending once the support's ties are
-// passed) and keeps the best of the first threshold_ties.
+// id and keeps the best of the first threshold_ties: rows of up to 163,840
+// tokens rank them from per-chunk tie counts kept in LDS during the first
+// pass (one scan), longer rows by a block scan per round of chunks.
 #include "common.h"
 #include "launch.h"
 
@@ -77,10 +81,15 @@ __device__ __forceinline__ Best wave_best(Best b) {
   return b;
 }
 
+// Rows of up to kLdsChunks 8-token chunks keep one tie count per chunk in LDS
+// (then an exclusive scan in place): V <= 163,840.
+constexpr int kLdsChunks = 20480;
+
 struct SampleSmem {
   double best_s[kSampleThreads / 64];
   int64_t best_id[kSampleThreads / 64];
   uint32_t wcount[2][kSampleThreads / 64];
+  uint32_t chunk_ties[kLdsChunks];
 };
 
 // The workgroup's best of every thread's candidate, in every thread.
@@ -151,14 +160,79 @@ __device__ __forceinline__ void load_chunk(const uint16_t* rowp, bool vec, int64
 struct DrawArgs {
   int64_t row;
   double tau, xmax;
+  float xmaxf, inv_tau;
   uint32_t k0, k1, off_lo, off_hi;
 };
 
-// The Gumbel score of token v from its 32-bit number r.
+// The Gumbel score of token v from its 32-bit number r, in fp64: the decision.
 __device__ __forceinline__ double gumbel_score(float x, uint32_t r, const DrawArgs& d) {
   const double u = (double(r) + 0.5) * 0x1p-32;
   const double g = -log(-log(u));
   return (double(x) - d.xmax) / d.tau + g;
+}
+
+// The same score in fp32, and a bound on its distance from the fp64 one.
+// -ln u: from u rounded to 24 bits, which moves -ln u by at most 2^-14 of its
+// value while u < 1 - 2^-10; above that, from the series eps + eps^2/2 +
+// eps^3/3 in eps = 1 - u, exact in fp32 there (truncation below 2^-30
+// relative).  With two fp32 logarithms and the product, the score is off by
+// less than 2^-21 |dz| + 1e-4; the bound returned, 2^-18 |dz| + 1e-3, has a
+// wide margin.
+__device__ __forceinline__ float score32(float x, uint32_t r, const DrawArgs& d, float& err) {
+  float e;
+  if (r >= 0xFFC00000u) {
+    const float eps = (float(0xFFFFFFFFu - r) + 0.5f) * 0x1p-32f;
+    e = eps * (1.0f + eps * (0.5f + eps * (1.0f / 3.0f)));
+  } else {
+    e = -kLn2 * log2_hw((float(r) + 0.5f) * 0x1p-32f);
+  }
+  const float g = -kLn2 * log2_hw(e);
+  const float dz = (x - d.xmaxf) * d.inv_tau;
+  err = 0x1p-18f * fabsf(dz) + 1e-3f;
+  return dz + g;
+}
+
+// A thread's two best tokens of one category by the upper end of their fp32
+// score intervals (lower id first on equal ends), the largest upper end of
+// every other token, and the largest lower end of all.  The true best token
+// of a category has its upper end at or above every lower end, so it is among
+// the tokens whose upper end reaches the workgroup's largest lower end.
+struct Top2 {
+  float hi1, hi2, b3, max_lo;
+  float x1, x2;
+  uint32_t r1, r2;
+  int64_t id1, id2;
+};
+__device__ __forceinline__ Top2 top2_empty(int V) {
+  const float ni = -__builtin_inff();
+  return Top2{ni, ni, ni, ni, 0.0f, 0.0f, 0u, 0u, int64_t(V), int64_t(V)};
+}
+__device__ __forceinline__ void top2_add(Top2& t, float s, float err, float x, uint32_t r, int64_t id) {
+  const float hi = s + err;
+  t.max_lo = fmaxf(t.max_lo, s - err);
+  if (hi > t.hi1 || (hi == t.hi1 && id < t.id1)) {
+    t.b3 = fmaxf(t.b3, t.hi2);
+    t.hi2 = t.hi1, t.x2 = t.x1, t.r2 = t.r1, t.id2 = t.id1;
+    t.hi1 = hi, t.x1 = x, t.r1 = r, t.id1 = id;
+  } else if (hi > t.hi2 || (hi == t.hi2 && id < t.id2)) {
+    t.b3 = fmaxf(t.b3, t.hi2);
+    t.hi2 = hi, t.x2 = x, t.r2 = r, t.id2 = id;
+  } else {
+    t.b3 = fmaxf(t.b3, hi);
+  }
+}
+
+__device__ __forceinline__ float block_max_f(float v, SampleSmem& sm) {
+  constexpr int NW = kSampleThreads / 64;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.best_s[threadIdx.x >> 6] = double(v);
+  __syncthreads();
+  float r = float(sm.best_s[0]);
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, float(sm.best_s[i]));
+  return r;
 }
 
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
@@ -178,6 +252,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   d.row = row;
   d.tau = double(temp ? temp[row] : temp_scalar);
   d.xmax = double(row_max[row]);
+  d.xmaxf = row_max[row];
+  d.inv_tau = 1.0f / float(d.tau);
   d.k0 = uint32_t(seed);
   d.k1 = uint32_t(seed >> 32);
   d.off_lo = uint32_t(offset);
@@ -187,40 +263,95 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const uint16_t* rowp = logits + row * ld;
   const bool vec = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
   const int64_t nchunk = (int64_t(V) + 7) / 8;
+  const bool lds_ranks = nchunk <= kLdsChunks;
+  const auto block_ctr = [&](int64_t q, int b) {
+    return philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+  };
 
-  // ---- pass 1: every token at or above the threshold ----
-  Best gt{-__builtin_inf(), int64_t(V)}, eq{-__builtin_inf(), int64_t(V)};
-  uint32_t n_eq = 0;
-  for (int64_t q = tid; q < nchunk; q += kSampleThreads) {
-    float x[8];
-    load_chunk(rowp, vec, q, V, x);
+  // Every token above the threshold (f_gt) and every token equal to it
+  // (f_eq, with its count written to LDS when lds_ranks): one pass over the row.
+  auto each_token = [&](bool count_ties, auto f_gt, auto f_eq) {
+    uint32_t n_eq = 0;
+    for (int64_t q = tid; q < nchunk; q += kSampleThreads) {
+      float x[8];
+      load_chunk(rowp, vec, q, V, x);
+      if (count_ties && lds_ranks) {
+        uint32_t c = 0;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      bool any = false;
+        for (int i = 0; i < 8; ++i) c += x[i] == thr ? 1u : 0u;
+        sm.chunk_ties[q] = c;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) any |= x[4 * b + i] >= thr;
-      if (!any) continue;
-      const Ctr r = philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+      for (int b = 0; b < 2; ++b) {
+        bool any = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xv = x[4 * b + i];
-        if (!(xv >= thr)) continue;
-        const Best c{gumbel_score(xv, ctr_word(r, i), d), 8 * q + 4 * b + i};
-        if (xv == thr) {
-          ++n_eq;
-          if (better(c, eq)) eq = c;
-        } else if (better(c, gt)) {
-          gt = c;
+        for (int i = 0; i < 4; ++i) any |= x[4 * b + i] >= thr;
+        if (!any) continue;
+        const Ctr r = block_ctr(q, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xv = x[4 * b + i];
+          if (!(xv >= thr)) continue;
+          const int64_t id = 8 * q + 4 * b + i;
+          if (xv == thr) {
+            ++n_eq;
+            f_eq(xv, ctr_word(r, i), id);
+          } else {
+            f_gt(xv, ctr_word(r, i), id);
+          }
         }
       }
     }
-  }
-  uint32_t n_eq_total;
-  (void)block_excl_scan(n_eq, n_eq_total, sm, 0);
-  gt = block_best(gt, sm);
-  if (n_eq_total > ties) {
-    // ---- pass 2: the support takes only the first `ties` threshold-equal tokens by id ----
-    eq = Best{-__builtin_inf(), int64_t(V)};
+    return n_eq;
+  };
+  // The first `ties` threshold-equal tokens by id (f), when the row holds
+  // more: ranked from the LDS chunk counts of the first pass (`ranked` tells
+  // that the in-place scan has run), or by a block scan per round of chunks.
+  // Every thread calls it (barriers inside).
+  bool ranked = false;
+  auto each_ranked_tie = [&](auto f) {
+    if (lds_ranks) {
+      if (!ranked) {
+        const int64_t seg = (nchunk + kSampleThreads - 1) / kSampleThreads;
+        const int64_t s0 = tid * seg, s1 = s0 + seg < nchunk ? s0 + seg : nchunk;
+        uint32_t run = 0;
+        for (int64_t q = s0; q < s1; ++q) run += sm.chunk_ties[q];
+        uint32_t total;
+        uint32_t acc = block_excl_scan(run, total, sm, 1);
+        for (int64_t q = s0; q < s1; ++q) {
+          const uint32_t c = sm.chunk_ties[q];
+          sm.chunk_ties[q] = acc;
+          acc += c;
+        }
+        if (tid == 0) sm.wcount[0][0] = total;  // (wcount[0] is free again: the last scan used slot 1)
+        __syncthreads();
+        ranked = true;
+      }
+      const uint32_t total = sm.wcount[0][0];
+      for (int64_t q = tid; q < nchunk; q += kSampleThreads) {
+        const uint32_t first = sm.chunk_ties[q];
+        const uint32_t next = q + 1 < nchunk ? sm.chunk_ties[q + 1] : total;
+        if (next == first || first >= ties) continue;  // no ties here, or none of them in the support
+        float x[8];
+        load_chunk(rowp, vec, q, V, x);
+        uint32_t rank = first;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          bool any = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) any |= x[4 * b + i] == thr;
+          if (!any) continue;
+          const Ctr r = block_ctr(q, b);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!(x[4 * b + i] == thr)) continue;
+            if (rank < ties) f(x[4 * b + i], ctr_word(r, i), 8 * q + 4 * b + i);
+            ++rank;
+          }
+        }
+      }
+      return;
+    }
     uint32_t base = 0;
     int buf = 1;
     for (int64_t q0 = 0; q0 < nchunk && base < ties; q0 += kSampleThreads, buf ^= 1) {
@@ -233,30 +364,75 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
         for (int i = 0; i < 8; ++i) m |= (x[i] == thr ? 1u : 0u) << i;
       }
       uint32_t total;
-      const uint32_t before = base + block_excl_scan(__builtin_popcount(m), total, sm, buf);
+      uint32_t rank = base + block_excl_scan(__builtin_popcount(m), total, sm, buf);
       if (m) {
-        uint32_t rank = before;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const uint32_t mb = (m >> (4 * b)) & 0xFu;
           if (!mb) continue;
-          const Ctr r = philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+          const Ctr r = block_ctr(q, b);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (!((mb >> i) & 1u)) continue;
-            if (rank < ties) {
-              const Best c{gumbel_score(x[4 * b + i], ctr_word(r, i), d), 8 * q + 4 * b + i};
-              if (better(c, eq)) eq = c;
-            }
+            if (rank < ties) f(x[4 * b + i], ctr_word(r, i), 8 * q + 4 * b + i);
             ++rank;
           }
         }
       }
       base += total;
     }
+  };
+
+  // ---- pass 1: fp32 score intervals of every support candidate (a token at
+  // -inf has probability 0 and is never drawn) ----
+  Top2 gt = top2_empty(V), eq = top2_empty(V);
+  auto track = [&](Top2& t) {
+    return [&t, &d](float x, uint32_t r, int64_t id) {
+      if (x == -__builtin_inff()) return;
+      float err;
+      const float s32 = score32(x, r, d, err);
+      top2_add(t, s32, err, x, r, id);
+    };
+  };
+  const uint32_t n_eq = each_token(true, track(gt), track(eq));
+  uint32_t n_eq_total;
+  (void)block_excl_scan(n_eq, n_eq_total, sm, 0);
+  const bool partial = n_eq_total > ties;
+  if (partial) {  // ---- pass 2: only the first `ties` threshold-equal tokens by id ----
+    eq = top2_empty(V);
+    each_ranked_tie(track(eq));
   }
-  eq = block_best(eq, sm);
-  if (tid == 0) sampled[row] = better(eq, gt) ? eq.id : gt.id;
+
+  // ---- the decision in fp64, over the tokens that can still be the best ----
+  const float L = block_max_f(fmaxf(gt.max_lo, eq.max_lo), sm);
+  const float over = block_max_f((gt.b3 >= L || eq.b3 >= L) ? 1.0f : 0.0f, sm);
+  Best best{-__builtin_inf(), int64_t(V)};
+  auto exact = [&](float x, uint32_t r, int64_t id) {
+    if (x == -__builtin_inff()) return;
+    float err;
+    const float s32 = score32(x, r, d, err);
+    if (!(s32 + err >= L)) return;
+    const Best c{gumbel_score(x, r, d), id};
+    if (better(c, best)) best = c;
+  };
+  if (over == 0.0f) {
+    const Top2* ts[2] = {&gt, &eq};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const Top2& t = *ts[k];
+      if (t.id1 < V && t.hi1 >= L) exact(t.x1, t.r1, t.id1);
+      if (t.id2 < V && t.hi2 >= L) exact(t.x2, t.r2, t.id2);
+    }
+  } else {  // some thread's third token may be a winner: rescan the row in the exact mode (rare)
+    if (partial) {
+      each_token(false, exact, [](float, uint32_t, int64_t) {});
+      each_ranked_tie(exact);
+    } else {
+      each_token(false, exact, exact);
+    }
+  }
+  best = block_best(best, sm);
+  if (tid == 0) sampled[row] = best.id;
 }
 
 }  // namespace

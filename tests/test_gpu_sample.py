@@ -68,7 +68,7 @@ def test_workload_rows(vsa):
     assert torch.equal(again["sampled"], first["sampled"])
 
 
-@pytest.mark.parametrize("V", [5, 3001, 100000])
+@pytest.mark.parametrize("V", [5, 3001, 100000, 170001])
 def test_ties_at_the_threshold(vsa, V):
     # small integer logits: long runs of equal values, so top-k and top-p cut
     # inside a tie group (the support takes its lowest ids: the second pass)
