@@ -52,4 +52,6 @@ from .scoring import (  # noqa: F401
     score_prefix_support,
     l1_distance,
     weighted_l1_loss,
+    logit_vjp,
+    score_full_vjp,
 )

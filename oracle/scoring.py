@@ -536,3 +536,62 @@ def weighted_l1_loss(x_target, x_draft, weights=None, grad_scale: float = 1.0) -
         grad[t] = grad_scale * (w[t] / den) * q * (s - np.sum(s * q))
     return {"l1": base["l1"], "accept_rate": base["accept_rate"], "num": num, "den": den,
             "loss": num / den if den != 0.0 else np.nan, "grad": grad}
+
+
+# ---------------------------------------------------------------------------
+# O6: the vector-Jacobian product of full-vocabulary scoring (fused source)
+# ---------------------------------------------------------------------------
+
+def logit_vjp(x, tau, targets, grad_logprob=None, grad_entropy=None) -> np.ndarray:
+    """d(sum_t a_t logprob_t + b_t H_t) / d x[t, v] for full-vocabulary scores.
+
+    xorl issue #71, section 1 (the op ends in "selected logprob + VJP") and
+    SkyRL PR #2004 (gradients through logprob and entropy): with
+    ``z = x / tau``, ``p = softmax(z)``, ``ln p_v = z_v - LSE`` and
+    ``H = -sum p ln p``,
+
+        d logprob / d z_v = [v = y] - p_v
+        d H / d z_v       = -p_v (ln p_v + H)      (= -p_v (z_v - (LSE - H)))
+
+    and ``d / d x = (d / d z) / tau``.  ``a`` = grad_logprob, ``b`` =
+    grad_entropy ([R] each, None meaning 0).  A BAD_INPUT row of score_full
+    (invalid tau or target, or an LSE that is not finite) gets a zero row.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, V = x.shape
+    tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (R,))
+    a = np.zeros(R) if grad_logprob is None else np.asarray(grad_logprob, dtype=np.float64)
+    b = np.zeros(R) if grad_entropy is None else np.asarray(grad_entropy, dtype=np.float64)
+    targets = np.asarray(targets, dtype=np.int64)
+    out = np.zeros((R, V))
+    for t in range(R):
+        y = int(targets[t])
+        if not _valid_tau(tau[t]) or not (0 <= y < V):
+            continue
+        lse, lnp, h = _log_softmax(x[t], tau[t])
+        if not np.isfinite(lse):
+            continue
+        p = np.exp(lnp)
+        plnp = np.where(p > 0.0, p * np.where(np.isfinite(lnp), lnp, 0.0), 0.0)
+        dz = -a[t] * p - b[t] * (plnp + p * h)
+        dz[y] += a[t]
+        out[t] = dz / tau[t]
+    return out
+
+
+def score_full_vjp(hidden, hidden_dtype: str, weight_bits, tau, targets, grad_logprob=None,
+                   grad_entropy=None) -> dict:
+    """Gradients of sum_t (a_t logprob_t + b_t H_t) of the fused projection
+    ``x = bf16(hidden) W^T`` with respect to the hidden state and the weight.
+
+    ``d_hidden = dX W`` and ``d_weight = dX^T bf16(hidden)`` with
+    ``dX = logit_vjp(x, ...)``: the chain rule through the projection (the
+    cast of an fp32 hidden state to bf16 passes its gradient through
+    unchanged, as the cast's own derivative is the identity).  float64.
+    """
+    h = np.asarray(hidden)
+    h64 = widen_bf16(round_f32_to_bf16(h)) if hidden_dtype == "f32" else widen_bf16(h)
+    w64 = widen_bf16(np.asarray(weight_bits, dtype=np.uint16))
+    x = h64 @ w64.T
+    dx = logit_vjp(x, tau, targets, grad_logprob, grad_entropy)
+    return {"d_hidden": dx @ w64, "d_weight": dx.T @ h64, "d_logits": dx}

@@ -235,3 +235,63 @@ def test_logits_from_logits(dtype):
         arr, ref = v, v.astype(np.float64)
     np.testing.assert_array_equal(oracle.logits_from_logits(arr, dtype), ref)
     np.testing.assert_array_equal(oracle.logits_from_logits(arr, dtype, rows=[1]), ref[[1]])
+
+
+def _scores_objective(h, w, tau, y, a, b):
+    r = oracle.score_full(h @ w.T, tau, y)
+    return float(np.sum(a * r["logprob"] + b * r["entropy"]))
+
+
+def test_vjp_matches_finite_differences():
+    # the gradient of sum a logprob + b H with respect to the logits, the
+    # hidden state and the weight, against central differences of the scores
+    rng = np.random.default_rng(31)
+    T, H, V = 3, 5, 7
+    h = rng.normal(0, 1, (T, H))
+    w = rng.normal(0, 0.5, (V, H))
+    tau = np.array([1.0, 0.7, 1.6])
+    y = np.array([2, 0, 6])
+    a = np.array([1.0, -0.5, 2.0])
+    b = np.array([0.3, 1.0, -0.8])
+    x = h @ w.T
+    dx = oracle.logit_vjp(x, tau, y, a, b)
+    eps = 1e-6
+    for t in range(T):
+        for v in range(V):
+            xp, xm = x.copy(), x.copy()
+            xp[t, v] += eps
+            xm[t, v] -= eps
+            rp, rm = oracle.score_full(xp, tau, y), oracle.score_full(xm, tau, y)
+            fd = (np.sum(a * rp["logprob"] + b * rp["entropy"]) - np.sum(a * rm["logprob"] + b * rm["entropy"])) / (2 * eps)
+            assert abs(fd - dx[t, v]) < 1e-7, (t, v)
+    # through the projection: d_hidden = dX W, d_weight = dX^T h
+    for (m, arr) in (("h", h), ("w", w)):
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            hp, wp = (ap, w) if m == "h" else (h, ap)
+            hm, wm = (am, w) if m == "h" else (h, am)
+            fd = (_scores_objective(hp, wp, tau, y, a, b) - _scores_objective(hm, wm, tau, y, a, b)) / (2 * eps)
+            ref = (dx @ w)[idx] if m == "h" else (dx.T @ h)[idx]
+            assert abs(fd - ref) < 1e-7, (m, idx)
+
+
+def test_vjp_invariants():
+    rng = np.random.default_rng(32)
+    x = rng.normal(0, 2, (6, 40))
+    y = rng.integers(0, 40, 6)
+    a, b = rng.normal(size=6), rng.normal(size=6)
+    dx = oracle.logit_vjp(x, 1.3, y, a, b)
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-14)  # sum_v dp_v = 0 for both terms
+    # a one-token vocabulary: logprob and entropy are constant, the gradient exactly 0
+    assert (oracle.logit_vjp(x[:, :1], 1.0, np.zeros(6, int), a, b) == 0.0).all()
+    # logprob alone: onehot - p; entropy alone at uniform logits: 0 (H is at its maximum)
+    g = oracle.logit_vjp(x, 1.0, y, np.ones(6), None)
+    p = np.exp(x - x.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(g, np.eye(40)[y] - p, atol=1e-15)
+    assert np.abs(oracle.logit_vjp(np.zeros((2, 9)), 1.0, [0, 3], None, [1.0, 2.0])).max() < 1e-15
+    # bad rows get zero rows
+    bad = oracle.logit_vjp(np.array([[0.0, np.nan], [1.0, 2.0]]), 1.0, [0, 5], [1, 1], [1, 1])
+    assert (bad == 0).all()
