@@ -82,7 +82,8 @@ enum {
   VS_OP_SCORE_TRANSFORMS = 2,
   VS_OP_L1_DISTANCE = 3,
   VS_OP_SAMPLE_TRANSFORMS = 4,
-  VS_OP_L1_LOSS = 5
+  VS_OP_L1_LOSS = 5,
+  VS_OP_SCORE_FULL_BACKWARD = 6
 };
 
 /* ---- per-row status bits (uint8 per row) -------------------------------- */
@@ -128,7 +129,8 @@ typedef struct vs_source {
 
 /*
  * Bytes of workspace the call `op` needs for this source (width = support
- * width for VS_OP_SCORE_SUPPORT, else 0).  For VS_OP_L1_DISTANCE only src->T
+ * width for VS_OP_SCORE_SUPPORT, the vocab_chunk for
+ * VS_OP_SCORE_FULL_BACKWARD, else 0).  For VS_OP_L1_DISTANCE only src->T
  * and src->V are read.  Returns 0 on a NULL src.
  */
 size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width);
@@ -156,6 +158,32 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width);
 int vs_score_full(const vs_source* src, const int64_t* target_ids, int64_t vocab_chunk, float* lse,
                   float* logprob, float* entropy, uint8_t* row_status, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * The vector-Jacobian product of full-vocabulary scoring through the fused
+ * projection (xorl issue #71 section 1: the op ends in "selected logprob +
+ * VJP"; SkyRL PR #2004: gradients through logprob and entropy).  Given the
+ * forward's lse and entropy and the upstream gradients a_t = grad_logprob[t],
+ * b_t = grad_entropy[t] of sum_t (a_t logprob_t + b_t entropy_t):
+ *   dX[t, v]          = (a_t ([v = y_t] - p_v) - b_t p_v (ln p_v + H_t)) / tau_t
+ *   grad_hidden[t, h] = sum_v dX[t, v] W[v, h]               [T, ld_grad_hidden] fp32
+ *   grad_weight[v, h] = sum_t dX[t, v] bf16(hidden)[t, h]    [V, ld_grad_weight] fp32
+ * (an fp32 hidden state's bf16 cast passes its gradient through: grad_hidden
+ * is also the gradient of the fp32 values).  dX is recomputed tile by tile
+ * by the forward's MFMA sweep, rounded to bf16 (nearest even) and kept only
+ * for one vocab_chunk-wide chunk of the vocabulary at a time; both products
+ * run on the same MFMA loop, in a fixed order (chunks ascending), so results
+ * are bitwise reproducible.  Source: VS_SRC_HIDDEN_WEIGHT (else
+ * VS_E_UNSUPPORTED).  grad_logprob / grad_entropy nullable (0); entropy is
+ * required with grad_entropy.  grad_hidden and grad_weight nullable (at
+ * least one).  A row the forward marked BAD_INPUT (its lse not finite, an
+ * invalid tau or target) contributes no gradient.  Workspace:
+ * vs_workspace_size(VS_OP_SCORE_FULL_BACKWARD, src, vocab_chunk).
+ */
+int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, const float* lse, const float* entropy,
+                           const float* grad_logprob, const float* grad_entropy, int64_t vocab_chunk,
+                           float* grad_hidden, int64_t ld_grad_hidden, float* grad_weight, int64_t ld_grad_weight,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Recorded-support scoring (SkyRL PR #2004, sections Problem and

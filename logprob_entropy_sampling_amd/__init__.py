@@ -6,6 +6,7 @@ name runs every step on the GPU, on torch's current stream.  There is no CPU
 path: importing this package fails if the library has not been built.
 
     score_full(...)          full-vocabulary LSE / selected logprob / entropy
+    score_full_backward(...) their gradients w.r.t. the hidden state and the LM-head weight
     score_support_ids(...)   recorded-support logprob / entropy (+ synthetic-EOS fallback)
     score_transforms(...)    top-k / top-p / min-p support scores and descriptor
     sample_transforms(...)   seeded Gumbel draw from the top-k / top-p / min-p support
@@ -44,7 +45,7 @@ class _Lazy:
 
 _lib = _Lazy()
 
-__all__ = ["score_full", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms",
+__all__ = ["score_full", "score_full_backward", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms",
            "sample_transforms", "l1_distance", "l1_loss", "workspace_size", "workspace_bytes",
            "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
@@ -207,6 +208,33 @@ def score_full(targets, *, logits=None, hidden=None, weight=None, temperature=1.
                             _ptr(o["entropy"]), _ptr(o["status"]), _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_score_full")
+    return o
+
+
+def score_full_backward(targets, lse, entropy=None, *, hidden, weight, grad_logprob=None, grad_entropy=None,
+                        temperature=1.0, vocab_chunk=8192, want_hidden=True, want_weight=True, out=None,
+                        workspace=None):
+    """Gradients of sum_t (grad_logprob[t] logprob_t + grad_entropy[t] entropy_t)
+    with respect to the hidden state and the LM-head weight
+    (vs_score_full_backward); lse / entropy are the forward's outputs.
+    Returns ``grad_hidden`` [T, H] and ``grad_weight`` [V, H] (fp32)."""
+    src, dev, _keep = _make_source(None, hidden, weight, temperature)
+    _ids("targets", targets, src.T)
+    T, H, V = src.T, src.H, src.V
+    for name, t in (("lse", lse), ("entropy", entropy), ("grad_logprob", grad_logprob),
+                    ("grad_entropy", grad_entropy)):
+        if t is not None:
+            _check_cuda(name, t, {torch.float32}, 1)
+            if t.numel() != T or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [T] float32 tensor")
+    o = _outputs({"grad_hidden": ((T, H), torch.float32) if want_hidden else None,
+                  "grad_weight": ((V, H), torch.float32) if want_weight else None}, dev, out)
+    ws, n = _workspace(_capi.VS_OP_SCORE_FULL_BACKWARD, src, dev, int(vocab_chunk), given=workspace)
+    rc = _lib.vs_score_full_backward(ctypes.byref(src), _ptr(targets), _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
+                                     _ptr(grad_entropy), int(vocab_chunk), _ptr(o["grad_hidden"]), H,
+                                     _ptr(o["grad_weight"]), H, _ptr(ws), n, _stream(dev))
+    if rc:
+        raise VsError(rc, "vs_score_full_backward")
     return o
 
 

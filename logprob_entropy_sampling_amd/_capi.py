@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocabsco
 VS_F32, VS_BF16 = 0, 1
 VS_SRC_LOGITS, VS_SRC_HIDDEN_WEIGHT = 0, 1
 (VS_OP_SCORE_FULL, VS_OP_SCORE_SUPPORT, VS_OP_SCORE_TRANSFORMS, VS_OP_L1_DISTANCE, VS_OP_SAMPLE_TRANSFORMS,
- VS_OP_L1_LOSS) = range(6)
+ VS_OP_L1_LOSS, VS_OP_SCORE_FULL_BACKWARD) = range(7)
 
 ROW_EMPTY_SUPPORT = 0x01
 ROW_TARGET_OUTSIDE_SUPPORT = 0x02
@@ -57,6 +57,8 @@ _SIGS = {
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "vs_l1_distance": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "vs_score_full_backward": (c_int32, [POINTER(VsSource), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                         c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
     "vs_score_full_noalloc": (c_int32, [POINTER(VsSource), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p]),
     "vs_noalloc_scratch_bytes": (c_size_t, []),

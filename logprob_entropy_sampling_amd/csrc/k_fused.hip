@@ -242,11 +242,158 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
   }
 }
 
+// Epilogue modes of the sweep kernels.  The K loop is the same in every mode
+// (C[m, n] = sum_k A[m, k] B[n, k], A the "weight" rows on M, B the "hidden"
+// rows on N, both contiguous in K):
+//   kEpiPartials  the softmax statistics above (the forward scoring op);
+//   kEpiGrad      the logits' gradient of sum_t (a_t logprob_t + b_t H_t):
+//                 dx = (a ([v = y] - p_v) - b p_v (ln p_v + H)) / tau, written
+//                 as bf16 twice, G[t][v] and G^T[v][t] (zeros in the padding
+//                 rows and columns up to the K-multiples of the GEMMs that read them);
+//   kEpiStore     C[m][n] = acc, or += acc (fp32, n contiguous): a plain GEMM.
+enum { kEpiPartials = 0, kEpiGrad = 1, kEpiStore = 2 };
+struct EpiArgs {
+  float4* partials;          // kEpiPartials
+  float* zy_raw;
+  const float* lse;          // kEpiGrad: the forward's outputs, per token row
+  const float* entropy;
+  const float* grad_logprob;  // nullable: 0
+  const float* grad_entropy;  // nullable: 0
+  uint16_t* g;               // [rows][ld_g]: column = vocabulary row of the sweep
+  int64_t ld_g;
+  uint16_t* gt;              // [vocab rows][ld_gt]: column = token
+  int64_t ld_gt;
+  int64_t v_begin;           // vocabulary id of the sweep's first row (the target test)
+  int64_t v_pad, t_pad;      // zero-filled up to these
+  float* c;                  // kEpiStore
+  int64_t ldc;
+  int accumulate;
+};
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The gradient of the tile's logits.  Row data of the lane's 4 token columns
+// are loaded here (one round of loads per tile).  A row whose LSE is not
+// finite (a BAD_INPUT row of the forward) gets a zero gradient.
+__device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t t0, int64_t rows_valid,
+                                              int64_t V, const float* __restrict__ temp, float temp_scalar,
+                                              const int64_t* __restrict__ targets, const EpiArgs& ep) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wv = w & 1;
+  const int wt = w >> 1;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  // tile-relative limits (32-bit): rows vr < nv exist, rows vr < np are written
+  const int vrow0 = wv * 128 + 4 * lh;  // + 32 i + 8 q + e
+  const int nv = int(V - v0 < BV ? V - v0 : BV);
+  const int np = int(ep.v_pad - v0 < BV ? ep.v_pad - v0 : BV);
+  uint16_t* const gt_tile = ep.gt + v0 * ep.ld_gt + t0;  // + vr * ld_gt + col
+  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;     // + col * ld_g + vr
+  const int ldgt = int(ep.ld_gt), ldg = int(ep.ld_g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // the accumulators of the columns not written yet stay in AGPRs until their turn
+#pragma unroll
+    for (int jj = j + 1; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    const int col = wt * 128 + 32 * j + lr;
+    const int64_t t = t0 + col;
+    const bool tvalid = t < rows_valid;
+    const bool tpad = t < ep.t_pad;
+    float c = 0.0f, inv_tau = 0.0f, l2 = 0.0f, h = 0.0f, ga = 0.0f, gb = 0.0f;
+    int yr = -1;  // the target's tile-relative row, if it is in this tile
+    if (tvalid) {
+      const float tau = temp ? temp[t] : temp_scalar;
+      const float lse = ep.lse[t];
+      const int64_t y = targets[t];
+      ga = ep.grad_logprob ? ep.grad_logprob[t] : 0.0f;
+      gb = ep.grad_entropy ? ep.grad_entropy[t] : 0.0f;
+      h = gb != 0.0f ? ep.entropy[t] : 0.0f;
+      if (!(tau_ok(tau) && lse > -__builtin_inff() && lse < __builtin_inff() && h == h && y >= 0)) {
+        ga = 0.0f;  // no gradient through a bad row
+        gb = 0.0f;
+        h = 0.0f;
+      }
+      const int64_t yv = y - ep.v_begin - v0;
+      yr = (yv >= 0 && yv < BV) ? int(yv) : -1;
+      c = kLog2e / tau;
+      inv_tau = 1.0f / tau;
+      l2 = lse * kLog2e;  // base-2 LSE
+    }
+    const bool live = tvalid && (ga != 0.0f || gb != 0.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vb = vrow0 + 32 * i + 8 * q;  // rows vb .. vb+3 of the tile
+        uint16_t gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float dx = 0.0f;
+          if (live && vb + e < nv) {
+            const float d2 = __builtin_fmaf(acc[i][j][4 * q + e], c, -l2);
+            const float pv = exp2_hw(d2);
+            float dz = -pv * __builtin_fmaf(gb, __builtin_fmaf(d2, kLn2, h), ga);
+            if (vb + e == yr) dz += ga;
+            dx = dz * inv_tau;
+          }
+          gv[e] = bf16_rne_bits(dx);
+        }
+        if (tpad) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (vb + e < np) gt_tile[(vb + e) * ldgt + col] = gv[e];
+        }
+        if (tvalid && vb < np) {  // v_pad is a multiple of 4
+          *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
+              make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
+        }
+      }
+  }
+}
+
+// C[m][n] (+)= acc for the rows m < M and columns n < N of the tile.
+__device__ __forceinline__ void store_epilogue(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int64_t N, int64_t M,
+                                               const EpiArgs& ep) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wv = w & 1;
+  const int wt = w >> 1;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int jj = j + 1; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    const int64_t n = n0 + wt * 128 + 32 * j + lr;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wv * 128 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < M) {
+          float* dst = ep.c + m * ep.ldc + n;
+          *dst = ep.accumulate ? *dst + acc[i][j][r] : acc[i][j][r];
+        }
+      }
+  }
+}
+
+template <int MODE>
 __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
     const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
-    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+    int n_vtiles, int n_ttiles, int gv, EpiArgs ep) {
   int vt, tt;
   if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
   const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
@@ -256,7 +403,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
 
   __shared__ uint4 As[2][BV * CH];
   __shared__ uint4 Bs[2][BT * CH];
-  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, row_map);
+  ColumnLoads cl{};
+  if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, row_map);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -342,7 +490,13 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     cur ^= 1;
   }
 
-  tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials, zy_raw);
+  if constexpr (MODE == kEpiPartials)
+    tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
+                  ep.zy_raw);
+  else if constexpr (MODE == kEpiGrad)
+    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+  else
+    store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
 
 
@@ -377,12 +531,12 @@ constexpr int DMA_PER_STAGE = 2 * DMA_PER_OP;
 // dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format, no swizzle
 constexpr int kBufferFlags = 0x00020000;
 
-template <bool BUF, int REM>
+template <bool BUF, int REM, int MODE>
 __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
     const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
-    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+    int n_vtiles, int n_ttiles, int gv, EpiArgs ep) {
   int vt, tt;
   if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
   const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
@@ -392,7 +546,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
 
   __shared__ uint4 A0[BV * CH], A1[BV * CH], A2[BV * CH], A3[BV * CH];
   __shared__ uint4 B0[BT * CH], B1[BT * CH], B2[BT * CH], B3[BT * CH];
-  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
+  ColumnLoads cl{};
+  if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
   // slot indices are compile-time constants after unrolling
   auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : i == 1 ? A1 : i == 2 ? A2 : A3; };
   auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : i == 1 ? B1 : i == 2 ? B2 : B3; };
@@ -543,8 +698,13 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
   if (REM > 2) step(2, nk4 + 2, fa0, fb0, fa1, fb1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
   __syncthreads();
-  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials,
-                zy_raw);
+  if constexpr (MODE == kEpiPartials)
+    tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
+                  ep.zy_raw);
+  else if constexpr (MODE == kEpiGrad)
+    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+  else
+    store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,12 +731,12 @@ constexpr int DMA2_PER_OP = BV * CH2 / NT;    // loads per lane per operand per 
 constexpr int DMA2_PER_STAGE = 2 * DMA2_PER_OP;
 __device__ __forceinline__ int swz8(int r, int c) { return r * CH2 + (c ^ ((r >> 1) & 7)); }
 
-template <bool BUF, int REM>
+template <bool BUF, int REM, int MODE>
 __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight, int64_t ld_w,
     int64_t rows, int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar,
     const int64_t* __restrict__ targets, const int32_t* __restrict__ row_map, const int32_t* __restrict__ row_count,
-    int n_vtiles, int n_ttiles, int gv, float4* __restrict__ partials, float* __restrict__ zy_raw) {
+    int n_vtiles, int n_ttiles, int gv, EpiArgs ep) {
   int vt, tt;
   if (!map_tile(int(blockIdx.x), n_vtiles, n_ttiles, gv, vt, tt)) return;
   const int64_t rows_valid = row_count ? int64_t(*row_count) : rows;
@@ -588,7 +748,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
   __shared__ uint4 B0[BT * CH2], B1[BT * CH2];
   auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : A1; };
   auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : B1; };
-  const ColumnLoads cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
+  ColumnLoads cl{};
+  if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -728,8 +889,32 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
   if (REM) stage(0, nk2);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped duplicate refills may still be landing
   __syncthreads();
-  tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, partials,
-                zy_raw);
+  if constexpr (MODE == kEpiPartials)
+    tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
+                  ep.zy_raw);
+  else if constexpr (MODE == kEpiGrad)
+    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+  else
+    store_epilogue(acc, v0, t0, rows_valid, V, ep);
+}
+
+// dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < R_pad: a bf16
+// transpose through a 64 x 64 LDS tile (reads and writes along rows of 64).
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t ld_s, int64_t R,
+                                                            int64_t C, uint16_t* __restrict__ dst, int64_t ld_d,
+                                                            int64_t R_pad) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < R && c < C) ? src[r * ld_s + c] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t c = c0 + k, r = r0 + tx;
+    if (c < C && r < R_pad) dst[c * ld_d + r] = tile[tx][k];
+  }
 }
 
 __global__ void round_hidden_kernel(const float* __restrict__ h, int64_t ld, int64_t rows, int64_t H,
@@ -750,10 +935,14 @@ __global__ void round_hidden_kernel(const float* __restrict__ h, int64_t ld, int
 
 }  // namespace
 
-int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
-                          int64_t rows, int64_t H, int64_t V, const float* temp, float temp_scalar,
-                          const int64_t* targets, const int32_t* row_map, const int32_t* row_count,
-                          void* partials, float* zy_raw, void* stream) {
+namespace {
+
+// One sweep over every (vocabulary tile, token tile) of weight rows [0, V) x
+// hidden rows [0, rows), K = H, in the epilogue mode MODE.
+template <int MODE>
+int launch_sweep(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight, int64_t rows,
+                 int64_t H, int64_t V, const float* temp, float temp_scalar, const int64_t* targets,
+                 const int32_t* row_map, const int32_t* row_count, const EpiArgs& ep, void* stream) {
   const int64_t n_vtiles = (V + BV - 1) / BV;
   const int64_t n_ttiles = (rows + BT - 1) / BT;
   if (n_vtiles <= 0 || n_ttiles <= 0) return 0;
@@ -764,14 +953,13 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 g{unsigned(grid)}, b{unsigned(NT)};
   const int nv = int(n_vtiles), nt = int(n_ttiles);
-  float4* part = static_cast<float4*>(partials);
   // buffer offsets are 32-bit: a 256-row tile of either operand must span < 2 GiB
   const bool buf_ok = !row_map && int64_t(BV) * ld_weight * 2 <= 0x7FFFFFFF && int64_t(BT) * ld_hidden * 2 <= 0x7FFFFFFF;
   if (H % BK2 == 0) {
     const int rem = int((H / BK2) % 2);
-#define VS_LAUNCH_WIDE(B, R)                                                                                     \
-  fused_partials_wide_kernel<B, R><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,        \
-                                                   temp_scalar, targets, row_map, row_count, nv, nt, gv, part, zy_raw)
+#define VS_LAUNCH_WIDE(B, R)                                                                                       \
+  fused_partials_wide_kernel<B, R, MODE><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,    \
+                                                         temp_scalar, targets, row_map, row_count, nv, nt, gv, ep)
     switch (rem + (buf_ok ? 0 : 2)) {
       case 0: VS_LAUNCH_WIDE(true, 0); break;
       case 1: VS_LAUNCH_WIDE(true, 1); break;
@@ -782,9 +970,9 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
   } else if (H % BK == 0) {
     const int rem = int((H / BK) % NSTAGE);
 #define VS_LAUNCH_PIPELINED(B, R)                                                                                  \
-  fused_partials_pipelined_kernel<B, R><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp,     \
-                                                        temp_scalar, targets, row_map, row_count, nv, nt, gv, part, \
-                                                        zy_raw)
+  fused_partials_pipelined_kernel<B, R, MODE><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V,     \
+                                                              temp, temp_scalar, targets, row_map, row_count, nv,  \
+                                                              nt, gv, ep)
     switch (rem + (buf_ok ? 0 : 4)) {
       case 0: VS_LAUNCH_PIPELINED(true, 0); break;
       case 1: VS_LAUNCH_PIPELINED(true, 1); break;
@@ -797,9 +985,63 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
     }
 #undef VS_LAUNCH_PIPELINED
   } else {
-    fused_partials_kernel<<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar,
-                                          targets, row_map, row_count, nv, nt, gv, part, zy_raw);
+    fused_partials_kernel<MODE><<<g, b, 0, s>>>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar,
+                                                targets, row_map, row_count, nv, nt, gv, ep);
   }
+  return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                          int64_t rows, int64_t H, int64_t V, const float* temp, float temp_scalar,
+                          const int64_t* targets, const int32_t* row_map, const int32_t* row_count,
+                          void* partials, float* zy_raw, void* stream) {
+  EpiArgs ep{};
+  ep.partials = static_cast<float4*>(partials);
+  ep.zy_raw = zy_raw;
+  return launch_sweep<kEpiPartials>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets,
+                                    row_map, row_count, ep, stream);
+}
+
+int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                      int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
+                      const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, uint16_t* gt, int64_t ld_gt,
+                      int64_t v_pad, int64_t t_pad, void* stream) {
+  EpiArgs ep{};
+  ep.lse = lse;
+  ep.entropy = entropy;
+  ep.grad_logprob = grad_logprob;
+  ep.grad_entropy = grad_entropy;
+  ep.g = g;
+  ep.ld_g = ld_g;
+  ep.gt = gt;
+  ep.ld_gt = ld_gt;
+  ep.v_begin = v_begin;
+  ep.v_pad = v_pad;
+  ep.t_pad = t_pad;
+  return launch_sweep<kEpiGrad>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets,
+                                nullptr, nullptr, ep, stream);
+}
+
+int launch_gemm_nt(const uint16_t* a, int64_t lda, int64_t M, const uint16_t* b, int64_t ldb, int64_t N, int64_t K,
+                   float* c, int64_t ldc, bool accumulate, void* stream) {
+  EpiArgs ep{};
+  ep.c = c;
+  ep.ldc = ldc;
+  ep.accumulate = accumulate ? 1 : 0;
+  // the sweep's "weight" rows are the M axis, its "hidden" rows the N axis
+  return launch_sweep<kEpiStore>(b, ldb, a, lda, N, K, M, nullptr, 1.0f, nullptr, nullptr, nullptr, ep, stream);
+}
+
+int launch_transpose_pad(const uint16_t* src, int64_t ld_s, int64_t R, int64_t C, uint16_t* dst, int64_t ld_d,
+                         int64_t R_pad, void* stream) {
+  if (C <= 0 || R_pad <= 0) return 0;
+  const int64_t gx = (C + 63) / 64, gy = (R_pad + 63) / 64;
+  if (gx > 0x7FFFFFFF || gy > 65535) return int(hipErrorInvalidConfiguration);
+  transpose_pad_kernel<<<dim3(unsigned(gx), unsigned(gy)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      src, ld_s, R, C, dst, ld_d, R_pad);
   return int(hipGetLastError());
 }
 

@@ -35,6 +35,25 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
                           const int64_t* targets, const int32_t* row_map, const int32_t* row_count,
                           void* partials, float* zy_raw, void* stream);
 
+// The gradient sweep: the same tiles over weight rows [0, V) (vocabulary ids
+// v_begin + v) x hidden rows [0, rows); writes the logits' gradient as bf16
+// into g [rows][ld_g] and gt [V][ld_gt], zeros up to column v_pad / t_pad.
+int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                      int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
+                      const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, uint16_t* gt, int64_t ld_gt,
+                      int64_t v_pad, int64_t t_pad, void* stream);
+
+// c[m][n] (+)= sum_k a[m][k] b[n][k] (bf16 in, fp32 out; K a multiple of 8,
+// lda, ldb multiples of 8, a and b 16-byte aligned): the sweep's MFMA loop
+// with a plain store.
+int launch_gemm_nt(const uint16_t* a, int64_t lda, int64_t M, const uint16_t* b, int64_t ldb, int64_t N, int64_t K,
+                   float* c, int64_t ldc, bool accumulate, void* stream);
+
+// dst[c][r] = src[r][c] (bf16), zeros for R <= r < R_pad.
+int launch_transpose_pad(const uint16_t* src, int64_t ld_s, int64_t R, int64_t C, uint16_t* dst, int64_t ld_d,
+                         int64_t R_pad, void* stream);
+
 // fp32 -> bf16 (round to nearest even) of hidden rows into a packed [rows, H] buffer.
 int launch_round_hidden(const float* hidden, int64_t ld_hidden, int64_t rows, int64_t H, uint16_t* out,
                         void* stream);

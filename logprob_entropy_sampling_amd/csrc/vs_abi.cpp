@@ -98,6 +98,34 @@ size_t sample_ws_bytes(const vs_source* s) {
          round_up(vs::transforms_workspace_bytes(s->T, s->V));
 }
 
+// Backward of full-vocabulary scoring through the fused projection: per
+// vocabulary chunk of Vc rows (a multiple of the 256-row tile), the logits'
+// gradient G [T][Vc] and G^T [Vc][Tp] (bf16), W^T of the chunk [H][Vc], and
+// once the hidden state's transpose [H][Tp] (Tp = T rounded up to 64, the
+// GEMMs' K multiple) and, for an fp32 hidden state, its bf16 copy.
+struct BwdDims {
+  int64_t vc, tp;
+};
+BwdDims bwd_dims(const vs_source* s, int64_t vocab_chunk) {
+  const int64_t tile = vs::kFusedTileV;
+  int64_t vc = vocab_chunk < tile ? tile : (vocab_chunk + tile - 1) / tile * tile;
+  const int64_t vmax = (s->V + tile - 1) / tile * tile;
+  if (vc > vmax) vc = vmax;
+  return BwdDims{vc, (s->T + 63) / 64 * 64};
+}
+size_t backward_ws_bytes(const vs_source* s, int64_t vocab_chunk) {
+  if (s->kind != VS_SRC_HIDDEN_WEIGHT) return 0;
+  const BwdDims d = bwd_dims(s, vocab_chunk);
+  const size_t T = size_t(s->T), H = size_t(s->H);
+  size_t b = 0;
+  if (s->hidden_dtype == VS_F32) b += round_up(T * H * 2);
+  b += round_up(H * size_t(d.tp) * 2);         // hidden^T
+  b += round_up(T * size_t(d.vc) * 2);         // G
+  b += round_up(size_t(d.vc) * size_t(d.tp) * 2);  // G^T
+  b += round_up(H * size_t(d.vc) * 2);         // W^T of a chunk
+  return b;
+}
+
 size_t support_ws_bytes(const vs_source* s) {
   return round_up(size_t(s->T) * 4) + round_up(4) + full_ws_bytes(s, s->T);
 }
@@ -163,7 +191,6 @@ const char* vs_status_string(int32_t code) {
 }
 
 size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
-  (void)width;
   if (!src) return 0;
   switch (op) {
     case VS_OP_SCORE_FULL: return full_ws_bytes(src, src->T);
@@ -172,6 +199,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
     case VS_OP_SAMPLE_TRANSFORMS: return sample_ws_bytes(src);
     case VS_OP_L1_LOSS: return round_up(vs::l1_loss_workspace_bytes(src->T));
+    case VS_OP_SCORE_FULL_BACKWARD: return backward_ws_bytes(src, width);
     default: return 0;
   }
 }
@@ -283,6 +311,61 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
                          row_max, seed, offset, sampled_ids, row_status, stream);
   vs::timer_mark(1, stream);
   return rc ? VS_E_DEVICE : VS_OK;
+}
+
+int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, const float* lse, const float* entropy,
+                           const float* grad_logprob, const float* grad_entropy, int64_t vocab_chunk,
+                           float* grad_hidden, int64_t ld_grad_hidden, float* grad_weight, int64_t ld_grad_weight,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_source(src);
+  if (rc) return rc;
+  if (src->kind != VS_SRC_HIDDEN_WEIGHT) return VS_E_UNSUPPORTED;
+  if (!target_ids || !lse || (grad_entropy && !entropy)) return VS_E_NULL;
+  if (!grad_hidden && !grad_weight) return VS_E_NULL;
+  if (vocab_chunk < 1) return VS_E_PARAM;
+  if ((grad_hidden && ld_grad_hidden < src->H) || (grad_weight && ld_grad_weight < src->H)) return VS_E_SHAPE;
+  if (!aligned(grad_hidden, 4) || !aligned(grad_weight, 4)) return VS_E_ALIGN;
+  rc = check_workspace(workspace, workspace_bytes, backward_ws_bytes(src, vocab_chunk));
+  if (rc) return rc;
+  const int64_t T = src->T, H = src->H, V = src->V;
+  const BwdDims dm = bwd_dims(src, vocab_chunk);
+  Carver c(workspace);
+  const uint16_t* hid = static_cast<const uint16_t*>(src->hidden);
+  int64_t ldh = src->ld_hidden;
+  if (src->hidden_dtype == VS_F32) {
+    uint16_t* hb = static_cast<uint16_t*>(c.take(size_t(T) * size_t(H) * 2));
+    if (vs::launch_round_hidden(static_cast<const float*>(src->hidden), src->ld_hidden, T, H, hb, stream))
+      return VS_E_DEVICE;
+    hid = hb;
+    ldh = H;
+  }
+  uint16_t* hT = static_cast<uint16_t*>(c.take(size_t(H) * size_t(dm.tp) * 2));
+  uint16_t* G = static_cast<uint16_t*>(c.take(size_t(T) * size_t(dm.vc) * 2));
+  uint16_t* GT = static_cast<uint16_t*>(c.take(size_t(dm.vc) * size_t(dm.tp) * 2));
+  uint16_t* WT = static_cast<uint16_t*>(c.take(size_t(H) * size_t(dm.vc) * 2));
+  const uint16_t* W = static_cast<const uint16_t*>(src->weight);
+  if (grad_weight && vs::launch_transpose_pad(hid, ldh, T, H, hT, dm.tp, dm.tp, stream)) return VS_E_DEVICE;
+  vs::timer_mark(0, stream);
+  for (int64_t v0 = 0; v0 < V; v0 += dm.vc) {
+    const int64_t vn = V - v0 < dm.vc ? V - v0 : dm.vc;
+    const int64_t vp = (vn + 63) / 64 * 64;
+    if (vs::launch_fused_grad(hid, ldh, W + v0 * src->ld_weight, src->ld_weight, T, H, vn, v0, src->temperature,
+                              src->temperature_scalar, target_ids, lse, entropy, grad_logprob, grad_entropy, G, dm.vc,
+                              GT, dm.tp, vp, dm.tp, stream))
+      return VS_E_DEVICE;
+    if (grad_hidden) {  // d_hidden [T][H] (+)= G [T][vp] . (W^T [H][vp])^T
+      if (vs::launch_transpose_pad(W + v0 * src->ld_weight, src->ld_weight, vn, H, WT, dm.vc, vp, stream) ||
+          vs::launch_gemm_nt(G, dm.vc, T, WT, dm.vc, H, vp, grad_hidden, ld_grad_hidden, v0 > 0, stream))
+        return VS_E_DEVICE;
+    }
+    if (grad_weight) {  // d_weight [vn][H] = G^T [vn][Tp] . (hidden^T [H][Tp])^T
+      if (vs::launch_gemm_nt(GT, dm.tp, vn, hT, dm.tp, H, dm.tp, grad_weight + v0 * ld_grad_weight, ld_grad_weight,
+                             false, stream))
+        return VS_E_DEVICE;
+    }
+  }
+  vs::timer_mark(1, stream);
+  return VS_OK;
 }
 
 int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T, int64_t V,

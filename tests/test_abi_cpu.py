@@ -239,3 +239,25 @@ def test_l1_loss_validation(lib):
     assert call(scale=float("inf")) == C.VS_E_PARAM
     assert call(ws=None) == C.VS_E_WORKSPACE
     assert call(grad=None, ldg=0, gdt=7, ws=None) == C.VS_E_WORKSPACE  # no gradient: its dtype is not read
+
+
+def test_backward_validation(lib):
+    from logprob_entropy_sampling_amd import _capi as C
+    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT)
+
+    def call(src, targets=FAKE, lse=FAKE, ent=FAKE, ge=None, chunk=8192, gh=FAKE, ldgh=64, gw=FAKE, ldgw=64,
+             ws=FAKE, nws=1 << 40):
+        return lib.vs_score_full_backward(ctypes.byref(src), targets, lse, ent, FAKE, ge, chunk, gh, ldgh, gw, ldgw,
+                                          ws, nws, None)
+    assert call(_src()) == C.VS_E_UNSUPPORTED  # a logits source
+    assert call(_src(**hw), lse=None) == C.VS_E_NULL
+    assert call(_src(**hw), ent=None, ge=FAKE) == C.VS_E_NULL
+    assert call(_src(**hw), gh=None, gw=None) == C.VS_E_NULL
+    assert call(_src(**hw), chunk=0) == C.VS_E_PARAM
+    assert call(_src(**hw), ldgh=63) == C.VS_E_SHAPE
+    assert call(_src(**hw), gw=FAKE + 2) == C.VS_E_ALIGN
+    assert call(_src(**hw), ws=None) == C.VS_E_WORKSPACE
+    big = _src(T=4096, H=4096, V=151936, ld_hidden=4096, ld_weight=4096, **hw)
+    n = lib.vs_workspace_size(C.VS_OP_SCORE_FULL_BACKWARD, ctypes.byref(big), 8192)
+    # hidden^T, G, G^T and one chunk of W^T, bf16
+    assert n >= 2 * (4096 * 4096 + 4096 * 8192 + 8192 * 4096 + 4096 * 8192)

@@ -1,0 +1,119 @@
+"""GPU parity: the VJP of full-vocabulary scoring through the fused projection vs the fp64 oracle.
+
+Tolerance, from the arithmetic: the kernel rounds each logit gradient dX to
+bf16 (relative 2^-9) before the two products, whose bf16 x bf16 terms are
+exact and whose sums are fp32, so element by element
+  |grad_hidden - ref| <= (2^-8 + 1e-4) (|dX| |W|)[t, h]
+  |grad_weight - ref| <= (2^-8 + 1e-4) (|dX|^T |bf16(hidden)|)[v, h]
+with |dX| the oracle's (the 1e-4 covers the fp32 sums and the forward's
+fp32 logits inside p)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import bf16_tensor, say, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+REL = 2.0 ** -8 + 1e-4
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    import logprob_entropy_sampling_amd as m
+    m.lib()
+    return m
+
+
+def _close(label, got, ref, bound):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    worst = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+    say(f"  {label}: max |err| {err.max():.3e}, max |err|/bound {(err / np.maximum(bound, 1e-30)).max():.3f}")
+    assert (err <= bound).all(), f"{label}: gpu {got[worst]!r} oracle {ref[worst]!r} bound {bound[worst]!r} at {worst}"
+
+
+def _case(vsa, T, H, V, chunk, hidden_dtype, seed, with_lp=True, with_ent=True, bad_rows=()):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.08).astype(np.float32))
+    tau = rng.uniform(0.6, 1.4, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    for r in bad_rows:
+        y[r] = V + 3  # a bad target: the forward marks the row BAD, it gets no gradient
+    a = rng.normal(0, 1, T).astype(np.float32) if with_lp else None
+    b = rng.normal(0, 1, T).astype(np.float32) if with_ent else None
+    if hidden_dtype == "bf16":
+        hb = workloads.to_bf16_bits(h)
+        hid, h_arg = bf16_tensor(hb), hb
+    else:
+        hid, h_arg = to_dev(h), h
+    w = bf16_tensor(wb)
+    fw = vsa.score_full(to_dev(y), hidden=hid, weight=w, temperature=to_dev(tau))
+    got = vsa.score_full_backward(to_dev(y), fw["lse"], fw["entropy"], hidden=hid, weight=w,
+                                  grad_logprob=None if a is None else to_dev(a),
+                                  grad_entropy=None if b is None else to_dev(b), temperature=to_dev(tau),
+                                  vocab_chunk=chunk)
+    again = vsa.score_full_backward(to_dev(y), fw["lse"], fw["entropy"], hidden=hid, weight=w,
+                                    grad_logprob=None if a is None else to_dev(a),
+                                    grad_entropy=None if b is None else to_dev(b), temperature=to_dev(tau),
+                                    vocab_chunk=chunk)
+    assert torch.equal(got["grad_hidden"], again["grad_hidden"]) and torch.equal(got["grad_weight"], again["grad_weight"])
+    ref = oracle.score_full_vjp(h_arg, hidden_dtype, wb, tau, y, a, b)
+    adx = np.abs(ref["d_logits"])
+    h64 = oracle.widen_bf16(oracle.round_f32_to_bf16(h) if hidden_dtype == "f32" else h_arg)
+    w64 = oracle.widen_bf16(wb)
+    _close("grad_hidden", got["grad_hidden"].cpu().numpy(), ref["d_hidden"], REL * (adx @ np.abs(w64)) + 1e-30)
+    _close("grad_weight", got["grad_weight"].cpu().numpy(), ref["d_weight"], REL * (adx.T @ np.abs(h64)) + 1e-30)
+    for r in bad_rows:
+        assert (got["grad_hidden"][r] == 0).all()
+    return got
+
+
+@pytest.mark.parametrize("T,H,V,chunk,hdt", [
+    (300, 256, 5003, 1024, "bf16"),    # 5 vocabulary chunks, the last ragged; H: 64-wide K stages
+    (77, 96, 700, 256, "f32"),         # T and every chunk ragged; H = 96: the 32-wide pipelined sweep
+    (130, 40, 2000, 600, "bf16"),      # H = 40: the register-staged sweep; chunk rounded up to 768
+    (513, 1024, 30000, 8192, "bf16"),  # 4 chunks of 8192 rows
+])
+def test_backward_matches_oracle(vsa, T, H, V, chunk, hdt):
+    say(f"backward: T={T} H={H} V={V} vocab_chunk={chunk} hidden {hdt}, logprob and entropy gradients, bad rows")
+    _case(vsa, T, H, V, chunk, hdt, seed=T + H + V, bad_rows=(3, T - 1))
+
+
+@pytest.mark.parametrize("lp,ent", [(True, False), (False, True)])
+def test_backward_one_term(vsa, lp, ent):
+    say(f"backward: only the {'logprob' if lp else 'entropy'} gradient")
+    _case(vsa, 200, 128, 3000, 1024, "bf16", seed=7, with_lp=lp, with_ent=ent)
+
+
+def test_backward_full_size(vsa):
+    say("backward: the fused workload T=4096 H=4096 V=151936 (chunk 8192): sampled rows, column sums, determinism")
+    c = workload(4)
+    T, V = c["T"], c["V"]
+    rng = np.random.default_rng(44)
+    a = rng.normal(0, 1, T).astype(np.float32)
+    b = rng.normal(0, 1, T).astype(np.float32)
+    hid, w = bf16_tensor(c["hidden"]), bf16_tensor(c["weight"])
+    y = to_dev(c["targets"])
+    fw = vsa.score_full(y, hidden=hid, weight=w)
+    got = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
+                                  grad_entropy=to_dev(b))
+    again = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
+                                    grad_entropy=to_dev(b))
+    assert torch.equal(got["grad_hidden"], again["grad_hidden"]) and torch.equal(got["grad_weight"], again["grad_weight"])
+    # grad_hidden of rows spread over every token tile, against the oracle row by row
+    rows = np.array([0, 255, 256, 1500, 2047, 3000, 4095])
+    x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
+    dx = oracle.logit_vjp(x, 1.0, c["targets"][rows], a[rows], b[rows])
+    w64_abs = np.abs(oracle.widen_bf16(c["weight"]))
+    ref = dx @ oracle.widen_bf16(c["weight"])
+    _close("grad_hidden rows", got["grad_hidden"].cpu().numpy()[rows], ref, REL * (np.abs(dx) @ w64_abs) + 1e-30)
+    # every row of dX sums to 0, so the columns of grad_weight sum to 0 up to the rounding of its terms
+    gw = got["grad_weight"]
+    colsum = gw.sum(0, dtype=torch.float64).abs().cpu().numpy()
+    scale = gw.abs().sum(0, dtype=torch.float64).cpu().numpy()
+    assert (colsum <= 2.0 ** -7 * scale + 1e-6).all(), float((colsum / scale).max())
+    assert torch.isfinite(gw).all() and torch.isfinite(got["grad_hidden"]).all()
