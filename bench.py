@@ -167,6 +167,35 @@ def bench_fused(vsa, dev, steps, warmup):
     }
 
 
+def bench_backward(vsa, dev, c, steps, warmup):
+    """The VJP of the fused workload (same inputs as the headline): recomputed
+    logits, their gradient, d_hidden and d_weight; three 2 T H V products."""
+    import torch
+    T, H, V = c["T"], c["H"], c["V"]
+    hid, w, y = _bf16(c["hidden"], dev), _bf16(c["weight"], dev), _dev(c["targets"], dev)
+    fw = vsa.score_full(y, hidden=hid, weight=w)
+    rng = np.random.default_rng(44)
+    a = _dev(rng.normal(0, 1, T).astype(np.float32), dev)
+    b = _dev(rng.normal(0, 1, T).astype(np.float32), dev)
+    # the whole vocabulary as one chunk: one d_hidden product with K = V (no
+    # accumulate passes); its workspace is 3 x T x V bf16 (3.7 GB here)
+    chunk = V
+    o = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=a, grad_entropy=b,
+                                vocab_chunk=chunk)
+    wsp = torch.empty(vsa.workspace_bytes("score_full_backward", hidden=hid, weight=w, width=chunk),
+                      dtype=torch.uint8, device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w,
+                                                               grad_logprob=a, grad_entropy=b, vocab_chunk=chunk,
+                                                               out=o, workspace=wsp), steps, warmup)
+    med, iqr = _median_iqr(ev)
+    flops = 3 * 2.0 * T * H * V
+    return {"T": T, "H": H, "V": V, "vocab_chunk": chunk, "workspace_bytes": int(wsp.numel()),
+            "ms_median": round(med, 4), "ms_iqr": round(iqr, 4),
+            "tokens_per_s": round(T / (med * 1e-3), 1), "flop_per_call": flops,
+            "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def _oracle_threads():
     """(threads the oracle runs on, CPUs in this process's affinity set): every
     CPU the process may use, at most 16 (one GPU's share of the host)."""
@@ -339,6 +368,20 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
             lambda r: oracle.l1_distance(oracle.logits_from_logits(c["logits"], "bf16", rows=r),
                                          oracle.logits_from_logits(c["draft"], "bf16", rows=r)), T, cpu_budget_s),
             "transforms_l1 rows (two softmaxes, L1, accept_rate)")
+    del o
+    # the weighted L1 distillation loss and its draft-logit gradient (bf16): the page's loss-path
+    # shapes (V = 151,936 at 128 and 512 rows) and the full draft workload (2048 rows)
+    for T_l in (128, 512, T):
+        tl, dl = lg[:T_l], dr[:T_l]
+        wl = torch.ones(T_l, dtype=torch.float32, device=dev)
+        o = vsa.l1_loss(tl, dl, weights=wl)
+        wsp = torch.empty(max(1, vsa.workspace_bytes("l1_loss", logits=tl)), dtype=torch.uint8, device=dev)
+        ev, sw = _event_times(vsa, lambda: vsa.l1_loss(tl, dl, weights=wl, out=o, workspace=wsp), steps, warmup, flush)
+        # reads: both rows twice (distance pass), both again (gradient pass); writes: the bf16 gradient
+        byts = 3 * 2 * T_l * V * 2 + T_l * V * 2 + T_l * (4 + 8) + 12
+        res[f"l1_loss_T{T_l}"] = _path_entry(T_l, ev, sw, byts, byts, V=V, grad_dtype="bf16",
+                                             context_rtx4090_loss_path_ms={128: 2.531, 512: 11.593}.get(T_l))
+        del o, wsp
     torch.cuda.synchronize()
     return res
 
@@ -409,6 +452,8 @@ def main():
         "roofline": fused["roofline"],
     }
     if args.paths == "all":
+        print("bench: fused backward", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(vsa, dev, c, max(3, min(args.steps, 10)), 1)
         print("bench: secondary paths", file=sys.stderr, flush=True)
         out["paths"] = bench_paths(vsa, dev, max(5, min(args.steps, 20)), 2, cpu=args.cpu_baseline == "on")
     if probe is not None:

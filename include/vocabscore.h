@@ -178,7 +178,10 @@ int vs_score_full(const vs_source* src, const int64_t* target_ids, int64_t vocab
  * required with grad_entropy.  grad_hidden and grad_weight nullable (at
  * least one).  A row the forward marked BAD_INPUT (its lse not finite, an
  * invalid tau or target) contributes no gradient.  Workspace:
- * vs_workspace_size(VS_OP_SCORE_FULL_BACKWARD, src, vocab_chunk).
+ * vs_workspace_size(VS_OP_SCORE_FULL_BACKWARD, src, vocab_chunk), about
+ * 2 (2T + H) vocab_chunk + 2 H T bytes (bf16 dX, its transpose and the
+ * chunk's transposed weight rows); vocab_chunk >= V makes one chunk, the
+ * fastest form (one d_hidden product over the whole vocabulary).
  */
 int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, const float* lse, const float* entropy,
                            const float* grad_logprob, const float* grad_entropy, int64_t vocab_chunk,

@@ -172,10 +172,12 @@ def _outputs(spec, dev, out):
 def workspace_bytes(op: str, *, logits=None, hidden=None, weight=None, width: int = 0) -> int:
     """Bytes of workspace an entry point needs for these inputs (vs_workspace_size);
     op is one of "score_full", "score_support_ids", "score_transforms", "l1_distance",
-    "sample_transforms", "l1_loss"."""
+    "sample_transforms", "l1_loss", "score_full_backward" (width = the support width, or the
+    backward's vocab_chunk)."""
     ops = {"score_full": _capi.VS_OP_SCORE_FULL, "score_support_ids": _capi.VS_OP_SCORE_SUPPORT,
            "score_transforms": _capi.VS_OP_SCORE_TRANSFORMS, "l1_distance": _capi.VS_OP_L1_DISTANCE,
-           "sample_transforms": _capi.VS_OP_SAMPLE_TRANSFORMS, "l1_loss": _capi.VS_OP_L1_LOSS}
+           "sample_transforms": _capi.VS_OP_SAMPLE_TRANSFORMS, "l1_loss": _capi.VS_OP_L1_LOSS,
+           "score_full_backward": _capi.VS_OP_SCORE_FULL_BACKWARD}
     src, _, _ = _make_source(logits, hidden, weight, 1.0)
     return workspace_size(ops[op], src, width)
 

@@ -248,8 +248,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
 //   kEpiPartials  the softmax statistics above (the forward scoring op);
 //   kEpiGrad      the logits' gradient of sum_t (a_t logprob_t + b_t H_t):
 //                 dx = (a ([v = y] - p_v) - b p_v (ln p_v + H)) / tau, written
-//                 as bf16 twice, G[t][v] and G^T[v][t] (zeros in the padding
-//                 rows and columns up to the K-multiples of the GEMMs that read them);
+//                 as bf16 into G[t][v] (zeros in the padding columns up to
+//                 v_pad, the K multiple of the GEMM that reads them);
 //   kEpiStore     C[m][n] = acc, or += acc (fp32, n contiguous): a plain GEMM.
 enum { kEpiPartials = 0, kEpiGrad = 1, kEpiStore = 2 };
 struct EpiArgs {
@@ -261,10 +261,8 @@ struct EpiArgs {
   const float* grad_entropy;  // nullable: 0
   uint16_t* g;               // [rows][ld_g]: column = vocabulary row of the sweep
   int64_t ld_g;
-  uint16_t* gt;              // [vocab rows][ld_gt]: column = token
-  int64_t ld_gt;
   int64_t v_begin;           // vocabulary id of the sweep's first row (the target test)
-  int64_t v_pad, t_pad;      // zero-filled up to these
+  int64_t v_pad;             // G's columns are zero-filled up to this
   float* c;                  // kEpiStore
   int64_t ldc;
   int accumulate;
@@ -276,12 +274,50 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// The gradient of the tile's logits.  Row data of the lane's 4 token columns
-// are loaded here (one round of loads per tile).  A row whose LSE is not
-// finite (a BAD_INPUT row of the forward) gets a zero gradient.
+// The row data of the lane's 4 token columns for the gradient, loaded when
+// the workgroup starts (their latency hides behind the K loop): base-2 scale,
+// 1/tau, base-2 LSE, entropy, the two upstream gradients (0 on a bad row) and
+// the target's row relative to the sweep's first row.
+struct GradColumns {
+  float c[4], inv_tau[4], l2[4], h[4], ga[4], gb[4];
+  int64_t y[4];
+};
+__device__ __forceinline__ GradColumns load_grad_columns(int64_t t0, int64_t rows_valid, const float* __restrict__ temp,
+                                                         float temp_scalar, const int64_t* __restrict__ targets,
+                                                         const EpiArgs& ep) {
+  const int lane = threadIdx.x & 63;
+  const int wt = threadIdx.x >> 7;
+  GradColumns g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + wt * 128 + 32 * j + (lane & 31);
+    const int64_t tr = t < rows_valid ? t : 0;
+    const float tau = temp ? temp[tr] : temp_scalar;
+    const float lse = ep.lse[tr];
+    const int64_t y = targets[tr];
+    float ga = ep.grad_logprob ? ep.grad_logprob[tr] : 0.0f;
+    float gb = ep.grad_entropy ? ep.grad_entropy[tr] : 0.0f;
+    float h = gb != 0.0f ? ep.entropy[tr] : 0.0f;
+    if (!(t < rows_valid && tau_ok(tau) && lse > -__builtin_inff() && lse < __builtin_inff() && h == h && y >= 0)) {
+      ga = 0.0f;  // no gradient through a bad row (or a column past the last row)
+      gb = 0.0f;
+      h = 0.0f;
+    }
+    g.c[j] = kLog2e / tau;
+    g.inv_tau[j] = 1.0f / tau;
+    g.l2[j] = lse * kLog2e;  // base-2 LSE
+    g.h[j] = h;
+    g.ga[j] = ga;
+    g.gb[j] = gb;
+    g.y[j] = y - ep.v_begin;
+  }
+  return g;
+}
+
+// The gradient of the tile's logits into G (bf16, nearest even).  A row whose
+// LSE is not finite (a BAD_INPUT row of the forward) gets a zero gradient.
 __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t t0, int64_t rows_valid,
-                                              int64_t V, const float* __restrict__ temp, float temp_scalar,
-                                              const int64_t* __restrict__ targets, const EpiArgs& ep) {
+                                              int64_t V, const GradColumns& gc, const EpiArgs& ep) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wv = w & 1;
@@ -292,9 +328,8 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
   const int vrow0 = wv * 128 + 4 * lh;  // + 32 i + 8 q + e
   const int nv = int(V - v0 < BV ? V - v0 : BV);
   const int np = int(ep.v_pad - v0 < BV ? ep.v_pad - v0 : BV);
-  uint16_t* const gt_tile = ep.gt + v0 * ep.ld_gt + t0;  // + vr * ld_gt + col
-  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;     // + col * ld_g + vr
-  const int ldgt = int(ep.ld_gt), ldg = int(ep.ld_g);
+  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;  // + col * ld_g + vr
+  const int ldg = int(ep.ld_g);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // the accumulators of the columns not written yet stay in AGPRs until their turn
@@ -303,35 +338,18 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
     const int col = wt * 128 + 32 * j + lr;
-    const int64_t t = t0 + col;
-    const bool tvalid = t < rows_valid;
-    const bool tpad = t < ep.t_pad;
-    float c = 0.0f, inv_tau = 0.0f, l2 = 0.0f, h = 0.0f, ga = 0.0f, gb = 0.0f;
-    int yr = -1;  // the target's tile-relative row, if it is in this tile
-    if (tvalid) {
-      const float tau = temp ? temp[t] : temp_scalar;
-      const float lse = ep.lse[t];
-      const int64_t y = targets[t];
-      ga = ep.grad_logprob ? ep.grad_logprob[t] : 0.0f;
-      gb = ep.grad_entropy ? ep.grad_entropy[t] : 0.0f;
-      h = gb != 0.0f ? ep.entropy[t] : 0.0f;
-      if (!(tau_ok(tau) && lse > -__builtin_inff() && lse < __builtin_inff() && h == h && y >= 0)) {
-        ga = 0.0f;  // no gradient through a bad row
-        gb = 0.0f;
-        h = 0.0f;
-      }
-      const int64_t yv = y - ep.v_begin - v0;
-      yr = (yv >= 0 && yv < BV) ? int(yv) : -1;
-      c = kLog2e / tau;
-      inv_tau = 1.0f / tau;
-      l2 = lse * kLog2e;  // base-2 LSE
-    }
+    const bool tvalid = t0 + col < rows_valid;
+    const float c = gc.c[j], inv_tau = gc.inv_tau[j], l2 = gc.l2[j], h = gc.h[j], ga = gc.ga[j], gb = gc.gb[j];
+    const int64_t yv = gc.y[j] - v0;
+    const int yr = (yv >= 0 && yv < BV) ? int(yv) : -1;  // the target's tile-relative row
     const bool live = tvalid && (ga != 0.0f || gb != 0.0f);
+    if (!tvalid) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int vb = vrow0 + 32 * i + 8 * q;  // rows vb .. vb+3 of the tile
+        if (vb >= np) continue;
         uint16_t gv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -345,15 +363,9 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
           }
           gv[e] = bf16_rne_bits(dx);
         }
-        if (tpad) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (vb + e < np) gt_tile[(vb + e) * ldgt + col] = gv[e];
-        }
-        if (tvalid && vb < np) {  // v_pad is a multiple of 4
-          *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
-              make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
-        }
+        // v_pad is a multiple of 4
+        *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
+            make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
       }
   }
 }
@@ -404,7 +416,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
   __shared__ uint4 As[2][BV * CH];
   __shared__ uint4 Bs[2][BT * CH];
   ColumnLoads cl{};
+  GradColumns gcol{};
   if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, row_map);
+  if (MODE == kEpiGrad) gcol = load_grad_columns(t0, rows_valid, temp, temp_scalar, targets, ep);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -494,7 +508,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -547,7 +561,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
   __shared__ uint4 A0[BV * CH], A1[BV * CH], A2[BV * CH], A3[BV * CH];
   __shared__ uint4 B0[BT * CH], B1[BT * CH], B2[BT * CH], B3[BT * CH];
   ColumnLoads cl{};
+  GradColumns gcol{};
   if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
+  if (MODE == kEpiGrad) gcol = load_grad_columns(t0, rows_valid, temp, temp_scalar, targets, ep);
   // slot indices are compile-time constants after unrolling
   auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : i == 1 ? A1 : i == 2 ? A2 : A3; };
   auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : i == 1 ? B1 : i == 2 ? B2 : B3; };
@@ -702,7 +718,7 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
     tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -749,7 +765,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
   auto SA = [&](int i) -> uint4* { return i == 0 ? A0 : A1; };
   auto SB = [&](int i) -> uint4* { return i == 0 ? B0 : B1; };
   ColumnLoads cl{};
+  GradColumns gcol{};
   if (MODE == kEpiPartials) cl = load_columns(t0, rows_valid, temp, temp_scalar, targets, BUF ? nullptr : row_map);
+  if (MODE == kEpiGrad) gcol = load_grad_columns(t0, rows_valid, temp, temp_scalar, targets, ep);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -893,27 +911,55 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
     tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, temp, temp_scalar, targets, ep);
+    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
 
 // dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < R_pad: a bf16
 // transpose through a 64 x 64 LDS tile (reads and writes along rows of 64).
+// dst[c][r] = src[r][c] for c < C, r < R_pad (0 for r >= R), by 64 x 64
+// tiles through LDS.  A thread moves 16 consecutive values (two 16-byte
+// accesses where the row's alignment and extent allow, else one value at a
+// time) on both sides.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t ld_s, int64_t R,
                                                             int64_t C, uint16_t* __restrict__ dst, int64_t ld_d,
                                                             int64_t R_pad) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][72];  // row stride 144 B: 16-byte aligned, rows spread over the banks
   const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k, c = c0 + tx;
-    tile[k][tx] = (r < R && c < C) ? src[r * ld_s + c] : uint16_t(0);
+  const int a = threadIdx.x >> 2, b = (threadIdx.x & 3) * 16;  // row a, columns b .. b+15 of the tile
+  {
+    const int64_t r = r0 + a, c = c0 + b;
+    uint4 v[2];
+    uint16_t* h = reinterpret_cast<uint16_t*>(v);
+    const uint16_t* p = src + r * ld_s + c;
+    if (r < R && c + 16 <= C && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
+      v[0] = reinterpret_cast<const uint4*>(p)[0];
+      v[1] = reinterpret_cast<const uint4*>(p)[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) h[k] = (r < R && c + k < C) ? p[k] : uint16_t(0);
+    }
+    *reinterpret_cast<uint4*>(&tile[a][b]) = v[0];
+    *reinterpret_cast<uint4*>(&tile[a][b + 8]) = v[1];
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t c = c0 + k, r = r0 + tx;
-    if (c < C && r < R_pad) dst[c * ld_d + r] = tile[tx][k];
+  {
+    const int64_t c = c0 + a, r = r0 + b;  // output row c, its columns r .. r+15
+    if (c >= C || r >= R_pad) return;
+    uint4 v[2];
+    uint16_t* h = reinterpret_cast<uint16_t*>(v);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) h[k] = tile[b + k][a];
+    uint16_t* p = dst + c * ld_d + r;
+    if (r + 16 <= R_pad && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
+      reinterpret_cast<uint4*>(p)[0] = v[0];
+      reinterpret_cast<uint4*>(p)[1] = v[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (r + k < R_pad) p[k] = h[k];
+    }
   }
 }
 
@@ -1007,8 +1053,7 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
 int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                       int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
                       const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
-                      const float* grad_entropy, uint16_t* g, int64_t ld_g, uint16_t* gt, int64_t ld_gt,
-                      int64_t v_pad, int64_t t_pad, void* stream) {
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, void* stream) {
   EpiArgs ep{};
   ep.lse = lse;
   ep.entropy = entropy;
@@ -1016,11 +1061,8 @@ int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t*
   ep.grad_entropy = grad_entropy;
   ep.g = g;
   ep.ld_g = ld_g;
-  ep.gt = gt;
-  ep.ld_gt = ld_gt;
   ep.v_begin = v_begin;
   ep.v_pad = v_pad;
-  ep.t_pad = t_pad;
   return launch_sweep<kEpiGrad>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets,
                                 nullptr, nullptr, ep, stream);
 }

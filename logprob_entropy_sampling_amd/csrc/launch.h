@@ -37,12 +37,11 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
 
 // The gradient sweep: the same tiles over weight rows [0, V) (vocabulary ids
 // v_begin + v) x hidden rows [0, rows); writes the logits' gradient as bf16
-// into g [rows][ld_g] and gt [V][ld_gt], zeros up to column v_pad / t_pad.
+// into g [rows][ld_g], zeros in columns V .. v_pad-1 (v_pad a multiple of 4).
 int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                       int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
                       const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
-                      const float* grad_entropy, uint16_t* g, int64_t ld_g, uint16_t* gt, int64_t ld_gt,
-                      int64_t v_pad, int64_t t_pad, void* stream);
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, void* stream);
 
 // c[m][n] (+)= sum_k a[m][k] b[n][k] (bf16 in, fp32 out; K a multiple of 8,
 // lda, ldb multiples of 8, a and b 16-byte aligned): the sweep's MFMA loop

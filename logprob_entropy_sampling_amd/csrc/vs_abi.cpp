@@ -351,7 +351,7 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
     const int64_t vp = (vn + 63) / 64 * 64;
     if (vs::launch_fused_grad(hid, ldh, W + v0 * src->ld_weight, src->ld_weight, T, H, vn, v0, src->temperature,
                               src->temperature_scalar, target_ids, lse, entropy, grad_logprob, grad_entropy, G, dm.vc,
-                              GT, dm.tp, vp, dm.tp, stream))
+                              vp, stream))
       return VS_E_DEVICE;
     if (grad_hidden) {  // d_hidden [T][H] (+)= G [T][vp] . (W^T [H][vp])^T
       if (vs::launch_transpose_pad(W + v0 * src->ld_weight, src->ld_weight, vn, H, WT, dm.vc, vp, stream) ||
@@ -359,7 +359,8 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
         return VS_E_DEVICE;
     }
     if (grad_weight) {  // d_weight [vn][H] = G^T [vn][Tp] . (hidden^T [H][Tp])^T
-      if (vs::launch_gemm_nt(GT, dm.tp, vn, hT, dm.tp, H, dm.tp, grad_weight + v0 * ld_grad_weight, ld_grad_weight,
+      if (vs::launch_transpose_pad(G, dm.vc, T, vn, GT, dm.tp, dm.tp, stream) ||
+          vs::launch_gemm_nt(GT, dm.tp, vn, hT, dm.tp, H, dm.tp, grad_weight + v0 * ld_grad_weight, ld_grad_weight,
                              false, stream))
         return VS_E_DEVICE;
     }

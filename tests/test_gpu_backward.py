@@ -90,7 +90,8 @@ def test_backward_one_term(vsa, lp, ent):
 
 
 def test_backward_full_size(vsa):
-    say("backward: the fused workload T=4096 H=4096 V=151936 (chunk 8192): sampled rows, column sums, determinism")
+    say("backward: the fused workload T=4096 H=4096 V=151936, vocab_chunk 8192 and V (one chunk): sampled rows, "
+        "column sums, the trace identity, determinism")
     c = workload(4)
     T, V = c["T"], c["V"]
     rng = np.random.default_rng(44)
@@ -99,21 +100,45 @@ def test_backward_full_size(vsa):
     hid, w = bf16_tensor(c["hidden"]), bf16_tensor(c["weight"])
     y = to_dev(c["targets"])
     fw = vsa.score_full(y, hidden=hid, weight=w)
-    got = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
-                                  grad_entropy=to_dev(b))
-    again = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
-                                    grad_entropy=to_dev(b))
-    assert torch.equal(got["grad_hidden"], again["grad_hidden"]) and torch.equal(got["grad_weight"], again["grad_weight"])
-    # grad_hidden of rows spread over every token tile, against the oracle row by row
     rows = np.array([0, 255, 256, 1500, 2047, 3000, 4095])
     x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=rows)
     dx = oracle.logit_vjp(x, 1.0, c["targets"][rows], a[rows], b[rows])
-    w64_abs = np.abs(oracle.widen_bf16(c["weight"]))
-    ref = dx @ oracle.widen_bf16(c["weight"])
-    _close("grad_hidden rows", got["grad_hidden"].cpu().numpy()[rows], ref, REL * (np.abs(dx) @ w64_abs) + 1e-30)
-    # every row of dX sums to 0, so the columns of grad_weight sum to 0 up to the rounding of its terms
-    gw = got["grad_weight"]
-    colsum = gw.sum(0, dtype=torch.float64).abs().cpu().numpy()
-    scale = gw.abs().sum(0, dtype=torch.float64).cpu().numpy()
-    assert (colsum <= 2.0 ** -7 * scale + 1e-6).all(), float((colsum / scale).max())
-    assert torch.isfinite(gw).all() and torch.isfinite(got["grad_hidden"]).all()
+    w64 = oracle.widen_bf16(c["weight"])
+    ref = dx @ w64
+    bound = REL * (np.abs(dx) @ np.abs(w64)) + 1e-30
+    h64 = oracle.widen_bf16(c["hidden"])
+    first = None
+    for chunk in (8192, V):
+        say(f"  vocab_chunk {chunk}")
+        got = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
+                                      grad_entropy=to_dev(b), vocab_chunk=chunk)
+        again = vsa.score_full_backward(y, fw["lse"], fw["entropy"], hidden=hid, weight=w, grad_logprob=to_dev(a),
+                                        grad_entropy=to_dev(b), vocab_chunk=chunk)
+        assert torch.equal(got["grad_hidden"], again["grad_hidden"])
+        assert torch.equal(got["grad_weight"], again["grad_weight"])
+        del again
+        # grad_hidden of rows spread over every token tile, against the oracle row by row
+        _close(f"grad_hidden rows (chunk {chunk})", got["grad_hidden"].cpu().numpy()[rows], ref, bound)
+        gw = got["grad_weight"]
+        # every row of dX sums to 0, so the columns of grad_weight sum to 0 up to the rounding of its terms
+        colsum = gw.sum(0, dtype=torch.float64).abs().cpu().numpy()
+        scale = gw.abs().sum(0, dtype=torch.float64).cpu().numpy()
+        assert (colsum <= 2.0 ** -7 * scale + 1e-6).all(), float((colsum / scale).max())
+        assert torch.isfinite(gw).all() and torch.isfinite(got["grad_hidden"]).all()
+        # both products hold the same dX: sum(grad_hidden * hidden) = sum(grad_weight * W) = sum(dX * logits)
+        gh64 = got["grad_hidden"].cpu().numpy().astype(np.float64)
+        lhs, lhs_abs = float((gh64 * h64).sum()), float(np.abs(gh64 * h64).sum())
+        gw_cpu = gw.cpu().numpy()
+        rhs = rhs_abs = 0.0
+        for v0 in range(0, V, 16384):
+            prod = gw_cpu[v0:v0 + 16384].astype(np.float64) * w64[v0:v0 + 16384]
+            rhs += float(prod.sum())
+            rhs_abs += float(np.abs(prod).sum())
+        say(f"  trace identity: {lhs:.6e} vs {rhs:.6e}")
+        assert abs(lhs - rhs) <= 1e-4 * (lhs_abs + rhs_abs), (lhs, rhs)
+        if first is None:
+            first = got
+        else:  # the chunking changes only grad_hidden's summation order, and grad_weight not at all
+            assert torch.equal(first["grad_weight"], got["grad_weight"])
+            dh = float((first["grad_hidden"] - got["grad_hidden"]).abs().max())
+            assert dh <= 1e-4 * float(got["grad_hidden"].abs().max()), dh
