@@ -232,15 +232,24 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  *   support_ids_out       [T, support_ids_cap] int64: pi[0:min(L, cap)], -1
  *                         padded; SUPPORT_TRUNCATED if L > cap (nullable)
  *   full_lse[t]           full-vocabulary LSE of z (nullable)
- * Source must be VS_SRC_LOGITS with VS_BF16 logits (else VS_E_UNSUPPORTED);
- * the transform parameters are never ignored.  support_ids_cap > 4096 with a
+ * Sources: VS_BF16 logits (VS_F32 logits give VS_E_UNSUPPORTED), or a
+ * hidden/weight source (xorl issue #71, "Proposed direction" item 3: support
+ * masking over the chunked projection), whose logits are
+ *   x[t, v] = bf16_rne(sum_h bf16(hidden[t, h]) W[v, h])   (fp32 sums)
+ * - the fused sweep's fp32 logits rounded to bf16, nearest even - computed by
+ * the MFMA sweep for blocks of up to 2048 token rows into the workspace and
+ * scored block by block; the caller never sees them.
+ * The transform parameters are never ignored.  support_ids_cap > 4096 with a
  * non-NULL support_ids_out gives VS_E_UNSUPPORTED.  A target outside S_t gives
  * logprob -inf and TARGET_OUTSIDE_SUPPORT.  BAD_INPUT rows: NaN floats,
  * support_len 0, ids -1.  entropy, row_status, support_len, threshold_logit,
- * threshold_ties, full_lse nullable; logprob required.  Workspace: T bytes for
- * V <= 81920; above that also a per-row record of 149,760 bytes (the count
+ * threshold_ties, full_lse nullable; logprob required.  Workspace
+ * (vs_workspace_size(VS_OP_SCORE_TRANSFORMS, src, 0)): T bytes for V <= 81920;
+ * above that also a per-row record of 149,760 bytes, its worst case (the count
  * pass hands the finishing pass each row's non-empty key counts and dense-id
- * candidates through it).
+ * candidates through it).  A hidden/weight source needs these for one block
+ * of min(T, 2048) rows, plus that block's logits (rows x V rounded up to 8,
+ * bf16) and, for an fp32 hidden state, its bf16 copy (T x H x 2 bytes).
  */
 int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float* top_p,
                         const float* min_p, const int64_t* target_ids, float* logprob,
@@ -261,8 +270,10 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
  *   (v div 4, t, offset mod 2^32, offset div 2^32) under the key
  *   (seed mod 2^32, seed div 2^32).
  * A (seed, offset) pair gives a fixed draw on every run; distinct offsets
- * give independent draws.  Parameters and source rules as for
- * vs_score_transforms (bf16 logits only).  Outputs:
+ * give independent draws.  Parameters and sources as for
+ * vs_score_transforms (bf16 logits, or a hidden/weight source through its
+ * bf16-rounded logits; t is always the row's index in the whole batch).
+ * Outputs:
  *   sampled_ids [T] int64 (-1 on a BAD_INPUT row)
  *   row_status, support_len, threshold_logit, threshold_ties  (nullable) the
  *                row's BAD_INPUT bit and support descriptor.

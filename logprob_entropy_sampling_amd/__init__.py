@@ -292,11 +292,13 @@ def score_support_ids(targets, support_ids, *, logits=None, hidden=None, weight=
     return o
 
 
-def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, cap=0, with_full_lse=True, out=None,
-                     workspace=None):
+def score_transforms(targets, logits, top_k, top_p, min_p, *, hidden=None, weight=None, temperature=1.0, cap=0,
+                     with_full_lse=True, out=None, workspace=None):
     """Top-k / top-p / min-p support scores and support descriptor
-    (vs_score_transforms); ``out`` and ``workspace`` as for score_full."""
-    src, dev, _keep = _make_source(logits=logits, temperature=temperature)
+    (vs_score_transforms) over bf16 ``logits``, or (``logits=None``) over the
+    bf16-rounded projection of ``hidden`` and ``weight``; ``out`` and
+    ``workspace`` as for score_full."""
+    src, dev, _keep = _make_source(logits, hidden, weight, temperature)
     T = src.T
     _ids("targets", targets, T)
     for name, t, dt in (("top_k", top_k, torch.int32), ("top_p", top_p, torch.float32),
@@ -325,12 +327,14 @@ def score_transforms(targets, logits, top_k, top_p, min_p, *, temperature=1.0, c
     return out
 
 
-def sample_transforms(logits, top_k, top_p, min_p, *, seed, offset=0, temperature=1.0, out=None, workspace=None):
+def sample_transforms(logits, top_k, top_p, min_p, *, seed, offset=0, hidden=None, weight=None, temperature=1.0,
+                      out=None, workspace=None):
     """Seeded Gumbel draw of one token per row from the top-k / top-p / min-p
-    support (vs_sample_transforms).  Returns ``sampled`` (int64, -1 on a
-    BAD_INPUT row), ``status`` and the support descriptor; ``out`` and
-    ``workspace`` as for score_full."""
-    src, dev, _keep = _make_source(logits=logits, temperature=temperature)
+    support (vs_sample_transforms), over bf16 ``logits`` or (``logits=None``)
+    the bf16-rounded projection of ``hidden`` and ``weight``.  Returns
+    ``sampled`` (int64, -1 on a BAD_INPUT row), ``status`` and the support
+    descriptor; ``out`` and ``workspace`` as for score_full."""
+    src, dev, _keep = _make_source(logits, hidden, weight, temperature)
     T = src.T
     for name, t, dt in (("top_k", top_k, torch.int32), ("top_p", top_p, torch.float32),
                         ("min_p", min_p, torch.float32)):

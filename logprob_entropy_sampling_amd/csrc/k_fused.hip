@@ -250,8 +250,10 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[4][4], float* red, i
 //                 dx = (a ([v = y] - p_v) - b p_v (ln p_v + H)) / tau, written
 //                 as bf16 into G[t][v] (zeros in the padding columns up to
 //                 v_pad, the K multiple of the GEMM that reads them);
-//   kEpiStore     C[m][n] = acc, or += acc (fp32, n contiguous): a plain GEMM.
-enum { kEpiPartials = 0, kEpiGrad = 1, kEpiStore = 2 };
+//   kEpiStore     C[m][n] = acc, or += acc (fp32, n contiguous): a plain GEMM;
+//   kEpiLogits    the logits themselves, rounded to bf16 (nearest even) into
+//                 G[t][v] (0 in the columns from V up to the next multiple of 4).
+enum { kEpiPartials = 0, kEpiGrad = 1, kEpiStore = 2, kEpiLogits = 3 };
 struct EpiArgs {
   float4* partials;          // kEpiPartials
   float* zy_raw;
@@ -364,6 +366,43 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
           gv[e] = bf16_rne_bits(dx);
         }
         // v_pad is a multiple of 4
+        *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
+            make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
+      }
+  }
+}
+
+// The tile's logits as bf16 into G [token][vocabulary row], 8-byte stores of
+// 4 consecutive vocabulary rows (the row stride ld_g a multiple of 4).
+__device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t t0, int64_t rows_valid,
+                                                int64_t V, const EpiArgs& ep) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wv = w & 1;
+  const int wt = w >> 1;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int vrow0 = wv * 128 + 4 * lh;  // + 32 i + 8 q + e
+  const int nv = int(V - v0 < BV ? V - v0 : BV);
+  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;
+  const int ldg = int(ep.ld_g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int jj = j + 1; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    const int col = wt * 128 + 32 * j + lr;
+    if (t0 + col >= rows_valid) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vb = vrow0 + 32 * i + 8 * q;
+        if (vb >= nv) continue;
+        uint16_t gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv[e] = vb + e < nv ? bf16_rne_bits(acc[i][j][4 * q + e]) : uint16_t(0);
         *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
             make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
       }
@@ -509,6 +548,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
     grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
+  else if constexpr (MODE == kEpiLogits)
+    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -719,6 +760,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
     grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
+  else if constexpr (MODE == kEpiLogits)
+    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -912,6 +955,8 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
     grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
+  else if constexpr (MODE == kEpiLogits)
+    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -1065,6 +1110,15 @@ int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t*
   ep.v_pad = v_pad;
   return launch_sweep<kEpiGrad>(hidden, ld_hidden, weight, ld_weight, rows, H, V, temp, temp_scalar, targets,
                                 nullptr, nullptr, ep, stream);
+}
+
+int launch_fused_logits(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                        int64_t rows, int64_t H, int64_t V, uint16_t* out, int64_t ld_out, void* stream) {
+  EpiArgs ep{};
+  ep.g = out;
+  ep.ld_g = ld_out;
+  return launch_sweep<kEpiLogits>(hidden, ld_hidden, weight, ld_weight, rows, H, V, nullptr, 1.0f, nullptr, nullptr,
+                                  nullptr, ep, stream);
 }
 
 int launch_gemm_nt(const uint16_t* a, int64_t lda, int64_t M, const uint16_t* b, int64_t ldb, int64_t N, int64_t K,

@@ -239,9 +239,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     const uint16_t* __restrict__ logits, int64_t ld, int V, const float* __restrict__ temp, float temp_scalar,
     const uint8_t* __restrict__ status, const float* __restrict__ threshold_logit,
     const int32_t* __restrict__ threshold_ties, const float* __restrict__ row_max, uint64_t seed, uint64_t offset,
-    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status) {
+    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status, int64_t row0) {
   __shared__ SampleSmem sm;
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x;  // local row; row0 + row is the generator's row word
   const int tid = threadIdx.x;
   if (tid == 0 && out_status) out_status[row] = status[row] & kRowBad;
   if (status[row] & kRowBad) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     return;
   }
   DrawArgs d;
-  d.row = row;
+  d.row = row0 + row;
   d.tau = double(temp ? temp[row] : temp_scalar);
   d.xmax = double(row_max[row]);
   d.xmaxf = row_max[row];
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const int64_t nchunk = (int64_t(V) + 7) / 8;
   const bool lds_ranks = nchunk <= kLdsChunks;
   const auto block_ctr = [&](int64_t q, int b) {
-    return philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(row), d.off_lo, d.off_hi}, d.k0, d.k1);
+    return philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(d.row), d.off_lo, d.off_hi}, d.k0, d.k1);
   };
 
   // Every token above the threshold (f_gt) and every token equal to it
@@ -440,11 +440,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                   const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
                   const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
-                  void* stream) {
+                  int64_t row0, void* stream) {
   if (rows <= 0) return 0;
   sample_kernel<<<dim3(unsigned(rows)), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream)>>>(
       logits, ld, int(V), temp, temp_scalar, status, threshold_logit, threshold_ties, row_max, seed, offset, sampled,
-      out_status);
+      out_status, row0);
   return int(hipGetLastError());
 }
 

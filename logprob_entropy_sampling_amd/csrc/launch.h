@@ -49,6 +49,11 @@ int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t*
 int launch_gemm_nt(const uint16_t* a, int64_t lda, int64_t M, const uint16_t* b, int64_t ldb, int64_t N, int64_t K,
                    float* c, int64_t ldc, bool accumulate, void* stream);
 
+// logits [rows][ld_out] (bf16, nearest even) = hidden [rows][H] . weight [V][H]^T:
+// the sweep's MFMA loop with a bf16 store (ld_out a multiple of 4, >= V).
+int launch_fused_logits(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                        int64_t rows, int64_t H, int64_t V, uint16_t* out, int64_t ld_out, void* stream);
+
 // dst[c][r] = src[r][c] (bf16), zeros for R <= r < R_pad.
 int launch_transpose_pad(const uint16_t* src, int64_t ld_s, int64_t R, int64_t C, uint16_t* dst, int64_t ld_d,
                          int64_t R_pad, void* stream);
@@ -97,11 +102,12 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
 
 // Seeded Gumbel draw over the transforms' support descriptor (status and
 // descriptor from launch_transforms, row_max its largest logit per row);
-// out_status (nullable) gets the BAD_INPUT bit.
+// out_status (nullable) gets the BAD_INPUT bit.  Local row r draws with the
+// generator's row word row0 + r.
 int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                   const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
                   const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
-                  void* stream);
+                  int64_t row0, void* stream);
 
 // Draft/target softmax L1.
 int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float* l1, float* accept,

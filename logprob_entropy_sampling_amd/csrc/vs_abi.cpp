@@ -90,12 +90,66 @@ FullWs carve_full(Carver& c, const vs_source* s, int64_t rows) {
   return w;
 }
 
+// Transforms over a hidden/weight source: the sweep writes the bf16 logits of
+// blocks of up to kXfRows token rows into the workspace ([rows][ld], ld = V
+// rounded up to 8 so that every row is 16-byte aligned), and the transforms
+// (and the sampler) run on each block before the next is written.  An fp32
+// hidden state is rounded to bf16 first.
+constexpr int64_t kXfRows = 2048;
+struct XfDims {
+  int64_t rows, ld;
+};
+XfDims xf_dims(const vs_source* s) {
+  return XfDims{s->T < kXfRows ? s->T : kXfRows, (s->V + 7) / 8 * 8};
+}
+// the transforms' workspace, plus (hidden/weight source) the logits block and
+// the rounded hidden state
+size_t xf_ws_bytes(const vs_source* s) {
+  if (s->kind != VS_SRC_HIDDEN_WEIGHT) return round_up(vs::transforms_workspace_bytes(s->T, s->V));
+  const XfDims d = xf_dims(s);
+  size_t b = round_up(size_t(d.rows) * size_t(d.ld) * 2) + round_up(vs::transforms_workspace_bytes(d.rows, s->V));
+  if (s->hidden_dtype == VS_F32) b += round_up(size_t(s->T) * size_t(s->H) * 2);
+  return b;
+}
+
 // the sampler: dummy targets, logprob, status, row maxima, threshold logit and
 // ties (when the caller passes none), then the transforms' own workspace
 size_t sample_ws_bytes(const vs_source* s) {
   const size_t T = size_t(s->T);
-  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 3 * round_up(T * 4) +
-         round_up(vs::transforms_workspace_bytes(s->T, s->V));
+  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 3 * round_up(T * 4) + xf_ws_bytes(s);
+}
+
+template <class P>
+P* at_row(P* p, int64_t row, int64_t stride = 1) {
+  return p ? p + row * stride : nullptr;
+}
+
+// The logits blocks of a hidden/weight source, one after the other: for each
+// block, fn(logits, ld, first row, rows, transforms workspace) runs after the
+// block's sweep.  Returns a VS_ status.
+template <class Fn>
+int over_logit_blocks(const vs_source* src, Carver& c, void* stream, Fn fn) {
+  const XfDims d = xf_dims(src);
+  const uint16_t* hid = static_cast<const uint16_t*>(src->hidden);
+  int64_t ldh = src->ld_hidden;
+  if (src->hidden_dtype == VS_F32) {
+    uint16_t* hb = static_cast<uint16_t*>(c.take(size_t(src->T) * size_t(src->H) * 2));
+    if (vs::launch_round_hidden(static_cast<const float*>(src->hidden), src->ld_hidden, src->T, src->H, hb, stream))
+      return VS_E_DEVICE;
+    hid = hb;
+    ldh = src->H;
+  }
+  uint16_t* L = static_cast<uint16_t*>(c.take(size_t(d.rows) * size_t(d.ld) * 2));
+  uint8_t* tws = static_cast<uint8_t*>(c.take(vs::transforms_workspace_bytes(d.rows, src->V)));
+  for (int64_t r0 = 0; r0 < src->T; r0 += d.rows) {
+    const int64_t n = src->T - r0 < d.rows ? src->T - r0 : d.rows;
+    if (vs::launch_fused_logits(hid + r0 * ldh, ldh, static_cast<const uint16_t*>(src->weight), src->ld_weight, n,
+                                src->H, src->V, L, d.ld, stream))
+      return VS_E_DEVICE;
+    const int rc = fn(static_cast<const uint16_t*>(L), d.ld, r0, n, tws);
+    if (rc) return rc;
+  }
+  return VS_OK;
 }
 
 // Backward of full-vocabulary scoring through the fused projection: per
@@ -195,7 +249,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
   switch (op) {
     case VS_OP_SCORE_FULL: return full_ws_bytes(src, src->T);
     case VS_OP_SCORE_SUPPORT: return support_ws_bytes(src);
-    case VS_OP_SCORE_TRANSFORMS: return round_up(vs::transforms_workspace_bytes(src->T, src->V));
+    case VS_OP_SCORE_TRANSFORMS: return xf_ws_bytes(src);
     case VS_OP_L1_DISTANCE: return round_up(vs::l1_workspace_bytes(src->T, src->V));
     case VS_OP_SAMPLE_TRANSFORMS: return sample_ws_bytes(src);
     case VS_OP_L1_LOSS: return round_up(vs::l1_loss_workspace_bytes(src->T));
@@ -263,21 +317,32 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
                         size_t workspace_bytes, void* stream) {
   int rc = check_source(src);
   if (rc) return rc;
-  if (src->kind != VS_SRC_LOGITS || src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
+  if (src->kind == VS_SRC_LOGITS && src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
   if (!top_k || !top_p || !min_p || !target_ids || !logprob) return VS_E_NULL;
   if (support_ids_cap < 0 || support_ids_cap > kMaxDim) return VS_E_PARAM;
   if (support_ids_cap == 0) support_ids_out = nullptr;
   if (support_ids_out && support_ids_cap > vs::kTransformsMaxCap) return VS_E_UNSUPPORTED;
-  rc = check_workspace(workspace, workspace_bytes, round_up(vs::transforms_workspace_bytes(src->T, src->V)));
+  rc = check_workspace(workspace, workspace_bytes, xf_ws_bytes(src));
   if (rc) return rc;
+  const float* temp = src->temperature;
+  // rows [r0, r0 + n) of the program over logits [n][ld]
+  auto run = [&](const uint16_t* lg, int64_t ld, int64_t r0, int64_t n, uint8_t* tws) -> int {
+    const int r = vs::launch_transforms(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, top_k + r0,
+                                        top_p + r0, min_p + r0, target_ids + r0, logprob + r0, at_row(entropy, r0),
+                                        at_row(row_status, r0), at_row(support_len, r0), at_row(threshold_logit, r0),
+                                        at_row(threshold_ties, r0), at_row(support_ids_out, r0, support_ids_cap),
+                                        support_ids_cap, at_row(full_lse, r0), nullptr, tws, stream);
+    return r == -1 ? VS_E_UNSUPPORTED : r ? VS_E_DEVICE : VS_OK;
+  };
   vs::timer_mark(0, stream);
-  rc = vs::launch_transforms(static_cast<const uint16_t*>(src->logits), src->ld_logits, src->T, src->V,
-                             src->temperature, src->temperature_scalar, top_k, top_p, min_p, target_ids, logprob,
-                             entropy, row_status, support_len, threshold_logit, threshold_ties, support_ids_out,
-                             support_ids_cap, full_lse, nullptr, static_cast<uint8_t*>(workspace), stream);
+  if (src->kind == VS_SRC_LOGITS) {
+    rc = run(static_cast<const uint16_t*>(src->logits), src->ld_logits, 0, src->T, static_cast<uint8_t*>(workspace));
+  } else {
+    Carver c(workspace);
+    rc = over_logit_blocks(src, c, stream, run);
+  }
   vs::timer_mark(1, stream);
-  if (rc == -1) return VS_E_UNSUPPORTED;
-  return rc ? VS_E_DEVICE : VS_OK;
+  return rc;
 }
 
 int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float* top_p, const float* min_p,
@@ -286,7 +351,7 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
                          size_t workspace_bytes, void* stream) {
   int rc = check_source(src);
   if (rc) return rc;
-  if (src->kind != VS_SRC_LOGITS || src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
+  if (src->kind == VS_SRC_LOGITS && src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
   if (!top_k || !top_p || !min_p || !sampled_ids) return VS_E_NULL;
   rc = check_workspace(workspace, workspace_bytes, sample_ws_bytes(src));
   if (rc) return rc;
@@ -298,19 +363,29 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   float* row_max = static_cast<float*>(c.take(size_t(T) * 4));
   float* thr = threshold_logit ? threshold_logit : static_cast<float*>(c.take(size_t(T) * 4));
   int32_t* ties = threshold_ties ? threshold_ties : static_cast<int32_t*>(c.take(size_t(T) * 4));
-  uint8_t* tws = static_cast<uint8_t*>(c.take(vs::transforms_workspace_bytes(T, src->V)));
   // the transforms need a target per row: token 0 (its score is discarded)
   if (vs::launch_zero_i32(reinterpret_cast<int32_t*>(dummy_targets), 2 * T, stream)) return VS_E_DEVICE;
+  const float* temp = src->temperature;
+  // rows [r0, r0 + n): the support descriptor, then the draw from it
+  auto run = [&](const uint16_t* lg, int64_t ld, int64_t r0, int64_t n, uint8_t* tws) -> int {
+    int r = vs::launch_transforms(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, top_k + r0,
+                                  top_p + r0, min_p + r0, dummy_targets + r0, lp + r0, nullptr, st + r0,
+                                  at_row(support_len, r0), thr + r0, ties + r0, nullptr, 0, nullptr, row_max + r0, tws,
+                                  stream);
+    if (r) return r == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
+    r = vs::launch_sample(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, st + r0, thr + r0, ties + r0,
+                          row_max + r0, seed, offset, sampled_ids + r0, at_row(row_status, r0), r0, stream);
+    return r ? VS_E_DEVICE : VS_OK;
+  };
   vs::timer_mark(0, stream);
-  const uint16_t* lg = static_cast<const uint16_t*>(src->logits);
-  rc = vs::launch_transforms(lg, src->ld_logits, T, src->V, src->temperature, src->temperature_scalar, top_k, top_p,
-                             min_p, dummy_targets, lp, nullptr, st, support_len, thr, ties, nullptr, 0, nullptr,
-                             row_max, tws, stream);
-  if (rc) return rc == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
-  rc = vs::launch_sample(lg, src->ld_logits, T, src->V, src->temperature, src->temperature_scalar, st, thr, ties,
-                         row_max, seed, offset, sampled_ids, row_status, stream);
+  if (src->kind == VS_SRC_LOGITS) {
+    rc = run(static_cast<const uint16_t*>(src->logits), src->ld_logits, 0, T,
+             static_cast<uint8_t*>(c.take(vs::transforms_workspace_bytes(T, src->V))));
+  } else {
+    rc = over_logit_blocks(src, c, stream, run);
+  }
   vs::timer_mark(1, stream);
-  return rc ? VS_E_DEVICE : VS_OK;
+  return rc;
 }
 
 int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, const float* lse, const float* entropy,

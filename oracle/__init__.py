@@ -19,7 +19,8 @@ what the method computes, written from these pages:
   (section 1's description of the LM-head op, section 3's transform
   program name): chunked projection -> log-sum-exp -> sampling support ->
   selected logprob; temperature, then stable token-id top-k, inclusive
-  top-p, min-p against the original row max.
+  top-p, min-p against the original row max; the same program over the
+  projection ("Proposed direction" item 3), on its bf16-rounded logits.
 * DeepSpec PR #87 "[Perf] Reuse DSpark probability distance" (sections
   Purpose and Test Plan): per-token L1 distance between draft and target
   softmaxes, accept_rate = clamp(1 - 0.5 * L1, 0, 1), and the weighted L1
@@ -44,8 +45,10 @@ from .scoring import (  # noqa: F401
     ST_SUPPORT_TRUNCATED,
     widen_bf16,
     round_f32_to_bf16,
+    round_f64_to_bf16,
     logits_from_logits,
     logits_from_hidden,
+    bf16_logits_from_hidden,
     score_full,
     score_support,
     score_transforms,

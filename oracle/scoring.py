@@ -70,6 +70,29 @@ def round_f32_to_bf16(x) -> np.ndarray:
     return out
 
 
+def round_f64_to_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns, one rounding to nearest, ties to even.
+
+    Written from the IEEE rule for an 8-bit significand: with
+    x = m 2^e (0.5 <= |m| < 1), the unit in the last place is 2^(e - 8), but
+    never below 2^-133, the spacing of the subnormal bf16 numbers; x is
+    scaled by that power of two (exact), rounded to an integer, ties to
+    even, and scaled back.  Magnitudes that round to 2^128 or beyond become
+    infinities; NaN becomes the quiet NaN 0x7FC0; the sign of zero is kept.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(x)
+    xs = np.where(nan, 0.0, x)
+    _, e = np.frexp(xs)
+    q = np.maximum(e - 8, -133)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = np.ldexp(np.rint(np.ldexp(xs, -q)), q)
+    y = np.where(np.abs(y) >= 2.0 ** 128, np.copysign(np.inf, xs), y)
+    bits = (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits[nan] = np.uint16(0x7FC0)
+    return bits
+
+
 # ---------------------------------------------------------------------------
 # Logits (the input to every score)
 # ---------------------------------------------------------------------------
@@ -121,6 +144,18 @@ def logits_from_hidden(hidden, hidden_dtype: str, weight_bits, rows=None, cols=N
 # ---------------------------------------------------------------------------
 # Helpers on one row of tempered logits
 # ---------------------------------------------------------------------------
+
+def bf16_logits_from_hidden(hidden, hidden_dtype: str, weight_bits, rows=None) -> np.ndarray:
+    """The bf16 logits of the hidden/weight source for the sampling transforms.
+
+    xorl issue #71 (section 3 and "Proposed direction" item 3) asks for the
+    transform program on the chunked projection; it ranks bf16 logits.  The
+    reading taken here: the logits it ranks are the projection rounded once
+    to bf16 (nearest, ties to even), ``round_f64_to_bf16(logits_from_hidden)``.
+    (A device computes the projection in fp32 first; the two agree wherever
+    that fp32 sum is exact.)  Returns bf16 bit patterns ``[rows, V]``."""
+    return round_f64_to_bf16(logits_from_hidden(hidden, hidden_dtype, weight_bits, rows=rows))
+
 
 def _valid_tau(tau) -> bool:
     return bool(np.isfinite(tau) and tau > 0.0)

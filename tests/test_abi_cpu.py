@@ -156,13 +156,28 @@ def test_support_validation(lib):
 def test_transforms_validation(lib):
     from logprob_entropy_sampling_amd import _capi as C
 
-    def call(src, topk=FAKE, cap=0):
+    def call(src, topk=FAKE, cap=0, ws=None, nws=0):
         return lib.vs_score_transforms(ctypes.byref(src), topk, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                       FAKE, FAKE, cap, FAKE, None, 0, None)
-    assert call(_src(kind=C.VS_SRC_HIDDEN_WEIGHT)) == C.VS_E_UNSUPPORTED
+                                       FAKE, FAKE, cap, FAKE, ws, nws, None)
     assert call(_src(logits_dtype=C.VS_F32)) == C.VS_E_UNSUPPORTED
     assert call(_src(), topk=None) == C.VS_E_NULL
     assert call(_src(), cap=-1) == C.VS_E_PARAM
+    assert call(_src(), cap=4097, ws=FAKE, nws=1 << 40) == C.VS_E_UNSUPPORTED
+    # a hidden/weight source: its bf16 logits are written block by block into the workspace
+    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT, H=4096, V=151936, ld_hidden=4096, ld_weight=4096)
+    assert call(_src(T=100, **hw)) == C.VS_E_WORKSPACE
+    assert call(_src(T=100, hidden=FAKE + 8, **hw)) == C.VS_E_ALIGN
+    small = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS, ctypes.byref(_src(T=100, **hw)), 0)
+    block = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS, ctypes.byref(_src(T=2048, **hw)), 0)
+    big = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS, ctypes.byref(_src(T=8192, **hw)), 0)
+    logits_only = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS,
+                                        ctypes.byref(_src(T=100, V=151936, ld_logits=151936)), 0)
+    assert small >= 100 * 151936 * 2 + logits_only
+    assert big == block >= 2048 * 151936 * 2  # blocks of at most 2048 rows
+    f32 = lib.vs_workspace_size(C.VS_OP_SCORE_TRANSFORMS,
+                                ctypes.byref(_src(T=8192, hidden_dtype=C.VS_F32, **hw)), 0)
+    assert f32 >= big + 8192 * 4096 * 2  # and the bf16 copy of an fp32 hidden state
+    assert call(_src(T=100, **hw), ws=FAKE, nws=small - 1) == C.VS_E_WORKSPACE
 
 
 def test_l1_validation(lib):
@@ -214,7 +229,7 @@ def test_sample_validation(lib):
     def call(src, topk=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
         return lib.vs_sample_transforms(ctypes.byref(src), topk, FAKE, FAKE, 1, 0, out, None, None, None, None, ws,
                                         nws, None)
-    assert call(_src(kind=C.VS_SRC_HIDDEN_WEIGHT)) == C.VS_E_UNSUPPORTED
+    assert call(_src(kind=C.VS_SRC_HIDDEN_WEIGHT), ws=None) == C.VS_E_WORKSPACE
     assert call(_src(logits_dtype=C.VS_F32)) == C.VS_E_UNSUPPORTED
     assert call(_src(), topk=None) == C.VS_E_NULL
     assert call(_src(), out=None) == C.VS_E_NULL

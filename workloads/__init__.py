@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five scoring workloads.
+"""Seeded synthetic inputs for the six scoring workloads.
 
 This module is shared by the HIP path's tests/bench and by the CPU oracle's
 tests; it holds none of the scoring arithmetic (no log-sum-exp, no entropy,
@@ -6,7 +6,7 @@ no support selection).  Random numbers a method would draw (the sampled
 target ids) are drawn here and passed in as inputs.
 
 Each workload draws from ``numpy.random.Generator(PCG64(SeedSequence(seed)))``
-with ``seed = 1000 + i`` (i = 1..5) and child streams spawned in a fixed order
+with ``seed = 1000 + i`` (i = 1..6) and child streams spawned in a fixed order
 (hidden, weight, logits, ids, targets, params, noise), so a workload and its
 sizes determine every byte.  float32 -> bf16 uses round-to-nearest-even.
 
@@ -30,6 +30,13 @@ Workloads (sizes overridable for small parity cases):
    {0,0.05} x tau {0.7,1.0}; a uniform ``u[t]`` for drawing the in-support
    target by inverse CDF (done by the caller, who knows the support); draft
    logits = bf16(float32(x) + 0.5 N(0,1)).
+6. ``transforms_hidden``: the transform program of workload 5 on a fused
+   source, T=2048, H=4096, V=151,936, with hidden and W on grids that make
+   every fp32 sum of the projection exact: hidden = k/4 and W = j/128 with
+   k, j = round(4 N(0,1)) clipped to [-16, 16] (so x ~ N(0, 2), like workload
+   5's logits; every product is a multiple of 2^-9 of magnitude <= 1/2, so
+   any partial sum over H <= 65536 terms fits 24 bits); targets are the
+   plain row argmax of the projected bf16 logits (computed by the caller).
 """
 
 from __future__ import annotations
@@ -38,7 +45,8 @@ import hashlib
 
 import numpy as np
 
-NAMES = {1: "tiny", 2: "logits_full", 3: "support_replay", 4: "fused_full", 5: "transforms_l1"}
+NAMES = {1: "tiny", 2: "logits_full", 3: "support_replay", 4: "fused_full", 5: "transforms_l1",
+         6: "transforms_hidden"}
 
 FULL_SIZES = {
     1: dict(T=64, H=256, V=4096, W=8),
@@ -46,6 +54,7 @@ FULL_SIZES = {
     3: dict(T=2048, H=7168, V=129280, W=64),
     4: dict(T=4096, H=4096, V=151936),
     5: dict(T=2048, V=151936),
+    6: dict(T=2048, H=4096, V=151936),
 }
 
 _STREAMS = ("hidden", "weight", "logits", "ids", "targets", "params", "noise")
@@ -85,6 +94,31 @@ def _normal_bf16(rng, shape, std) -> np.ndarray:
             blk *= np.float32(std)
         out[r0:r1] = to_bf16_bits(blk)
     return out
+
+
+def _grid_bf16(rng, shape, unit) -> np.ndarray:
+    """bf16(unit * k), k = round(4 N(0,1)) clipped to [-16, 16]: exact in bf16."""
+    out = np.empty(shape, dtype=np.uint16)
+    rows = shape[0]
+    step = max(1, (1 << 26) // max(1, int(np.prod(shape[1:]))))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        k = np.rint(rng.standard_normal((r1 - r0,) + tuple(shape[1:]), dtype=np.float32) * np.float32(4.0))
+        np.clip(k, -16, 16, out=k)
+        out[r0:r1] = to_bf16_bits(k * np.float32(unit))
+    return out
+
+
+def _transform_params(T: int) -> dict:
+    """Row t takes combination t mod 36 of top_k {0,20,50} x top_p {1,0.95,0.8}
+    x min_p {0,0.05} x tau {0.7,1}."""
+    combo = np.arange(T) % 36
+    ks = np.array([0, 20, 50], dtype=np.int32)
+    ps = np.array([1.0, 0.95, 0.8], dtype=np.float32)
+    ms = np.array([0.0, 0.05], dtype=np.float32)
+    ts = np.array([0.7, 1.0], dtype=np.float32)
+    return {"top_k": ks[combo // 12], "top_p": ps[(combo // 4) % 3], "min_p": ms[(combo // 2) % 2],
+            "temperature": ts[combo % 2]}
 
 
 def _distinct_ids(rng, V: int, n: int, exclude: int = -1) -> np.ndarray:
@@ -203,15 +237,7 @@ def make(i: int, **sizes) -> dict:
         out["kind"] = "logits"
         out["logits"] = _normal_bf16(r["logits"], (T, V), 2.0)
         out["logits_dtype"] = "bf16"
-        combo = np.arange(T) % 36
-        ks = np.array([0, 20, 50], dtype=np.int32)
-        ps = np.array([1.0, 0.95, 0.8], dtype=np.float32)
-        ms = np.array([0.0, 0.05], dtype=np.float32)
-        ts = np.array([0.7, 1.0], dtype=np.float32)
-        out["top_k"] = ks[combo // 12]
-        out["top_p"] = ps[(combo // 4) % 3]
-        out["min_p"] = ms[(combo // 2) % 2]
-        out["temperature"] = ts[combo % 2]
+        out.update(_transform_params(T))
         out["u"] = r["targets"].random(T)
         # plain row argmax (lowest id among equal maxima): always inside any
         # top-k/top-p/min-p support; used where no support-aware draw is made
@@ -225,6 +251,15 @@ def make(i: int, **sizes) -> dict:
             noise += bf16_bits_to_f32(out["logits"][r0:r1])
             draft[r0:r1] = to_bf16_bits(noise)
         out["draft"] = draft
+        out["support_cap"] = 64
+
+    elif i == 6:
+        H = cfg["H"]
+        out["kind"] = "hidden_weight"
+        out["hidden"] = _grid_bf16(r["hidden"], (T, H), 0.25)
+        out["hidden_dtype"] = "bf16"
+        out["weight"] = _grid_bf16(r["weight"], (V, H), 1.0 / 128)
+        out.update(_transform_params(T))
         out["support_cap"] = 64
     return out
 
