@@ -382,6 +382,37 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
         res[f"l1_loss_T{T_l}"] = _path_entry(T_l, ev, sw, byts, byts, V=V, grad_dtype="bf16",
                                              context_rtx4090_loss_path_ms={128: 2.531, 512: 11.593}.get(T_l))
         del o, wsp
+    del lg, dr
+
+    # the transform program on a hidden/weight source: T=2048, H=4096, V=151,936 (grid inputs
+    # whose fp32 sums are exact; the timing does not depend on the values)
+    c = workloads.make(6)
+    T, H, V = c["T"], c["H"], c["V"]
+    hid, w = _bf16(c["hidden"], dev), _bf16(c["weight"], dev)
+    tk, tp, mp, tau = (_dev(c["top_k"], dev), _dev(c["top_p"], dev), _dev(c["min_p"], dev),
+                       _dev(c["temperature"], dev))
+    y = torch.zeros(T, dtype=torch.int64, device=dev)  # (the support and its scores cost the same for any target)
+    o = vsa.score_transforms(y, None, tk, tp, mp, hidden=hid, weight=w, temperature=tau, cap=64)
+    wsp = torch.empty(max(1, vsa.workspace_bytes("score_transforms", hidden=hid, weight=w)), dtype=torch.uint8,
+                      device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, None, tk, tp, mp, hidden=hid, weight=w, temperature=tau,
+                                                            cap=64, out=o, workspace=wsp), steps, warmup, flush)
+    med, iqr = _median_iqr(ev)
+    flops = 2.0 * T * H * V
+    res["transforms_hidden"] = {
+        "T": T, "H": H, "V": V, "support_ids_cap": 64, "ms_median": round(med, 4), "ms_iqr": round(iqr, 4),
+        "tokens_per_s": round(T / (med * 1e-3), 1), "flop_per_call": flops,
+        "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+        "mfma_frac": round(flops / (med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernel_ms_mean": round(statistics.mean(sw), 4), "workspace_bytes": int(wsp.numel())}
+    if cpu:
+        res["transforms_hidden"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
+            lambda r: oracle.score_transforms(
+                oracle.widen_bf16(oracle.bf16_logits_from_hidden(c["hidden"], "bf16", c["weight"], rows=r)),
+                c["temperature"][r], c["top_k"][r], c["top_p"][r], c["min_p"][r], np.zeros(r.size, np.int64),
+                cap=64), T, cpu_budget_s),
+            "transforms_hidden rows (projection, bf16 rounding, sort, top-k/top-p/min-p, support scores)")
+    del hid, w, o, wsp
     torch.cuda.synchronize()
     return res
 

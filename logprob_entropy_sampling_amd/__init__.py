@@ -45,9 +45,9 @@ class _Lazy:
 
 _lib = _Lazy()
 
-__all__ = ["score_full", "score_full_backward", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids", "score_transforms",
-           "sample_transforms", "l1_distance", "l1_loss", "workspace_size", "workspace_bytes",
-           "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
+__all__ = ["score_full", "score_full_backward", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids",
+           "score_transforms", "sample_transforms", "l1_distance", "l1_loss", "workspace_size",
+           "workspace_bytes", "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
 
 def lib() -> ctypes.CDLL:
