@@ -57,4 +57,5 @@ from .scoring import (  # noqa: F401
     weighted_l1_loss,
     logit_vjp,
     score_full_vjp,
+    score_support_vjp,
 )

@@ -614,6 +614,75 @@ def logit_vjp(x, tau, targets, grad_logprob=None, grad_entropy=None) -> np.ndarr
     return out
 
 
+def score_support_vjp(hidden, hidden_dtype: str, weight_bits, ids, tau, targets, grad_logprob=None,
+                      grad_entropy=None, weight_rows=None) -> dict:
+    """Gradients of sum_t (a_t logprob_t + b_t H_t) of the recorded-support
+    scores over the fused projection (``score_support`` with
+    ``x = bf16(hidden) W^T``) with respect to the hidden state and the weight.
+
+    SkyRL PR #2004 (Implementation: entropy and gradient tracking over the
+    recorded support; the description: a singleton support has exactly zero
+    entropy and zero entropy gradient): over ``S_t`` the scores are those of
+    ``p = softmax(z_S)``, so for v in S_t
+
+        d logprob / d z_v = [v = y] - p_v,   d H / d z_v = -p_v (ln p_v + H_S)
+
+    and nothing outside S_t; ``d/dx = (d/dz) / tau``, then the chain rule
+    through the projection: ``d_hidden[t] = sum_{v in S_t} dX[t, v] W[v]``,
+    ``d_weight[v] = sum_{t : v in S_t} dX[t, v] bf16(hidden[t])``.
+    Rows that get no gradient: BAD_INPUT rows of score_support, rows with an
+    empty support (their scores are constants; a synthetic-EOS row's
+    full-vocabulary logprob is score_full_vjp's), and - for the logprob term
+    only - a target outside the support (its logprob is the constant -inf).
+
+    ``weight_rows``: the vocabulary ids whose d_weight rows are returned
+    (default every id).  Returns ``d_hidden`` [R, H], ``d_weight``
+    [len(weight_rows), H] and ``d_support`` [R, width] (dX at each id's
+    position, 0 at padding), float64."""
+    h = np.asarray(hidden)
+    h64 = widen_bf16(round_f32_to_bf16(h)) if hidden_dtype == "f32" else widen_bf16(h)
+    w = np.asarray(weight_bits, dtype=np.uint16)
+    V = w.shape[0]
+    ids = np.asarray(ids, dtype=np.int64)
+    R, width = ids.shape
+    tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (R,))
+    a = np.zeros(R) if grad_logprob is None else np.asarray(grad_logprob, dtype=np.float64)
+    b = np.zeros(R) if grad_entropy is None else np.asarray(grad_entropy, dtype=np.float64)
+    targets = np.asarray(targets, dtype=np.int64)
+    rows = np.arange(V) if weight_rows is None else np.asarray(weight_rows, dtype=np.int64)
+    where = {int(v): i for i, v in enumerate(rows)}
+    d_hidden = np.zeros((R, h64.shape[1]))
+    d_weight = np.zeros((rows.size, h64.shape[1]))
+    d_support = np.zeros((R, width))
+    for t in range(R):
+        pos = np.nonzero(ids[t] >= 0)[0]
+        sup = ids[t, pos]
+        if not _valid_tau(tau[t]) or (sup >= V).any() or len(np.unique(sup)) != len(sup):
+            continue
+        y = int(targets[t])
+        if sup.size == 0 or not (0 <= y < V):
+            continue
+        w_sup = widen_bf16(w[sup])
+        lse, lnp, hs = _log_softmax(h64[t] @ w_sup.T, tau[t])
+        if not np.isfinite(lse):
+            continue
+        p = np.exp(lnp)
+        plnp = np.where(p > 0.0, p * np.where(np.isfinite(lnp), lnp, 0.0), 0.0)
+        hit = np.nonzero(sup == y)[0]
+        a_t = a[t] if hit.size else 0.0
+        dz = -a_t * p - b[t] * (plnp + p * hs)
+        if hit.size:
+            dz[hit[0]] += a_t
+        dx = dz / tau[t]
+        d_support[t, pos] = dx
+        d_hidden[t] = dx @ w_sup
+        for j, v in enumerate(sup):
+            i = where.get(int(v))
+            if i is not None:
+                d_weight[i] += dx[j] * h64[t]
+    return {"d_hidden": d_hidden, "d_weight": d_weight, "d_support": d_support}
+
+
 def score_full_vjp(hidden, hidden_dtype: str, weight_bits, tau, targets, grad_logprob=None,
                    grad_entropy=None) -> dict:
     """Gradients of sum_t (a_t logprob_t + b_t H_t) of the fused projection

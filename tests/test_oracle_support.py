@@ -144,3 +144,88 @@ def test_ties_at_large_magnitude():
         assert abs(r["logprob"][0] + math.log(3)) < 1e-12, mag
         r = oracle.score_support(lambda t, cols: x[t, cols], 50, ids[:, 1:2], 1.0, [3])
         assert r["entropy"][0] == 0.0 and r["logprob"][0] == 0.0
+
+
+def _support_objective(h64, w64, ids, tau, y, a, b):
+    """sum_t a_t logprob_t + b_t H_t of score_support over x = h w^T (float64), where finite."""
+    r = oracle.score_support(lambda t, cols: h64[t] @ w64[np.asarray(cols)].T, w64.shape[0], ids, tau, y)
+    lp = np.where(np.isfinite(r["logprob"]), r["logprob"], 0.0)  # a -inf logprob is a constant
+    ent = np.where(np.isfinite(r["entropy"]), r["entropy"], 0.0)
+    return float(np.sum(a * lp + b * ent))
+
+
+def test_support_vjp_matches_finite_differences():
+    # the gradient of sum a logprob_S + b H_S with respect to the hidden state
+    # and every weight row, against central differences of score_support itself
+    rng = np.random.default_rng(41)
+    T, H, V, W = 5, 6, 11, 6
+    hb = oracle.round_f32_to_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    wb = oracle.round_f32_to_bf16(rng.normal(0, 0.5, (V, H)).astype(np.float32))
+    h64, w64 = oracle.widen_bf16(hb), oracle.widen_bf16(wb)
+    ids = np.full((T, W), -1, np.int64)
+    ids[0, :4] = [3, 7, 1, 9]          # target inside
+    ids[1, [0, 2, 5]] = [2, 10, 4]     # padding in the middle, target outside the support
+    ids[2, :1] = [5]                   # singleton
+    ids[3, :6] = [0, 1, 2, 3, 4, 5]
+    ids[4, 1:3] = [8, 6]
+    y = np.array([7, 0, 5, 4, 6])
+    tau = np.array([1.0, 0.7, 1.3, 0.9, 2.0])
+    a = np.array([1.0, -0.5, 2.0, 0.7, -1.2])
+    b = np.array([0.3, 1.0, -0.8, 0.5, 0.9])
+    g = oracle.score_support_vjp(hb, "bf16", wb, ids, tau, y, a, b)
+    eps = 1e-6
+    for (name, arr, ref) in (("hidden", h64, g["d_hidden"]), ("weight", w64, g["d_weight"])):
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            hp, wp = (ap, w64) if name == "hidden" else (h64, ap)
+            hm, wm = (am, w64) if name == "hidden" else (h64, am)
+            fd = (_support_objective(hp, wp, ids, tau, y, a, b) - _support_objective(hm, wm, ids, tau, y, a, b)) / (2 * eps)
+            assert abs(fd - ref[idx]) < 1e-7, (name, idx, fd, ref[idx])
+
+
+def test_support_vjp_singleton_and_empty_rows_are_exactly_zero():
+    rng = np.random.default_rng(42)
+    T, H, V = 4, 8, 20
+    hb = oracle.round_f32_to_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    wb = oracle.round_f32_to_bf16(rng.normal(0, 0.5, (V, H)).astype(np.float32))
+    ids = np.array([[7, -1, -1], [-1, -1, -1], [3, 3, -1], [25, 1, -1]])  # singleton, empty, repeated, id >= V
+    y = np.array([7, 0, 3, 1])
+    g = oracle.score_support_vjp(hb, "bf16", wb, ids, 1.0, y, np.ones(T), np.ones(T))
+    assert (g["d_hidden"] == 0).all() and (g["d_weight"] == 0).all() and (g["d_support"] == 0).all()
+
+
+def test_full_support_vjp_equals_full_vocabulary_vjp():
+    # a support holding every id (in any order) is the full vocabulary
+    rng = np.random.default_rng(43)
+    T, H, V = 4, 16, 30
+    hb = oracle.round_f32_to_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    wb = oracle.round_f32_to_bf16(rng.normal(0, 0.5, (V, H)).astype(np.float32))
+    ids = np.stack([rng.permutation(V) for _ in range(T)])
+    y = rng.integers(0, V, T)
+    tau = np.array([1.0, 0.6, 1.7, 1.1])
+    a, b = rng.normal(0, 1, T), rng.normal(0, 1, T)
+    s = oracle.score_support_vjp(hb, "bf16", wb, ids, tau, y, a, b)
+    f = oracle.score_full_vjp(hb, "bf16", wb, tau, y, a, b)
+    assert np.allclose(s["d_hidden"], f["d_hidden"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(s["d_weight"], f["d_weight"], rtol=1e-12, atol=1e-14)
+    for t in range(T):
+        assert np.allclose(s["d_support"][t], f["d_logits"][t, ids[t]], rtol=1e-12, atol=1e-15)
+
+
+def test_support_vjp_weight_rows_and_outside_target():
+    rng = np.random.default_rng(44)
+    T, H, V, W = 6, 8, 40, 5
+    hb = oracle.round_f32_to_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    wb = oracle.round_f32_to_bf16(rng.normal(0, 0.5, (V, H)).astype(np.float32))
+    ids = np.stack([rng.choice(V, W, replace=False) for _ in range(T)])
+    y = ids[:, 0].copy()
+    y[2] = int(np.setdiff1d(np.arange(V), ids[2])[0])  # outside its support
+    a, b = rng.normal(0, 1, T), rng.normal(0, 1, T)
+    full = oracle.score_support_vjp(hb, "bf16", wb, ids, 1.0, y, a, b)
+    some = oracle.score_support_vjp(hb, "bf16", wb, ids, 1.0, y, a, b, weight_rows=[ids[1, 2], 0, ids[4, 4]])
+    assert np.array_equal(some["d_weight"], full["d_weight"][[ids[1, 2], 0, ids[4, 4]]])
+    # outside the support only the entropy term remains
+    only_b = oracle.score_support_vjp(hb[2:3], "bf16", wb, ids[2:3], 1.0, y[2:3], np.zeros(1), b[2:3])
+    assert np.allclose(full["d_hidden"][2], only_b["d_hidden"][0], rtol=0, atol=1e-15)
