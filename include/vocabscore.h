@@ -83,7 +83,8 @@ enum {
   VS_OP_L1_DISTANCE = 3,
   VS_OP_SAMPLE_TRANSFORMS = 4,
   VS_OP_L1_LOSS = 5,
-  VS_OP_SCORE_FULL_BACKWARD = 6
+  VS_OP_SCORE_FULL_BACKWARD = 6,
+  VS_OP_SCORE_SUPPORT_BACKWARD = 7
 };
 
 /* ---- per-row status bits (uint8 per row) -------------------------------- */
@@ -129,8 +130,8 @@ typedef struct vs_source {
 
 /*
  * Bytes of workspace the call `op` needs for this source (width = support
- * width for VS_OP_SCORE_SUPPORT, the vocab_chunk for
- * VS_OP_SCORE_FULL_BACKWARD, else 0).  For VS_OP_L1_DISTANCE only src->T
+ * width for VS_OP_SCORE_SUPPORT and VS_OP_SCORE_SUPPORT_BACKWARD, the
+ * vocab_chunk for VS_OP_SCORE_FULL_BACKWARD, else 0).  For VS_OP_L1_DISTANCE only src->T
  * and src->V are read.  Returns 0 on a NULL src.
  */
 size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width);
@@ -187,6 +188,37 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
                            const float* grad_logprob, const float* grad_entropy, int64_t vocab_chunk,
                            float* grad_hidden, int64_t ld_grad_hidden, float* grad_weight, int64_t ld_grad_weight,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The vector-Jacobian product of recorded-support scoring through the fused
+ * projection (SkyRL PR #2004, Implementation: gradients through the replayed
+ * support's logprob and entropy; the description: a singleton support has
+ * exactly zero entropy and zero entropy gradient).  With the scores of
+ * vs_score_support_ids and a_t = grad_logprob[t], b_t = grad_entropy[t] of
+ * sum_t (a_t logprob_t + b_t entropy_t), for each id v = support_ids[t, j]
+ * of the support S_t (p the softmax of z over S_t, H_S its entropy):
+ *   dX[t, j]          = (a_t ([v = y_t] - p_v) - b_t p_v (ln p_v + H_S)) / tau_t
+ *   grad_hidden[t, h] = sum_j dX[t, j] W[v_j, h]          (j ascending)
+ *   grad_weight[v, h] = sum over (t, j) with v_j = v of dX[t, j] bf16(hidden)[t, h]
+ *                       (pairs in ascending (t, j) order; 0 for ids in no support)
+ * dX stays fp32; both sums are fp32 in a fixed order, so results are bitwise
+ * reproducible.  Rows without gradient (their rows of grad_hidden are 0): the
+ * BAD_INPUT rows of vs_score_support_ids (invalid tau, an id >= V, a repeated
+ * id, a target outside [0, V), a support LSE that is not finite) and rows
+ * with an empty support (their scores are constants; the full-vocabulary
+ * logprob of a synthetic-EOS row has its gradient from
+ * vs_score_full_backward).  A target outside the support drops the logprob
+ * term (that logprob is the constant -inf).  Source: VS_SRC_HIDDEN_WEIGHT
+ * with H <= 16384 (else VS_E_UNSUPPORTED).  support_ids, width, ld_ids as for
+ * vs_score_support_ids.  grad_logprob / grad_entropy nullable (0);
+ * grad_hidden [T, ld_grad_hidden] and grad_weight [V, ld_grad_weight] fp32,
+ * nullable (at least one; every row of a given output is written).
+ * Workspace: vs_workspace_size(VS_OP_SCORE_SUPPORT_BACKWARD, src, width).
+ */
+int vs_score_support_backward(const vs_source* src, const int64_t* support_ids, int64_t width, int64_t ld_ids,
+                              const int64_t* target_ids, const float* grad_logprob, const float* grad_entropy,
+                              float* grad_hidden, int64_t ld_grad_hidden, float* grad_weight, int64_t ld_grad_weight,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Recorded-support scoring (SkyRL PR #2004, sections Problem and

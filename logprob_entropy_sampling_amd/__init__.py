@@ -46,6 +46,7 @@ class _Lazy:
 _lib = _Lazy()
 
 __all__ = ["score_full", "score_full_backward", "score_full_noalloc", "noalloc_scratch_bytes", "score_support_ids",
+           "score_support_backward",
            "score_transforms", "sample_transforms", "l1_distance", "l1_loss", "workspace_size",
            "workspace_bytes", "status_string", "sweep_timer", "sweep_timer_ms", "VsError", "lib"]
 
@@ -172,12 +173,13 @@ def _outputs(spec, dev, out):
 def workspace_bytes(op: str, *, logits=None, hidden=None, weight=None, width: int = 0) -> int:
     """Bytes of workspace an entry point needs for these inputs (vs_workspace_size);
     op is one of "score_full", "score_support_ids", "score_transforms", "l1_distance",
-    "sample_transforms", "l1_loss", "score_full_backward" (width = the support width, or the
-    backward's vocab_chunk)."""
+    "sample_transforms", "l1_loss", "score_full_backward", "score_support_backward" (width =
+    the support width, or the backward's vocab_chunk)."""
     ops = {"score_full": _capi.VS_OP_SCORE_FULL, "score_support_ids": _capi.VS_OP_SCORE_SUPPORT,
            "score_transforms": _capi.VS_OP_SCORE_TRANSFORMS, "l1_distance": _capi.VS_OP_L1_DISTANCE,
            "sample_transforms": _capi.VS_OP_SAMPLE_TRANSFORMS, "l1_loss": _capi.VS_OP_L1_LOSS,
-           "score_full_backward": _capi.VS_OP_SCORE_FULL_BACKWARD}
+           "score_full_backward": _capi.VS_OP_SCORE_FULL_BACKWARD,
+           "score_support_backward": _capi.VS_OP_SCORE_SUPPORT_BACKWARD}
     src, _, _ = _make_source(logits, hidden, weight, 1.0)
     return workspace_size(ops[op], src, width)
 
@@ -237,6 +239,37 @@ def score_full_backward(targets, lse, entropy=None, *, hidden, weight, grad_logp
                                      _ptr(o["grad_weight"]), H, _ptr(ws), n, _stream(dev))
     if rc:
         raise VsError(rc, "vs_score_full_backward")
+    return o
+
+
+def score_support_backward(targets, support_ids, *, hidden, weight, grad_logprob=None, grad_entropy=None,
+                           temperature=1.0, want_hidden=True, want_weight=True, out=None, workspace=None):
+    """Gradients of sum_t (grad_logprob[t] logprob_t + grad_entropy[t] entropy_t)
+    of the recorded-support scores (score_support_ids) with respect to the
+    hidden state and the LM-head weight (vs_score_support_backward).  Returns
+    ``grad_hidden`` [T, H] and ``grad_weight`` [V, H] (fp32)."""
+    src, dev, _keep = _make_source(None, hidden, weight, temperature)
+    T, H, V = src.T, src.H, src.V
+    _ids("targets", targets, T)
+    _check_cuda("support_ids", support_ids, {torch.int64}, 2)
+    if support_ids.size(0) != T:
+        raise ValueError("support_ids must have T rows")
+    width = support_ids.size(1)
+    ld_ids = _rowmajor("support_ids", support_ids) if width > 0 else 0
+    for name, t in (("grad_logprob", grad_logprob), ("grad_entropy", grad_entropy)):
+        if t is not None:
+            _check_cuda(name, t, {torch.float32}, 1)
+            if t.numel() != T or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [T] float32 tensor")
+    o = _outputs({"grad_hidden": ((T, H), torch.float32) if want_hidden else None,
+                  "grad_weight": ((V, H), torch.float32) if want_weight else None}, dev, out)
+    ws, n = _workspace(_capi.VS_OP_SCORE_SUPPORT_BACKWARD, src, dev, int(width), given=workspace)
+    rc = _lib.vs_score_support_backward(ctypes.byref(src), _ptr(support_ids) if width else None, int(width),
+                                        int(ld_ids), _ptr(targets),
+                                        _ptr(grad_logprob), _ptr(grad_entropy), _ptr(o["grad_hidden"]), H,
+                                        _ptr(o["grad_weight"]), H, _ptr(ws), n, _stream(dev))
+    if rc:
+        raise VsError(rc, "vs_score_support_backward")
     return o
 
 

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocabsco
 VS_F32, VS_BF16 = 0, 1
 VS_SRC_LOGITS, VS_SRC_HIDDEN_WEIGHT = 0, 1
 (VS_OP_SCORE_FULL, VS_OP_SCORE_SUPPORT, VS_OP_SCORE_TRANSFORMS, VS_OP_L1_DISTANCE, VS_OP_SAMPLE_TRANSFORMS,
- VS_OP_L1_LOSS, VS_OP_SCORE_FULL_BACKWARD) = range(7)
+ VS_OP_L1_LOSS, VS_OP_SCORE_FULL_BACKWARD, VS_OP_SCORE_SUPPORT_BACKWARD) = range(8)
 
 ROW_EMPTY_SUPPORT = 0x01
 ROW_TARGET_OUTSIDE_SUPPORT = 0x02
@@ -64,6 +64,8 @@ _SIGS = {
     "vs_noalloc_scratch_bytes": (c_size_t, []),
     "vs_l1_loss": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_void_p, c_float,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_size_t, c_void_p]),
+    "vs_score_support_backward": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
     "vs_sweep_timer": (c_int32, [c_int32]),
     "vs_sweep_timer_ms": (c_int32, [POINTER(c_float)]),
 }

@@ -85,6 +85,17 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
 // Zero a small int32 buffer with a kernel (not a memset node).
 int launch_zero_i32(int32_t* p, int64_t n, void* stream);
 
+// Backward of recorded-support scoring through the projection (bf16 hidden
+// [rows][ld_hidden], W [V][ld_weight]): d_hidden [rows][ld_dh] (every row
+// written, zeros where no gradient), d_weight [V][ld_dw] (every row written)
+// or nullptr.  Workspace: support_backward_workspace_bytes(rows, width, V).
+size_t support_backward_workspace_bytes(int64_t rows, int64_t width, int64_t V);
+int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
+                            int64_t rows, int64_t H, int64_t V, const float* temp, float temp_scalar,
+                            const int64_t* ids, int64_t width, int64_t ld_ids, const int64_t* targets,
+                            const float* grad_logprob, const float* grad_entropy, float* d_hidden, int64_t ld_dh,
+                            float* d_weight, int64_t ld_dw, void* workspace, void* stream);
+
 // Sampling transforms over bf16 logits (one workgroup per row).  Rows up to
 // 20 * 512 * 8 tokens are held in registers; longer ones are counted by one
 // kernel and finished by another (several rows per CU), which pass a record

@@ -180,6 +180,16 @@ size_t backward_ws_bytes(const vs_source* s, int64_t vocab_chunk) {
   return b;
 }
 
+// the backward of recorded-support scoring: the bf16 copy of an fp32 hidden
+// state, then the kernels' own arrays (dX per pair, row flags, per-id counts,
+// offsets and fill, the pair list)
+size_t support_bwd_ws_bytes(const vs_source* s, int64_t width) {
+  if (s->kind != VS_SRC_HIDDEN_WEIGHT) return 0;
+  size_t b = round_up(vs::support_backward_workspace_bytes(s->T, width, s->V));
+  if (s->hidden_dtype == VS_F32) b += round_up(size_t(s->T) * size_t(s->H) * 2);
+  return b;
+}
+
 size_t support_ws_bytes(const vs_source* s) {
   return round_up(size_t(s->T) * 4) + round_up(4) + full_ws_bytes(s, s->T);
 }
@@ -254,6 +264,7 @@ size_t vs_workspace_size(int32_t op, const vs_source* src, int64_t width) {
     case VS_OP_SAMPLE_TRANSFORMS: return sample_ws_bytes(src);
     case VS_OP_L1_LOSS: return round_up(vs::l1_loss_workspace_bytes(src->T));
     case VS_OP_SCORE_FULL_BACKWARD: return backward_ws_bytes(src, width);
+    case VS_OP_SCORE_SUPPORT_BACKWARD: return support_bwd_ws_bytes(src, width);
     default: return 0;
   }
 }
@@ -442,6 +453,42 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
   }
   vs::timer_mark(1, stream);
   return VS_OK;
+}
+
+int vs_score_support_backward(const vs_source* src, const int64_t* support_ids, int64_t width, int64_t ld_ids,
+                              const int64_t* target_ids, const float* grad_logprob, const float* grad_entropy,
+                              float* grad_hidden, int64_t ld_grad_hidden, float* grad_weight, int64_t ld_grad_weight,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_source(src);
+  if (rc) return rc;
+  if (src->kind != VS_SRC_HIDDEN_WEIGHT) return VS_E_UNSUPPORTED;
+  if ((!support_ids && width > 0) || !target_ids) return VS_E_NULL;
+  if (!grad_hidden && !grad_weight) return VS_E_NULL;
+  if (width < 0 || width > kMaxWidth || ld_ids < width) return VS_E_SHAPE;
+  if (src->T * width > 0x7FFFFFFF) return VS_E_SHAPE;
+  if (src->H > kMaxSupportH) return VS_E_UNSUPPORTED;
+  if ((grad_hidden && ld_grad_hidden < src->H) || (grad_weight && ld_grad_weight < src->H)) return VS_E_SHAPE;
+  if (!aligned(grad_hidden, 4) || !aligned(grad_weight, 4)) return VS_E_ALIGN;
+  rc = check_workspace(workspace, workspace_bytes, support_bwd_ws_bytes(src, width));
+  if (rc) return rc;
+  Carver c(workspace);
+  const uint16_t* hid = static_cast<const uint16_t*>(src->hidden);
+  int64_t ldh = src->ld_hidden;
+  if (src->hidden_dtype == VS_F32) {
+    uint16_t* hb = static_cast<uint16_t*>(c.take(size_t(src->T) * size_t(src->H) * 2));
+    if (vs::launch_round_hidden(static_cast<const float*>(src->hidden), src->ld_hidden, src->T, src->H, hb, stream))
+      return VS_E_DEVICE;
+    hid = hb;
+    ldh = src->H;
+  }
+  void* ws = c.take(vs::support_backward_workspace_bytes(src->T, width, src->V));
+  vs::timer_mark(0, stream);
+  rc = vs::launch_support_backward(hid, ldh, static_cast<const uint16_t*>(src->weight), src->ld_weight, src->T, src->H,
+                                   src->V, src->temperature, src->temperature_scalar, support_ids, width, ld_ids,
+                                   target_ids, grad_logprob, grad_entropy, grad_hidden, ld_grad_hidden, grad_weight,
+                                   ld_grad_weight, ws, stream);
+  vs::timer_mark(1, stream);
+  return rc ? VS_E_DEVICE : VS_OK;
 }
 
 int vs_l1_distance(const void* target_logits, const void* draft_logits, int32_t dtype, int64_t T, int64_t V,

@@ -240,6 +240,30 @@ def test_sample_validation(lib):
     assert call(_src(T=100, V=151936, ld_logits=151936), nws=need - 1) == C.VS_E_WORKSPACE
 
 
+def test_support_backward_validation(lib):
+    from logprob_entropy_sampling_amd import _capi as C
+
+    def call(src, ids=FAKE, width=8, ld=8, gh=FAKE, gw=FAKE, ws=FAKE, nws=1 << 40):
+        return lib.vs_score_support_backward(ctypes.byref(src), ids, width, ld, FAKE, FAKE, FAKE, gh, 64, gw, 64, ws,
+                                             nws, None)
+    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT)
+    assert call(_src()) == C.VS_E_UNSUPPORTED  # a logits source
+    assert call(_src(**hw), ids=None) == C.VS_E_NULL
+    assert call(_src(**hw), gh=None, gw=None) == C.VS_E_NULL
+    assert call(_src(**hw), width=1025, ld=1025) == C.VS_E_SHAPE
+    assert call(_src(**hw), width=8, ld=7) == C.VS_E_SHAPE
+    assert call(_src(**hw), gh=FAKE + 2) == C.VS_E_ALIGN
+    assert call(_src(H=16392, ld_hidden=16392, ld_weight=16392, **hw)) == C.VS_E_UNSUPPORTED
+    assert call(_src(**hw), ws=None) == C.VS_E_WORKSPACE
+    need = lib.vs_workspace_size(C.VS_OP_SCORE_SUPPORT_BACKWARD, ctypes.byref(_src(T=2048, V=129280, **hw)), 64)
+    # dX and the pair list per (row, id), and three per-id arrays
+    assert need >= 2048 * 64 * 8 + 3 * 129280 * 4
+    assert call(_src(T=2048, V=129280, **hw), width=64, ld=64, nws=need - 1) == C.VS_E_WORKSPACE
+    f32 = lib.vs_workspace_size(C.VS_OP_SCORE_SUPPORT_BACKWARD,
+                                ctypes.byref(_src(T=2048, V=129280, hidden_dtype=C.VS_F32, **hw)), 64)
+    assert f32 >= need + 2048 * 64 * 2
+
+
 def test_l1_loss_validation(lib):
     from logprob_entropy_sampling_amd import _capi as C
 
