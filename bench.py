@@ -321,6 +321,30 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
             return oracle.score_support(fn, V, c["support_ids"][r], 1.0, c["targets"][r])
         res["support_replay"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(support_rows, T, cpu_budget_s),
                                                            "support_replay rows (selected projections + scores)")
+    # the VJP of the same scores (both gradients, upstream gradients ~N(0,1)); the dense fp32
+    # weight gradient is written whole (zeros for the ids in no support)
+    rng = np.random.default_rng(45)
+    a_np, b_np = rng.normal(0, 1, T).astype(np.float32), rng.normal(0, 1, T).astype(np.float32)
+    ga, gb = _dev(a_np, dev), _dev(b_np, dev)
+    o = vsa.score_support_backward(y, ids, hidden=hid, weight=w, grad_logprob=ga, grad_entropy=gb)
+    wsp = torch.empty(max(1, vsa.workspace_bytes("score_support_backward", hidden=hid, weight=w,
+                                                 width=ids.shape[1])), dtype=torch.uint8, device=dev)
+    ev, sw = _event_times(vsa, lambda: vsa.score_support_backward(y, ids, hidden=hid, weight=w, grad_logprob=ga,
+                                                                  grad_entropy=gb, out=o, workspace=wsp),
+                          steps, warmup, flush)
+    # distinct W rows read twice (logits, then d_hidden), hidden read twice (the row, then d_weight's
+    # gathers), ids, the two dense fp32 gradients written once
+    byts = 2 * uniq * H * 2 + 2 * T * H * 2 + c["support_ids"].nbytes + T * (8 + 2 * 4) + (T + V) * H * 4
+    res["support_backward"] = _path_entry(T, ev, sw, byts, byts, H=H, V=V, width=int(c["support_ids"].shape[1]),
+                                          unique_rows=uniq)
+    if cpu:
+        def support_bwd_rows(r):
+            ids_r = c["support_ids"][r]
+            return oracle.score_support_vjp(c["hidden"][r], "bf16", c["weight"], ids_r, 1.0, c["targets"][r],
+                                            a_np[r], b_np[r], weight_rows=np.unique(ids_r[ids_r >= 0]))
+        res["support_backward"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(support_bwd_rows, T, cpu_budget_s),
+                                                             "support_replay rows (support logits, dX, d_hidden, "
+                                                             "d_weight contributions)")
     del hid, w, o, wsp
 
     # sampling transforms and draft/target L1: T=2048, V=151,936 bf16
