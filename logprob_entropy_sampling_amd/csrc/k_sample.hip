@@ -12,16 +12,17 @@
 // The support is the transforms' descriptor: every token with x above the
 // threshold logit, and the first threshold_ties tokens (by id) equal to it.
 //
-// One workgroup per row streams the row once.  Every token at or above the
-// threshold gets an fp32 score with a bound on its error (its Philox block
-// computed once per 4 tokens); each thread keeps its two best by the upper
-// end of that interval, so the fp64 score - the decision - is taken only for
+// One workgroup per row streams the row once, two chunks ahead of the one it
+// scores.  Every token at or above the threshold gets an fp32 score with a
+// bound on its error (its Philox block computed once per 4 tokens); each
+// thread keeps its best by the upper end of that interval (its id only, a few
+// selects per token), so the fp64 score - the decision - is taken only for
 // the few tokens that can still be the best, without divergent fp64 work in
-// the loop.  Tokens equal to the threshold are tracked apart.  When the row holds more
-// threshold-equal tokens than the support takes, a second pass ranks them by
-// id and keeps the best of the first threshold_ties: rows of up to 163,840
-// tokens rank them from per-chunk tie counts kept in LDS during the first
-// pass (one scan), longer rows by a block scan per round of chunks.
+// the loop.  Tokens equal to the threshold are tracked apart.  When the row
+// holds more threshold-equal tokens than the support takes, a second pass
+// ranks them by id and keeps the best of the first threshold_ties: rows of
+// up to 155,648 tokens rank them from per-chunk tie counts kept in LDS during
+// the first pass (one scan), longer rows by a block scan per round of chunks.
 #include "common.h"
 #include "launch.h"
 
@@ -29,7 +30,9 @@ namespace vs {
 
 namespace {
 
-constexpr int kSampleThreads = 1024;
+// 512 threads and 78 KiB of LDS: two rows per CU, so one row's reductions
+// overlap the other's stream
+constexpr int kSampleThreads = 512;
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
 constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
@@ -82,8 +85,8 @@ __device__ __forceinline__ Best wave_best(Best b) {
 }
 
 // Rows of up to kLdsChunks 8-token chunks keep one tie count per chunk in LDS
-// (then an exclusive scan in place): V <= 163,840.
-constexpr int kLdsChunks = 20480;
+// (then an exclusive scan in place): V <= 155,648.
+constexpr int kLdsChunks = 19456;
 
 struct SampleSmem {
   double best_s[kSampleThreads / 64];
@@ -192,34 +195,29 @@ __device__ __forceinline__ float score32(float x, uint32_t r, const DrawArgs& d,
   return dz + g;
 }
 
-// A thread's two best tokens of one category by the upper end of their fp32
-// score intervals (lower id first on equal ends), the largest upper end of
-// every other token, and the largest lower end of all.  The true best token
-// of a category has its upper end at or above every lower end, so it is among
-// the tokens whose upper end reaches the workgroup's largest lower end.
-struct Top2 {
-  float hi1, hi2, b3, max_lo;
-  float x1, x2;
-  uint32_t r1, r2;
-  int64_t id1, id2;
+// A thread's best token of one category by the upper end of its fp32 score
+// interval (the lower id on equal ends), the largest upper end of every other
+// token, and the largest lower end of all.  The true best token of a category
+// has its upper end at or above every lower end, so it is a kept token whose
+// upper end reaches the workgroup's largest lower end - unless some other
+// token's upper end reaches it too, which the caller detects from b2 and then
+// rescans.  Only the id is kept: the token's logit and number are recomputed
+// for the one or two tokens the decision needs.
+struct Top1 {
+  float hi1, b2, max_lo;
+  int32_t id1;
 };
-__device__ __forceinline__ Top2 top2_empty(int V) {
+__device__ __forceinline__ Top1 top1_empty(int V) {
   const float ni = -__builtin_inff();
-  return Top2{ni, ni, ni, ni, 0.0f, 0.0f, 0u, 0u, int64_t(V), int64_t(V)};
+  return Top1{ni, ni, ni, V};
 }
-__device__ __forceinline__ void top2_add(Top2& t, float s, float err, float x, uint32_t r, int64_t id) {
+__device__ __forceinline__ void top1_add(Top1& t, float s, float err, int32_t id) {
   const float hi = s + err;
   t.max_lo = fmaxf(t.max_lo, s - err);
-  if (hi > t.hi1 || (hi == t.hi1 && id < t.id1)) {
-    t.b3 = fmaxf(t.b3, t.hi2);
-    t.hi2 = t.hi1, t.x2 = t.x1, t.r2 = t.r1, t.id2 = t.id1;
-    t.hi1 = hi, t.x1 = x, t.r1 = r, t.id1 = id;
-  } else if (hi > t.hi2 || (hi == t.hi2 && id < t.id2)) {
-    t.b3 = fmaxf(t.b3, t.hi2);
-    t.hi2 = hi, t.x2 = x, t.r2 = r, t.id2 = id;
-  } else {
-    t.b3 = fmaxf(t.b3, hi);
-  }
+  const bool take = hi > t.hi1 || (hi == t.hi1 && id < t.id1);
+  t.b2 = fmaxf(t.b2, take ? t.hi1 : hi);
+  t.hi1 = take ? hi : t.hi1;
+  t.id1 = take ? id : t.id1;
 }
 
 __device__ __forceinline__ float block_max_f(float v, SampleSmem& sm) {
@@ -270,11 +268,35 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 
   // Every token above the threshold (f_gt) and every token equal to it
   // (f_eq, with its count written to LDS when lds_ranks): one pass over the row.
+  // The raw bf16 bits of chunk q (NaN past V, which no threshold admits).
+  auto load_raw = [&](int64_t q) -> uint4 {
+    if (vec && 8 * q + 8 <= V) return *reinterpret_cast<const uint4*>(rowp + 8 * q);
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = 8 * q + i < V ? uint32_t(rowp[8 * q + i]) : 0x7FC0u;
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  };
+  // The row pass keeps the thread's next two chunks in flight while it scores
+  // the current one.
   auto each_token = [&](bool count_ties, auto f_gt, auto f_eq) {
     uint32_t n_eq = 0;
-    for (int64_t q = tid; q < nchunk; q += kSampleThreads) {
+    constexpr int64_t NT = kSampleThreads;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    uint4 n1 = tid < nchunk ? load_raw(tid) : zero;
+    uint4 n2 = tid + NT < nchunk ? load_raw(tid + NT) : zero;
+    for (int64_t q = tid; q < nchunk; q += NT) {
+      const uint4 w = n1;
+      n1 = n2;
+      if (q + 2 * NT < nchunk) n2 = load_raw(q + 2 * NT);
       float x[8];
-      load_chunk(rowp, vec, q, V, x);
+      x[0] = bf16_lo(w.x);
+      x[1] = bf16_hi(w.x);
+      x[2] = bf16_lo(w.y);
+      x[3] = bf16_hi(w.y);
+      x[4] = bf16_lo(w.z);
+      x[5] = bf16_hi(w.z);
+      x[6] = bf16_lo(w.w);
+      x[7] = bf16_hi(w.w);
       if (count_ties && lds_ranks) {
         uint32_t c = 0;
 #pragma unroll
@@ -385,13 +407,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 
   // ---- pass 1: fp32 score intervals of every support candidate (a token at
   // -inf has probability 0 and is never drawn) ----
-  Top2 gt = top2_empty(V), eq = top2_empty(V);
-  auto track = [&](Top2& t) {
+  Top1 gt = top1_empty(V), eq = top1_empty(V);
+  auto track = [&](Top1& t) {
     return [&t, &d](float x, uint32_t r, int64_t id) {
       if (x == -__builtin_inff()) return;
       float err;
       const float s32 = score32(x, r, d, err);
-      top2_add(t, s32, err, x, r, id);
+      top1_add(t, s32, err, int32_t(id));
     };
   };
   const uint32_t n_eq = each_token(true, track(gt), track(eq));
@@ -399,13 +421,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   (void)block_excl_scan(n_eq, n_eq_total, sm, 0);
   const bool partial = n_eq_total > ties;
   if (partial) {  // ---- pass 2: only the first `ties` threshold-equal tokens by id ----
-    eq = top2_empty(V);
+    eq = top1_empty(V);
     each_ranked_tie(track(eq));
   }
 
   // ---- the decision in fp64, over the tokens that can still be the best ----
   const float L = block_max_f(fmaxf(gt.max_lo, eq.max_lo), sm);
-  const float over = block_max_f((gt.b3 >= L || eq.b3 >= L) ? 1.0f : 0.0f, sm);
+  const float over = block_max_f((gt.b2 >= L || eq.b2 >= L) ? 1.0f : 0.0f, sm);
   Best best{-__builtin_inf(), int64_t(V)};
   auto exact = [&](float x, uint32_t r, int64_t id) {
     if (x == -__builtin_inff()) return;
@@ -416,14 +438,17 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     if (better(c, best)) best = c;
   };
   if (over == 0.0f) {
-    const Top2* ts[2] = {&gt, &eq};
+    const Top1* ts[2] = {&gt, &eq};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const Top2& t = *ts[k];
-      if (t.id1 < V && t.hi1 >= L) exact(t.x1, t.r1, t.id1);
-      if (t.id2 < V && t.hi2 >= L) exact(t.x2, t.r2, t.id2);
+      const Top1& t = *ts[k];
+      if (t.id1 < V && t.hi1 >= L) {
+        const int64_t id = t.id1;
+        const Ctr r = block_ctr(id >> 3, int((id >> 2) & 1));
+        exact(bf16_to_f32(rowp[id]), ctr_word(r, int(id & 3)), id);
+      }
     }
-  } else {  // some thread's third token may be a winner: rescan the row in the exact mode (rare)
+  } else {  // some token not kept may be a winner: rescan the row in the exact mode (rare)
     if (partial) {
       each_token(false, exact, [](float, uint32_t, int64_t) {});
       each_ranked_tie(exact);
