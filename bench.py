@@ -11,9 +11,10 @@ timing starts.
 Prints ONE JSON line.  Besides the contract fields it carries
     roofline      the fused sweep kernel vs bf16 dense MFMA peak (2.5 PFLOP/s)
     cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
-    paths         the other scoring paths (and the seeded sampler), each on its
-                  own workload, with an Infinity-Cache flush between timed
-                  calls, vs HBM peak (8 TB/s)
+    paths         the other scoring paths (and the seeded sampler, the L1 loss,
+                  the support VJP), each on its own workload: 20 warmup calls,
+                  then the median and IQR of 100 timed calls, each after an
+                  Infinity-Cache flush, vs HBM peak (8 TB/s) or the MFMA peak
 """
 
 from __future__ import annotations
@@ -115,6 +116,23 @@ def _flusher(dev):
     return flush
 
 
+def _clocks():
+    """The shader and memory clock levels the driver reports right now (sysfs
+    pp_dpm_sclk / pp_dpm_mclk, the line marked '*'), or None where unreadable."""
+    import glob
+    out = {}
+    for name in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}")):
+            try:
+                cur = [ln for ln in open(path).read().splitlines() if ln.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[name] = cur[0].split(":", 1)[-1].replace("*", "").strip()
+                break
+    return out or None
+
+
 def _median_iqr(ts):
     q = np.percentile(ts, [25, 50, 75])
     return float(q[1]), float(q[2] - q[0])
@@ -139,6 +157,7 @@ def bench_fused(vsa, dev, steps, warmup):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks = _clocks()  # read while the part is still at its working clocks
     # per-call event timing of the same op (its kernels run on this stream)
     ev, sw = _event_times(vsa, step, steps, 0)
     med, iqr = _median_iqr(ev)
@@ -151,6 +170,7 @@ def bench_fused(vsa, dev, steps, warmup):
         "ms_per_step": wall * 1e3 / steps,
         "event_ms_median": med,
         "event_ms_iqr": iqr,
+        "clocks_after_timed_region": clocks,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -290,7 +310,7 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     o = vsa.score_full(y, logits=lg, temperature=tau)
     ev, sw = _event_times(vsa, lambda: vsa.score_full(y, logits=lg, temperature=tau, out=o), steps, warmup, flush)
     byts = T * V * 2 + T * (4 + 8) + T * (3 * 4 + 1)  # logits, tau, targets in; lse, logprob, entropy, status out
-    res["logits_full"] = _path_entry(T, ev, sw, byts, byts, V=V)
+    res["logits_full"] = _path_entry(T, ev, sw, byts, byts, V=V, inputs_sha256=workloads.digest(c))
     if cpu:
         res["logits_full"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
             lambda r: oracle.score_full(oracle.logits_from_logits(c["logits"], "bf16", rows=r), c["temperature"][r],
@@ -312,7 +332,7 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     # unique basis: each distinct W row and each hidden row read once
     byts = uniq * H * 2 + T * H * 2 + c["support_ids"].nbytes + T * (8 + 2 * 4 + 1)
     res["support_replay"] = _path_entry(T, ev, sw, byts, byts, H=H, V=V, width=int(c["support_ids"].shape[1]),
-                                        pairs=int(sup.size), unique_rows=uniq,
+                                        pairs=int(sup.size), unique_rows=uniq, inputs_sha256=workloads.digest(c),
                                         bytes_pairs_basis=int(sup.size * H * 2 + T * H * 2 + c["support_ids"].nbytes))
     if cpu:
         def support_rows(r):
@@ -368,7 +388,8 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
     ev, sw = _event_times(vsa, lambda: vsa.score_transforms(y, lg, tk, tp, mp, temperature=tau, cap=64, out=o,
                                                             workspace=wsp), steps, warmup, flush)
     byts = T * V * 2 + T * (4 * 4 + 8) + T * (4 * 4 + 4 + 1 + 64 * 8 + 4)
-    res["transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, support_ids_cap=64)
+    res["transforms"] = _path_entry(T, ev, sw, byts, byts, V=V, support_ids_cap=64,
+                                    inputs_sha256=workloads.digest(c))
     if cpu:
         # (the oracle takes its own inputs: the workload's row-argmax targets, which lie in every
         # support; a target changes no step of the program's cost)
@@ -428,7 +449,8 @@ def bench_paths(vsa, dev, steps, warmup, cpu=True, cpu_budget_s=8.0):
         "tokens_per_s": round(T / (med * 1e-3), 1), "flop_per_call": flops,
         "tflops": round(flops / (med * 1e-3) / 1e12, 1),
         "mfma_frac": round(flops / (med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernel_ms_mean": round(statistics.mean(sw), 4), "workspace_bytes": int(wsp.numel())}
+        "kernel_ms_mean": round(statistics.mean(sw), 4), "workspace_bytes": int(wsp.numel()),
+        "inputs_sha256": workloads.digest(c)}
     if cpu:
         res["transforms_hidden"]["cpu_baseline"] = _cpu_entry(*_timed_oracle(
             lambda r: oracle.score_transforms(
@@ -469,6 +491,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--paths", choices=["all", "none"], default="all")
+    # the paths' timing protocol: 20 warmup calls, then the median and IQR of 100 timed calls
+    ap.add_argument("--path-steps", type=int, default=100)
+    ap.add_argument("--path-warmup", type=int, default=20)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain fp32 copy of MIB MiB --steps times (counter calibration)")
@@ -479,6 +504,7 @@ def main():
         sys.exit(2)
     import torch
     import logprob_entropy_sampling_amd as vsa
+    import workloads
     vsa.lib()
     dev = torch.device("cuda:0")
     probe = None
@@ -504,13 +530,15 @@ def main():
                    "parallelism": "single-gpu"},
         "event_ms_median": round(fused["event_ms_median"], 4),
         "event_ms_iqr": round(fused["event_ms_iqr"], 4),
+        "clocks_after_timed_region": fused["clocks_after_timed_region"],
+        "inputs_sha256": {"fused_full": workloads.digest(c)},
         "roofline": fused["roofline"],
     }
     if args.paths == "all":
         print("bench: fused backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(vsa, dev, c, max(3, min(args.steps, 10)), 1)
         print("bench: secondary paths", file=sys.stderr, flush=True)
-        out["paths"] = bench_paths(vsa, dev, max(5, min(args.steps, 20)), 2, cpu=args.cpu_baseline == "on")
+        out["paths"] = bench_paths(vsa, dev, args.path_steps, args.path_warmup, cpu=args.cpu_baseline == "on")
     if probe is not None:
         out["copy_probe"] = probe
     if args.cpu_baseline == "on":

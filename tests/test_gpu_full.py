@@ -227,6 +227,28 @@ def test_fused_full_size_rows_in_every_tile(vsa):
         _cmp_full(other, ref, rows=rows)
 
 
+def test_fused_agrees_with_logits_input_path(vsa):
+    # the fused sweep against the logits-input kernel fed the oracle's
+    # projection rounded to fp32: both match the oracle, and each other
+    # up to the fp32 roundings of the projection
+    say("fused vs logits-input path on the same projection: T=300 H=512 V=30001, per-row tau")
+    rng = np.random.default_rng(123)
+    T, H, V = 300, 512, 30001
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * 0.1).astype(np.float32))
+    tau = rng.uniform(0.6, 1.2, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    x = oracle.logits_from_hidden(hb, "bf16", wb)
+    fused = vsa.score_full(to_dev(y), hidden=bf16_tensor(hb), weight=bf16_tensor(wb), temperature=to_dev(tau))
+    direct = vsa.score_full(to_dev(y), logits=to_dev(x.astype(np.float32)), temperature=to_dev(tau))
+    ref = oracle.score_full(x, tau, y)
+    _cmp_full(fused, ref)
+    _cmp_full(direct, ref)
+    for k in ("lse", "logprob", "entropy"):
+        d = float((fused[k] - direct[k]).abs().max())
+        assert d <= 1e-4 * (1.0 + float(direct[k].abs().max())), (k, d)
+
+
 def test_fp32_range_of_the_tempered_logits(vsa):
     # The kernels work in fp32 base-2 units u = x * log2(e) / tau.  A row whose
     # largest logit has |x| * log2(e) / tau beyond the fp32 range is

@@ -147,6 +147,31 @@ def test_replay_workload_reduced(vsa):
     _cmp(got, ref)
 
 
+def test_permuted_ids_and_moved_padding(vsa):
+    # the support is a set: permuting a row's ids or moving its padding changes
+    # only the order of the fold's fp32 sums
+    say("support: ids permuted and padding moved to the front, fused and logits sources")
+    c = workloads.make(3, T=96, V=20000, H=512)
+    rng = np.random.default_rng(21)
+    ids = c["support_ids"]
+    moved = np.full_like(ids, -1)
+    for t in range(ids.shape[0]):
+        sup = rng.permutation(ids[t][ids[t] >= 0])
+        moved[t, ids.shape[1] - sup.size:] = sup
+    hid, w, y = bf16_tensor(c["hidden"]), bf16_tensor(c["weight"]), to_dev(c["targets"])
+    x = oracle.logits_from_hidden(c["hidden"], "bf16", c["weight"])
+    lg = to_dev(x.astype(np.float32))
+    for src in (dict(hidden=hid, weight=w), dict(logits=lg)):
+        a = vsa.score_support_ids(y, to_dev(ids), **src)
+        b = vsa.score_support_ids(y, to_dev(moved), **src)
+        assert torch.equal(a["status"], b["status"])
+        for k in ("logprob", "entropy"):
+            d = (a[k] - b[k]).abs().nan_to_num(0.0)
+            assert float(d.max()) <= 1e-5 * (1.0 + float(a[k].abs().nan_to_num(0.0).max())), k
+    ref = oracle.score_support(lambda t, cols: x[t, np.asarray(cols)], c["V"], moved, 1.0, c["targets"])
+    _cmp(b, ref)
+
+
 def test_replay_workload_full_size_all_rows(vsa):
     say("support replay full size T=2048 H=7168 V=129280 width 64: every row vs the oracle; determinism")
     c = workload(3)
