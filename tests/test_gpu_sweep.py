@@ -197,3 +197,156 @@ def test_sweep_support_logits(vsa, seed):
     got = vsa.score_support_ids(to_dev(y), to_dev(ids), logits=lg, temperature=to_dev(tau), fallback=to_dev(fb))
     ref = oracle.score_support(lambda t, cols: x64[t, cols], V, ids, tau, y, fb)
     _cmp_support(got, ref)
+
+
+# ---- the entry points added with the backward, the loss, the draw and the hidden/weight transforms ----
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_backward(vsa, seed):
+    from tests.test_gpu_backward import REL, _close, term_sizes
+    rng = np.random.default_rng(10000 + seed)
+    T = int(rng.integers(1, 260))
+    H = int(rng.choice([8, 40, 64, 96, 128, 264]))
+    V = int(rng.choice([1, 7, 300, 5000, 20001]))
+    chunk = int(rng.choice([1, 256, 1000, 100000]))
+    hdt = str(rng.choice(["bf16", "f32"]))
+    terms = str(rng.choice(["both", "logprob", "entropy"]))
+    say(f"sweep backward seed={seed}: T={T} H={H} V={V} chunk={chunk} hidden {hdt} terms={terms}")
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * (1.0 / np.sqrt(H))).astype(np.float32))
+    tau = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    y = rng.integers(0, V, T).astype(np.int64)
+    a = rng.normal(0, 1, T).astype(np.float32) if terms != "entropy" else None
+    b = rng.normal(0, 1, T).astype(np.float32) if terms != "logprob" else None
+    if hdt == "bf16":
+        hb = workloads.to_bf16_bits(h)
+        hid, h_arg = bf16_tensor(hb), hb
+    else:
+        hid, h_arg = to_dev(h), h
+    w = bf16_tensor(wb)
+    fw = vsa.score_full(to_dev(y), hidden=hid, weight=w, temperature=to_dev(tau))
+    got = vsa.score_full_backward(to_dev(y), fw["lse"], fw["entropy"], hidden=hid, weight=w,
+                                  grad_logprob=None if a is None else to_dev(a),
+                                  grad_entropy=None if b is None else to_dev(b), temperature=to_dev(tau),
+                                  vocab_chunk=chunk)
+    ref = oracle.score_full_vjp(h_arg, hdt, wb, tau, y, a, b)
+    adx = np.abs(ref["d_logits"])
+    h64 = oracle.widen_bf16(oracle.round_f32_to_bf16(h) if hdt == "f32" else h_arg)
+    w64 = oracle.widen_bf16(wb)
+    M, eps = term_sizes(h64 @ w64.T, tau, y, a, b)
+    eM = eps[:, None] * M
+    _close("grad_hidden", got["grad_hidden"].cpu().numpy(), ref["d_hidden"],
+           REL * (adx @ np.abs(w64)) + eM @ np.abs(w64) + 1e-30)
+    _close("grad_weight", got["grad_weight"].cpu().numpy(), ref["d_weight"],
+           REL * (adx.T @ np.abs(h64)) + eM.T @ np.abs(h64) + 1e-30)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_support_backward(vsa, seed):
+    from tests.test_gpu_support_backward import _check, _magnitudes
+    rng = np.random.default_rng(11000 + seed)
+    T = int(rng.integers(1, 80))
+    H = int(rng.choice([8, 16, 40, 128, 520]))
+    V = int(rng.choice([1, 6, 50, 3000]))
+    W = int(rng.choice([1, 2, 7, 64, 300]))
+    hdt = str(rng.choice(["bf16", "f32"]))
+    say(f"sweep support backward seed={seed}: T={T} H={H} V={V} width={W} hidden {hdt}")
+    hb = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = workloads.to_bf16_bits((rng.standard_normal((V, H)) * (1.5 / np.sqrt(H))).astype(np.float32))
+    ids = np.full((T, W), -1, np.int64)
+    y = rng.integers(0, V, T).astype(np.int64)
+    for t in range(T):
+        w = int(rng.integers(0, min(W, V) + 1))
+        row = rng.choice(V, w, replace=False)
+        ids[t, rng.choice(W, w, replace=False)] = row
+        if w and rng.random() < 0.8:
+            y[t] = row[int(rng.integers(0, w))]
+        if w >= 2 and rng.random() < 0.1:
+            ids[t, np.nonzero(ids[t] >= 0)[0][1]] = row[0]  # a repeated id: no gradient
+    tau = rng.uniform(0.4, 2.0, T).astype(np.float32)
+    a, b = rng.normal(0, 1, T).astype(np.float32), rng.normal(0, 1, T).astype(np.float32)
+    h_arg = hb if hdt == "bf16" else workloads.bf16_bits_to_f32(hb).copy()
+    got = vsa.score_support_backward(to_dev(y), to_dev(ids), hidden=bf16_tensor(hb) if hdt == "bf16" else to_dev(h_arg),
+                                     weight=bf16_tensor(wb), grad_logprob=to_dev(a), grad_entropy=to_dev(b),
+                                     temperature=to_dev(tau))
+    ref = oracle.score_support_vjp(h_arg, hdt, wb, ids, tau, y, a, b)
+    h64, w64 = oracle.widen_bf16(hb), oracle.widen_bf16(wb)
+    M = _magnitudes(h64, w64, ids, tau.astype(np.float64), y, a.astype(np.float64), b.astype(np.float64))
+    _check(got, ref, M, h64, w64, ids, f"sweep seed={seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_sweep_sample(vsa, seed):
+    from oracle import sampling
+    rng = np.random.default_rng(12000 + seed)
+    T = int(rng.integers(1, 24))
+    V = int(rng.choice([1, 3, 64, 1000, 30001, 100003]))
+    kind = str(rng.choice(["normal", "ties", "peaked", "neg_inf", "zeros"]))
+    say(f"sweep sample seed={seed}: T={T} V={V} values={kind}")
+    bits = workloads.to_bf16_bits(_values(rng, kind, (T, V)))
+    k = rng.choice([0, 1, 5, 50, V], size=T).astype(np.int32)
+    p = np.where(rng.random(T) < 0.5, 1.0, rng.uniform(0.05, 0.99, T)).astype(np.float32)
+    mp = np.where(rng.random(T) < 0.5, 0.0, 10.0 ** rng.uniform(-4, -0.1, T)).astype(np.float32)
+    tau = rng.uniform(0.2, 2.5, T).astype(np.float32)
+    s, off = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40))
+    got = vsa.sample_transforms(bf16_tensor(bits), to_dev(k), to_dev(p), to_dev(mp), temperature=to_dev(tau), seed=s,
+                                offset=off)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    ref = sampling.sample_transforms(x64, tau, k, p, mp, seed=s, offset=off)
+    assert np.array_equal(got["status"].cpu().numpy(), ref["status"])
+    drawn = got["sampled"].cpu().numpy()
+    diff = np.nonzero(drawn != ref["sampled"])[0]
+    assert all(ref["margin"][i] <= 1e-9 for i in diff), (diff[:5], drawn[diff[:5]], ref["sampled"][diff[:5]])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_l1_loss(vsa, seed):
+    import torch
+    from tests.test_gpu_l1_loss import _grad_close, sign_flip_bound
+    rng = np.random.default_rng(13000 + seed)
+    T = int(rng.integers(1, 12))
+    V = int(rng.choice([1, 2, 9, 1000, 65537]))
+    kind = str(rng.choice(["normal", "ties", "peaked", "zeros"]))
+    noise = float(rng.choice([0.0, 0.1, 2.0]))
+    gdt = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    wt = str(rng.choice(["none", "mixed"]))
+    say(f"sweep l1 loss seed={seed}: T={T} V={V} values={kind} noise={noise} grad {gdt} weights={wt}")
+    a = _values(rng, kind, (T, V))
+    b = (a + rng.standard_normal((T, V)) * noise).astype(np.float32)
+    w = None if wt == "none" else np.where(rng.random(T) < 0.3, 0.0, rng.uniform(0.1, 3.0, T)).astype(np.float32)
+    ab, bb = workloads.to_bf16_bits(a), workloads.to_bf16_bits(b)
+    a64, b64 = oracle.logits_from_logits(ab, "bf16"), oracle.logits_from_logits(bb, "bf16")
+    scale = float(rng.choice([1.0, -0.5, 4.0]))
+    got = vsa.l1_loss(bf16_tensor(ab), bf16_tensor(bb), weights=None if w is None else to_dev(w), grad_scale=scale,
+                      grad_dtype=gdt)
+    ref = oracle.weighted_l1_loss(a64, b64, w, grad_scale=scale)
+    assert_close("l1", got["l1"].cpu().numpy(), ref["l1"])
+    if np.isfinite(ref["den"]) and ref["den"] > 0:
+        assert_close("loss", got["loss"].cpu().numpy(), np.array([ref["num"], ref["den"], ref["loss"]]))
+        wv = np.ones(T) if w is None else w.astype(np.float64)
+        extra = sign_flip_bound(a64, b64, np.abs(scale * wv / ref["den"]))
+        _grad_close("grad", got["grad"].float().cpu().numpy(), ref["grad"], bf16=gdt == torch.bfloat16, extra=extra)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_transforms_hidden(vsa, seed):
+    from tests.test_gpu_transforms_hidden import _grid
+    rng = np.random.default_rng(14000 + seed)
+    T = int(rng.choice([1, 5, 70, 2049]))
+    H = int(rng.choice([8, 64, 96, 200]))
+    V = int(rng.choice([1, 17, 3000, 90001]))
+    if T > 2048:
+        V = min(V, 3000)  # two logits blocks; the oracle's sorts stay short
+    cap = int(rng.choice([0, 4, 64]))
+    say(f"sweep transforms on hidden x W seed={seed}: T={T} H={H} V={V} cap={cap} (exact-sum grid inputs)")
+    hb, wb = _grid(rng, (T, H), 0.25), _grid(rng, (V, H), 1.0 / 128)
+    k = rng.choice([0, 1, 5, V], size=T).astype(np.int32)
+    p = np.where(rng.random(T) < 0.5, 1.0, rng.uniform(0.05, 0.99, T)).astype(np.float32)
+    mp = np.where(rng.random(T) < 0.5, 0.0, 10.0 ** rng.uniform(-4, -0.1, T)).astype(np.float32)
+    tau = rng.uniform(0.3, 2.0, T).astype(np.float32)
+    x64 = oracle.widen_bf16(oracle.bf16_logits_from_hidden(hb, "bf16", wb))
+    y = np.argmax(x64, axis=1)
+    got = vsa.score_transforms(to_dev(y), None, to_dev(k), to_dev(p), to_dev(mp), hidden=bf16_tensor(hb),
+                               weight=bf16_tensor(wb), temperature=to_dev(tau), cap=cap)
+    ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
+    _cmp_transforms(got, ref, cap, f"sweep hidden seed={seed}", x64, tau, y)
