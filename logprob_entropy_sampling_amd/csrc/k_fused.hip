@@ -270,10 +270,13 @@ struct EpiArgs {
   int accumulate;
 };
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+// Two fp32 values as packed bf16, a in the low half: round to nearest even
+// (one v_cvt_pk_bf16_f32; a NaN stays a NaN).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // The row data of the lane's 4 token columns for the gradient, loaded when
@@ -352,22 +355,21 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
       for (int q = 0; q < 4; ++q) {
         const int vb = vrow0 + 32 * i + 8 * q;  // rows vb .. vb+3 of the tile
         if (vb >= np) continue;
-        uint16_t gv[4];
+        float dx[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float dx = 0.0f;
+          dx[e] = 0.0f;
           if (live && vb + e < nv) {
             const float d2 = __builtin_fmaf(acc[i][j][4 * q + e], c, -l2);
             const float pv = exp2_hw(d2);
             float dz = -pv * __builtin_fmaf(gb, __builtin_fmaf(d2, kLn2, h), ga);
             if (vb + e == yr) dz += ga;
-            dx = dz * inv_tau;
+            dx[e] = dz * inv_tau;
           }
-          gv[e] = bf16_rne_bits(dx);
         }
         // v_pad is a multiple of 4
         *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
-            make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
+            make_uint2(pack_bf16_rne(dx[0], dx[1]), pack_bf16_rne(dx[2], dx[3]));
       }
   }
 }
@@ -400,11 +402,11 @@ __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0,
       for (int q = 0; q < 4; ++q) {
         const int vb = vrow0 + 32 * i + 8 * q;
         if (vb >= nv) continue;
-        uint16_t gv[4];
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gv[e] = vb + e < nv ? bf16_rne_bits(acc[i][j][4 * q + e]) : uint16_t(0);
+        for (int e = 0; e < 4; ++e) x[e] = vb + e < nv ? acc[i][j][4 * q + e] : 0.0f;
         *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
-            make_uint2(uint32_t(gv[0]) | (uint32_t(gv[1]) << 16), uint32_t(gv[2]) | (uint32_t(gv[3]) << 16));
+            make_uint2(pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3]));
       }
   }
 }
