@@ -181,8 +181,9 @@ int vs_score_full(const vs_source* src, const int64_t* target_ids, int64_t vocab
  * invalid tau or target) contributes no gradient.  Workspace:
  * vs_workspace_size(VS_OP_SCORE_FULL_BACKWARD, src, vocab_chunk), about
  * 2 (2T + H) vocab_chunk + 2 H T bytes (bf16 dX, its transpose and the
- * chunk's transposed weight rows); vocab_chunk >= V makes one chunk, the
- * fastest form (one d_hidden product over the whole vocabulary).
+ * chunk's transposed weight rows); vocab_chunk is rounded up to a multiple
+ * of 256 and capped at V rounded up and at 2^23; vocab_chunk >= V makes one
+ * chunk, the fastest form (one d_hidden product over the whole vocabulary).
  */
 int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, const float* lse, const float* entropy,
                            const float* grad_logprob, const float* grad_entropy, int64_t vocab_chunk,
@@ -270,7 +271,9 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  *   x[t, v] = bf16_rne(sum_h bf16(hidden[t, h]) W[v, h])   (fp32 sums)
  * - the fused sweep's fp32 logits rounded to bf16, nearest even - computed by
  * the MFMA sweep for blocks of up to 2048 token rows into the workspace and
- * scored block by block; the caller never sees them.
+ * scored block by block; the caller never sees them.  That source takes
+ * V <= 2^23 - 7 (VS_E_UNSUPPORTED above: the block's row stride stays under
+ * 2^23 elements).
  * The transform parameters are never ignored.  support_ids_cap > 4096 with a
  * non-NULL support_ids_out gives VS_E_UNSUPPORTED.  A target outside S_t gives
  * logprob -inf and TARGET_OUTSIDE_SUPPORT.  BAD_INPUT rows: NaN floats,

@@ -265,6 +265,9 @@ struct EpiArgs {
   int64_t ld_g;
   int64_t v_begin;           // vocabulary id of the sweep's first row (the target test)
   int64_t v_pad;             // G's columns are zero-filled up to this
+  uint16_t* gt;              // nullable: G^T [V][ld_gt] (64-wide sweep only), zeros in columns rows .. t_pad-1
+  int64_t ld_gt;
+  int64_t t_pad;
   float* c;                  // kEpiStore
   int64_t ldc;
   int accumulate;
@@ -319,10 +322,95 @@ __device__ __forceinline__ GradColumns load_grad_columns(int64_t t0, int64_t row
   return g;
 }
 
+// The bf16 epilogues hand each lane's 8-byte pieces (4 consecutive vocabulary
+// rows vb .. vb+3 of token column col, tile-relative) to a sink: DirectStore
+// writes them to G [token][vocabulary row] (ld_g a multiple of 4), the staged
+// form below collects the tile in LDS and writes whole rows.
+struct DirectStore {
+  static constexpr bool kAllColumns = false;  // the epilogue may skip columns past the last row
+  uint16_t* g_tile;  // G + t0 * ld_g + v0
+  int ldg;           // < 2^31 / 256 (checked at launch): tile offsets stay 32-bit
+  __device__ __forceinline__ void operator()(int col, int vb, uint2 v, bool tvalid) const {
+    if (tvalid) *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) = v;
+  }
+};
+
+// The tile as bf16 in the LDS of the K loop (free after its last barrier):
+// part k holds token columns 64k .. 64k+63, one 512-byte row of 256 vocabulary
+// rows each; 16-byte chunk c of row r sits at c ^ (r & 31), so the puts (32
+// columns, one chunk) and the row reads (one row, 32 chunks) are both free
+// of bank conflicts.  flush() writes rows r < trows, columns below lim (a
+// multiple of 4): 16-byte stores where G's rows are 16-byte aligned (an
+// 8-byte one for a half chunk), so each wave store covers two whole 512-byte
+// rows where the direct pieces touch 32 rows; else 8-byte stores.
+struct StagedStore {
+  static constexpr bool kAllColumns = false;
+  uint4 *p0, *p1, *p2, *p3;  // (selected, not indexed: an indexed array would be placed in LDS itself)
+  __device__ __forceinline__ uint4* part(int k) const { return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3; }
+  __device__ __forceinline__ void operator()(int col, int vb, uint2 v, bool) const {
+    uint4* row = part(col >> 6) + (col & 63) * 32;
+    reinterpret_cast<uint2*>(row + ((vb >> 3) ^ (col & 31)))[(vb >> 2) & 1] = v;
+  }
+  __device__ __forceinline__ void flush(uint16_t* g_tile, int64_t ldg, int trows, int lim) const {
+    const int c = threadIdx.x & 31;
+    const int r0 = threadIdx.x >> 5;  // 8 rows per pass
+    const bool wide = ((ldg & 7) | (reinterpret_cast<uintptr_t>(g_tile) & 15)) == 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int r = r0 + 8 * k;  // part k >> 3 holds it
+      if (r < trows && 8 * c + 4 <= lim) {
+        const uint4 v = part(k >> 3)[(r & 63) * 32 + (c ^ (r & 31))];
+        uint16_t* dst = g_tile + r * ldg + 8 * c;
+        if (wide && 8 * c + 8 <= lim) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+          if (8 * c + 8 <= lim) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(v.z, v.w);
+        }
+      }
+    }
+  }
+};
+
+// The gradient sink of the 64-wide sweep: G directly, and G^T through the
+// K loop's LDS: each value goes as 2 bytes into an LDS tile [vocabulary row]
+// [256 tokens] (part k: rows 64k .. 64k+63, 512 bytes each; 16-byte chunk c
+// of row r at c ^ (((r >> 1) & 3) << 2), so the two rows of one put and the
+// row reads of flush_t fall on distinct banks).
+struct GradStore {
+  static constexpr bool kAllColumns = true;  // every column (zeros past the last row) for G^T
+  DirectStore g;
+  uint4 *p0, *p1, *p2, *p3;
+  __device__ __forceinline__ uint4* part(int k) const { return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3; }
+  __device__ __forceinline__ void operator()(int col, int vb, uint2 v, bool tvalid) const {
+    g(col, vb, v, tvalid);
+    const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = vb + e;
+      uint4* row = part(r >> 6) + (r & 63) * 32;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(row + ((col >> 3) ^ (((r >> 1) & 3) << 2))) + (col & 7);
+      *dst = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+  // G^T rows r < nrows (vocabulary rows of the tile), token columns below ncols (a multiple of 8)
+  __device__ __forceinline__ void flush_t(uint16_t* gt_tile, int64_t ld, int nrows, int ncols) const {
+    const int c = threadIdx.x & 31;
+    const int r0 = threadIdx.x >> 5;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int r = r0 + 8 * k;  // part k >> 3 holds it
+      if (r < nrows && 8 * c < ncols)
+        *reinterpret_cast<uint4*>(gt_tile + r * ld + 8 * c) = part(k >> 3)[(r & 63) * 32 + (c ^ (((r >> 1) & 3) << 2))];
+    }
+  }
+};
+
 // The gradient of the tile's logits into G (bf16, nearest even).  A row whose
 // LSE is not finite (a BAD_INPUT row of the forward) gets a zero gradient.
+template <class Sink>
 __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t t0, int64_t rows_valid,
-                                              int64_t V, const GradColumns& gc, const EpiArgs& ep) {
+                                              int64_t V, const GradColumns& gc, const EpiArgs& ep, const Sink& put) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wv = w & 1;
@@ -333,8 +421,6 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
   const int vrow0 = wv * 128 + 4 * lh;  // + 32 i + 8 q + e
   const int nv = int(V - v0 < BV ? V - v0 : BV);
   const int np = int(ep.v_pad - v0 < BV ? ep.v_pad - v0 : BV);
-  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;  // + col * ld_g + vr
-  const int ldg = int(ep.ld_g);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // the accumulators of the columns not written yet stay in AGPRs until their turn
@@ -347,8 +433,8 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
     const float c = gc.c[j], inv_tau = gc.inv_tau[j], l2 = gc.l2[j], h = gc.h[j], ga = gc.ga[j], gb = gc.gb[j];
     const int64_t yv = gc.y[j] - v0;
     const int yr = (yv >= 0 && yv < BV) ? int(yv) : -1;  // the target's tile-relative row
-    const bool live = tvalid && (ga != 0.0f || gb != 0.0f);
-    if (!tvalid) continue;
+    const bool live = tvalid && (ga != 0.0f || gb != 0.0f);  // else dx = 0
+    if (!Sink::kAllColumns && !tvalid) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -367,17 +453,16 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], int64_t v0, i
             dx[e] = dz * inv_tau;
           }
         }
-        // v_pad is a multiple of 4
-        *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
-            make_uint2(pack_bf16_rne(dx[0], dx[1]), pack_bf16_rne(dx[2], dx[3]));
+        put(col, vb, make_uint2(pack_bf16_rne(dx[0], dx[1]), pack_bf16_rne(dx[2], dx[3])), tvalid);
       }
   }
 }
 
-// The tile's logits as bf16 into G [token][vocabulary row], 8-byte stores of
-// 4 consecutive vocabulary rows (the row stride ld_g a multiple of 4).
+// The tile's logits as bf16 into G [token][vocabulary row], in pieces of 4
+// consecutive vocabulary rows (0 past V).
+template <class Sink>
 __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t t0, int64_t rows_valid,
-                                                int64_t V, const EpiArgs& ep) {
+                                                int64_t V, const Sink& put) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wv = w & 1;
@@ -386,8 +471,6 @@ __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0,
   const int lh = lane >> 5;
   const int vrow0 = wv * 128 + 4 * lh;  // + 32 i + 8 q + e
   const int nv = int(V - v0 < BV ? V - v0 : BV);
-  uint16_t* const g_tile = ep.g + t0 * ep.ld_g + v0;
-  const int ldg = int(ep.ld_g);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -405,8 +488,7 @@ __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0,
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = vb + e < nv ? acc[i][j][4 * q + e] : 0.0f;
-        *reinterpret_cast<uint2*>(g_tile + col * ldg + vb) =
-            make_uint2(pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3]));
+        put(col, vb, make_uint2(pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3])), true);
       }
   }
 }
@@ -549,9 +631,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_kernel(
     tile_epilogue(acc, reinterpret_cast<float*>(&As[0][0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
+    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep, DirectStore{ep.g + t0 * ep.ld_g + v0, int(ep.ld_g)});
   else if constexpr (MODE == kEpiLogits)
-    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
+    logits_epilogue(acc, v0, t0, rows_valid, V, DirectStore{ep.g + t0 * ep.ld_g + v0, int(ep.ld_g)});
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -761,9 +843,9 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_pipelined_kernel(
     tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
   else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
+    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep, DirectStore{ep.g + t0 * ep.ld_g + v0, int(ep.ld_g)});
   else if constexpr (MODE == kEpiLogits)
-    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
+    logits_epilogue(acc, v0, t0, rows_valid, V, DirectStore{ep.g + t0 * ep.ld_g + v0, int(ep.ld_g)});
   else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
@@ -955,11 +1037,22 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
   if constexpr (MODE == kEpiPartials)
     tile_epilogue(acc, reinterpret_cast<float*>(&A0[0]), v0, t0, vt, rows_valid, V, cl, n_vtiles, ep.partials,
                   ep.zy_raw);
-  else if constexpr (MODE == kEpiGrad)
-    grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep);
-  else if constexpr (MODE == kEpiLogits)
-    logits_epilogue(acc, v0, t0, rows_valid, V, ep);
-  else
+  else if constexpr (MODE == kEpiGrad) {
+    const DirectStore gd{ep.g + t0 * ep.ld_g + v0, int(ep.ld_g)};
+    if constexpr (BUF && REM == 0) {  // G^T too (the other forms have no registers to spare for it)
+      const GradStore st{gd, A0, A1, B0, B1};
+      grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep, st);
+      __syncthreads();
+      st.flush_t(ep.gt + v0 * ep.ld_gt + t0, ep.ld_gt, int(vrows), int(ep.t_pad - t0 < BT ? ep.t_pad - t0 : BT));
+    } else {
+      grad_epilogue(acc, v0, t0, rows_valid, V, gcol, ep, gd);
+    }
+  } else if constexpr (MODE == kEpiLogits) {
+    const StagedStore st{A0, A1, B0, B1};
+    logits_epilogue(acc, v0, t0, rows_valid, V, st);
+    __syncthreads();
+    st.flush(ep.g + t0 * ep.ld_g + v0, ep.ld_g, int(trows), (int(vrows) + 3) & ~3);
+  } else
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
 
@@ -1097,11 +1190,25 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
                                     row_map, row_count, ep, stream);
 }
 
+bool fused_grad_writes_transpose(int64_t H, int64_t ld_hidden, int64_t ld_weight) {
+  // the 64-wide sweep with an even stage count and 32-bit buffer offsets (as launch_sweep picks it)
+  return H % (2 * BK2) == 0 && int64_t(BV) * ld_weight * 2 <= 0x7FFFFFFF && int64_t(BT) * ld_hidden * 2 <= 0x7FFFFFFF;
+}
+
 int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                       int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
                       const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
-                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, void* stream) {
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, uint16_t* gt,
+                      int64_t ld_gt, int64_t t_pad, void* stream) {
+  // the 64-wide sweep with an even stage count writes G^T and needs it; the other forms never do
+  if (v_pad % 64 != 0 || ld_g > kMaxTileLd || (gt != nullptr) != fused_grad_writes_transpose(H, ld_hidden, ld_weight) ||
+      (gt && (t_pad % 8 != 0 || t_pad < rows || ld_gt % 8 != 0 || ld_gt < t_pad ||
+              (reinterpret_cast<uintptr_t>(gt) & 15) != 0)))
+    return int(hipErrorInvalidValue);
   EpiArgs ep{};
+  ep.gt = gt;
+  ep.ld_gt = ld_gt;
+  ep.t_pad = t_pad;
   ep.lse = lse;
   ep.entropy = entropy;
   ep.grad_logprob = grad_logprob;
@@ -1116,6 +1223,7 @@ int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t*
 
 int launch_fused_logits(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                         int64_t rows, int64_t H, int64_t V, uint16_t* out, int64_t ld_out, void* stream) {
+  if (ld_out > kMaxTileLd || ld_out % 4 != 0) return int(hipErrorInvalidValue);
   EpiArgs ep{};
   ep.g = out;
   ep.ld_g = ld_out;

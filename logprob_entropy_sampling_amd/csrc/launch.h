@@ -35,13 +35,22 @@ int launch_fused_partials(const uint16_t* hidden, int64_t ld_hidden, const uint1
                           const int64_t* targets, const int32_t* row_map, const int32_t* row_count,
                           void* partials, float* zy_raw, void* stream);
 
+// Largest row stride of the bf16 outputs of the sweep (G, the logits block):
+// a tile's element offsets stay below 2^31.
+constexpr int64_t kMaxTileLd = int64_t(1) << 23;
+
 // The gradient sweep: the same tiles over weight rows [0, V) (vocabulary ids
 // v_begin + v) x hidden rows [0, rows); writes the logits' gradient as bf16
-// into g [rows][ld_g], zeros in columns V .. v_pad-1 (v_pad a multiple of 4).
+// into g [rows][ld_g] (ld_g <= kMaxTileLd), zeros in columns V .. v_pad-1 (v_pad a multiple of 64),
+// and, where fused_grad_writes_transpose(H, ld_hidden, ld_weight), its transpose into gt [V][ld_gt],
+// zeros in columns rows .. t_pad-1 (t_pad and ld_gt multiples of 8, gt 16-byte
+// aligned).  gt must be given exactly where that holds (else an error is returned).
+bool fused_grad_writes_transpose(int64_t H, int64_t ld_hidden, int64_t ld_weight);
 int launch_fused_grad(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                       int64_t rows, int64_t H, int64_t V, int64_t v_begin, const float* temp, float temp_scalar,
                       const int64_t* targets, const float* lse, const float* entropy, const float* grad_logprob,
-                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, void* stream);
+                      const float* grad_entropy, uint16_t* g, int64_t ld_g, int64_t v_pad, uint16_t* gt,
+                      int64_t ld_gt, int64_t t_pad, void* stream);
 
 // c[m][n] (+)= sum_k a[m][k] b[n][k] (bf16 in, fp32 out; K a multiple of 8,
 // lda, ldb multiples of 8, a and b 16-byte aligned): the sweep's MFMA loop
@@ -50,7 +59,8 @@ int launch_gemm_nt(const uint16_t* a, int64_t lda, int64_t M, const uint16_t* b,
                    float* c, int64_t ldc, bool accumulate, void* stream);
 
 // logits [rows][ld_out] (bf16, nearest even) = hidden [rows][H] . weight [V][H]^T:
-// the sweep's MFMA loop with a bf16 store (ld_out a multiple of 4, >= V).
+// the sweep's MFMA loop with a bf16 store (ld_out a multiple of 4, >= V,
+// <= kMaxTileLd; else an error is returned).
 int launch_fused_logits(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
                         int64_t rows, int64_t H, int64_t V, uint16_t* out, int64_t ld_out, void* stream);
 

@@ -165,6 +165,7 @@ BwdDims bwd_dims(const vs_source* s, int64_t vocab_chunk) {
   int64_t vc = vocab_chunk < tile ? tile : (vocab_chunk + tile - 1) / tile * tile;
   const int64_t vmax = (s->V + tile - 1) / tile * tile;
   if (vc > vmax) vc = vmax;
+  if (vc > vs::kMaxTileLd) vc = vs::kMaxTileLd;  // G's row stride (a multiple of the tile)
   return BwdDims{vc, (s->T + 63) / 64 * 64};
 }
 size_t backward_ws_bytes(const vs_source* s, int64_t vocab_chunk) {
@@ -329,6 +330,7 @@ int vs_score_transforms(const vs_source* src, const int32_t* top_k, const float*
   int rc = check_source(src);
   if (rc) return rc;
   if (src->kind == VS_SRC_LOGITS && src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
+  if (src->kind == VS_SRC_HIDDEN_WEIGHT && xf_dims(src).ld > vs::kMaxTileLd) return VS_E_UNSUPPORTED;
   if (!top_k || !top_p || !min_p || !target_ids || !logprob) return VS_E_NULL;
   if (support_ids_cap < 0 || support_ids_cap > kMaxDim) return VS_E_PARAM;
   if (support_ids_cap == 0) support_ids_out = nullptr;
@@ -363,6 +365,7 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   int rc = check_source(src);
   if (rc) return rc;
   if (src->kind == VS_SRC_LOGITS && src->logits_dtype != VS_BF16) return VS_E_UNSUPPORTED;
+  if (src->kind == VS_SRC_HIDDEN_WEIGHT && xf_dims(src).ld > vs::kMaxTileLd) return VS_E_UNSUPPORTED;
   if (!top_k || !top_p || !min_p || !sampled_ids) return VS_E_NULL;
   rc = check_workspace(workspace, workspace_bytes, sample_ws_bytes(src));
   if (rc) return rc;
@@ -435,9 +438,11 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
   for (int64_t v0 = 0; v0 < V; v0 += dm.vc) {
     const int64_t vn = V - v0 < dm.vc ? V - v0 : dm.vc;
     const int64_t vp = (vn + 63) / 64 * 64;
+    // G^T comes from the sweep itself where it can write it, else from a transpose of G
+    const bool gt_direct = vs::fused_grad_writes_transpose(H, ldh, src->ld_weight);
     if (vs::launch_fused_grad(hid, ldh, W + v0 * src->ld_weight, src->ld_weight, T, H, vn, v0, src->temperature,
                               src->temperature_scalar, target_ids, lse, entropy, grad_logprob, grad_entropy, G, dm.vc,
-                              vp, stream))
+                              vp, gt_direct ? GT : nullptr, dm.tp, dm.tp, stream))
       return VS_E_DEVICE;
     if (grad_hidden) {  // d_hidden [T][H] (+)= G [T][vp] . (W^T [H][vp])^T
       if (vs::launch_transpose_pad(W + v0 * src->ld_weight, src->ld_weight, vn, H, WT, dm.vc, vp, stream) ||
@@ -445,7 +450,7 @@ int vs_score_full_backward(const vs_source* src, const int64_t* target_ids, cons
         return VS_E_DEVICE;
     }
     if (grad_weight) {  // d_weight [vn][H] = G^T [vn][Tp] . (hidden^T [H][Tp])^T
-      if (vs::launch_transpose_pad(G, dm.vc, T, vn, GT, dm.tp, dm.tp, stream) ||
+      if ((!gt_direct && vs::launch_transpose_pad(G, dm.vc, T, vn, GT, dm.tp, dm.tp, stream)) ||
           vs::launch_gemm_nt(GT, dm.tp, vn, hT, dm.tp, H, dm.tp, grad_weight + v0 * ld_grad_weight, ld_grad_weight,
                              false, stream))
         return VS_E_DEVICE;

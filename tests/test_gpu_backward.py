@@ -110,6 +110,8 @@ def _case(vsa, T, H, V, chunk, hidden_dtype, seed, with_lp=True, with_ent=True, 
     (77, 96, 700, 256, "f32"),         # T and every chunk ragged; H = 96: the 32-wide pipelined sweep
     (130, 40, 2000, 600, "bf16"),      # H = 40: the register-staged sweep; chunk rounded up to 768
     (513, 1024, 30000, 8192, "bf16"),  # 4 chunks of 8192 rows
+    (77, 128, 700, 256, "f32"),        # G^T from the sweep itself: T odd (a token pair with one missing row)
+    (150, 192, 1500, 512, "bf16"),     # an odd number of 64-wide stages: G^T from the transpose kernel
 ])
 def test_backward_matches_oracle(vsa, T, H, V, chunk, hdt):
     say(f"backward: T={T} H={H} V={V} vocab_chunk={chunk} hidden {hdt}, logprob and entropy gradients, bad rows")

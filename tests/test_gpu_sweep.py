@@ -206,7 +206,7 @@ def test_sweep_backward(vsa, seed):
     from tests.test_gpu_backward import REL, _close, term_sizes
     rng = np.random.default_rng(10000 + seed)
     T = int(rng.integers(1, 260))
-    H = int(rng.choice([8, 40, 64, 96, 128, 264]))
+    H = int(rng.choice([8, 40, 64, 96, 128, 192, 264]))
     V = int(rng.choice([1, 7, 300, 5000, 20001]))
     chunk = int(rng.choice([1, 256, 1000, 100000]))
     hdt = str(rng.choice(["bf16", "f32"]))
