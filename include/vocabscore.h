@@ -272,8 +272,8 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  * - the fused sweep's fp32 logits rounded to bf16, nearest even - computed by
  * the MFMA sweep for blocks of up to 2048 token rows into the workspace and
  * scored block by block; the caller never sees them.  That source takes
- * V <= 2^23 - 7 (VS_E_UNSUPPORTED above: the block's row stride stays under
- * 2^23 elements).
+ * V <= 2^23 (VS_E_UNSUPPORTED above: the block's row stride, V rounded up to
+ * 8, stays at most 2^23 elements).
  * The transform parameters are never ignored.  support_ids_cap > 4096 with a
  * non-NULL support_ids_out gives VS_E_UNSUPPORTED.  A target outside S_t gives
  * logprob -inf and TARGET_OUTSIDE_SUPPORT.  BAD_INPUT rows: NaN floats,

@@ -300,3 +300,22 @@ def test_backward_validation(lib):
     n = lib.vs_workspace_size(C.VS_OP_SCORE_FULL_BACKWARD, ctypes.byref(big), 8192)
     # hidden^T, G, G^T and one chunk of W^T, bf16
     assert n >= 2 * (4096 * 4096 + 4096 * 8192 + 8192 * 4096 + 4096 * 8192)
+    # the chunk is capped at 2^23 vocabulary rows (the row stride of G): a larger one needs no more workspace
+    huge = _src(T=16, H=64, V=(1 << 24) + 5, ld_hidden=64, ld_weight=64, **hw)
+    capped = lib.vs_workspace_size(C.VS_OP_SCORE_FULL_BACKWARD, ctypes.byref(huge), 1 << 23)
+    assert capped == lib.vs_workspace_size(C.VS_OP_SCORE_FULL_BACKWARD, ctypes.byref(huge), 1 << 30)
+    assert capped > lib.vs_workspace_size(C.VS_OP_SCORE_FULL_BACKWARD, ctypes.byref(huge), 1 << 22)
+
+
+def test_hidden_source_transforms_vocabulary_limit(lib):
+    """The logits block of a hidden/weight source keeps a row stride (V rounded up to 8) of at most 2^23."""
+    from logprob_entropy_sampling_amd import _capi as C
+    hw = dict(kind=C.VS_SRC_HIDDEN_WEIGHT, T=4, H=64, ld_hidden=64, ld_weight=64)
+    for V, rc in ((1 << 23, C.VS_E_WORKSPACE), ((1 << 23) + 1, C.VS_E_UNSUPPORTED)):
+        src = _src(V=V, **hw)
+        got = lib.vs_score_transforms(ctypes.byref(src), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, 0, FAKE, None, 0, None)
+        assert got == rc, (V, got)
+        got = lib.vs_sample_transforms(ctypes.byref(src), FAKE, FAKE, FAKE, 1, 0, FAKE, None, None, None, None, None,
+                                       0, None)
+        assert got == rc, (V, got)
