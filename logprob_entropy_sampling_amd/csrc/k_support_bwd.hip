@@ -18,7 +18,10 @@
 //                        workspace array), then d_hidden by 8-wide chunks of H
 //                        over the ids in order; each id of a scored row is
 //                        counted into cnt[id].
-//   pair_scan_kernel     one workgroup: exclusive scan of cnt into offs, fill = 0.
+//   span_sum_kernel, scan_one_kernel, span_scan_kernel
+//                        exclusive scan of cnt into offs (the totals of spans of
+//                        8192 ids, their scan, then each span from its offset);
+//                        fill = 0.
 //   pair_scatter_kernel  every counted pair into its id's bucket (any order).
 //   weight_grad_kernel   one workgroup per vocabulary row: its bucket sorted by
 //                        pair index (so the sum's order is fixed), then
@@ -211,50 +214,82 @@ __global__ __launch_bounds__(NT) void support_grad_kernel(
 }
 
 // offs[v] = sum_{u < v} cnt[u], offs[V] = the total; fill[v] = 0.
-__global__ __launch_bounds__(kScanThreads) void pair_scan_kernel(const int32_t* __restrict__ cnt, int64_t V,
-                                                                 int32_t* __restrict__ offs,
-                                                                 int32_t* __restrict__ fill) {
-  constexpr int ITEMS = 8;
+// Exclusive scan of in[base, base + span) (span = kScanSpan, clipped to n)
+// into out, starting from carry; returns the span's total to every thread.
+// ITEMS consecutive entries per thread (16-byte loads where aligned), a
+// wave scan of the thread totals, then the wave totals in order: integer
+// sums, so the result does not depend on the order.
+constexpr int kScanItems = 8;
+constexpr int64_t kScanSpan = int64_t(kScanThreads) * kScanItems;
+__device__ __forceinline__ int32_t scan_span(const int32_t* __restrict__ in, int64_t n, int64_t base, int32_t carry,
+                                             int32_t* __restrict__ out, int32_t* wsum) {
   constexpr int NW = kScanThreads / 64;
-  __shared__ int32_t wsum[NW];
-  __shared__ int32_t carry;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry = 0;
+  const int64_t k0 = base + int64_t(tid) * kScanItems;
+  int32_t v[kScanItems];
+  if (k0 + kScanItems <= n) {
+    const int4 a = reinterpret_cast<const int4*>(in + k0)[0], b = reinterpret_cast<const int4*>(in + k0)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) v[i] = k0 + i < n ? in[k0 + i] : 0;
+  }
+  int32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) local += v[i];
+  int32_t incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();  // wsum is free (an earlier span's readers are done)
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  for (int64_t base = 0; base < V; base += int64_t(kScanThreads) * ITEMS) {
-    int32_t v[ITEMS];
-    int32_t local = 0;
+  int32_t run = carry + incl - local;
+  int32_t total = carry;
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int64_t k = base + int64_t(tid) * ITEMS + i;
-      v[i] = k < V ? cnt[k] : 0;
-      if (k < V) fill[k] = 0;
-      local += v[i];
-    }
-    // inclusive scan of the thread totals inside the wave, then across waves
-    int32_t incl = local;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) run += wsum[w];
+    total += wsum[w];
+  }
+  if (out) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int32_t before = carry;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    int32_t run = before + incl - local;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int64_t k = base + int64_t(tid) * ITEMS + i;
-      if (k < V) offs[k] = run;
+    for (int i = 0; i < kScanItems; ++i) {
+      if (k0 + i < n) out[k0 + i] = run;
       run += v[i];
     }
-    __syncthreads();
-    if (tid == kScanThreads - 1) carry = run;
-    __syncthreads();
   }
-  if (tid == 0) offs[V] = carry;
+  return total;
+}
+
+// bsum[b] = the total of cnt's span b; fill = 0 over it.
+__global__ __launch_bounds__(kScanThreads) void span_sum_kernel(const int32_t* __restrict__ cnt, int64_t V,
+                                                                int32_t* __restrict__ bsum, int32_t* __restrict__ fill) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int64_t base = int64_t(blockIdx.x) * kScanSpan;
+  for (int64_t k = base + threadIdx.x; k < V && k < base + kScanSpan; k += kScanThreads) fill[k] = 0;
+  const int32_t t = scan_span(cnt, V, base, 0, nullptr, wsum);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = t;
+}
+
+// One workgroup: exclusive scan of in[0, n) into out[0, n], out[n] the total.
+__global__ __launch_bounds__(kScanThreads) void scan_one_kernel(const int32_t* __restrict__ in, int64_t n,
+                                                                int32_t* __restrict__ out) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  int32_t carry = 0;
+  for (int64_t base = 0; base < n; base += kScanSpan) carry = scan_span(in, n, base, carry, out, wsum);
+  if (threadIdx.x == 0) out[n] = carry;
+}
+
+// offs = exclusive scan of cnt: span b from its offset bpre[b]; offs[V] the total.
+__global__ __launch_bounds__(kScanThreads) void span_scan_kernel(const int32_t* __restrict__ cnt, int64_t V,
+                                                                 const int32_t* __restrict__ bpre, int64_t nb,
+                                                                 int32_t* __restrict__ offs) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  scan_span(cnt, V, int64_t(blockIdx.x) * kScanSpan, bpre[blockIdx.x], offs, wsum);
+  if (blockIdx.x == 0 && threadIdx.x == 0) offs[V] = bpre[nb];
 }
 
 __global__ void pair_scatter_kernel(const int64_t* __restrict__ ids, int width, int64_t ld_ids, int64_t rows,
@@ -341,8 +376,9 @@ size_t support_bwd_lds(int64_t H, int64_t width) { return size_t(H / 8) * 16 + s
 
 size_t support_backward_workspace_bytes(int64_t rows, int64_t width, int64_t V) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t nb = size_t((V + kScanSpan - 1) / kScanSpan);
   return up(size_t(rows) * size_t(width) * 4) + up(size_t(rows)) + up(size_t(V) * 4) + up(size_t(V + 1) * 4) +
-         up(size_t(V) * 4) + up(size_t(rows) * size_t(width) * 4);
+         up(size_t(V) * 4) + up(size_t(rows) * size_t(width) * 4) + up(nb * 4) + up((nb + 1) * 4);
 }
 
 int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
@@ -365,6 +401,12 @@ int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uin
   int32_t* fill = reinterpret_cast<int32_t*>(p);
   p += up(size_t(V) * 4);
   int32_t* list = reinterpret_cast<int32_t*>(p);
+  p += up(size_t(rows) * size_t(width) * 4);
+  const int64_t nb = (V + kScanSpan - 1) / kScanSpan;
+  int32_t* bsum = reinterpret_cast<int32_t*>(p);
+  p += up(size_t(nb) * 4);
+  int32_t* bpre = reinterpret_cast<int32_t*>(p);
+  if (nb > 0x7FFFFFFF) return int(hipErrorInvalidValue);
   if (d_weight) {
     const int rc = launch_zero_i32(cnt, V, stream);
     if (rc) return rc;
@@ -374,7 +416,9 @@ int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uin
       grad_entropy, d_hidden, ld_dh, dx, row_ok, d_weight ? cnt : nullptr);
   int rc = int(hipGetLastError());
   if (rc || !d_weight) return rc;
-  pair_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(cnt, V, offs, fill);
+  span_sum_kernel<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(cnt, V, bsum, fill);
+  scan_one_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(bsum, nb, bpre);
+  span_scan_kernel<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(cnt, V, bpre, nb, offs);
   const int64_t pairs = rows * width;
   if (pairs > 0) {
     pair_scatter_kernel<<<dim3(unsigned((pairs + 255) / 256)), dim3(256), 0, s>>>(ids, int(width), ld_ids, rows,
