@@ -316,10 +316,13 @@ __global__ __launch_bounds__(NT) void weight_grad_kernel(const uint16_t* __restr
   for (int64_t v = blockIdx.x; v < V; v += gridDim.x) {
     const int32_t b0 = offs[v], n = offs[v + 1] - b0;
     float* dw = d_weight + v * ld_dw;
-    if (n == 0) {
-      for (int64_t q = tid; q < nch; q += NT) {
-        const float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        store8(dw + 8 * q, z);
+    if (n == 0) {  // zeros, 16 bytes per lane over consecutive addresses
+      for (int64_t q = tid; q < 2 * nch; q += NT) {
+        float* d = dw + 4 * q;
+        d[0] = 0.0f;
+        d[1] = 0.0f;
+        d[2] = 0.0f;
+        d[3] = 0.0f;
       }
       continue;  // uniform across the workgroup
     }
