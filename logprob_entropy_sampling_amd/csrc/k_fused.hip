@@ -1056,8 +1056,6 @@ __global__ __launch_bounds__(NT, 1) void fused_partials_wide_kernel(
     store_epilogue(acc, v0, t0, rows_valid, V, ep);
 }
 
-// dst[c][r] = src[r][c] for r < R, c < C, and 0 for R <= r < R_pad: a bf16
-// transpose through a 64 x 64 LDS tile (reads and writes along rows of 64).
 // dst[c][r] = src[r][c] for c < C, r < R_pad (0 for r >= R), by 64 x 64
 // tiles through LDS.  A thread moves 16 consecutive values (two 16-byte
 // accesses where the row's alignment and extent allow, else one value at a
