@@ -18,6 +18,8 @@ namespace {
 
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 8;
+constexpr int kRowBufFlags = 0x00020000;  // dword 3 of a raw buffer resource: 32-bit data format
+constexpr int kRowNtAux = 2;              // buffer-load cache policy bit: non-temporal
 
 // Fold n raw logits into the state (base-2 units, u = x * c) against its
 // reference m, which moves only when it must: a block whose terms sum to 2^32
@@ -31,9 +33,12 @@ constexpr int kRowUnroll = 8;
 // applied only inside the entropy term, so a -inf logit adds exactly 0 and a
 // NaN poisons s.
 __device__ __forceinline__ void fold_terms(float m, const float* v, int n, float c, float& cs, float& ca) {
-  cs = 0.0f;
-  ca = 0.0f;
-  for (int i = 0; i < n; ++i) {
+  // the first term starts the sums (adding it to zero would change nothing
+  // but the sign of a zero entropy term, which no later sum keeps)
+  const float d0 = __builtin_fmaf(v[0], c, -m);
+  cs = exp2_hw(d0);
+  ca = cs * fmaxf(d0, kDFloor);
+  for (int i = 1; i < n; ++i) {
     const float d = __builtin_fmaf(v[i], c, -m);
     const float e = exp2_hw(d);
     cs += e;
@@ -91,40 +96,55 @@ __device__ __forceinline__ Part row_state(const void* rowp, int64_t V, float c) 
   int64_t q = tid;
   float v[VEC];
   if (DT == VS_BF16) {
-    // a ring of kRowUnroll loads: chunk k's slot is refilled with chunk
-    // k + kRowUnroll as soon as k is taken, so the loads stay in flight while
-    // the thread folds (chunks in ascending order, as a plain loop would)
-    const uint4* pv = static_cast<const uint4*>(rowp) + tid;
-    const int64_t n = nvec > tid ? (nvec - 1 - tid) / kRowThreads + 1 : 0;  // this thread's chunks
+    // A ring of kRowUnroll buffer loads: chunk k's slot is unpacked, refilled
+    // with chunk k + kRowUnroll, then folded, so the loads stay in flight
+    // while the thread folds and no register is copied.  The ring covers the
+    // nu chunks every thread has (a uniform count, so a chunk's offset is a
+    // scalar operand and costs no vector instruction); a thread's one extra
+    // chunk comes last.  Chunks are folded in ascending order, as a plain loop
+    // would fold them.
+    const int64_t nu = nvec / kRowThreads;
     constexpr int U = kRowUnroll;
-    if (n >= U) {
+    if (nu >= U) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(rowp), (short)0, int(nvec * 16), kRowBufFlags);
+      const uint32_t vo = uint32_t(tid) * 16u;
+      auto chunk = [&](int64_t k) -> uint4 {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, uint32_t(k) * uint32_t(kRowThreads * 16),
+                                                              kRowNtAux);
+        return make_uint4(x.x, x.y, x.z, x.w);
+      };
       uint4 w[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[u] = stream_load(pv + int64_t(u) * kRowThreads);
+      for (int u = 0; u < U; ++u) w[u] = chunk(u);
       int64_t i = 0;
-      for (; i + 2 * U <= n; i += U) {
+      for (; i + 2 * U <= nu; i += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const uint4 cur = w[u];
-          w[u] = stream_load(pv + (i + U + u) * kRowThreads);
-          unpack<DT>(cur, v);
+          unpack<DT>(w[u], v);
+          w[u] = chunk(i + U + u);
           fold_values(p, v, VEC, c);
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {  // chunks i .. i+U-1; refills only inside the row
-        const uint4 cur = w[u];
-        if (i + U + u < n) w[u] = stream_load(pv + (i + U + u) * kRowThreads);
-        unpack<DT>(cur, v);
+      for (int u = 0; u < U; ++u) {  // chunks i .. i+U-1; refills only below nu
+        unpack<DT>(w[u], v);
+        if (i + U + u < nu) w[u] = chunk(i + U + u);
         fold_values(p, v, VEC, c);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)  // the last n - i - U < U chunks
-        if (i + U + u < n) {
+      for (int u = 0; u < U; ++u)  // the last nu - i - U < U chunks
+        if (i + U + u < nu) {
           unpack<DT>(w[u], v);
           fold_values(p, v, VEC, c);
         }
+      if (tid + nu * kRowThreads < nvec) {  // this thread's extra chunk
+        unpack<DT>(chunk(nu), v);
+        fold_values(p, v, VEC, c);
+      }
     } else {
+      const uint4* pv = static_cast<const uint4*>(rowp) + tid;
+      const int64_t n = nvec > tid ? (nvec - 1 - tid) / kRowThreads + 1 : 0;  // this thread's chunks
       for (int64_t k = 0; k < n; ++k) {
         unpack<DT>(stream_load(pv + k * kRowThreads), v);
         fold_values(p, v, VEC, c);
