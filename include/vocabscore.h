@@ -280,9 +280,10 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
  * support_len 0, ids -1.  entropy, row_status, support_len, threshold_logit,
  * threshold_ties, full_lse nullable; logprob required.  Workspace
  * (vs_workspace_size(VS_OP_SCORE_TRANSFORMS, src, 0)): T bytes for V <= 81920;
- * above that also a per-row record of 149,760 bytes, its worst case (the count
- * pass hands the finishing pass each row's non-empty key counts and dense-id
- * candidates through it).  A hidden/weight source needs these for one block
+ * above that also a per-row record of 51,456 bytes (the count pass hands the
+ * finishing pass each row's non-empty key counts, up to 256 segments of 64
+ * keys, and dense-id candidates through it; a row whose keys fill more
+ * segments is redone by a kernel that re-reads it, with the same results).  A hidden/weight source needs these for one block
  * of min(T, 2048) rows, plus that block's logits (rows x V rounded up to 8,
  * bf16) and, for an fp32 hidden state, its bf16 copy (T x H x 2 bytes).
  */

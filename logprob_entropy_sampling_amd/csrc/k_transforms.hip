@@ -58,13 +58,19 @@ constexpr int COLLECT_MAX = 4096;
 //   [kRecCand]   u64[COLLECT_SPLIT] candidate entries: tokens (key << 32 |
 //                ~column), or units (vector index of the first 8 tokens |
 //                vector index of the second 8, or ~0, << 32)
-//   [kRecBlocks] u32[NSEG][32]: the packed count words of list entry e at e
+//   [kRecBlocks] u32[kRecMaxSegs][32]: the packed count words of list entry e
+//                at e
+// A row with more than kRecMaxSegs non-empty segments (keys spread over more
+// than a quarter of the 1024 segments: bf16 logits of ordinary rows fill a
+// few dozen) is handed to the stream kernel, as a counter overflow is, so the
+// record is sized for what ordinary rows write.
 constexpr int NT_FIN = 256;
 constexpr int COLLECT_SPLIT = 2048;
+constexpr int kRecMaxSegs = 256;
 constexpr size_t kRecHead = 0, kRecList = 256, kRecCand = kRecList + size_t(NSEG) * 2;
 constexpr uint32_t kCandTokens = 1, kCandUnits = 2;
 constexpr size_t kRecBlocks = kRecCand + size_t(COLLECT_SPLIT) * 8;
-constexpr size_t kRecBytes = kRecBlocks + size_t(NSEG) * 128;
+constexpr size_t kRecBytes = kRecBlocks + size_t(kRecMaxSegs) * 128;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 constexpr uint32_t KEY_NEG_INF = 0x007Fu;
 constexpr int kInFlight = 4;  // 16-byte loads per thread in flight in a streaming pass (1024 threads)
@@ -1368,8 +1374,9 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
   }
   uint32_t total, above, entry, n_ne;
   block_excl_scan2_u32<NW>(cnt, cnt ? 1u : 0u, above, entry, total, n_ne, sm);
-  // every counter stayed below 2^16 iff the counts add up to the token count
-  if (total != uint32_t(V) || sm.zero_overflow) {
+  // every counter stayed below 2^16 iff the counts add up to the token count;
+  // the record holds the count words of at most kRecMaxSegs segments
+  if (total != uint32_t(V) || sm.zero_overflow || n_ne > uint32_t(kRecMaxSegs)) {
     if (tid == 0) handoff[a.row] = 1;
     return;
   }
@@ -1448,7 +1455,8 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
 // (the finish kernel's segment sums and key queries read them), and, for the
 // dense ids, every token with key >= K_cap, the key at rank min(cap, V) - 1
 // (the dense-id cut lies at or above it), up to COLLECT_SPLIT of them.
-// handoff[row]: 0 = done here (bad row), 1 = counter overflow (32-bit kernel),
+// handoff[row]: 0 = done here (bad row), 1 = counter overflow or more than
+// kRecMaxSegs non-empty segments (32-bit kernel),
 // 2 = the finish kernel completes the row.
 __global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNEL_ARGS,
                                                                        uint8_t *__restrict__ recs) {

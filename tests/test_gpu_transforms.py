@@ -244,10 +244,10 @@ def test_streamed_rows_cap_paths(vsa):
 def test_streamed_rows_spread_over_many_segments(vsa):
     """Long rows whose keys spread over most of the 1024 key segments (random
     finite bf16 patterns over the whole finite range, subnormals to 2^127):
-    more non-empty segments than the finish kernel keeps in LDS, so its sums
-    and key queries also read segments from the record; segments whose
-    weights cannot follow one geometric recurrence; and ties at the largest
-    magnitudes.  The masses are fp64, so no tempered logit overflows."""
+    more non-empty segments than the split path's record holds, so these rows
+    go to the 32-bit stream kernel; segments whose weights cannot follow one
+    geometric recurrence; and ties at the largest magnitudes.  The masses are
+    fp64, so no tempered logit overflows."""
     say("transforms: V=100000 rows of random finite bf16 patterns (|x| < 2^128), caps 0 / 64 / 2048")
     T, V = 8, 100000
     rng = np.random.default_rng(12)
@@ -274,6 +274,44 @@ def test_streamed_rows_spread_over_many_segments(vsa):
             assert ref["support_len"][t] >= 2 and not ref["borderline_top_p"][t]
             assert abs(ref["entropy"][t] - np.log(ref["support_len"][t])) < 1e-12
         _compare(got, ref, cap, f"spread V={V} cap={cap}", x64, tau, y)
+
+
+def _segment_rows(rng, T, V, n_exp):
+    """Rows of bf16 logits whose keys fill about 4 * n_exp[t] of the 1024 key
+    segments: both signs, biased exponents 100 .. 100 + n_exp[t] - 1, every
+    mantissa (a segment is a sign, an exponent and the top mantissa bit)."""
+    bits = np.empty((T, V), np.uint16)
+    for t in range(T):
+        sign = rng.integers(0, 2, size=V) << 15
+        expo = (100 + rng.integers(0, n_exp[t], size=V)) << 7
+        bits[t] = (sign | expo | rng.integers(0, 128, size=V)).astype(np.uint16)
+    return bits
+
+
+def test_split_path_segment_counts_around_the_record(vsa):
+    """Long rows (the split path) with 64 to 520 non-empty key segments: up to
+    128 the finish kernel keeps every segment's counts in LDS, up to 256 it also
+    reads them from the row's record, beyond 256 the record cannot hold them
+    and the row is redone by the 32-bit stream kernel.  Descriptor, ids and
+    status bit-exact, scores within the tolerance, at caps 0 and 64."""
+    say("transforms: V=100000 rows with 64 .. 520 non-empty key segments (record limit 256), caps 0 / 64")
+    T, V = 8, 100000
+    rng = np.random.default_rng(31)
+    n_exp = [16, 32, 40, 60, 64, 65, 80, 130]  # about 4 segments per exponent: 64 .. 520 segments
+    bits = _segment_rows(rng, T, V, n_exp)
+    keys = np.where(bits >> 15, 0xFFFF - bits.astype(np.int64), bits.astype(np.int64) | 0x8000)
+    nseg = [len(np.unique(keys[t] >> 6)) for t in range(T)]
+    assert min(nseg) <= 128 and any(128 < n <= 256 for n in nseg) and max(nseg) > 256, nseg
+    k = np.array([0, 20, 0, 50, 0, 0, 1000, 0], np.int32)
+    p = np.array([0.9, 1.0, 0.5, 0.95, 1.0, 0.8, 1.0, 0.9], np.float32)
+    mp = np.array([0.0, 0.0, 0.05, 0.0, 0.0, 0.0, 0.0, 1e-3], np.float32)
+    tau = np.array([1.0, 0.7, 1.0, 2.0, 1.0, 1.0, 0.5, 1.0], np.float32)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    y = rng.integers(0, V, T)
+    for cap in (0, 64):
+        got = _run(vsa, bits, tau, k, p, mp, y, cap)
+        ref = oracle.score_transforms(x64, tau, k, p, mp, y, cap=cap)
+        _compare(got, ref, cap, f"segments {nseg} cap={cap}", x64, tau, y)
 
 
 def test_identity_and_singleton(vsa):
