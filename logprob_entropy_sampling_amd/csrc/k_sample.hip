@@ -50,10 +50,10 @@ __device__ __forceinline__ Ctr philox4x32_10(Ctr c, uint32_t k0, uint32_t k1) {
   for (int i = 0; i < 10; ++i) {
     const uint64_t p0 = uint64_t(kPhiloxM0) * c.c0;
     const uint64_t p1 = uint64_t(kPhiloxM1) * c.c2;
-    Ctr n;
-    n.c0 = uint32_t(p1 >> 32) ^ c.c1 ^ k0;
+    Ctr n;  // (three-way XORs as one gfx950 three-input bit operation each: truth table 0x96)
+    n.c0 = __builtin_amdgcn_bitop3_b32(uint32_t(p1 >> 32), c.c1, k0, 0x96);
     n.c1 = uint32_t(p1);
-    n.c2 = uint32_t(p0 >> 32) ^ c.c3 ^ k1;
+    n.c2 = __builtin_amdgcn_bitop3_b32(uint32_t(p0 >> 32), c.c3, k1, 0x96);
     n.c3 = uint32_t(p0);
     c = n;
     k0 += kPhiloxW0;
