@@ -237,9 +237,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     const uint16_t* __restrict__ logits, int64_t ld, int V, const float* __restrict__ temp, float temp_scalar,
     const uint8_t* __restrict__ status, const float* __restrict__ threshold_logit,
     const int32_t* __restrict__ threshold_ties, const float* __restrict__ row_max, uint64_t seed, uint64_t offset,
-    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status, int64_t row0) {
+    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status, int64_t row0, const int32_t* __restrict__ order) {
   __shared__ SampleSmem sm;
-  const int64_t row = blockIdx.x;  // local row; row0 + row is the generator's row word
+  // local row (taken in the order `order` gives, when given); row0 + row is
+  // the generator's row word, so the order changes no draw
+  const int64_t row = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);
   const int tid = threadIdx.x;
   if (tid == 0 && out_status) out_status[row] = status[row] & kRowBad;
   if (status[row] & kRowBad) {
@@ -460,16 +462,60 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   if (tid == 0) sampled[row] = best.id;
 }
 
+// The order in which sample_kernel takes its rows: the largest supports first.
+// A row's cost grows with its support (a Philox block and two logarithms per
+// support token, on top of one read of the row), and a whole-vocabulary
+// support costs tens of times a small one; rows taken in index order leave
+// the last large ones running alone at the end of the grid.  One workgroup:
+// rows go to kOrderBuckets buckets by support size (bad rows last), the
+// buckets are laid out largest first, and each row takes the next place in
+// its bucket (the order inside a bucket is whatever the atomics give: every
+// row is drawn independently of the others).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 5;
+__device__ __forceinline__ int support_bucket(int32_t len, uint8_t st) {
+  if (st & kRowBad) return kOrderBuckets - 1;
+  return len >= 65536 ? 0 : len >= 16384 ? 1 : len >= 4096 ? 2 : len >= 1024 ? 3 : 4;
+}
+__global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(const int32_t* __restrict__ support_len,
+                                                                   const uint8_t* __restrict__ status, int64_t rows,
+                                                                   int32_t* __restrict__ order) {
+  __shared__ uint32_t cnt[kOrderBuckets], place[kOrderBuckets];
+  const int tid = threadIdx.x;
+  if (tid < kOrderBuckets) cnt[tid] = 0u;
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kOrderThreads) atomicAdd(&cnt[support_bucket(support_len[r], status[r])], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t b = 0;
+    for (int i = 0; i < kOrderBuckets; ++i) {
+      place[i] = b;
+      b += cnt[i];
+    }
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kOrderThreads)
+    order[atomicAdd(&place[support_bucket(support_len[r], status[r])], 1u)] = int32_t(r);
+}
+
 }  // namespace
+
+int launch_order_rows(const int32_t* support_len, const uint8_t* status, int64_t rows, int32_t* order,
+                      void* stream) {
+  if (rows <= 0) return 0;
+  order_rows_kernel<<<dim3(1), dim3(kOrderThreads), 0, static_cast<hipStream_t>(stream)>>>(support_len, status, rows,
+                                                                                          order);
+  return int(hipGetLastError());
+}
 
 int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                   const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
                   const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
-                  int64_t row0, void* stream) {
+                  int64_t row0, const int32_t* order, void* stream) {
   if (rows <= 0) return 0;
   sample_kernel<<<dim3(unsigned(rows)), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream)>>>(
       logits, ld, int(V), temp, temp_scalar, status, threshold_logit, threshold_ties, row_max, seed, offset, sampled,
-      out_status, row0);
+      out_status, row0, order);
   return int(hipGetLastError());
 }
 

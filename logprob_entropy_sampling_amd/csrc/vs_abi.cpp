@@ -112,11 +112,12 @@ size_t xf_ws_bytes(const vs_source* s) {
   return b;
 }
 
-// the sampler: dummy targets, logprob, status, row maxima, threshold logit and
-// ties (when the caller passes none), then the transforms' own workspace
+// the sampler: dummy targets, logprob, status, row maxima, threshold logit,
+// ties and support lengths (when the caller passes none), the rows' draw
+// order, then the transforms' own workspace
 size_t sample_ws_bytes(const vs_source* s) {
   const size_t T = size_t(s->T);
-  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 3 * round_up(T * 4) + xf_ws_bytes(s);
+  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 5 * round_up(T * 4) + xf_ws_bytes(s);
 }
 
 template <class P>
@@ -377,18 +378,21 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   float* row_max = static_cast<float*>(c.take(size_t(T) * 4));
   float* thr = threshold_logit ? threshold_logit : static_cast<float*>(c.take(size_t(T) * 4));
   int32_t* ties = threshold_ties ? threshold_ties : static_cast<int32_t*>(c.take(size_t(T) * 4));
+  int32_t* slen = support_len ? support_len : static_cast<int32_t*>(c.take(size_t(T) * 4));
+  int32_t* order = static_cast<int32_t*>(c.take(size_t(T) * 4));
   // the transforms need a target per row: token 0 (its score is discarded)
   if (vs::launch_zero_i32(reinterpret_cast<int32_t*>(dummy_targets), 2 * T, stream)) return VS_E_DEVICE;
   const float* temp = src->temperature;
   // rows [r0, r0 + n): the support descriptor, then the draw from it
   auto run = [&](const uint16_t* lg, int64_t ld, int64_t r0, int64_t n, uint8_t* tws) -> int {
     int r = vs::launch_transforms(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, top_k + r0,
-                                  top_p + r0, min_p + r0, dummy_targets + r0, lp + r0, nullptr, st + r0,
-                                  at_row(support_len, r0), thr + r0, ties + r0, nullptr, 0, nullptr, row_max + r0, tws,
-                                  stream);
+                                  top_p + r0, min_p + r0, dummy_targets + r0, lp + r0, nullptr, st + r0, slen + r0,
+                                  thr + r0, ties + r0, nullptr, 0, nullptr, row_max + r0, tws, stream);
     if (r) return r == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
+    // the block's rows, the largest supports first (the draws do not depend on it)
+    if (vs::launch_order_rows(slen + r0, st + r0, n, order, stream)) return VS_E_DEVICE;
     r = vs::launch_sample(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, st + r0, thr + r0, ties + r0,
-                          row_max + r0, seed, offset, sampled_ids + r0, at_row(row_status, r0), r0, stream);
+                          row_max + r0, seed, offset, sampled_ids + r0, at_row(row_status, r0), r0, order, stream);
     return r ? VS_E_DEVICE : VS_OK;
   };
   vs::timer_mark(0, stream);
