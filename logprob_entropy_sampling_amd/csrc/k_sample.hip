@@ -278,18 +278,17 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     for (int i = 0; i < 8; ++i) h[i] = 8 * q + i < V ? uint32_t(rowp[8 * q + i]) : 0x7FC0u;
     return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
   };
-  // The row pass keeps the thread's next two chunks in flight while it scores
-  // the current one.
+  // The row pass.  An aligned row's first 4 * floor(nfull / (4 NT)) * NT whole
+  // 16-byte chunks go through a ring of four loads per thread in fixed slots
+  // (a slot is copied, refilled with the chunk four ahead, then scored; the
+  // refills past the ring's last chunk re-read it, unused), so each wait is
+  // for the oldest load alone and no register moves under a load in flight;
+  // the thread's remaining chunks (and every chunk of an unaligned row) are
+  // loaded one by one.  A thread's chunks are scored in ascending order.
   auto each_token = [&](bool count_ties, auto f_gt, auto f_eq) {
     uint32_t n_eq = 0;
     constexpr int64_t NT = kSampleThreads;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 n1 = tid < nchunk ? load_raw(tid) : zero;
-    uint4 n2 = tid + NT < nchunk ? load_raw(tid + NT) : zero;
-    for (int64_t q = tid; q < nchunk; q += NT) {
-      const uint4 w = n1;
-      n1 = n2;
-      if (q + 2 * NT < nchunk) n2 = load_raw(q + 2 * NT);
+    auto chunk = [&](int64_t q, const uint4& w) {
       float x[8];
       x[0] = bf16_lo(w.x);
       x[1] = bf16_hi(w.x);
@@ -325,7 +324,26 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
           }
         }
       }
+    };
+    const int64_t n4 = vec ? int64_t(V) / 8 / (4 * NT) * 4 : 0;  // ring chunks per thread (uniform)
+    if (n4 > 0) {
+      const uint4* pv = reinterpret_cast<const uint4*>(rowp) + tid;
+      // the thread's k-th chunk, a streaming (non-temporal) load: the row is
+      // read once here
+      auto ld = [&](int64_t k) { return stream_load(pv + (k < n4 ? k : n4 - 1) * NT); };
+      uint4 b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[u] = ld(u);
+      for (int64_t i = 0; i < n4; i += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 w = b[u];
+          b[u] = ld(i + u + 4);
+          chunk(tid + (i + u) * NT, w);
+        }
+      }
     }
+    for (int64_t q = n4 * NT + tid; q < nchunk; q += NT) chunk(q, load_raw(q));
     return n_eq;
   };
   // The first `ties` threshold-equal tokens by id (f), when the row holds
