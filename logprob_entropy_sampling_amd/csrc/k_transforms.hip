@@ -1503,10 +1503,11 @@ __global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNE
 // ascending order); a key query loads one segment's words; then everything
 // after the histogram exactly as in the one-kernel path.
 __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_ARGS,
-                                                                  const uint8_t *__restrict__ recs) {
+                                                                  const uint8_t *__restrict__ recs,
+                                                                  const int32_t *__restrict__ order) {
   constexpr int NTH = NT_FIN;
   __shared__ SmemFin sm;
-  VS_ROW_ARGS
+  VS_ROW_ARGS_AT(int64_t(order[blockIdx.x]))
   if (handoff[a.row] != 2) return;
   const int tid = threadIdx.x;
   const uint8_t* rec = recs + size_t(a.row) * kRecBytes;
@@ -1632,14 +1633,41 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
 #undef VS_ROW_ARGS_AT
 #undef VS_KERNEL_ARGS
 
+// The finish kernel's row order: rows whose top-p cut runs without top-k
+// (the mass query walks the row's whole prefix) first, then the others, so
+// the costlier rows do not end the grid alone.  One workgroup, two buckets;
+// the order inside a bucket is whatever the atomics give (rows are finished
+// independently of one another).
+constexpr int kFinOrderThreads = 1024;
+__device__ __forceinline__ int finish_bucket(int32_t k, float p, int V) { return (k <= 0 || k >= V) && p < 1.0f ? 0 : 1; }
+__global__ __launch_bounds__(kFinOrderThreads) void finish_order_kernel(const int32_t* __restrict__ top_k,
+                                                                        const float* __restrict__ top_p, int V,
+                                                                        int64_t rows, int32_t* __restrict__ order) {
+  __shared__ uint32_t cnt[2], place[2];
+  const int tid = threadIdx.x;
+  if (tid < 2) cnt[tid] = 0u;
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kFinOrderThreads) atomicAdd(&cnt[finish_bucket(top_k[r], top_p[r], V)], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    place[0] = 0u;
+    place[1] = cnt[0];
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kFinOrderThreads)
+    order[atomicAdd(&place[finish_bucket(top_k[r], top_p[r], V)], 1u)] = int32_t(r);
+}
+
 }  // namespace
 
 // Rows longer than the register kernels hold take the split path, whose
 // records follow the handoff bytes.
 static bool split_rows(int64_t V) { return (V + 7) / 8 > int64_t(20) * NT; }
 static size_t handoff_bytes(int64_t rows) { return (size_t(rows) + 255) & ~size_t(255); }
+// the finish kernel's row order, after the records
+static size_t order_bytes(int64_t rows) { return (size_t(rows) * 4 + 255) & ~size_t(255); }
 size_t transforms_workspace_bytes(int64_t rows, int64_t V) {
-  return split_rows(V) ? handoff_bytes(rows) + size_t(rows) * kRecBytes : size_t(rows);
+  return split_rows(V) ? handoff_bytes(rows) + size_t(rows) * kRecBytes + order_bytes(rows) : size_t(rows);
 }
 
 int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,
@@ -1661,7 +1689,9 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
   else if (!ids_out || cap <= int64_t(COLLECT_SPLIT)) {
     uint8_t* recs = handoff + handoff_bytes(rows);
     transforms_count_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff, recs);
-    transforms_finish_kernel<<<dim3(unsigned(rows)), dim3(NT_FIN), 0, s>>>(VS_ARGS, handoff, recs);
+    int32_t* order = reinterpret_cast<int32_t*>(recs + size_t(rows) * kRecBytes);
+    finish_order_kernel<<<dim3(1), dim3(kFinOrderThreads), 0, s>>>(top_k, top_p, int(V), rows, order);
+    transforms_finish_kernel<<<dim3(unsigned(rows)), dim3(NT_FIN), 0, s>>>(VS_ARGS, handoff, recs, order);
   } else {
     transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);
   }
