@@ -128,3 +128,37 @@ def test_full_size_all_rows(vsa):
     diff = np.nonzero(s != ref["sampled"])[0]
     assert all(ref["margin"][i] <= NEAR for i in diff), diff[:10]
     say(f"  full size: {T - diff.size} of {T} draws identical, {diff.size} within {NEAR} of a tie")
+
+
+def test_row_order_mixed_supports_and_bad_rows(vsa):
+    """1100 rows (the row-order kernels loop past one workgroup's 1024
+    threads) of V = 90,000 (the split transforms path, with its finish-order
+    kernel) whose supports range from one token to the whole row in shuffled
+    order, with BAD rows (a NaN temperature) among them: every draw is the
+    oracle's, whatever order the rows were drawn in."""
+    T, V = 1100, 90000
+    say(f"sample: T={T} V={V}, supports from 1 token to the whole row in shuffled order, 7 BAD rows")
+    rng = np.random.default_rng(77)
+    bits = workloads.to_bf16_bits((rng.standard_normal((T, V)) * 2.0).astype(np.float32))
+    kind = rng.integers(0, 5, T)
+    k = np.where(kind == 0, 1, np.where(kind == 1, 50, 0)).astype(np.int32)
+    p = np.where(kind == 2, 0.9, 1.0).astype(np.float32)
+    mp = np.where(kind == 3, 0.05, 0.0).astype(np.float32)  # kind 4: the whole row
+    tau = rng.uniform(0.6, 1.2, T).astype(np.float32)
+    tau[rng.choice(T, 7, replace=False)] = np.nan
+    seed, off = 99, 5
+    got = _draw(vsa, bits, tau, k, p, mp, seed=seed, offset=off)
+
+    def ref_rows(r):
+        x = oracle.logits_from_logits(bits, "bf16", rows=r)
+        out = sampling.sample_transforms(x, tau[r], k[r], p[r], mp[r], seed=seed, offset=off, rows=r)
+        return {"sampled": out["sampled"], "status": out["status"], "margin": out["margin"]}
+    ref = oracle_by_rows(ref_rows, T)
+    s = got["sampled"].cpu().numpy()
+    assert np.array_equal(got["status"].cpu().numpy(), ref["status"])
+    assert (s[np.isnan(tau)] == -1).all() and (ref["status"][np.isnan(tau)] & 0x04).all()
+    diff = np.nonzero(s != ref["sampled"])[0]
+    assert all(ref["margin"][i] <= NEAR for i in diff), diff[:10]
+    sl = got["support_len"].cpu().numpy()
+    assert sl[kind == 4][~np.isnan(tau[kind == 4])].min() == V and sl[kind == 0][~np.isnan(tau[kind == 0])].max() == 1
+    say(f"  {T - diff.size} of {T} draws identical, {diff.size} within {NEAR} of a tie")
