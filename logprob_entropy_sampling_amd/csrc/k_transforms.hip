@@ -1211,7 +1211,7 @@ __device__ void finish_row(const RowArgs& a, Keys& keys, uint32_t kmax, double t
   a.kk = top_k[a.row];                                \
   a.pf = top_p[a.row];                                \
   a.mpf = min_p[a.row];                               \
-  a.y = targets[a.row];                               \
+  a.y = targets ? targets[a.row] : 0;                 \
   a.rowp = logits + a.row * ld;                       \
   a.logprob = logprob;                                \
   a.entropy = entropy;                                \
@@ -1449,6 +1449,30 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
   }
 }
 
+// The finish kernel's row order: rows whose top-p cut runs without top-k
+// (the mass query walks the row's whole prefix) first, then the others, so
+// the costlier rows do not end the grid alone.  Two buckets; the order inside
+// a bucket is whatever the atomics give (rows are finished independently of
+// one another).  Run by the count kernel's first workgroup before its row
+// (the finish kernel starts after the whole count kernel).
+__device__ __forceinline__ int finish_bucket(int32_t k, float p, int V) { return (k <= 0 || k >= V) && p < 1.0f ? 0 : 1; }
+template <int NTH>
+__device__ void finish_order(const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int V, int64_t rows,
+                             int32_t* __restrict__ order, uint32_t* cnt /* 4 words of LDS */) {
+  const int tid = threadIdx.x;
+  if (tid < 2) cnt[tid] = 0u;
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += NTH) atomicAdd(&cnt[finish_bucket(top_k[r], top_p[r], V)], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    cnt[2] = 0u;
+    cnt[3] = cnt[0];
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += NTH) order[atomicAdd(&cnt[2 + finish_bucket(top_k[r], top_p[r], V)], 1u)] = int32_t(r);
+  __syncthreads();
+}
+
 // Split path, first half: one workgroup per row (one thread per segment)
 // builds the packed histogram and checks the row as the one-kernel path does,
 // then writes the row's record: the count words of every non-empty segment
@@ -1459,11 +1483,13 @@ __device__ __forceinline__ void count_row_tail(const RowArgs& a, StreamKeys& key
 // kRecMaxSegs non-empty segments (32-bit kernel),
 // 2 = the finish kernel completes the row.
 __global__ __launch_bounds__(NT_STREAM, 1) void transforms_count_kernel(VS_KERNEL_ARGS,
-                                                                       uint8_t *__restrict__ recs) {
+                                                                       uint8_t *__restrict__ recs,
+                                                                       int32_t *__restrict__ order) {
   constexpr int NTH = NT_STREAM;
   constexpr int NW = NTH / 64;
   static_assert(NTH == NSEG, "one thread per segment");
   __shared__ Smem sm;
+  if (blockIdx.x == 0) finish_order<NTH>(top_k, top_p, V, int64_t(gridDim.x), order, sm.bu);
   VS_ROW_ARGS
   const int tid = threadIdx.x;
   uint8_t* rec = recs + size_t(a.row) * kRecBytes;
@@ -1633,30 +1659,6 @@ __global__ __launch_bounds__(NT_FIN, 4) void transforms_finish_kernel(VS_KERNEL_
 #undef VS_ROW_ARGS_AT
 #undef VS_KERNEL_ARGS
 
-// The finish kernel's row order: rows whose top-p cut runs without top-k
-// (the mass query walks the row's whole prefix) first, then the others, so
-// the costlier rows do not end the grid alone.  One workgroup, two buckets;
-// the order inside a bucket is whatever the atomics give (rows are finished
-// independently of one another).
-constexpr int kFinOrderThreads = 1024;
-__device__ __forceinline__ int finish_bucket(int32_t k, float p, int V) { return (k <= 0 || k >= V) && p < 1.0f ? 0 : 1; }
-__global__ __launch_bounds__(kFinOrderThreads) void finish_order_kernel(const int32_t* __restrict__ top_k,
-                                                                        const float* __restrict__ top_p, int V,
-                                                                        int64_t rows, int32_t* __restrict__ order) {
-  __shared__ uint32_t cnt[2], place[2];
-  const int tid = threadIdx.x;
-  if (tid < 2) cnt[tid] = 0u;
-  __syncthreads();
-  for (int64_t r = tid; r < rows; r += kFinOrderThreads) atomicAdd(&cnt[finish_bucket(top_k[r], top_p[r], V)], 1u);
-  __syncthreads();
-  if (tid == 0) {
-    place[0] = 0u;
-    place[1] = cnt[0];
-  }
-  __syncthreads();
-  for (int64_t r = tid; r < rows; r += kFinOrderThreads)
-    order[atomicAdd(&place[finish_bucket(top_k[r], top_p[r], V)], 1u)] = int32_t(r);
-}
 
 }  // namespace
 
@@ -1688,9 +1690,8 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
   else if (nv <= 20) transforms_fast_kernel<20><<<dim3(unsigned(rows)), dim3(NT), 0, s>>>(VS_ARGS, handoff);
   else if (!ids_out || cap <= int64_t(COLLECT_SPLIT)) {
     uint8_t* recs = handoff + handoff_bytes(rows);
-    transforms_count_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff, recs);
     int32_t* order = reinterpret_cast<int32_t*>(recs + size_t(rows) * kRecBytes);
-    finish_order_kernel<<<dim3(1), dim3(kFinOrderThreads), 0, s>>>(top_k, top_p, int(V), rows, order);
+    transforms_count_kernel<<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff, recs, order);
     transforms_finish_kernel<<<dim3(unsigned(rows)), dim3(NT_FIN), 0, s>>>(VS_ARGS, handoff, recs, order);
   } else {
     transforms_fast_kernel<0><<<dim3(unsigned(rows)), dim3(NT_STREAM), 0, s>>>(VS_ARGS, handoff);

@@ -112,7 +112,8 @@ int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uin
 // per row through the workspace (up to 2048 dense ids; more use a one-kernel
 // streaming form).  A row that repeats one logit 65536+ times is re-done by a
 // 32-bit-count streaming kernel (flagged in `handoff`, the first bytes of the
-// workspace).  More than kTransformsMaxCap dense ids: returns -1.
+// workspace).  More than kTransformsMaxCap dense ids: returns -1.  targets may
+// be null (every row then scores token 0: the caller wants the support only).
 constexpr int64_t kTransformsMaxCap = 4096;  // dense ids are sorted in LDS
 size_t transforms_workspace_bytes(int64_t rows, int64_t V);
 int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp,

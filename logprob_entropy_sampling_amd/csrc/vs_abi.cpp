@@ -112,12 +112,12 @@ size_t xf_ws_bytes(const vs_source* s) {
   return b;
 }
 
-// the sampler: dummy targets, logprob, status, row maxima, threshold logit,
-// ties and support lengths (when the caller passes none), the rows' draw
-// order, then the transforms' own workspace
+// the sampler: logprob, status, row maxima, threshold logit, ties and support
+// lengths (when the caller passes none), the rows' draw order, then the
+// transforms' own workspace
 size_t sample_ws_bytes(const vs_source* s) {
   const size_t T = size_t(s->T);
-  return round_up(T * 8) + round_up(T * 4) + round_up(T) + 5 * round_up(T * 4) + xf_ws_bytes(s);
+  return round_up(T * 4) + round_up(T) + 5 * round_up(T * 4) + xf_ws_bytes(s);
 }
 
 template <class P>
@@ -372,7 +372,6 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   if (rc) return rc;
   const int64_t T = src->T;
   Carver c(workspace);
-  int64_t* dummy_targets = static_cast<int64_t*>(c.take(size_t(T) * 8));
   float* lp = static_cast<float*>(c.take(size_t(T) * 4));
   uint8_t* st = static_cast<uint8_t*>(c.take(size_t(T)));
   float* row_max = static_cast<float*>(c.take(size_t(T) * 4));
@@ -380,13 +379,11 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   int32_t* ties = threshold_ties ? threshold_ties : static_cast<int32_t*>(c.take(size_t(T) * 4));
   int32_t* slen = support_len ? support_len : static_cast<int32_t*>(c.take(size_t(T) * 4));
   int32_t* order = static_cast<int32_t*>(c.take(size_t(T) * 4));
-  // the transforms need a target per row: token 0 (its score is discarded)
-  if (vs::launch_zero_i32(reinterpret_cast<int32_t*>(dummy_targets), 2 * T, stream)) return VS_E_DEVICE;
   const float* temp = src->temperature;
   // rows [r0, r0 + n): the support descriptor, then the draw from it
   auto run = [&](const uint16_t* lg, int64_t ld, int64_t r0, int64_t n, uint8_t* tws) -> int {
     int r = vs::launch_transforms(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, top_k + r0,
-                                  top_p + r0, min_p + r0, dummy_targets + r0, lp + r0, nullptr, st + r0, slen + r0,
+                                  top_p + r0, min_p + r0, nullptr, lp + r0, nullptr, st + r0, slen + r0,
                                   thr + r0, ties + r0, nullptr, 0, nullptr, row_max + r0, tws, stream);
     if (r) return r == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
     // the block's rows, the largest supports first (the draws do not depend on it)
