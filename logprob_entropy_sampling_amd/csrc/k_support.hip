@@ -42,7 +42,7 @@ __global__ __launch_bounds__(NT) void support_kernel(
     int64_t H, int64_t V, const float* __restrict__ temp, float temp_scalar, const int64_t* __restrict__ ids,
     int width, int64_t ld_ids, const int64_t* __restrict__ targets, const uint8_t* __restrict__ fallback,
     float* __restrict__ logprob, float* __restrict__ entropy, uint8_t* __restrict__ status,
-    int32_t* __restrict__ fb_list, int32_t* __restrict__ fb_count) {
+    int32_t* __restrict__ fb_list, int32_t* __restrict__ fb_count, const int32_t* __restrict__ order) {
   // No contraction in this kernel: u = x * c is rounded before u - max, so
   // the maximum's own term is exactly 2^0 = 1 with d = 0.
 #pragma clang fp contract(off)
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(NT) void support_kernel(
   float* sx = reinterpret_cast<float*>(sid + width);
   __shared__ int s_bad, s_count;
 
-  const int64_t row = blockIdx.x;
+  const int64_t row = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);
   const int tid = threadIdx.x;
   const float tau = temp ? temp[row] : temp_scalar;
   if (tid == 0) {
@@ -210,12 +210,72 @@ __global__ __launch_bounds__(NT) void support_kernel(
   }
 }
 
+// Workgroup order of the hidden/weight source.  A row costs in proportion to
+// its number of ids, and the workgroups of one launch all run at once, eight
+// to a CU, workgroup b on CU b mod (CU count) when the grid is dealt out in
+// order; a CU then finishes with its heaviest share.  The rows are ranked by
+// their id count (descending) and rank r = m * G + j (G = CU count) goes to
+// workgroup m * G + j for even m and m * G + G - 1 - j for odd m, so each CU
+// gets ranks j, 2G - 1 - j, 2G + j, ...: near-equal shares.  A last partial
+// group keeps rank order.  The outputs do not depend on the order.
+constexpr int kWidthThreads = 256;
+__global__ __launch_bounds__(kWidthThreads) void support_width_kernel(const int64_t* __restrict__ ids, int width,
+                                                                     int64_t ld_ids, int64_t rows,
+                                                                     int32_t* __restrict__ count) {
+  const int64_t row = int64_t(blockIdx.x) * (kWidthThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int j = lane; j < width; j += 64) n += ids[row * ld_ids + j] >= 0 ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
+  if (lane == 0) count[row] = n;
+}
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void support_order_kernel(const int32_t* __restrict__ count, int width,
+                                                                     int64_t rows, int G, int32_t* __restrict__ order) {
+  extern __shared__ uint32_t bucket[];  // width + 1 counters, then their starts
+  const int tid = threadIdx.x;
+  for (int w = tid; w <= width; w += kOrderThreads) bucket[w] = 0u;
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kOrderThreads) atomicAdd(&bucket[count[r]], 1u);
+  __syncthreads();
+  if (tid == 0) {  // starts in descending width
+    uint32_t b = 0;
+    for (int w = width; w >= 0; --w) {
+      const uint32_t c = bucket[w];
+      bucket[w] = b;
+      b += c;
+    }
+  }
+  __syncthreads();
+  const int64_t full = rows / G * G;
+  for (int64_t r = tid; r < rows; r += kOrderThreads) {
+    const int64_t rank = int64_t(atomicAdd(&bucket[count[r]], 1u));
+    const int64_t m = rank / G, j = rank - m * G;
+    const int64_t b = rank >= full ? rank : m * G + ((m & 1) ? G - 1 - j : j);
+    order[b] = int32_t(r);
+  }
+}
+
 // dynamic LDS of one workgroup: [bf16 hidden row][ids int64][logits fp32]
 size_t support_lds_bytes(bool fused, int64_t H, int64_t width) {
   return (fused ? size_t(H / 8) * 16 : 0) + size_t(width) * 8 + size_t(width) * 4;
 }
 
 }  // namespace
+
+const int32_t* support_row_order(const int64_t* ids, int64_t width, int64_t ld_ids, int64_t rows, int32_t* ws,
+                                 void* stream) {
+  int ncu = 0;
+  if (width <= 1 || device_cu_count(&ncu) != 0 || rows < 2 * int64_t(ncu)) return nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* count = ws + rows;  // [rows] id counts after the [rows] order
+  support_width_kernel<<<dim3(unsigned((rows + 3) / 4)), dim3(kWidthThreads), 0, s>>>(ids, int(width), ld_ids, rows,
+                                                                                      count);
+  support_order_kernel<<<dim3(1), dim3(kOrderThreads), size_t(width + 1) * 4, s>>>(count, int(width), rows, ncu, ws);
+  return hipGetLastError() == hipSuccess ? ws : nullptr;
+}
 
 int launch_support_logits(LogitsArg lg, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                           const int64_t* ids, int64_t width, int64_t ld_ids, const int64_t* targets,
@@ -225,7 +285,7 @@ int launch_support_logits(LogitsArg lg, int64_t rows, int64_t V, const float* te
   const size_t lds = support_lds_bytes(false, 0, width);
   support_kernel<false><<<dim3(unsigned(rows)), dim3(NT), lds, static_cast<hipStream_t>(stream)>>>(
       lg.ptr, lg.dtype, lg.ld, nullptr, 0, 0, V, temp, temp_scalar, ids, int(width), ld_ids, targets, fallback,
-      logprob, entropy, status, fb_list, fb_count);
+      logprob, entropy, status, fb_list, fb_count, nullptr);
   return int(hipGetLastError());
 }
 
@@ -233,12 +293,14 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
                          int64_t ld_weight, int64_t rows, int64_t H, int64_t V, const float* temp,
                          float temp_scalar, const int64_t* ids, int64_t width, int64_t ld_ids,
                          const int64_t* targets, const uint8_t* fallback, float* logprob, float* entropy,
-                         uint8_t* status, int32_t* fb_list, int32_t* fb_count, void* stream) {
+                         uint8_t* status, int32_t* fb_list, int32_t* fb_count, int32_t* order_ws, void* stream) {
   if (rows <= 0) return 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* order = order_ws ? support_row_order(ids, width, ld_ids, rows, order_ws, stream) : nullptr;
   const size_t lds = support_lds_bytes(true, H, width);
-  support_kernel<true><<<dim3(unsigned(rows)), dim3(NT), lds, static_cast<hipStream_t>(stream)>>>(
+  support_kernel<true><<<dim3(unsigned(rows)), dim3(NT), lds, s>>>(
       hidden, hidden_dtype, ld_hidden, weight, ld_weight, H, V, temp, temp_scalar, ids, int(width), ld_ids,
-      targets, fallback, logprob, entropy, status, fb_list, fb_count);
+      targets, fallback, logprob, entropy, status, fb_list, fb_count, order);
   return int(hipGetLastError());
 }
 

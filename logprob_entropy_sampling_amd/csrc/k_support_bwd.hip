@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT) void support_grad_kernel(
     int64_t V, const float* __restrict__ temp, float temp_scalar, const int64_t* __restrict__ ids, int width,
     int64_t ld_ids, const int64_t* __restrict__ targets, const float* __restrict__ grad_logprob,
     const float* __restrict__ grad_entropy, float* __restrict__ d_hidden, int64_t ld_dh, float* __restrict__ dx_out,
-    uint8_t* __restrict__ row_ok, int32_t* __restrict__ cnt) {
+    uint8_t* __restrict__ row_ok, int32_t* __restrict__ cnt, const int32_t* __restrict__ order) {
   // no contraction: the fold's arithmetic is the forward's, so a singleton's
   // only term has d = 0 exactly and its gradient is exactly 0
 #pragma clang fp contract(off)
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(NT) void support_grad_kernel(
   float* sx = reinterpret_cast<float*>(sid + width);  // support logits, then dX
   __shared__ int s_bad, s_count, s_ok;
 
-  const int64_t row = blockIdx.x;
+  const int64_t row = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);  // (results do not depend on it)
   const int tid = threadIdx.x;
   const int64_t nch = H / 8;
   const float tau = temp ? temp[row] : temp_scalar;
@@ -381,7 +381,8 @@ size_t support_backward_workspace_bytes(int64_t rows, int64_t width, int64_t V) 
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t nb = size_t((V + kScanSpan - 1) / kScanSpan);
   return up(size_t(rows) * size_t(width) * 4) + up(size_t(rows)) + up(size_t(V) * 4) + up(size_t(V + 1) * 4) +
-         up(size_t(V) * 4) + up(size_t(rows) * size_t(width) * 4) + up(nb * 4) + up((nb + 1) * 4);
+         up(size_t(V) * 4) + up(size_t(rows) * size_t(width) * 4) + up(nb * 4) + up((nb + 1) * 4) +
+         up(size_t(rows) * 8);
 }
 
 int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* weight, int64_t ld_weight,
@@ -409,14 +410,17 @@ int launch_support_backward(const uint16_t* hidden, int64_t ld_hidden, const uin
   int32_t* bsum = reinterpret_cast<int32_t*>(p);
   p += up(size_t(nb) * 4);
   int32_t* bpre = reinterpret_cast<int32_t*>(p);
+  p += up((nb + 1) * 4);
+  int32_t* order_ws = reinterpret_cast<int32_t*>(p);  // the rows' workgroup order, then their id counts
   if (nb > 0x7FFFFFFF) return int(hipErrorInvalidValue);
   if (d_weight) {
     const int rc = launch_zero_i32(cnt, V, stream);
     if (rc) return rc;
   }
+  const int32_t* order = support_row_order(ids, width, ld_ids, rows, order_ws, stream);
   support_grad_kernel<<<dim3(unsigned(rows)), dim3(NT), support_bwd_lds(H, width), s>>>(
       hidden, ld_hidden, weight, ld_weight, H, V, temp, temp_scalar, ids, int(width), ld_ids, targets, grad_logprob,
-      grad_entropy, d_hidden, ld_dh, dx, row_ok, d_weight ? cnt : nullptr);
+      grad_entropy, d_hidden, ld_dh, dx, row_ok, d_weight ? cnt : nullptr, order);
   int rc = int(hipGetLastError());
   if (rc || !d_weight) return rc;
   span_sum_kernel<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(cnt, V, bsum, fill);

@@ -90,7 +90,14 @@ int launch_support_fused(const void* hidden, int hidden_dtype, int64_t ld_hidden
                          int64_t ld_weight, int64_t rows, int64_t H, int64_t V, const float* temp,
                          float temp_scalar, const int64_t* ids, int64_t width, int64_t ld_ids,
                          const int64_t* targets, const uint8_t* fallback, float* logprob, float* entropy,
-                         uint8_t* status, int32_t* fb_list, int32_t* fb_count, void* stream);
+                         uint8_t* status, int32_t* fb_list, int32_t* fb_count, int32_t* order_ws, void* stream);
+// The workgroup order of the per-row support kernels on a hidden/weight source
+// (rows ranked by their id count, dealt out so each CU gets a near-equal
+// share) in ws[0, rows), using ws[rows, 2 rows) for the counts; returns ws, or
+// null when there is nothing to balance (width <= 1, fewer than 2 rows per CU).
+// A row's results do not depend on the order.
+const int32_t* support_row_order(const int64_t* ids, int64_t width, int64_t ld_ids, int64_t rows, int32_t* ws,
+                                 void* stream);
 
 // Zero a small int32 buffer with a kernel (not a memset node).
 int launch_zero_i32(int32_t* p, int64_t n, void* stream);

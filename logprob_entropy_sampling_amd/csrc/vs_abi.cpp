@@ -193,7 +193,7 @@ size_t support_bwd_ws_bytes(const vs_source* s, int64_t width) {
 }
 
 size_t support_ws_bytes(const vs_source* s) {
-  return round_up(size_t(s->T) * 4) + round_up(4) + full_ws_bytes(s, s->T);
+  return round_up(size_t(s->T) * 4) + round_up(4) + 2 * round_up(size_t(s->T) * 4) + full_ws_bytes(s, s->T);
 }
 
 // Full-vocabulary sweep + merge over `rows` slots (row_map/row_count nullable).
@@ -301,6 +301,7 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
   Carver c(workspace);
   int32_t* fb_list = static_cast<int32_t*>(c.take(size_t(src->T) * 4));
   int32_t* fb_count = static_cast<int32_t*>(c.take(4));
+  int32_t* order_ws = static_cast<int32_t*>(c.take(size_t(src->T) * 8));  // row order, then id counts
   FullWs w = carve_full(c, src, src->T);
   if (full_vocab_fallback && vs::launch_zero_i32(fb_count, 1, stream)) return VS_E_DEVICE;
   vs::timer_mark(0, stream);
@@ -313,7 +314,8 @@ int vs_score_support_ids(const vs_source* src, const int64_t* support_ids, int64
     rc = vs::launch_support_fused(src->hidden, src->hidden_dtype, src->ld_hidden,
                                   static_cast<const uint16_t*>(src->weight), src->ld_weight, src->T, src->H, src->V,
                                   src->temperature, src->temperature_scalar, support_ids, width, ld_ids, target_ids,
-                                  full_vocab_fallback, logprob, entropy, row_status, fb_list, fb_count, stream);
+                                  full_vocab_fallback, logprob, entropy, row_status, fb_list, fb_count, order_ws,
+                                  stream);
   }
   vs::timer_mark(1, stream);
   if (rc) return VS_E_DEVICE;
