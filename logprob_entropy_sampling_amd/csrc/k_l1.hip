@@ -588,28 +588,30 @@ __device__ __forceinline__ float sgn(float d) { return d > 0.0f ? 1.0f : d < 0.0
 // Calls f(a, b, n) on this thread's share of a row pair: U 16-byte chunks per
 // step in flight (n = VEC values each), then the remaining chunks, then the
 // scalar tail (n = 1).
+// (A row split over several workgroups runs this as thread g of G per row:
+// g = slice * NT + threadIdx.x, G = slices * NT.)
 template <int DT, int NT, int U, class F>
-__device__ __forceinline__ void row_pairs(const char* trow, const char* drow, int64_t nvec, int64_t V, F f) {
+__device__ __forceinline__ void row_pairs(const char* trow, const char* drow, int64_t nvec, int64_t V, F f,
+                                          int g = int(threadIdx.x), int64_t G = NT) {
   constexpr int VEC = DT == VS_BF16 ? 8 : 4;
-  const int tid = threadIdx.x;
-  int64_t q = tid;
-  for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+  int64_t q = g;
+  for (; q + int64_t(U - 1) * G < nvec; q += int64_t(U) * G) {
     float a[U][VEC], b[U][VEC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      load_chunk<DT>(trow, q + u * NT, a[u]);
-      load_chunk<DT>(drow, q + u * NT, b[u]);
+      load_chunk<DT>(trow, q + u * G, a[u]);
+      load_chunk<DT>(drow, q + u * G, b[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) f(a[u], b[u], VEC);
   }
-  for (; q < nvec; q += NT) {
+  for (; q < nvec; q += G) {
     float a[VEC], b[VEC];
     load_chunk<DT>(trow, q, a);
     load_chunk<DT>(drow, q, b);
     f(a, b, VEC);
   }
-  for (int64_t i = nvec * VEC + tid; i < V; i += NT) {
+  for (int64_t i = nvec * VEC + g; i < V; i += G) {
     float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
     f(&a, &b, 1);
   }
@@ -720,17 +722,183 @@ __global__ __launch_bounds__(NT) void l1_stats_kernel(const void* __restrict__ t
   }
 }
 
+// The stats pass with each row split over S workgroups (slices), for batches
+// with few rows per CU.  Slice s of row t is thread g = s * NT + threadIdx.x
+// of S * NT.  l1_part1_kernel: each slice's online maxima and sums of both
+// rows (merged in its workgroup as in the one-workgroup form) into
+// part1[t * S + s].  l1_part2_kernel: every slice merges the row's S partials
+// in slice order (all get the same normalisers), runs pass 2 over its share
+// and writes its sums of |p - q| and sign(q - p) q into part2[t * S + s];
+// slice 0 writes the row's normalisers.  l1_loss_kernel then adds each row's
+// S partial sums in slice order.
+template <int NT>
+__device__ __forceinline__ void block_pair(Part& px, Part& py, float (*red)[4], float* fin) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  px = wave_merge_to_lane0(px);
+  py = wave_merge_to_lane0(py);
+  if ((tid & 63) == 0) {
+    red[tid >> 6][0] = px.m;
+    red[tid >> 6][1] = px.s;
+    red[tid >> 6][2] = py.m;
+    red[tid >> 6][3] = py.s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    Part qx{kNegInf, 0.0f, 0.0f}, qy{kNegInf, 0.0f, 0.0f};
+    if (tid < NW) {
+      qx = Part{red[tid][0], red[tid][1], 0.0f};
+      qy = Part{red[tid][2], red[tid][3], 0.0f};
+    }
+    qx = wave_merge_to_lane0(qx);
+    qy = wave_merge_to_lane0(qy);
+    if (tid == 0) {
+      fin[0] = qx.m;
+      fin[1] = qx.s;
+      fin[2] = qy.m;
+      fin[3] = qy.s;
+    }
+  }
+  __syncthreads();
+}
+
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void l1_part1_kernel(const void* __restrict__ tgt, int64_t ld_t,
+                                                      const void* __restrict__ dft, int64_t ld_d, int64_t V, int S,
+                                                      float4* __restrict__ part1) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int NW = NT / 64;
+  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
+  __shared__ float red[NW][4];
+  __shared__ float fin[4];
+  const int64_t row = blockIdx.x / S;
+  const int sl = int(blockIdx.x - row * S);
+  const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
+  const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
+  const int64_t nvec = vec_ok ? V / VEC : 0;
+  float mx = kNegInf, sx = 0.0f, my = kNegInf, sy = 0.0f;
+  row_pairs<DT, NT, U>(
+      trow, drow, nvec, V,
+      [&](const float* a, const float* b, int n) {
+        online(mx, sx, a, n, l2e);
+        online(my, sy, b, n, l2e);
+      },
+      sl * NT + int(threadIdx.x), int64_t(S) * NT);
+  Part px{mx * l2e, sx, 0.0f}, py{my * l2e, sy, 0.0f};
+  block_pair<NT>(px, py, red, fin);
+  if (threadIdx.x == 0) part1[blockIdx.x] = make_float4(fin[0], fin[1], fin[2], fin[3]);
+}
+
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void l1_part2_kernel(const void* __restrict__ tgt, int64_t ld_t,
+                                                      const void* __restrict__ dft, int64_t ld_d, int64_t V, int S,
+                                                      const float4* __restrict__ part1, float2* __restrict__ part2,
+                                                      RowStats* __restrict__ stats) {
+  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
+  constexpr int ES = DT == VS_BF16 ? 2 : 4;
+  constexpr int NW = NT / 64;
+  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
+  __shared__ float red[NW][2];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / S;
+  const int sl = int(blockIdx.x - row * S);
+  Part qx{kNegInf, 0.0f, 0.0f}, qy{kNegInf, 0.0f, 0.0f};
+  for (int k = 0; k < S; ++k) {
+    const float4 p = part1[row * S + k];
+    qx = merge(qx, Part{p.x, p.y, 0.0f});
+    qy = merge(qy, Part{p.z, p.w, 0.0f});
+  }
+  const Norm nx = make_norm(qx.m, qx.s), ny = make_norm(qy.m, qy.s);
+  if (!(norm_ok(nx) && norm_ok(ny))) {
+    if (tid == 0) {
+      const float nan = __builtin_nanf("");
+      part2[blockIdx.x] = make_float2(nan, nan);
+      if (sl == 0) stats[row] = RowStats{nan, nan, nan, nan, nan};
+    }
+    return;
+  }
+  const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
+  const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
+  const int64_t nvec = vec_ok ? V / VEC : 0;
+  float d1 = 0.0f, ds = 0.0f;
+  auto pass2 = [&](auto acc_form) {
+    constexpr bool ACC = decltype(acc_form)::value;
+    row_pairs<DT, NT, U>(
+        trow, drow, nvec, V,
+        [&](const float* a, const float* b, int n) {
+          for (int i = 0; i < n; ++i) {
+            float pp, qq;
+            pq_pair<ACC>(a[i], b[i], nx, ny, l2e, pp, qq);
+            d1 += fabsf(pp - qq);
+            ds = __builtin_fmaf(sgn(qq - pp), qq, ds);
+          }
+        },
+        sl * NT + tid, int64_t(S) * NT);
+  };
+  if (norms_big(nx, ny))
+    pass2(std::true_type{});
+  else
+    pass2(std::false_type{});
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o1 = shfl_down_f(d1, off), o2 = shfl_down_f(ds, off);
+    if ((tid & ((off << 1) - 1)) == 0) {
+      d1 += o1;
+      ds += o2;
+    }
+  }
+  if ((tid & 63) == 0) {
+    red[tid >> 6][0] = d1;
+    red[tid >> 6][1] = ds;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = 0.0f, Sv = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      v += red[w][0];
+      Sv += red[w][1];
+    }
+    part2[blockIdx.x] = make_float2(v, Sv);
+    if (sl == 0) stats[row] = RowStats{nx.m, nx.l2s, ny.m, ny.l2s, 0.0f};
+  }
+}
+
 // num = sum_t w_t l1_t over rows of nonzero weight, den = sum_t w_t: thread i
 // takes rows i, i + 256, ... in order, then a fixed tree.  out = {num, den, num / den}.
-__global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(const float* __restrict__ l1,
+// With part2 (rows split over S slices): row t's distance and sum s q are
+// first added up from its S partials in slice order, and l1, accept and the
+// row's S_t written.
+__global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(float* __restrict__ l1, float* __restrict__ accept,
                                                                const float* __restrict__ weights, int64_t rows,
-                                                               float* __restrict__ out) {
+                                                               float* __restrict__ out, const float2* __restrict__ part2,
+                                                               int S, RowStats* __restrict__ stats) {
   __shared__ float sn[kLossThreads], sd[kLossThreads];
   const int tid = threadIdx.x;
   float n = 0.0f, d = 0.0f;
   for (int64_t t = tid; t < rows; t += kLossThreads) {
+    float lt;
+    if (part2) {
+      const bool ok = stats[t].mx == stats[t].mx;
+      float v = 0.0f, Sv = 0.0f;
+      for (int k = 0; k < S; ++k) {
+        const float2 p = part2[t * S + k];
+        v += p.x;
+        Sv += p.y;
+      }
+      const float nan = __builtin_nanf("");
+      lt = ok ? fminf(fmaxf(v, 0.0f), 2.0f) : nan;
+      l1[t] = lt;
+      if (accept) accept[t] = ok ? fminf(fmaxf(1.0f - 0.5f * lt, 0.0f), 1.0f) : nan;
+      if (ok) stats[t].S = Sv;
+    } else {
+      lt = l1[t];
+    }
     const float w = weights ? weights[t] : 1.0f;
-    if (w != 0.0f) n = __builtin_fmaf(w, l1[t], n);
+    if (w != 0.0f) n = __builtin_fmaf(w, lt, n);
     d += w;
   }
   sn[tid] = n;
@@ -789,13 +957,16 @@ __global__ __launch_bounds__(NT) void l1_grad_kernel(const void* __restrict__ tg
                                                      const float* __restrict__ weights, float grad_scale,
                                                      const RowStats* __restrict__ stats,
                                                      const float* __restrict__ loss_out, void* __restrict__ grad,
-                                                     int64_t ld_g) {
+                                                     int64_t ld_g, int S) {
   constexpr int VEC = DT == VS_BF16 ? 8 : 4;
   constexpr int ES = DT == VS_BF16 ? 2 : 4;
   constexpr int GS = GDT == VS_BF16 ? 2 : 4;
   constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+  // row t over S workgroups: this is thread g of the row's G (each gradient
+  // element is computed on its own, so the split changes no value)
+  const int64_t row = blockIdx.x / S;
+  const int tid = int(blockIdx.x - row * S) * NT + int(threadIdx.x);
+  const int64_t G = int64_t(S) * NT;
   const float w = weights ? weights[row] : 1.0f;
   const RowStats st = stats[row];
   const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
@@ -806,7 +977,7 @@ __global__ __launch_bounds__(NT) void l1_grad_kernel(const void* __restrict__ tg
   const int64_t nvec = vec_ok ? V / VEC : 0;
   if (w == 0.0f || !(st.mx == st.mx)) {  // masked row: zeros; a bad row: NaN
     const float v = w == 0.0f ? 0.0f : __builtin_nanf("");
-    for (int64_t i = tid; i < V; i += NT) store_one<GDT>(grad, g0 + i, v);
+    for (int64_t i = tid; i < V; i += G) store_one<GDT>(grad, g0 + i, v);
     return;
   }
   const float scale = grad_scale * (w / loss_out[1]);
@@ -822,28 +993,28 @@ __global__ __launch_bounds__(NT) void l1_grad_kernel(const void* __restrict__ tg
     };
     int64_t q = tid;
     constexpr int U = 4;
-    for (; q + int64_t(U - 1) * NT < nvec; q += int64_t(U) * NT) {
+    for (; q + int64_t(U - 1) * G < nvec; q += int64_t(U) * G) {
       float a[U][VEC], b[U][VEC];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        load_chunk<DT>(trow, q + u * NT, a[u]);
-        load_chunk<DT>(drow, q + u * NT, b[u]);
+        load_chunk<DT>(trow, q + u * G, a[u]);
+        load_chunk<DT>(drow, q + u * G, b[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float g[VEC];
         grads(a[u], b[u], VEC, g);
-        store_run<GDT>(grad, g0 + (q + u * NT) * VEC, g, VEC);
+        store_run<GDT>(grad, g0 + (q + u * G) * VEC, g, VEC);
       }
     }
-    for (; q < nvec; q += NT) {
+    for (; q < nvec; q += G) {
       float a[VEC], b[VEC], g[VEC];
       load_chunk<DT>(trow, q, a);
       load_chunk<DT>(drow, q, b);
       grads(a, b, VEC, g);
       store_run<GDT>(grad, g0 + q * VEC, g, VEC);
     }
-    for (int64_t i = nvec * VEC + tid; i < V; i += NT) {
+    for (int64_t i = nvec * VEC + tid; i < V; i += G) {
       const float a = load_one<DT>(trow, i), b = load_one<DT>(drow, i);
       float g;
       grads(&a, &b, 1, &g);
@@ -890,39 +1061,76 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
   return int(hipGetLastError());
 }
 
-size_t l1_loss_workspace_bytes(int64_t rows) { return size_t(rows) * sizeof(RowStats) + 256 + 16; }
+// Rows split over at most kLossMaxSlices workgroups each when there are fewer
+// than 4 workgroups' worth of rows per CU (so that a small batch still fills
+// the chip); the stats then come from the part1 / part2 partials.
+constexpr int kLossMaxSlices = 16;
+
+int loss_slices(int64_t rows, int ncu) {
+  const int64_t want = 4 * int64_t(ncu);
+  if (rows >= want) return 1;
+  const int64_t s = (want + rows - 1) / rows;
+  return int(s < kLossMaxSlices ? s : kLossMaxSlices);
+}
+
+size_t l1_loss_workspace_bytes(int64_t rows) {
+  return size_t(rows) * sizeof(RowStats) + 256 + 16 + size_t(rows) * kLossMaxSlices * (sizeof(float4) + sizeof(float2));
+}
 
 int launch_l1_loss(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, const float* weights,
                    float grad_scale, float* l1, float* accept, float* loss_out, void* grad, int grad_dtype,
                    int64_t ld_grad, void* workspace, void* stream) {
   if (rows <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int ncu = 0;
+  if (const int e = device_cu_count(&ncu)) return e;
+  const int S = loss_slices(rows, ncu);
   RowStats* stats = static_cast<RowStats*>(workspace);
-  if (target.dtype == VS_BF16)
-    l1_stats_kernel<VS_BF16, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
-        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
-  else
-    l1_stats_kernel<VS_F32, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
-        target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
-  l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, weights, rows, loss_out);
+  // partials after the stats and the 256 + 16 bytes kept for alignment (16-byte aligned)
+  const uintptr_t pbase = (reinterpret_cast<uintptr_t>(stats + rows) + 255) & ~uintptr_t(255);
+  float4* part1 = reinterpret_cast<float4*>(pbase);
+  float2* part2 = reinterpret_cast<float2*>(part1 + rows * S);
+  if (S == 1) {
+    if (target.dtype == VS_BF16)
+      l1_stats_kernel<VS_BF16, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
+          target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
+    else
+      l1_stats_kernel<VS_F32, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
+          target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
+    l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, nullptr, 1, stats);
+  } else {
+    const dim3 g{unsigned(rows * S)}, b{unsigned(kLossThreads)};
+    if (target.dtype == VS_BF16) {
+      l1_part1_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
+                                                                          V, S, part1);
+      l1_part2_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
+                                                                          V, S, part1, part2, stats);
+    } else {
+      l1_part1_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
+                                                                         V, S, part1);
+      l1_part2_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
+                                                                         V, S, part1, part2, stats);
+    }
+    l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, part2, S, stats);
+  }
   if (grad) {
-    const dim3 g{unsigned(rows)}, b{unsigned(kLossThreads)};
+    const dim3 g{unsigned(rows * S)}, b{unsigned(kLossThreads)};
     if (target.dtype == VS_BF16 && grad_dtype == VS_BF16)
       l1_grad_kernel<VS_BF16, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                      weights, grad_scale, stats, loss_out, grad,
-                                                                     ld_grad);
+                                                                     ld_grad, S);
     else if (target.dtype == VS_BF16)
       l1_grad_kernel<VS_BF16, VS_F32, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                     weights, grad_scale, stats, loss_out, grad,
-                                                                    ld_grad);
+                                                                    ld_grad, S);
     else if (grad_dtype == VS_BF16)
       l1_grad_kernel<VS_F32, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                     weights, grad_scale, stats, loss_out, grad,
-                                                                    ld_grad);
+                                                                    ld_grad, S);
     else
       l1_grad_kernel<VS_F32, VS_F32, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                    weights, grad_scale, stats, loss_out, grad,
-                                                                   ld_grad);
+                                                                   ld_grad, S);
   }
   return int(hipGetLastError());
 }

@@ -151,3 +151,25 @@ def test_full_size_workload(vsa):
     sub = oracle.weighted_l1_loss(oracle.logits_from_logits(c["logits"], "bf16", rows=rows),
                                   oracle.logits_from_logits(c["draft"], "bf16", rows=rows), w[rows])
     _grad_close("grad rows", gr, sub["grad"] * (float(np.sum(w[rows].astype(np.float64))) / den), bf16=True)
+
+
+@pytest.mark.parametrize("T", [1, 300, 1023])
+def test_rows_split_over_workgroups(vsa, T):
+    # batches with fewer than four rows per CU split each row over several
+    # workgroups (partials merged in a fixed order): every row, the loss and
+    # the gradient against the oracle, a bad row of nonzero weight included
+    say(f"l1 loss: T={T} V=6000 (rows split over workgroups), a NaN row of weight 1")
+    rng = np.random.default_rng(T)
+    V = 6000
+    a = (rng.standard_normal((T, V)) * 3).astype(np.float32)
+    b = (a + rng.standard_normal((T, V)) * rng.uniform(0.1, 2.0, (T, 1))).astype(np.float32)
+    w = rng.uniform(0.0, 2.0, T).astype(np.float32)
+    if T > 1:
+        b[T // 2, 11] = np.nan
+        w[T // 2] = 1.0
+        w[T // 3] = 0.0
+    got = _case(vsa, a, b, w, 2.0, torch.float32, f"T={T}")
+    again = vsa.l1_loss(bf16_tensor(workloads.to_bf16_bits(a)), bf16_tensor(workloads.to_bf16_bits(b)),
+                        weights=to_dev(w), grad_scale=2.0, grad_dtype=torch.float32)
+    for k in ("l1", "accept_rate", "loss", "grad"):
+        assert torch.equal(got[k].nan_to_num(7.0), again[k].nan_to_num(7.0)), k
