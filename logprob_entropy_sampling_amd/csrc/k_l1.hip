@@ -557,11 +557,14 @@ constexpr int kL1Unroll = 8;
 // accept_rate and the weighted L1 loss num / den, num = sum_t w_t L1_t,
 // den = sum_t w_t; the loss's gradient goes to the draft logits):
 //   d L1_t / d b_v = q_v (s_v - S_t),  s_v = sign(q_v - p_v),  S_t = sum_u s_u q_u.
-// l1_stats_kernel: one workgroup per row, two passes (the L1 kernel's), the
-//   second also sums S_t; writes l1, accept and the row's normalisers and S_t.
-// l1_loss_kernel: one workgroup, num and den in a fixed order.
-// l1_grad_kernel: one workgroup per row, one pass: recomputes p_v, q_v and
-//   their sign with the same instructions as the stats pass, and writes
+// Every row is split over S workgroups (slices; S = 2 .. 8, more when the
+// batch has few rows per CU, so that small batches still fill the chip).
+// l1_part1_kernel, l1_part2_kernel: the L1 kernel's two passes, the second
+//   also summing S_t, each into per-slice partials.
+// l1_loss_kernel: one workgroup: adds each row's partials in slice order
+//   (l1, accept, S_t), then num and den in a fixed order.
+// l1_grad_kernel: one pass over each slice: recomputes p_v, q_v and their
+//   sign with the same instructions as the stats pass, and writes
 //   grad_scale (w_t / den) q_v (s_v - S_t).
 // A row of weight 0 adds nothing to num and gets a zero gradient (a loss
 // mask), even if its distance is NaN.
@@ -617,114 +620,8 @@ __device__ __forceinline__ void row_pairs(const char* trow, const char* drow, in
   }
 }
 
-template <int DT, int NT, int U>
-__global__ __launch_bounds__(NT) void l1_stats_kernel(const void* __restrict__ tgt, int64_t ld_t,
-                                                      const void* __restrict__ dft, int64_t ld_d, int64_t V,
-                                                      float* __restrict__ l1, float* __restrict__ accept,
-                                                      RowStats* __restrict__ stats) {
-  constexpr int VEC = DT == VS_BF16 ? 8 : 4;
-  constexpr int ES = DT == VS_BF16 ? 2 : 4;
-  constexpr int NW = NT / 64;
-  constexpr float l2e = DT == VS_BF16 ? kLog2eBf16 : kLog2e;
-  __shared__ float red[NW][4];
-  __shared__ float fin[4];
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const char* trow = static_cast<const char*>(tgt) + row * ld_t * ES;
-  const char* drow = static_cast<const char*>(dft) + row * ld_d * ES;
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
-  const int64_t nvec = vec_ok ? V / VEC : 0;
-
-  // ---- pass 1: online max / sum-exp of both rows ----
-  float mx = kNegInf, sx = 0.0f, my = kNegInf, sy = 0.0f;
-  row_pairs<DT, NT, U>(trow, drow, nvec, V, [&](const float* a, const float* b, int n) {
-    online(mx, sx, a, n, l2e);
-    online(my, sy, b, n, l2e);
-  });
-  Part px = wave_merge_to_lane0(Part{mx * l2e, sx, 0.0f});
-  Part py = wave_merge_to_lane0(Part{my * l2e, sy, 0.0f});
-  if ((tid & 63) == 0) {
-    red[tid >> 6][0] = px.m;
-    red[tid >> 6][1] = px.s;
-    red[tid >> 6][2] = py.m;
-    red[tid >> 6][3] = py.s;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    Part qx{kNegInf, 0.0f, 0.0f}, qy{kNegInf, 0.0f, 0.0f};
-    if (tid < NW) {
-      qx = Part{red[tid][0], red[tid][1], 0.0f};
-      qy = Part{red[tid][2], red[tid][3], 0.0f};
-    }
-    qx = wave_merge_to_lane0(qx);
-    qy = wave_merge_to_lane0(qy);
-    if (tid == 0) {
-      fin[0] = qx.m;
-      fin[1] = qx.s;
-      fin[2] = qy.m;
-      fin[3] = qy.s;
-    }
-  }
-  __syncthreads();
-  const Norm nx = make_norm(fin[0], fin[1]), ny = make_norm(fin[2], fin[3]);
-  if (!(norm_ok(nx) && norm_ok(ny))) {
-    if (tid == 0) {
-      const float nan = __builtin_nanf("");
-      l1[row] = nan;
-      if (accept) accept[row] = nan;
-      stats[row] = RowStats{nan, nan, nan, nan, nan};
-    }
-    return;
-  }
-
-  // ---- pass 2: sum |p - q| and sum sign(q - p) q ----
-  float d1 = 0.0f, ds = 0.0f;
-  auto pass2 = [&](auto acc_form) {
-    constexpr bool ACC = decltype(acc_form)::value;
-    row_pairs<DT, NT, U>(trow, drow, nvec, V, [&](const float* a, const float* b, int n) {
-      for (int i = 0; i < n; ++i) {
-        float pp, qq;
-        pq_pair<ACC>(a[i], b[i], nx, ny, l2e, pp, qq);
-        d1 += fabsf(pp - qq);
-        ds = __builtin_fmaf(sgn(qq - pp), qq, ds);
-      }
-    });
-  };
-  if (norms_big(nx, ny))
-    pass2(std::true_type{});
-  else
-    pass2(std::false_type{});
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o1 = shfl_down_f(d1, off), o2 = shfl_down_f(ds, off);
-    if ((tid & ((off << 1) - 1)) == 0) {
-      d1 += o1;
-      ds += o2;
-    }
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) {
-    red[tid >> 6][0] = d1;
-    red[tid >> 6][1] = ds;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float v = 0.0f, S = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      v += red[w][0];
-      S += red[w][1];
-    }
-    const float d = fminf(fmaxf(v, 0.0f), 2.0f);
-    l1[row] = d;
-    if (accept) accept[row] = fminf(fmaxf(1.0f - 0.5f * d, 0.0f), 1.0f);
-    stats[row] = RowStats{nx.m, nx.l2s, ny.m, ny.l2s, S};
-  }
-}
-
-// The stats pass with each row split over S workgroups (slices), for batches
-// with few rows per CU.  Slice s of row t is thread g = s * NT + threadIdx.x
-// of S * NT.  l1_part1_kernel: each slice's online maxima and sums of both
+// The stats passes with each row split over S workgroups (slices).  Slice s
+// of row t is thread g = s * NT + threadIdx.x of S * NT.  l1_part1_kernel: each slice's online maxima and sums of both
 // rows (merged in its workgroup as in the one-workgroup form) into
 // part1[t * S + s].  l1_part2_kernel: every slice merges the row's S partials
 // in slice order (all get the same normalisers), runs pass 2 over its share
@@ -869,9 +766,8 @@ __global__ __launch_bounds__(NT) void l1_part2_kernel(const void* __restrict__ t
 
 // num = sum_t w_t l1_t over rows of nonzero weight, den = sum_t w_t: thread i
 // takes rows i, i + 256, ... in order, then a fixed tree.  out = {num, den, num / den}.
-// With part2 (rows split over S slices): row t's distance and sum s q are
-// first added up from its S partials in slice order, and l1, accept and the
-// row's S_t written.
+// Row t's distance and sum s q are first added up from its S partials in
+// slice order, and l1, accept and the row's S_t written.
 __global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(float* __restrict__ l1, float* __restrict__ accept,
                                                                const float* __restrict__ weights, int64_t rows,
                                                                float* __restrict__ out, const float2* __restrict__ part2,
@@ -880,23 +776,18 @@ __global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(float* __restrict
   const int tid = threadIdx.x;
   float n = 0.0f, d = 0.0f;
   for (int64_t t = tid; t < rows; t += kLossThreads) {
-    float lt;
-    if (part2) {
-      const bool ok = stats[t].mx == stats[t].mx;
-      float v = 0.0f, Sv = 0.0f;
-      for (int k = 0; k < S; ++k) {
-        const float2 p = part2[t * S + k];
-        v += p.x;
-        Sv += p.y;
-      }
-      const float nan = __builtin_nanf("");
-      lt = ok ? fminf(fmaxf(v, 0.0f), 2.0f) : nan;
-      l1[t] = lt;
-      if (accept) accept[t] = ok ? fminf(fmaxf(1.0f - 0.5f * lt, 0.0f), 1.0f) : nan;
-      if (ok) stats[t].S = Sv;
-    } else {
-      lt = l1[t];
+    const bool ok = stats[t].mx == stats[t].mx;
+    float v = 0.0f, Sv = 0.0f;
+    for (int k = 0; k < S; ++k) {
+      const float2 p = part2[t * S + k];
+      v += p.x;
+      Sv += p.y;
     }
+    const float nan = __builtin_nanf("");
+    const float lt = ok ? fminf(fmaxf(v, 0.0f), 2.0f) : nan;
+    l1[t] = lt;
+    if (accept) accept[t] = ok ? fminf(fmaxf(1.0f - 0.5f * lt, 0.0f), 1.0f) : nan;
+    if (ok) stats[t].S = Sv;
     const float w = weights ? weights[t] : 1.0f;
     if (w != 0.0f) n = __builtin_fmaf(w, lt, n);
     d += w;
@@ -1061,16 +952,13 @@ int launch_l1(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, float*
   return int(hipGetLastError());
 }
 
-// Rows split over at most kLossMaxSlices workgroups each when there are fewer
-// than 4 workgroups' worth of rows per CU (so that a small batch still fills
-// the chip); the stats then come from the part1 / part2 partials.
-constexpr int kLossMaxSlices = 16;
+// Slices per row: enough for about 4 workgroups per CU, at least 2 (measured
+// faster than one workgroup per row even on large batches) and at most 8.
+constexpr int kLossMaxSlices = 8;
 
 int loss_slices(int64_t rows, int ncu) {
-  const int64_t want = 4 * int64_t(ncu);
-  if (rows >= want) return 1;
-  const int64_t s = (want + rows - 1) / rows;
-  return int(s < kLossMaxSlices ? s : kLossMaxSlices);
+  const int64_t s = (4 * int64_t(ncu) + rows - 1) / rows;
+  return int(s < 2 ? 2 : s > kLossMaxSlices ? kLossMaxSlices : s);
 }
 
 size_t l1_loss_workspace_bytes(int64_t rows) {
@@ -1090,31 +978,20 @@ int launch_l1_loss(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, c
   const uintptr_t pbase = (reinterpret_cast<uintptr_t>(stats + rows) + 255) & ~uintptr_t(255);
   float4* part1 = reinterpret_cast<float4*>(pbase);
   float2* part2 = reinterpret_cast<float2*>(part1 + rows * S);
-  if (S == 1) {
-    if (target.dtype == VS_BF16)
-      l1_stats_kernel<VS_BF16, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
-          target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
-    else
-      l1_stats_kernel<VS_F32, kLossThreads, kLossUnroll><<<dim3(unsigned(rows)), dim3(kLossThreads), 0, s>>>(
-          target.ptr, target.ld, draft.ptr, draft.ld, V, l1, accept, stats);
-    l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, nullptr, 1, stats);
+  const dim3 g{unsigned(rows * S)}, b{unsigned(kLossThreads)};
+  if (target.dtype == VS_BF16) {
+    l1_part1_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                        S, part1);
+    l1_part2_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                        S, part1, part2, stats);
   } else {
-    const dim3 g{unsigned(rows * S)}, b{unsigned(kLossThreads)};
-    if (target.dtype == VS_BF16) {
-      l1_part1_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
-                                                                          V, S, part1);
-      l1_part2_kernel<VS_BF16, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
-                                                                          V, S, part1, part2, stats);
-    } else {
-      l1_part1_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
-                                                                         V, S, part1);
-      l1_part2_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld,
-                                                                         V, S, part1, part2, stats);
-    }
-    l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, part2, S, stats);
+    l1_part1_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                       S, part1);
+    l1_part2_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
+                                                                       S, part1, part2, stats);
   }
+  l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, part2, S, stats);
   if (grad) {
-    const dim3 g{unsigned(rows * S)}, b{unsigned(kLossThreads)};
     if (target.dtype == VS_BF16 && grad_dtype == VS_BF16)
       l1_grad_kernel<VS_BF16, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                      weights, grad_scale, stats, loss_out, grad,

@@ -155,10 +155,10 @@ def test_full_size_workload(vsa):
 
 @pytest.mark.parametrize("T", [1, 300, 1023])
 def test_rows_split_over_workgroups(vsa, T):
-    # batches with fewer than four rows per CU split each row over several
-    # workgroups (partials merged in a fixed order): every row, the loss and
-    # the gradient against the oracle, a bad row of nonzero weight included
-    say(f"l1 loss: T={T} V=6000 (rows split over workgroups), a NaN row of weight 1")
+    # every row is split over 2..8 workgroups, more on small batches
+    # (partials merged in a fixed order): every row, the loss and the
+    # gradient against the oracle, a bad row of nonzero weight included
+    say(f"l1 loss: T={T} V=6000 (8, 4 and 2 workgroups per row), a NaN row of weight 1")
     rng = np.random.default_rng(T)
     V = 6000
     a = (rng.standard_normal((T, V)) * 3).astype(np.float32)
