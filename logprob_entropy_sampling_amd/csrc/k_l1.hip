@@ -815,6 +815,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return (v != v) ? ((u >> 16) | 0x40u) : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Two fp32 values as packed bf16, a in the low half: the hardware's round to
+// nearest even (v_cvt_pk_bf16_f32), the same result as bf16_rne off NaN.
+typedef __bf16 l1_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float l1_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_hw(float a, float b) {
+  const l1_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, l1_bf16x2));
+}
+
 template <int GDT>
 __device__ __forceinline__ void store_one(void* g, int64_t i, float v) {
   if (GDT == VS_BF16)
@@ -829,10 +838,10 @@ template <int GDT>
 __device__ __forceinline__ void store_run(void* g, int64_t i, const float* v, int n) {
   if (n == 8 && GDT == VS_BF16) {
     uint4 w;
-    w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-    w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-    w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-    w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+    w.x = pack_bf16_hw(v[0], v[1]);
+    w.y = pack_bf16_hw(v[2], v[3]);
+    w.z = pack_bf16_hw(v[4], v[5]);
+    w.w = pack_bf16_hw(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g) + i) = w;
   } else if (n % 4 == 0 && GDT == VS_F32) {
     for (int k = 0; k < n; k += 4)
