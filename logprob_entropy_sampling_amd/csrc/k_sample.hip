@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     const uint16_t* __restrict__ logits, int64_t ld, int V, const float* __restrict__ temp, float temp_scalar,
     const uint8_t* __restrict__ status, const float* __restrict__ threshold_logit,
     const int32_t* __restrict__ threshold_ties, const float* __restrict__ row_max, uint64_t seed, uint64_t offset,
-    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status, int64_t row0, const int32_t* __restrict__ order) {
+    int64_t* __restrict__ sampled, uint8_t* __restrict__ out_status, int64_t row0, const int32_t* __restrict__ order,
+    const int64_t* __restrict__ ids, int cap, const int32_t* __restrict__ support_len) {
   __shared__ SampleSmem sm;
   // local row (taken in the order `order` gives, when given); row0 + row is
   // the generator's row word, so the order changes no draw
@@ -258,15 +259,35 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   d.k1 = uint32_t(seed >> 32);
   d.off_lo = uint32_t(offset);
   d.off_hi = uint32_t(offset >> 32);
-  const float thr = threshold_logit[row];
-  const uint32_t ties = uint32_t(threshold_ties[row]);
   const uint16_t* rowp = logits + row * ld;
-  const bool vec = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
-  const int64_t nchunk = (int64_t(V) + 7) / 8;
-  const bool lds_ranks = nchunk <= kLdsChunks;
   const auto block_ctr = [&](int64_t q, int b) {
     return philox4x32_10(Ctr{uint32_t(2 * q + b), uint32_t(d.row), d.off_lo, d.off_hi}, d.k0, d.k1);
   };
+  // A support of at most cap (<= 64) tokens whose dense ids the transforms
+  // wrote: one lane per id scores it in fp64 (the decision itself), no row pass.
+  if (ids) {
+    const int32_t L = support_len[row];
+    if (L >= 1 && L <= cap) {
+      if (tid >= 64) return;
+      Best b{-__builtin_inf(), int64_t(V)};
+      if (tid < L) {
+        const int64_t id = ids[row * cap + tid];
+        const float x = bf16_to_f32(rowp[id]);
+        if (x != -__builtin_inff()) {
+          const Ctr r = block_ctr(id >> 3, int((id >> 2) & 1));
+          b = Best{gumbel_score(x, ctr_word(r, int(id & 3)), d), id};
+        }
+      }
+      b = wave_best(b);
+      if (tid == 0) sampled[row] = b.id;
+      return;
+    }
+  }
+  const float thr = threshold_logit[row];
+  const uint32_t ties = uint32_t(threshold_ties[row]);
+  const bool vec = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
+  const int64_t nchunk = (int64_t(V) + 7) / 8;
+  const bool lds_ranks = nchunk <= kLdsChunks;
 
   // Every token above the threshold (f_gt) and every token equal to it
   // (f_eq, with its count written to LDS when lds_ranks): one pass over the row.
@@ -529,11 +550,13 @@ int launch_order_rows(const int32_t* support_len, const uint8_t* status, int64_t
 int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                   const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
                   const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
-                  int64_t row0, const int32_t* order, void* stream) {
+                  int64_t row0, const int32_t* order, const int64_t* ids, int64_t cap, const int32_t* support_len,
+                  void* stream) {
   if (rows <= 0) return 0;
+  if (ids && (cap < 1 || cap > 64 || !support_len)) return int(hipErrorInvalidValue);
   sample_kernel<<<dim3(unsigned(rows)), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream)>>>(
       logits, ld, int(V), temp, temp_scalar, status, threshold_logit, threshold_ties, row_max, seed, offset, sampled,
-      out_status, row0, order);
+      out_status, row0, order, ids, int(cap), support_len);
   return int(hipGetLastError());
 }
 

@@ -134,10 +134,13 @@ int launch_transforms(const uint16_t* logits, int64_t ld, int64_t rows, int64_t 
 // out_status (nullable) gets the BAD_INPUT bit.  Local row r draws with the
 // generator's row word row0 + r.  order (nullable): the local rows in the
 // order the workgroups take them (launch_order_rows), which changes no draw.
+// ids (nullable): the transforms' dense support ids [rows][cap], cap <= 64,
+// with support_len: a row whose whole support is listed is drawn from the list.
 int launch_sample(const uint16_t* logits, int64_t ld, int64_t rows, int64_t V, const float* temp, float temp_scalar,
                   const uint8_t* status, const float* threshold_logit, const int32_t* threshold_ties,
                   const float* row_max, uint64_t seed, uint64_t offset, int64_t* sampled, uint8_t* out_status,
-                  int64_t row0, const int32_t* order, void* stream);
+                  int64_t row0, const int32_t* order, const int64_t* ids, int64_t cap, const int32_t* support_len,
+                  void* stream);
 // A permutation of rows [0, rows) into order[rows], the largest supports first
 // (support_len and status from launch_transforms): the sampler's row order.
 int launch_order_rows(const int32_t* support_len, const uint8_t* status, int64_t rows, int32_t* order, void* stream);

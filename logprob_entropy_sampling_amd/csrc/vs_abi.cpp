@@ -113,11 +113,12 @@ size_t xf_ws_bytes(const vs_source* s) {
 }
 
 // the sampler: logprob, status, row maxima, threshold logit, ties and support
-// lengths (when the caller passes none), the rows' draw order, then the
-// transforms' own workspace
+// lengths (when the caller passes none), the rows' draw order, the dense ids
+// of supports of up to kSampleIdsCap tokens, then the transforms' own workspace
+constexpr int64_t kSampleIdsCap = 64;
 size_t sample_ws_bytes(const vs_source* s) {
   const size_t T = size_t(s->T);
-  return round_up(T * 4) + round_up(T) + 5 * round_up(T * 4) + xf_ws_bytes(s);
+  return round_up(T * 4) + round_up(T) + 5 * round_up(T * 4) + round_up(T * kSampleIdsCap * 8) + xf_ws_bytes(s);
 }
 
 template <class P>
@@ -381,17 +382,20 @@ int vs_sample_transforms(const vs_source* src, const int32_t* top_k, const float
   int32_t* ties = threshold_ties ? threshold_ties : static_cast<int32_t*>(c.take(size_t(T) * 4));
   int32_t* slen = support_len ? support_len : static_cast<int32_t*>(c.take(size_t(T) * 4));
   int32_t* order = static_cast<int32_t*>(c.take(size_t(T) * 4));
+  int64_t* ids = static_cast<int64_t*>(c.take(size_t(T) * kSampleIdsCap * 8));
   const float* temp = src->temperature;
   // rows [r0, r0 + n): the support descriptor, then the draw from it
   auto run = [&](const uint16_t* lg, int64_t ld, int64_t r0, int64_t n, uint8_t* tws) -> int {
     int r = vs::launch_transforms(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, top_k + r0,
                                   top_p + r0, min_p + r0, nullptr, lp + r0, nullptr, st + r0, slen + r0,
-                                  thr + r0, ties + r0, nullptr, 0, nullptr, row_max + r0, tws, stream);
+                                  thr + r0, ties + r0, ids + r0 * kSampleIdsCap, kSampleIdsCap, nullptr,
+                                  row_max + r0, tws, stream);
     if (r) return r == -1 ? VS_E_UNSUPPORTED : VS_E_DEVICE;
     // the block's rows, the largest supports first (the draws do not depend on it)
     if (vs::launch_order_rows(slen + r0, st + r0, n, order, stream)) return VS_E_DEVICE;
     r = vs::launch_sample(lg, ld, n, src->V, at_row(temp, r0), src->temperature_scalar, st + r0, thr + r0, ties + r0,
-                          row_max + r0, seed, offset, sampled_ids + r0, at_row(row_status, r0), r0, order, stream);
+                          row_max + r0, seed, offset, sampled_ids + r0, at_row(row_status, r0), r0, order,
+                          ids + r0 * kSampleIdsCap, kSampleIdsCap, slen + r0, stream);
     return r ? VS_E_DEVICE : VS_OK;
   };
   vs::timer_mark(0, stream);
