@@ -561,7 +561,7 @@ constexpr int kL1Unroll = 8;
 // batch has few rows per CU, so that small batches still fill the chip).
 // l1_part1_kernel, l1_part2_kernel: the L1 kernel's two passes, the second
 //   also summing S_t, each into per-slice partials.
-// l1_loss_kernel: one workgroup: adds each row's partials in slice order
+// l1_loss_kernel: one 1024-thread workgroup: adds each row's partials in slice order
 //   (l1, accept, S_t), then num and den in a fixed order.
 // l1_grad_kernel: one pass over each slice: recomputes p_v, q_v and their
 //   sign with the same instructions as the stats pass, and writes
@@ -768,14 +768,15 @@ __global__ __launch_bounds__(NT) void l1_part2_kernel(const void* __restrict__ t
 // takes rows i, i + 256, ... in order, then a fixed tree.  out = {num, den, num / den}.
 // Row t's distance and sum s q are first added up from its S partials in
 // slice order, and l1, accept and the row's S_t written.
-__global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(float* __restrict__ l1, float* __restrict__ accept,
+constexpr int kLossFinThreads = 1024;
+__global__ __launch_bounds__(kLossFinThreads) void l1_loss_kernel(float* __restrict__ l1, float* __restrict__ accept,
                                                                const float* __restrict__ weights, int64_t rows,
                                                                float* __restrict__ out, const float2* __restrict__ part2,
                                                                int S, RowStats* __restrict__ stats) {
-  __shared__ float sn[kLossThreads], sd[kLossThreads];
+  __shared__ float sn[kLossFinThreads], sd[kLossFinThreads];
   const int tid = threadIdx.x;
   float n = 0.0f, d = 0.0f;
-  for (int64_t t = tid; t < rows; t += kLossThreads) {
+  for (int64_t t = tid; t < rows; t += kLossFinThreads) {
     const bool ok = stats[t].mx == stats[t].mx;
     float v = 0.0f, Sv = 0.0f;
     for (int k = 0; k < S; ++k) {
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(kLossThreads) void l1_loss_kernel(float* __restrict
   sn[tid] = n;
   sd[tid] = d;
   __syncthreads();
-  for (int h = kLossThreads / 2; h > 0; h >>= 1) {
+  for (int h = kLossFinThreads / 2; h > 0; h >>= 1) {
     if (tid < h) {
       sn[tid] += sn[tid + h];
       sd[tid] += sd[tid + h];
@@ -999,7 +1000,7 @@ int launch_l1_loss(LogitsArg target, LogitsArg draft, int64_t rows, int64_t V, c
     l1_part2_kernel<VS_F32, kLossThreads, kLossUnroll><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
                                                                        S, part1, part2, stats);
   }
-  l1_loss_kernel<<<dim3(1), dim3(kLossThreads), 0, s>>>(l1, accept, weights, rows, loss_out, part2, S, stats);
+  l1_loss_kernel<<<dim3(1), dim3(kLossFinThreads), 0, s>>>(l1, accept, weights, rows, loss_out, part2, S, stats);
   if (grad) {
     if (target.dtype == VS_BF16 && grad_dtype == VS_BF16)
       l1_grad_kernel<VS_BF16, VS_BF16, kLossThreads><<<g, b, 0, s>>>(target.ptr, target.ld, draft.ptr, draft.ld, V,
