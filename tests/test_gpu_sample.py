@@ -162,3 +162,29 @@ def test_row_order_mixed_supports_and_bad_rows(vsa):
     sl = got["support_len"].cpu().numpy()
     assert sl[kind == 4][~np.isnan(tau[kind == 4])].min() == V and sl[kind == 0][~np.isnan(tau[kind == 0])].max() == 1
     say(f"  {T - diff.size} of {T} draws identical, {diff.size} within {NEAR} of a tie")
+
+
+@pytest.mark.parametrize("V", [5000, 90000])
+def test_supports_around_the_listed_id_capacity(vsa, V):
+    # supports of 1..66 tokens, cut by top-k or min-p inside tie groups of
+    # small-integer logits: those of up to 64 tokens are drawn from their
+    # listed dense ids, larger ones from the row pass; every draw is the
+    # oracle's (the same support, ties taken by ascending id)
+    say(f"sample: V={V}, supports of 1 to 66 tokens around the 64 listed ids, cuts inside tie groups")
+    rng = np.random.default_rng(V + 64)
+    T = 48
+    vals = rng.integers(-6, 2, size=(T, V)).astype(np.float32) * np.float32(0.75)
+    vals[::5, ::7] = -np.inf
+    vals[:, rng.choice(V, 40, replace=False)] = 4.0  # a tie group of 40 at the top of every row
+    bits = workloads.to_bf16_bits(vals)
+    k = np.array([1, 2, 39, 40, 41, 63, 64, 65, 66, 0, 0, 0] * 4, np.int32)
+    p = np.ones(T, np.float32)
+    mp = np.where(k == 0, 0.5, 0.0).astype(np.float32)  # min-p alone: the 40 tied maxima
+    tau = rng.choice([0.5, 1.0], T).astype(np.float32)
+    x64 = oracle.logits_from_logits(bits, "bf16")
+    for seed in (3, 4):
+        got = _draw(vsa, bits, tau, k, p, mp, seed=seed)
+        ref = sampling.sample_transforms(x64, tau, k, p, mp, seed=seed)
+        _check(got, ref, x64, tau, seed, 0, np.arange(T), f"V={V} seed {seed}")
+    sl = got["support_len"].cpu().numpy()
+    assert np.array_equal(sl[k > 0], k[k > 0]) and (sl[k == 0] == 40).all()
